@@ -1,0 +1,184 @@
+"""fp64 CPU oracle for the selective scan (ctypes front end of ``sss_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()`` and
+``bench.py``'s cpu_baseline leg, never by the product package.  It shares no code with
+the HIP path; both sides receive the same seeded inputs from
+``selective_state_space_20_amd.inputs``.
+
+Arrays: x / delta / z are float32, or uint16 holding raw bf16 bits (io dtype "bf16");
+everything else float32.  Results are float64.
+
+What each function computes (pages cited by title and section):
+  * ``selective_scan`` -- "Selective Scan trong Mamba ..." (thecsnote.cc), sections on the
+    discrete recurrence h_t = Abar_t h_{t-1} + Bbar_t x_t, y_t = C_t h_t with
+    input-dependent Delta, B, C; Abar = exp(Delta*A); Bbar = Delta*B (or the page's
+    exact zero-order hold, ``exact_zoh=True``); plus D*x and the silu(z) gate.
+  * ``elementwise_scan`` -- "15. Selective (Data-Dependent) SSM Scan", reference solution.
+  * ``*_chunked`` -- the same results by pairs (a, b) composed with
+    (a2,b2)(x)(a1,b1) = (a2 a1, a2 b1 + b2), identity (1, 0): section "Scan bien
+    recurrence thanh phep toan co the song song hoa ra sao?".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sss_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+F32, BF16 = 0, 1
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (plain C, OpenMP, no fast-math, no contraction)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+               "-fno-fast-math", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB_PATH)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        lib.oracle_selective_scan.argtypes = [vp] * 10 + [i64] * 4 + [i32] * 3
+        lib.oracle_selective_scan_channels.argtypes = [vp] * 8 + [vp, i64, vp, vp] + [i64] * 4 + [i32] * 3
+        lib.oracle_selective_scan_chunked.argtypes = [vp] * 10 + [i64] * 4 + [i32] * 2 + [i64, i32]
+        lib.oracle_elementwise_scan.argtypes = [vp] * 7 + [i64] * 3 + [i32]
+        lib.oracle_elementwise_scan_channels.argtypes = [vp] * 5 + [vp, i64, vp, vp] + [i64] * 3 + [i32]
+        lib.oracle_elementwise_scan_chunked.argtypes = [vp] * 7 + [i64] * 4 + [i32]
+        for f in ("oracle_selective_scan", "oracle_selective_scan_channels", "oracle_selective_scan_chunked",
+                  "oracle_elementwise_scan", "oracle_elementwise_scan_channels",
+                  "oracle_elementwise_scan_chunked", "oracle_max_threads"):
+            getattr(lib, f).restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _io(a):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float32:
+        return a
+    if a.dtype == np.uint16:
+        return a
+    raise TypeError(f"x/delta/z must be float32 or uint16 (bf16 bits), got {a.dtype}")
+
+
+def _io_code(a):
+    return BF16 if a.dtype == np.uint16 else F32
+
+
+def _f32(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.float32)
+
+
+def _check(rc):
+    if rc != 0:
+        raise ValueError(f"oracle rejected its arguments (status {rc})")
+
+
+def selective_scan(x, delta, A, B, C, D=None, z=None, h0=None, *, exact_zoh=False, return_last=True,
+                   nthreads=0):
+    """x, delta, z: (Bt, L, Dm); A: (Dm, N); B, C: (Bt, L, N); D: (Dm,); h0: (Bt, Dm, N).
+
+    Returns (y (Bt, L, Dm) float64, h_last (Bt, Dm, N) float64 or None).
+    """
+    x, delta, z = _io(x), _io(delta), _io(z)
+    if delta.dtype != x.dtype or (z is not None and z.dtype != x.dtype):
+        raise TypeError("x, delta and z must share one dtype")
+    A, B, C, D, h0 = _f32(A), _f32(B), _f32(C), _f32(D), _f32(h0)
+    bt, L, dm = x.shape
+    n = A.shape[1]
+    y = np.empty((bt, L, dm), dtype=np.float64)
+    hl = np.empty((bt, dm, n), dtype=np.float64) if return_last else None
+    rc = _load().oracle_selective_scan(_p(x), _p(delta), _p(A), _p(B), _p(C), _p(D), _p(z), _p(h0), _p(y),
+                                       _p(hl), bt, L, dm, n, _io_code(x), int(bool(exact_zoh)), nthreads)
+    _check(rc)
+    return y, hl
+
+
+def selective_scan_channels(x, delta, A, B, C, D=None, z=None, h0=None, *, channels, exact_zoh=False,
+                            nthreads=0):
+    """Only the channels ``channels`` (flat b*Dm + d).  Returns y (k, L), h_last (k, N)."""
+    x, delta, z = _io(x), _io(delta), _io(z)
+    A, B, C, D, h0 = _f32(A), _f32(B), _f32(C), _f32(D), _f32(h0)
+    bt, L, dm = x.shape
+    n = A.shape[1]
+    ch = np.ascontiguousarray(channels, dtype=np.int64)
+    y = np.empty((ch.size, L), dtype=np.float64)
+    hl = np.empty((ch.size, n), dtype=np.float64)
+    rc = _load().oracle_selective_scan_channels(_p(x), _p(delta), _p(A), _p(B), _p(C), _p(D), _p(z), _p(h0),
+                                                _p(ch), ch.size, _p(y), _p(hl), bt, L, dm, n, _io_code(x),
+                                                int(bool(exact_zoh)), nthreads)
+    _check(rc)
+    return y, hl
+
+
+def selective_scan_chunked(x, delta, A, B, C, D=None, z=None, h0=None, *, chunk, exact_zoh=False,
+                           nthreads=0):
+    x, delta, z = _io(x), _io(delta), _io(z)
+    A, B, C, D, h0 = _f32(A), _f32(B), _f32(C), _f32(D), _f32(h0)
+    bt, L, dm = x.shape
+    n = A.shape[1]
+    y = np.empty((bt, L, dm), dtype=np.float64)
+    hl = np.empty((bt, dm, n), dtype=np.float64)
+    rc = _load().oracle_selective_scan_chunked(_p(x), _p(delta), _p(A), _p(B), _p(C), _p(D), _p(z), _p(h0),
+                                               _p(y), _p(hl), bt, L, dm, n, _io_code(x), int(bool(exact_zoh)),
+                                               int(chunk), nthreads)
+    _check(rc)
+    return y, hl
+
+
+def elementwise_scan(x, A, B, C, h0=None, *, return_last=True, nthreads=0):
+    """x, A, B, C: (Bt, L, Dm) float32; h0: (Bt, Dm).  Returns (y, h_last)."""
+    x, A, B, C, h0 = _f32(x), _f32(A), _f32(B), _f32(C), _f32(h0)
+    bt, L, dm = x.shape
+    y = np.empty((bt, L, dm), dtype=np.float64)
+    hl = np.empty((bt, dm), dtype=np.float64) if return_last else None
+    rc = _load().oracle_elementwise_scan(_p(x), _p(A), _p(B), _p(C), _p(h0), _p(y), _p(hl), bt, L, dm, nthreads)
+    _check(rc)
+    return y, hl
+
+
+def elementwise_scan_channels(x, A, B, C, h0=None, *, channels, nthreads=0):
+    x, A, B, C, h0 = _f32(x), _f32(A), _f32(B), _f32(C), _f32(h0)
+    bt, L, dm = x.shape
+    ch = np.ascontiguousarray(channels, dtype=np.int64)
+    y = np.empty((ch.size, L), dtype=np.float64)
+    hl = np.empty((ch.size,), dtype=np.float64)
+    rc = _load().oracle_elementwise_scan_channels(_p(x), _p(A), _p(B), _p(C), _p(h0), _p(ch), ch.size, _p(y),
+                                                  _p(hl), bt, L, dm, nthreads)
+    _check(rc)
+    return y, hl
+
+
+def elementwise_scan_chunked(x, A, B, C, h0=None, *, chunk, nthreads=0):
+    x, A, B, C, h0 = _f32(x), _f32(A), _f32(B), _f32(C), _f32(h0)
+    bt, L, dm = x.shape
+    y = np.empty((bt, L, dm), dtype=np.float64)
+    hl = np.empty((bt, dm), dtype=np.float64)
+    rc = _load().oracle_elementwise_scan_chunked(_p(x), _p(A), _p(B), _p(C), _p(h0), _p(y), _p(hl), bt, L, dm,
+                                                 int(chunk), nthreads)
+    _check(rc)
+    return y, hl

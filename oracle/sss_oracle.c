@@ -1,0 +1,334 @@
+/*
+ * sss_oracle.c -- plain, slow, fp64 CPU oracle for the selective scan.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or call
+ * this file: only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline
+ * leg use it.  It shares no code, header, table or constant with the HIP path.
+ *
+ * Every floating-point input is read in its stored type (fp32, or the raw 16
+ * bits of a bf16 value, widened exactly to fp32 and then to double) and all
+ * arithmetic is done in double with libm's exp/expm1.  Channels (b, d) are
+ * independent, so the only parallelism is an OpenMP loop over channels; the
+ * arithmetic inside a channel is exactly the stepwise definition.
+ *
+ * Sources (web pages on the subject; cited by title and section):
+ *  [P1] "Selective Scan trong Mamba toi uu chuoi dai the nao?" (thecsnote.cc):
+ *       sections "Tai sao Mamba can Selective Scan?" (discrete SSM recurrence
+ *       and readout), "Selection pha vo convolution kernel co dinh"
+ *       (time-varying A_t, B_t, C_t and Delta_t), "Scan bien recurrence ..."
+ *       (affine step as a pair, the compose rule and its identity), and the
+ *       Python example (zero-order hold with diagonal A, sequential loop,
+ *       prefix fold from the identity).
+ *  [P3] "15. Selective (Data-Dependent) SSM Scan" (cartesia-pytorch problems):
+ *       "Step-by-Step Approach" (update then read out from the updated state)
+ *       and "Reference solution" (elementwise per-channel recurrence).
+ *  The selective (Mamba) form with D skip, optional silu(z) gate, initial and
+ *  final state, and the first-order input term Delta_t*B_t*x_t is the reading
+ *  of those pages that the build targets (B-bar = Delta*B: the plain reading;
+ *  the exact zero-order-hold B-bar of the P1 example is kept as an option).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define OR_OK 0
+#define OR_ERR_ARG -1
+
+/* dtype codes for x / delta / z */
+#define OR_F32 0
+#define OR_BF16 1
+
+/* Exact widening of a stored value to double. */
+static double load_val(const void* p, int64_t i, int dtype) {
+  if (dtype == OR_BF16) {
+    uint16_t bits = ((const uint16_t*)p)[i];
+    uint32_t w = ((uint32_t)bits) << 16;
+    float f;
+    memcpy(&f, &w, sizeof f);
+    return (double)f;
+  }
+  return (double)((const float*)p)[i];
+}
+
+static void set_threads(int nthreads) {
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+}
+
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/*
+ * Selective form, one channel (b, d) -- [P1] "Tai sao ..." / "Selection ...":
+ *   h_{-1} = h0[b,d,:] (or 0)
+ *   for t: Abar_t[n] = exp(Delta_t * A[d,n])
+ *          h_t[n]    = Abar_t[n] * h_{t-1}[n] + Bbar_t[n] * x_t
+ *          y_t       = sum_n C_t[n] * h_t[n]  (+ D[d] * x_t)  (* silu(z_t))
+ *   with Bbar_t[n] = Delta_t * B_t[n]                      (exact_zoh == 0)
+ *     or Bbar_t[n] = expm1(Delta_t*A[d,n]) / A[d,n] * B_t[n] (exact_zoh != 0,
+ *        the P1 Python example's zero-order hold; Delta_t when A[d,n] == 0).
+ *   The readout uses the state after the update ([P3] step 4).
+ * Layouts: x, delta, z (B, L, D); B, C (B, L, N); A (D, N); D (D);
+ *          h0, h_last (B, D, N).  Outputs: y_out[t * y_stride] for t < L,
+ *          hl_out[n] for n < N.
+ */
+static void sel_channel(const void* x, const void* delta, const float* A, const float* Bm, const float* Cm,
+                        const float* Dsk, const void* z, const float* h0, int64_t b, int64_t d, int64_t L,
+                        int64_t Dm, int64_t N, int dtype, int exact_zoh, double* y_out, int64_t y_stride,
+                        double* hl_out, double* h /* scratch N */) {
+  for (int64_t n = 0; n < N; ++n) h[n] = h0 ? (double)h0[(b * Dm + d) * N + n] : 0.0;
+  for (int64_t t = 0; t < L; ++t) {
+    int64_t e = (b * L + t) * Dm + d;
+    double xt = load_val(x, e, dtype);
+    double dt = load_val(delta, e, dtype);
+    const float* Bt = Bm + (b * L + t) * N;
+    const float* Ct = Cm + (b * L + t) * N;
+    double v = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+      double a = (double)A[d * N + n];
+      double abar = exp(dt * a);
+      double bbar;
+      if (exact_zoh)
+        bbar = (a != 0.0 ? expm1(dt * a) / a : dt) * (double)Bt[n];
+      else
+        bbar = dt * (double)Bt[n];
+      h[n] = abar * h[n] + bbar * xt;
+      v += (double)Ct[n] * h[n];
+    }
+    if (Dsk) v += (double)Dsk[d] * xt;
+    if (z) {
+      double zt = load_val(z, e, dtype);
+      v *= zt / (1.0 + exp(-zt));
+    }
+    y_out[t * y_stride] = v;
+  }
+  if (hl_out)
+    for (int64_t n = 0; n < N; ++n) hl_out[n] = h[n];
+}
+
+static int sel_args_ok(const void* x, const void* delta, const float* A, const float* Bm, const float* Cm,
+                       int64_t batch, int64_t L, int64_t Dm, int64_t N, int dtype) {
+  if (!x || !delta || !A || !Bm || !Cm) return 0;
+  if (batch < 1 || L < 1 || Dm < 1 || N < 1 || N > 4096) return 0;
+  if (dtype != OR_F32 && dtype != OR_BF16) return 0;
+  return 1;
+}
+
+/* Full tensor: y (B, L, D) double, h_last (B, D, N) double (nullable). */
+int oracle_selective_scan(const void* x, const void* delta, const float* A, const float* Bm, const float* Cm,
+                          const float* Dsk, const void* z, const float* h0, double* y, double* h_last,
+                          int64_t batch, int64_t L, int64_t Dm, int64_t N, int dtype, int exact_zoh,
+                          int nthreads) {
+  if (!sel_args_ok(x, delta, A, Bm, Cm, batch, L, Dm, N, dtype) || !y) return OR_ERR_ARG;
+  set_threads(nthreads);
+  int64_t nch = batch * Dm;
+#pragma omp parallel
+  {
+    double hbuf[4096];
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t c = 0; c < nch; ++c) {
+      int64_t b = c / Dm, d = c % Dm;
+      sel_channel(x, delta, A, Bm, Cm, Dsk, z, h0, b, d, L, Dm, N, dtype, exact_zoh, y + b * L * Dm + d, Dm,
+                  h_last ? h_last + (b * Dm + d) * N : 0, hbuf);
+    }
+  }
+  return OR_OK;
+}
+
+/* Chosen channels only: chan[k] = b * D + d.  y_out (nchan, L), hl_out (nchan, N) (nullable). */
+int oracle_selective_scan_channels(const void* x, const void* delta, const float* A, const float* Bm,
+                                   const float* Cm, const float* Dsk, const void* z, const float* h0,
+                                   const int64_t* chan, int64_t nchan, double* y_out, double* hl_out,
+                                   int64_t batch, int64_t L, int64_t Dm, int64_t N, int dtype, int exact_zoh,
+                                   int nthreads) {
+  if (!sel_args_ok(x, delta, A, Bm, Cm, batch, L, Dm, N, dtype) || !chan || !y_out || nchan < 0)
+    return OR_ERR_ARG;
+  for (int64_t k = 0; k < nchan; ++k)
+    if (chan[k] < 0 || chan[k] >= batch * Dm) return OR_ERR_ARG;
+  set_threads(nthreads);
+#pragma omp parallel
+  {
+    double hbuf[4096];
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t k = 0; k < nchan; ++k) {
+      int64_t b = chan[k] / Dm, d = chan[k] % Dm;
+      sel_channel(x, delta, A, Bm, Cm, Dsk, z, h0, b, d, L, Dm, N, dtype, exact_zoh, y_out + k * L, 1,
+                  hl_out ? hl_out + k * N : 0, hbuf);
+    }
+  }
+  return OR_OK;
+}
+
+/*
+ * Elementwise form, one channel -- [P3] "Reference solution":
+ *   h = h0[b,d] (or 0); for t: h = A_t*h + B_t*x_t; y_t = C_t*h.
+ * All of x, A, B, C are (B, L, D) fp32; h0, h_last (B, D).
+ */
+static void ew_channel(const float* x, const float* A, const float* Bm, const float* Cm, const float* h0,
+                       int64_t b, int64_t d, int64_t L, int64_t Dm, double* y_out, int64_t y_stride,
+                       double* hl_out) {
+  double h = h0 ? (double)h0[b * Dm + d] : 0.0;
+  for (int64_t t = 0; t < L; ++t) {
+    int64_t e = (b * L + t) * Dm + d;
+    h = (double)A[e] * h + (double)Bm[e] * (double)x[e];
+    y_out[t * y_stride] = (double)Cm[e] * h;
+  }
+  if (hl_out) *hl_out = h;
+}
+
+int oracle_elementwise_scan(const float* x, const float* A, const float* Bm, const float* Cm, const float* h0,
+                            double* y, double* h_last, int64_t batch, int64_t L, int64_t Dm, int nthreads) {
+  if (!x || !A || !Bm || !Cm || !y || batch < 1 || L < 1 || Dm < 1) return OR_ERR_ARG;
+  set_threads(nthreads);
+  int64_t nch = batch * Dm;
+#pragma omp parallel for schedule(static)
+  for (int64_t c = 0; c < nch; ++c) {
+    int64_t b = c / Dm, d = c % Dm;
+    ew_channel(x, A, Bm, Cm, h0, b, d, L, Dm, y + b * L * Dm + d, Dm, h_last ? h_last + c : 0);
+  }
+  return OR_OK;
+}
+
+int oracle_elementwise_scan_channels(const float* x, const float* A, const float* Bm, const float* Cm,
+                                     const float* h0, const int64_t* chan, int64_t nchan, double* y_out,
+                                     double* hl_out, int64_t batch, int64_t L, int64_t Dm, int nthreads) {
+  if (!x || !A || !Bm || !Cm || !chan || !y_out || nchan < 0 || batch < 1 || L < 1 || Dm < 1) return OR_ERR_ARG;
+  for (int64_t k = 0; k < nchan; ++k)
+    if (chan[k] < 0 || chan[k] >= batch * Dm) return OR_ERR_ARG;
+  set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t k = 0; k < nchan; ++k) {
+    int64_t b = chan[k] / Dm, d = chan[k] % Dm;
+    ew_channel(x, A, Bm, Cm, h0, b, d, L, Dm, y_out + k * L, 1, hl_out ? hl_out + k : 0);
+  }
+  return OR_OK;
+}
+
+/*
+ * Second, independent evaluation by pairs -- [P1] "Scan bien recurrence ...":
+ * each step is the affine map T_t(h) = a_t*h + b_t, written as the pair (a_t, b_t);
+ * two steps compose as (a2, b2) (x) (a1, b1) = (a2*a1, a2*b1 + b2) with identity (1, 0).
+ * The sequence is cut into chunks of `chunk` steps (the last one may be short):
+ *   1. fold each chunk's pairs from the identity into one chunk pair;
+ *   2. fold the chunk pairs in order, starting from the pair (0, h0), to get
+ *      the state entering every chunk;
+ *   3. replay each chunk from its entering state, producing every h_t.
+ * It reaches the same states as the stepwise loop up to rounding order.
+ */
+typedef struct {
+  double a, b;
+} pair_t;
+
+static pair_t compose(pair_t cur, pair_t prefix) { /* cur (x) prefix : apply prefix, then cur */
+  pair_t r;
+  r.a = cur.a * prefix.a;
+  r.b = cur.a * prefix.b + cur.b;
+  return r;
+}
+
+/* step pair of the selective form for (b, t, d, n). */
+static pair_t sel_step(const void* x, const void* delta, const float* A, const float* Bm, int64_t b, int64_t t,
+                       int64_t d, int64_t n, int64_t L, int64_t Dm, int64_t N, int dtype, int exact_zoh) {
+  int64_t e = (b * L + t) * Dm + d;
+  double xt = load_val(x, e, dtype), dt = load_val(delta, e, dtype);
+  double a = (double)A[d * N + n];
+  double Bn = (double)Bm[(b * L + t) * N + n];
+  pair_t p;
+  p.a = exp(dt * a);
+  p.b = (exact_zoh ? (a != 0.0 ? expm1(dt * a) / a : dt) : dt) * Bn * xt;
+  return p;
+}
+
+int oracle_selective_scan_chunked(const void* x, const void* delta, const float* A, const float* Bm,
+                                  const float* Cm, const float* Dsk, const void* z, const float* h0, double* y,
+                                  double* h_last, int64_t batch, int64_t L, int64_t Dm, int64_t N, int dtype,
+                                  int exact_zoh, int64_t chunk, int nthreads) {
+  if (!sel_args_ok(x, delta, A, Bm, Cm, batch, L, Dm, N, dtype) || !y || chunk < 1) return OR_ERR_ARG;
+  set_threads(nthreads);
+  int64_t nchunks = (L + chunk - 1) / chunk;
+  int64_t nch = batch * Dm;
+  for (int64_t i = 0; i < batch * L * Dm; ++i) y[i] = 0.0;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t c = 0; c < nch; ++c) {
+    int64_t b = c / Dm, d = c % Dm;
+    for (int64_t n = 0; n < N; ++n) {
+      /* entering state of the whole sequence as the pair (0, h0) */
+      pair_t run;
+      run.a = 0.0;
+      run.b = h0 ? (double)h0[(b * Dm + d) * N + n] : 0.0;
+      for (int64_t k = 0; k < nchunks; ++k) {
+        int64_t t0 = k * chunk, t1 = t0 + chunk < L ? t0 + chunk : L;
+        /* 1. chunk pair */
+        pair_t agg = {1.0, 0.0};
+        for (int64_t t = t0; t < t1; ++t)
+          agg = compose(sel_step(x, delta, A, Bm, b, t, d, n, L, Dm, N, dtype, exact_zoh), agg);
+        /* 3. replay from the entering state run.b, accumulating C_t[n]*h_t[n] into y */
+        pair_t pre = run;
+        for (int64_t t = t0; t < t1; ++t) {
+          pre = compose(sel_step(x, delta, A, Bm, b, t, d, n, L, Dm, N, dtype, exact_zoh), pre);
+          y[(b * L + t) * Dm + d] += (double)Cm[(b * L + t) * N + n] * pre.b;
+        }
+        /* 2. state entering the next chunk */
+        run = compose(agg, run);
+      }
+      if (h_last) h_last[(b * Dm + d) * N + n] = run.b;
+    }
+    for (int64_t t = 0; t < L; ++t) {
+      int64_t e = (b * L + t) * Dm + d;
+      double v = y[e];
+      if (Dsk) v += (double)Dsk[d] * load_val(x, e, dtype);
+      if (z) {
+        double zt = load_val(z, e, dtype);
+        v *= zt / (1.0 + exp(-zt));
+      }
+      y[e] = v;
+    }
+  }
+  return OR_OK;
+}
+
+int oracle_elementwise_scan_chunked(const float* x, const float* A, const float* Bm, const float* Cm,
+                                    const float* h0, double* y, double* h_last, int64_t batch, int64_t L,
+                                    int64_t Dm, int64_t chunk, int nthreads) {
+  if (!x || !A || !Bm || !Cm || !y || batch < 1 || L < 1 || Dm < 1 || chunk < 1) return OR_ERR_ARG;
+  set_threads(nthreads);
+  int64_t nchunks = (L + chunk - 1) / chunk;
+  int64_t nch = batch * Dm;
+#pragma omp parallel for schedule(static)
+  for (int64_t c = 0; c < nch; ++c) {
+    int64_t b = c / Dm, d = c % Dm;
+    pair_t run;
+    run.a = 0.0;
+    run.b = h0 ? (double)h0[b * Dm + d] : 0.0;
+    for (int64_t k = 0; k < nchunks; ++k) {
+      int64_t t0 = k * chunk, t1 = t0 + chunk < L ? t0 + chunk : L;
+      pair_t agg = {1.0, 0.0};
+      for (int64_t t = t0; t < t1; ++t) {
+        int64_t e = (b * L + t) * Dm + d;
+        pair_t s = {(double)A[e], (double)Bm[e] * (double)x[e]};
+        agg = compose(s, agg);
+      }
+      pair_t pre = run;
+      for (int64_t t = t0; t < t1; ++t) {
+        int64_t e = (b * L + t) * Dm + d;
+        pair_t s = {(double)A[e], (double)Bm[e] * (double)x[e]};
+        pre = compose(s, pre);
+        y[e] = (double)Cm[e] * pre.b;
+      }
+      run = compose(agg, run);
+    }
+    if (h_last) h_last[c] = run.b;
+  }
+  return OR_OK;
+}
