@@ -1,0 +1,98 @@
+/*
+ * sss.h -- C ABI of the MI355X (gfx950) selective-scan library, libsss.so.
+ *
+ * Two operations, both fully computed by hand-written HIP kernels on the device:
+ *
+ *  selective_scan_fwd  -- the selective (input-dependent) state-space recurrence of
+ *      "Selective Scan trong Mamba toi uu chuoi dai the nao?" (thecsnote.cc), sections
+ *      "Tai sao Mamba can Selective Scan?" and "Selection pha vo convolution kernel co
+ *      dinh": per batch b, channel d and state n, with zero-order-hold decay
+ *        Abar_t[n] = exp(delta_t * A[d,n]),
+ *        h_t[n]    = Abar_t[n] * h_{t-1}[n] + delta_t * B_t[n] * x_t,
+ *        y_t       = (sum_n C_t[n] * h_t[n] + D[d] * x_t) * silu(z_t)   (D, z optional),
+ *      h_{-1} = h0 (or 0), read-out after the update, final state h_{L-1} returned.
+ *      delta arrives already passed through softplus: the projections that produce
+ *      delta, B and C are outside this library ("15. Selective (Data-Dependent) SSM
+ *      Scan", Problem: the data-dependent parameters are given).
+ *
+ *  elementwise_scan -- the per-channel form of "15. Selective (Data-Dependent) SSM
+ *      Scan" (Reference solution): h = A_t*h + B_t*x_t, y_t = C_t*h.
+ *
+ * Conventions (both calls)
+ *  - Pointers are DEVICE pointers owned by the caller.  Inputs are read-only; outputs
+ *    may not overlap any input (SSS_ERR_ALIAS).  Every pointer must be 16-byte aligned
+ *    (SSS_ERR_UNSUPPORTED otherwise).
+ *  - Layout is row-major, all indices 64-bit:
+ *      x, delta, z, y : (batch, seqlen, dim)        -- dim fastest
+ *      B, C           : (batch, seqlen, dstate)
+ *      A              : (dim, dstate)                -- selective form
+ *      D_skip         : (dim)
+ *      h0, h_last     : (batch, dim, dstate)         -- (batch, dim) for elementwise
+ *  - Work is enqueued on `stream` and the call returns without synchronising.  Launch
+ *    failures come back as SSS_ERR_HIP; a fault inside a kernel shows up at the
+ *    caller's next synchronisation.
+ *  - All validation happens before any device work; a rejected call writes nothing.
+ *  - Workspace: caller-allocated device memory of at least *_workspace_size() bytes
+ *    (may be NULL when that size is 0).  It is stream-ordered scratch: do not share
+ *    one workspace between calls that may run concurrently.
+ *  - The library allocates no device memory and keeps no state between calls other
+ *    than a per-device cache of the compute-unit count.  Calls are thread-safe.
+ *  - Environment: SSS_FORCE_SEGMENTS=<S> forces the number of time segments (the
+ *    two-pass split) for testing; SSS_LOG=1 prints the chosen launch plan to stderr.
+ */
+#ifndef SSS_H_
+#define SSS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* HIP stream handle (same type as hip/hip_runtime_api.h's hipStream_t). */
+typedef struct ihipStream_t* sss_stream_t;
+
+/* dtype of x, delta and z for selective_scan_fwd; every other tensor is float32. */
+typedef enum { SSS_F32 = 0, SSS_BF16 = 1 } sss_dtype;
+
+typedef enum {
+  SSS_OK = 0,
+  SSS_ERR_NULL_ARG = -1,    /* a required pointer is NULL                             */
+  SSS_ERR_BAD_DIM = -2,     /* a dimension is < 1 or a size overflows                 */
+  SSS_ERR_UNSUPPORTED = -3, /* dstate outside 1..64, unknown dtype, or a pointer not
+                               16-byte aligned                                         */
+  SSS_ERR_WORKSPACE = -4,   /* workspace smaller than the size query (or NULL)        */
+  SSS_ERR_ALIAS = -5,       /* an output overlaps an input or another output           */
+  SSS_ERR_HIP = -6          /* no usable device, or a HIP launch/runtime error         */
+} sss_status;
+
+/* Bytes of workspace selective_scan_fwd needs for these sizes on `device`
+ * (0 on invalid sizes).  Depends on the launch plan, hence on the device. */
+size_t selective_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                                         int device);
+
+/* Selective scan (Mamba form).  Required: x, delta (io_dtype), A, B, C (float32), y.
+ * Optional (NULL): D_skip, z (io_dtype), h0 (NULL = zero state), h_last.
+ * y and h_last are float32.  Returns an sss_status. */
+int selective_scan_fwd(const void* x, const void* delta, const float* A, const float* B, const float* C,
+                       const float* D_skip, const void* z, const float* h0, float* y, float* h_last,
+                       int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
+                       void* workspace, size_t workspace_bytes, sss_stream_t stream);
+
+/* Bytes of workspace elementwise_scan needs for these sizes on `device`. */
+size_t elementwise_scan_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int device);
+
+/* Elementwise scan, all float32.  Required: x, A, B, C, y.  Optional: h0, h_last. */
+int elementwise_scan(const float* x, const float* A, const float* B, const float* C, const float* h0, float* y,
+                     float* h_last, int64_t batch, int64_t seqlen, int64_t dim, void* workspace,
+                     size_t workspace_bytes, sss_stream_t stream);
+
+/* Human-readable name of a status code (static string). */
+const char* sss_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSS_H_ */

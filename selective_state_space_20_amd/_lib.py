@@ -1,0 +1,161 @@
+"""ctypes binding of libsss.so: argument marshalling only.
+
+Every step of the computation runs in the library's HIP kernels; this module checks
+tensor properties, allocates the workspace and outputs with torch (device memory and the
+current stream are the only things torch provides) and calls the C ABI of include/sss.h.
+There is no fallback: if the shared library is missing the import of the function fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libsss.so")
+
+SSS_F32, SSS_BF16 = 0, 1
+STATUS = {0: "SSS_OK", -1: "SSS_ERR_NULL_ARG", -2: "SSS_ERR_BAD_DIM", -3: "SSS_ERR_UNSUPPORTED",
+          -4: "SSS_ERR_WORKSPACE", -5: "SSS_ERR_ALIAS", -6: "SSS_ERR_HIP"}
+
+EXPORTED = ("selective_scan_fwd", "selective_scan_fwd_workspace_size", "elementwise_scan",
+            "elementwise_scan_workspace_size", "sss_status_string")
+
+
+class SSSError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({status_string(status)})")
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libsss.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with selective_state_space_20_amd.build.build()")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+        lib.selective_scan_fwd.argtypes = [vp] * 10 + [i64] * 4 + [i32, vp, sz, vp]
+        lib.selective_scan_fwd.restype = i32
+        lib.selective_scan_fwd_workspace_size.argtypes = [i64] * 4 + [i32]
+        lib.selective_scan_fwd_workspace_size.restype = sz
+        lib.elementwise_scan.argtypes = [vp] * 7 + [i64] * 3 + [vp, sz, vp]
+        lib.elementwise_scan.restype = i32
+        lib.elementwise_scan_workspace_size.argtypes = [i64] * 3 + [i32]
+        lib.elementwise_scan_workspace_size.restype = sz
+        lib.sss_status_string.argtypes = [i32]
+        lib.sss_status_string.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load().sss_status_string(int(status)).decode()
+
+
+# ---------------------------------------------------------------- raw-pointer entry points
+def selective_scan_fwd_raw(x, delta, A, B, C, D_skip, z, h0, y, h_last, batch, seqlen, dim, dstate, io_dtype,
+                           workspace, workspace_bytes, stream) -> int:
+    """Direct call of the C function with integer pointers (0 = NULL)."""
+    return load().selective_scan_fwd(x, delta, A, B, C, D_skip, z, h0, y, h_last, batch, seqlen, dim, dstate,
+                                     io_dtype, workspace, workspace_bytes, stream)
+
+
+def elementwise_scan_raw(x, A, B, C, h0, y, h_last, batch, seqlen, dim, workspace, workspace_bytes,
+                         stream) -> int:
+    return load().elementwise_scan(x, A, B, C, h0, y, h_last, batch, seqlen, dim, workspace, workspace_bytes,
+                                   stream)
+
+
+def selective_scan_fwd_workspace_size(batch, seqlen, dim, dstate, device=0) -> int:
+    return int(load().selective_scan_fwd_workspace_size(batch, seqlen, dim, dstate, device))
+
+
+def elementwise_scan_workspace_size(batch, seqlen, dim, device=0) -> int:
+    return int(load().elementwise_scan_workspace_size(batch, seqlen, dim, device))
+
+
+# ---------------------------------------------------------------- torch-tensor entry points
+def _ptr(t):
+    return 0 if t is None else t.data_ptr()
+
+
+def _need(t, name, dtype, shape, device):
+    import torch
+    if t is None:
+        return
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def selective_scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, return_last=True, out=None,
+                       out_last=None, workspace=None, stream=None):
+    """y (batch, seqlen, dim) float32 [, h_last (batch, dim, dstate) float32].
+
+    x, delta, z: float32 or bfloat16 (one dtype); A (dim, dstate), B, C (batch, seqlen,
+    dstate), D (dim), h0 (batch, dim, dstate): float32.  All on one GPU, contiguous.
+    """
+    import torch
+    dev = x.device
+    batch, seqlen, dim = x.shape
+    dstate = A.shape[1]
+    io = x.dtype
+    if io not in (torch.float32, torch.bfloat16):
+        raise ValueError("x must be float32 or bfloat16")
+    f32 = torch.float32
+    _need(x, "x", io, (batch, seqlen, dim), dev)
+    _need(delta, "delta", io, (batch, seqlen, dim), dev)
+    _need(z, "z", io, (batch, seqlen, dim), dev)
+    _need(A, "A", f32, (dim, dstate), dev)
+    _need(B, "B", f32, (batch, seqlen, dstate), dev)
+    _need(C, "C", f32, (batch, seqlen, dstate), dev)
+    _need(D, "D", f32, (dim,), dev)
+    _need(h0, "h0", f32, (batch, dim, dstate), dev)
+    y = out if out is not None else torch.empty((batch, seqlen, dim), dtype=f32, device=dev)
+    hl = out_last if out_last is not None else (
+        torch.empty((batch, dim, dstate), dtype=f32, device=dev) if return_last else None)
+    _need(y, "out", f32, (batch, seqlen, dim), dev)
+    _need(hl, "out_last", f32, (batch, dim, dstate), dev)
+    wsb = selective_scan_fwd_workspace_size(batch, seqlen, dim, dstate, dev.index or 0)
+    if workspace is None and wsb > 0:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    st = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
+    rc = selective_scan_fwd_raw(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y),
+                                _ptr(hl), batch, seqlen, dim, dstate, SSS_BF16 if io == torch.bfloat16 else SSS_F32,
+                                _ptr(workspace), 0 if workspace is None else workspace.numel(), st)
+    if rc != 0:
+        raise SSSError(rc, "selective_scan_fwd")
+    return (y, hl) if return_last or out_last is not None else y
+
+
+def elementwise_scan(x, A, B, C, h0=None, *, return_last=True, out=None, out_last=None, workspace=None,
+                     stream=None):
+    """y (batch, seqlen, dim) [, h_last (batch, dim)]; every tensor float32 on one GPU."""
+    import torch
+    dev = x.device
+    batch, seqlen, dim = x.shape
+    f32 = torch.float32
+    for t, n in ((x, "x"), (A, "A"), (B, "B"), (C, "C")):
+        _need(t, n, f32, (batch, seqlen, dim), dev)
+    _need(h0, "h0", f32, (batch, dim), dev)
+    y = out if out is not None else torch.empty((batch, seqlen, dim), dtype=f32, device=dev)
+    hl = out_last if out_last is not None else (
+        torch.empty((batch, dim), dtype=f32, device=dev) if return_last else None)
+    wsb = elementwise_scan_workspace_size(batch, seqlen, dim, dev.index or 0)
+    if workspace is None and wsb > 0:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    st = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
+    rc = elementwise_scan_raw(_ptr(x), _ptr(A), _ptr(B), _ptr(C), _ptr(h0), _ptr(y), _ptr(hl), batch, seqlen, dim,
+                              _ptr(workspace), 0 if workspace is None else workspace.numel(), st)
+    if rc != 0:
+        raise SSSError(rc, "elementwise_scan")
+    return (y, hl) if return_last or out_last is not None else y

@@ -1,0 +1,225 @@
+// api.cpp -- the C ABI of libsss.so (declared in include/sss.h): argument validation,
+// launch planning and dispatch to the gfx950 kernels.  No device memory is allocated here.
+#include "sss.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "kernels.h"
+
+namespace sss {
+
+int env_int(const char* name, int dflt) {
+  const char* v = std::getenv(name);
+  if (v == nullptr || *v == '\0') return dflt;
+  return std::atoi(v);
+}
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];  // 0 = unknown
+
+// Compute units of `device` (cached); -1 if it cannot be queried.
+int device_cus(int device) {
+  if (device < 0 || device >= kMaxDevices) return -1;
+  int v = g_cus[device].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus <= 0) {
+    (void)hipGetLastError();
+    return -1;
+  }
+  g_cus[device].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+int current_device_cus() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return -1;
+  }
+  return device_cus(dev);
+}
+
+// Sizes in bytes with overflow checks; false when a product leaves [0, 2^62).
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > (int64_t(1) << 62) / a) return false;
+  *out = a * b;
+  return true;
+}
+
+struct Range {
+  uintptr_t lo, hi;
+};
+
+bool overlap(const void* p, int64_t bytes, const void* q, int64_t qbytes) {
+  if (p == nullptr || q == nullptr || bytes <= 0 || qbytes <= 0) return false;
+  uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+  return a < b + (uintptr_t)qbytes && b < a + (uintptr_t)bytes;
+}
+
+bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+}  // namespace sss
+
+using namespace sss;
+
+extern "C" {
+
+const char* sss_status_string(int status) {
+  switch (status) {
+    case SSS_OK: return "SSS_OK";
+    case SSS_ERR_NULL_ARG: return "SSS_ERR_NULL_ARG: a required pointer is NULL";
+    case SSS_ERR_BAD_DIM: return "SSS_ERR_BAD_DIM: a dimension is < 1 or a size is too large";
+    case SSS_ERR_UNSUPPORTED: return "SSS_ERR_UNSUPPORTED: dstate outside 1..64, unknown dtype or misaligned pointer";
+    case SSS_ERR_WORKSPACE: return "SSS_ERR_WORKSPACE: workspace missing or smaller than the size query";
+    case SSS_ERR_ALIAS: return "SSS_ERR_ALIAS: an output overlaps an input, another output or the workspace";
+    case SSS_ERR_HIP: return "SSS_ERR_HIP: no usable HIP device or a launch failed";
+    default: return "unknown sss status";
+  }
+}
+
+static int sel_dims_ok(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
+  if (batch < 1 || seqlen < 1 || dim < 1 || dstate < 1) return SSS_ERR_BAD_DIM;
+  int64_t e = 0, t = 0;
+  if (!mul_ok(batch, seqlen, &t) || !mul_ok(t, dim, &e) || !mul_ok(e, 4, &t)) return SSS_ERR_BAD_DIM;
+  if (!mul_ok(batch, seqlen, &t) || !mul_ok(t, dstate, &e) || !mul_ok(e, 4, &t)) return SSS_ERR_BAD_DIM;
+  if (batch * ((dim + 3) / 4) > (int64_t)1 << 30) return SSS_ERR_BAD_DIM;  // grid size
+  if (dstate > 64) return SSS_ERR_UNSUPPORTED;
+  return SSS_OK;
+}
+
+size_t selective_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int device) {
+  if (sel_dims_ok(batch, seqlen, dim, dstate) != SSS_OK) return 0;
+  int cus = device_cus(device);
+  if (cus <= 0) cus = 256;
+  return plan_selective(batch, seqlen, dim, dstate, cus).ws_total;
+}
+
+int selective_scan_fwd(const void* x, const void* delta, const float* A, const float* B, const float* C,
+                       const float* D_skip, const void* z, const float* h0, float* y, float* h_last,
+                       int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
+                       void* workspace, size_t workspace_bytes, sss_stream_t stream) {
+  if (!x || !delta || !A || !B || !C || !y) return SSS_ERR_NULL_ARG;
+  int st = sel_dims_ok(batch, seqlen, dim, dstate);
+  if (st != SSS_OK) return st;
+  if (io_dtype != SSS_F32 && io_dtype != SSS_BF16) return SSS_ERR_UNSUPPORTED;
+  const void* ptrs[] = {x, delta, A, B, C, D_skip, z, h0, y, h_last, workspace};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return SSS_ERR_UNSUPPORTED;
+  const int64_t es = io_dtype == SSS_BF16 ? 2 : 4;
+  const int64_t E = batch * seqlen * dim;
+  const int64_t y_bytes = E * 4, hl_bytes = batch * dim * dstate * 4;
+  const void* in_p[] = {x, delta, A, B, C, D_skip, z, h0};
+  const int64_t in_b[] = {E * es, E * es, dim * dstate * 4, batch * seqlen * dstate * 4,
+                          batch * seqlen * dstate * 4, dim * 4, E * es, batch * dim * dstate * 4};
+  for (int i = 0; i < 8; ++i) {
+    if (overlap(y, y_bytes, in_p[i], in_b[i])) return SSS_ERR_ALIAS;
+    if (overlap(h_last, hl_bytes, in_p[i], in_b[i])) return SSS_ERR_ALIAS;
+  }
+  if (overlap(y, y_bytes, h_last, hl_bytes)) return SSS_ERR_ALIAS;
+  const int cus = current_device_cus();
+  if (cus <= 0) return SSS_ERR_HIP;
+  const SelPlan pl = plan_selective(batch, seqlen, dim, dstate, cus);
+  if (pl.ws_total > 0) {
+    if (workspace == nullptr || workspace_bytes < pl.ws_total) return SSS_ERR_WORKSPACE;
+    const int64_t wb = (int64_t)pl.ws_total;
+    if (overlap(workspace, wb, y, y_bytes) || overlap(workspace, wb, h_last, hl_bytes)) return SSS_ERR_ALIAS;
+    for (int i = 0; i < 8; ++i)
+      if (overlap(workspace, wb, in_p[i], in_b[i])) return SSS_ERR_ALIAS;
+  }
+  if (env_int("SSS_LOG", 0))
+    std::fprintf(stderr, "[sss] selective_scan_fwd B=%lld L=%lld D=%lld N=%lld %s: k=%d wpb=%d segments=%d seg_len=%lld ws=%zu\n",
+                 (long long)batch, (long long)seqlen, (long long)dim, (long long)dstate,
+                 io_dtype == SSS_BF16 ? "bf16" : "f32", pl.k, pl.wpb, pl.segments, (long long)pl.seg_len, pl.ws_total);
+  SelArgs a{};
+  a.x = x;
+  a.delta = delta;
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.Dsk = D_skip;
+  a.z = z;
+  a.h0 = h0;
+  a.y = y;
+  a.h_last = h_last;
+  a.batch = batch;
+  a.seqlen = seqlen;
+  a.dim = dim;
+  a.dstate = (int)dstate;
+  a.bf16 = io_dtype == SSS_BF16;
+  a.workspace = workspace;
+  hipError_t e = launch_selective(a, pl, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SSS_OK : SSS_ERR_HIP;
+}
+
+static int ew_dims_ok(int64_t batch, int64_t seqlen, int64_t dim) {
+  if (batch < 1 || seqlen < 1 || dim < 1) return SSS_ERR_BAD_DIM;
+  int64_t e = 0, t = 0;
+  if (!mul_ok(batch, seqlen, &t) || !mul_ok(t, dim, &e) || !mul_ok(e, 4, &t)) return SSS_ERR_BAD_DIM;
+  if ((batch * dim + 63) / 64 > (int64_t)1 << 30) return SSS_ERR_BAD_DIM;
+  return SSS_OK;
+}
+
+size_t elementwise_scan_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int device) {
+  if (ew_dims_ok(batch, seqlen, dim) != SSS_OK) return 0;
+  int cus = device_cus(device);
+  if (cus <= 0) cus = 256;
+  return plan_elementwise(batch, seqlen, dim, cus).ws_total;
+}
+
+int elementwise_scan(const float* x, const float* A, const float* B, const float* C, const float* h0, float* y,
+                     float* h_last, int64_t batch, int64_t seqlen, int64_t dim, void* workspace,
+                     size_t workspace_bytes, sss_stream_t stream) {
+  if (!x || !A || !B || !C || !y) return SSS_ERR_NULL_ARG;
+  int st = ew_dims_ok(batch, seqlen, dim);
+  if (st != SSS_OK) return st;
+  const void* ptrs[] = {x, A, B, C, h0, y, h_last, workspace};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return SSS_ERR_UNSUPPORTED;
+  const int64_t E = batch * seqlen * dim * 4, H = batch * dim * 4;
+  const void* in_p[] = {x, A, B, C, h0};
+  const int64_t in_b[] = {E, E, E, E, H};
+  for (int i = 0; i < 5; ++i) {
+    if (overlap(y, E, in_p[i], in_b[i])) return SSS_ERR_ALIAS;
+    if (overlap(h_last, H, in_p[i], in_b[i])) return SSS_ERR_ALIAS;
+  }
+  if (overlap(y, E, h_last, H)) return SSS_ERR_ALIAS;
+  const int cus = current_device_cus();
+  if (cus <= 0) return SSS_ERR_HIP;
+  const EwPlan pl = plan_elementwise(batch, seqlen, dim, cus);
+  if (pl.ws_total > 0) {
+    if (workspace == nullptr || workspace_bytes < pl.ws_total) return SSS_ERR_WORKSPACE;
+    const int64_t wb = (int64_t)pl.ws_total;
+    if (overlap(workspace, wb, y, E) || overlap(workspace, wb, h_last, H)) return SSS_ERR_ALIAS;
+    for (int i = 0; i < 5; ++i)
+      if (overlap(workspace, wb, in_p[i], in_b[i])) return SSS_ERR_ALIAS;
+  }
+  if (env_int("SSS_LOG", 0))
+    std::fprintf(stderr, "[sss] elementwise_scan B=%lld L=%lld D=%lld: segments=%d seg_len=%lld ws=%zu\n",
+                 (long long)batch, (long long)seqlen, (long long)dim, pl.segments, (long long)pl.seg_len, pl.ws_total);
+  EwArgs a{};
+  a.x = x;
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.h0 = h0;
+  a.y = y;
+  a.h_last = h_last;
+  a.batch = batch;
+  a.seqlen = seqlen;
+  a.dim = dim;
+  a.workspace = workspace;
+  hipError_t e = launch_elementwise(a, pl, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SSS_OK : SSS_ERR_HIP;
+}
+
+}  // extern "C"

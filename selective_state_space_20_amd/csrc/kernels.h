@@ -1,0 +1,63 @@
+// kernels.h -- launch interface between the C-ABI host code and the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sss {
+
+// Launch plan of the selective scan (chosen on the host, see api.cpp).
+struct SelPlan {
+  int k;             // steps per lane (time sub-chunk held in registers): 8 or 16
+  int wpb;           // waves per workgroup = channels per workgroup
+  int segments;      // time segments S (S > 1 -> two-pass: segment states, then outputs)
+  int64_t seg_len;   // steps per segment, a multiple of 64*k
+  int64_t lpad;      // seqlen rounded up to 4 (row length of the transposed B/C)
+  int vec4;          // staging with 4-channel vectors (dim % 4 == 0 and wpb % 4 == 0)
+  size_t ws_bt, ws_ct, ws_state, ws_dsum, ws_total;  // workspace offsets / total bytes
+};
+
+struct SelArgs {
+  const void* x;
+  const void* delta;
+  const float* A;
+  const float* B;
+  const float* C;
+  const float* Dsk;
+  const void* z;
+  const float* h0;
+  float* y;
+  float* h_last;
+  int64_t batch, seqlen, dim;
+  int dstate;
+  int bf16;
+  void* workspace;
+};
+
+SelPlan plan_selective(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int num_cus);
+hipError_t launch_selective(const SelArgs& a, const SelPlan& plan, hipStream_t stream);
+
+struct EwPlan {
+  int segments;
+  int64_t seg_len;
+  size_t ws_total;
+};
+
+struct EwArgs {
+  const float* x;
+  const float* A;
+  const float* B;
+  const float* C;
+  const float* h0;
+  float* y;
+  float* h_last;
+  int64_t batch, seqlen, dim;
+  void* workspace;
+};
+
+EwPlan plan_elementwise(int64_t batch, int64_t seqlen, int64_t dim, int num_cus);
+hipError_t launch_elementwise(const EwArgs& a, const EwPlan& plan, hipStream_t stream);
+
+int env_int(const char* name, int dflt);
+
+}  // namespace sss

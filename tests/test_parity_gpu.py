@@ -1,0 +1,219 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on identical inputs.
+
+Tolerances: max|gpu - oracle| <= 1e-4 * max|oracle| for fp32 inputs and 2e-3 * max|oracle|
+for bf16 inputs with fp32 state, per output tensor (y and h_last separately).
+Outputs are pre-filled with NaN so that an element the kernels never write fails.
+"""
+import os
+import zlib
+
+import numpy as np
+import pytest
+
+from selective_state_space_20_amd import inputs as gen
+from tests.gpu_util import TOL_BF16, TOL_F32, note, rel_err, run_elementwise, run_selective
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _no_forced_segments(monkeypatch):
+    monkeypatch.delenv("SSS_FORCE_SEGMENTS", raising=False)
+    yield
+
+
+def _check_sel(oracle_lib, inp, tag):
+    note(f"[selective] {tag} x{inp['x'].shape} N={inp['A'].shape[1]} io={inp['io']}")
+    y, hl = run_selective(inp)
+    yr, hlr = oracle_lib.selective_scan(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                                        inp["h0"])
+    tol = TOL_BF16 if inp["io"] == "bf16" else TOL_F32
+    ey, eh = rel_err(y, yr), rel_err(hl, hlr)
+    note(f"    err y={ey:.3e} h_last={eh:.3e} (tol {tol:g})")
+    assert ey <= tol and eh <= tol, (ey, eh)
+    return ey, eh
+
+
+SEL_CASES = [
+    # (batch, seqlen, dim, dstate, io, z, D, h0)
+    (1, 1, 1, 1, "f32", False, False, False),
+    (1, 2, 3, 4, "f32", True, True, True),
+    (2, 63, 4, 16, "f32", False, True, False),
+    (1, 64, 64, 16, "bf16", True, True, True),
+    (3, 65, 5, 8, "bf16", True, False, True),
+    (2, 1000, 100, 16, "f32", True, True, True),
+    (1, 1025, 8, 16, "bf16", True, True, True),
+    (2, 2049, 12, 64, "f32", False, True, True),
+    (1, 3000, 4, 2, "bf16", True, True, False),
+    (2, 700, 33, 32, "bf16", False, False, True),
+]
+
+
+@pytest.mark.parametrize("case", SEL_CASES, ids=[f"B{c[0]}L{c[1]}D{c[2]}N{c[3]}{c[4]}" for c in SEL_CASES])
+def test_selective_random_shapes(oracle_lib, case):
+    bt, L, dm, n, io, z, D, h0 = case
+    inp = gen.selective_inputs(bt, L, dm, n, io=io, with_z=z, with_D=D, h0=h0, seed=zlib.crc32(repr(case).encode()) % 100000)
+    _check_sel(oracle_lib, inp, "random")
+
+
+@pytest.mark.parametrize("segments", [2, 3, 7])
+def test_selective_two_pass_forced(oracle_lib, monkeypatch, segments):
+    """The two-pass split (segment states, then outputs) forced on shapes that span
+    several chunks, with a ragged last segment."""
+    monkeypatch.setenv("SSS_FORCE_SEGMENTS", str(segments))
+    inp = gen.selective_inputs(2, 5000, 8, 16, io="bf16", with_z=True, with_D=True, h0=True, seed=40 + segments)
+    _check_sel(oracle_lib, inp, f"S={segments}")
+    inp = gen.selective_inputs(1, 9000, 3, 4, io="f32", with_z=False, with_D=True, h0=True, seed=50 + segments)
+    _check_sel(oracle_lib, inp, f"S={segments}")
+
+
+def test_selective_special_values(oracle_lib):
+    """A = 0 (no decay: long carries), A = -inf (memoryless), z = 0 (gate closes)."""
+    inp = gen.selective_inputs(2, 3000, 8, 16, io="f32", with_z=False, with_D=True, h0=True, seed=61)
+    inp["A"][:, :4] = 0.0
+    inp["A"][:, 4:8] = -np.inf
+    _check_sel(oracle_lib, inp, "A=0/-inf")
+    inp = gen.selective_inputs(1, 300, 8, 16, io="bf16", with_z=True, with_D=True, h0=True, seed=62)
+    inp["z"][:] = 0
+    y, hl = run_selective(inp)
+    assert np.all(y == 0.0)
+
+
+def test_selective_hand_worked_fixture(oracle_lib):
+    """The hand-derived example of tests/golden (exact values) on the GPU."""
+    import json
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_worked_selective.json")))
+    f = lambda k: np.asarray(g[k], dtype=np.float32)
+    inp = dict(x=f("x"), delta=f("delta"), A=f("A"), B=f("B"), C=f("C"), D=f("D"), z=None, h0=f("h0"), io="f32")
+    y, hl = run_selective(inp)
+    assert rel_err(y, np.asarray(g["y"])) < 1e-6 and rel_err(hl, np.asarray(g["h_last"])) < 1e-6
+
+
+def test_selective_deterministic_and_no_h_last(oracle_lib):
+    """Bitwise-identical repeat runs (no race in LDS/DPP); h_last may be omitted."""
+    inp = gen.selective_inputs(2, 4100, 20, 16, io="bf16", with_z=True, with_D=True, h0=True, seed=63)
+    y1, h1 = run_selective(inp)
+    y2, h2 = run_selective(inp)
+    assert np.array_equal(y1, y2) and np.array_equal(h1, h2)
+    y3, _ = run_selective(inp, return_last=False)
+    assert np.array_equal(y1, y3)
+
+
+def test_selective_guard_bands():
+    """Writes stay inside y and h_last: canaries around both outputs survive."""
+    import torch
+    import selective_state_space_20_amd as sss
+    from tests.gpu_util import to_dev
+    inp = gen.selective_inputs(2, 777, 10, 16, io="bf16", with_z=True, with_D=True, h0=True, seed=64)
+    t = {k: to_dev(v, "cuda:0") for k, v in inp.items() if k != "io"}
+    pad = 1024
+    ybuf = torch.full((2 * 777 * 10 + 2 * pad,), 12345.0, device="cuda:0")
+    hbuf = torch.full((2 * 10 * 16 + 2 * pad,), 12345.0, device="cuda:0")
+    y = ybuf[pad:pad + 2 * 777 * 10].view(2, 777, 10)
+    hl = hbuf[pad:pad + 2 * 10 * 16].view(2, 10, 16)
+    sss.selective_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"], out=y, out_last=hl)
+    torch.cuda.synchronize()
+    for buf in (ybuf, hbuf):
+        assert torch.all(buf[:pad] == 12345.0) and torch.all(buf[-pad:] == 12345.0)
+
+
+# ---------------------------------------------------------------- elementwise
+def _check_ew(oracle_lib, inp, tag):
+    note(f"[elementwise] {tag} x{inp['x'].shape}")
+    y, hl = run_elementwise(inp)
+    yr, hlr = oracle_lib.elementwise_scan(inp["x"], inp["A"], inp["B"], inp["C"], inp["h0"])
+    ey, eh = rel_err(y, yr), rel_err(hl, hlr)
+    note(f"    err y={ey:.3e} h_last={eh:.3e}")
+    assert ey <= TOL_F32 and eh <= TOL_F32, (ey, eh)
+
+
+EW_CASES = [(1, 1, 1, False), (2, 6, 4, False), (2, 64, 4, False), (3, 1000, 65, True), (1, 5000, 3, True),
+            (4, 333, 130, True)]
+
+
+@pytest.mark.parametrize("case", EW_CASES, ids=[f"B{c[0]}L{c[1]}D{c[2]}" for c in EW_CASES])
+def test_elementwise_random_shapes(oracle_lib, case):
+    bt, L, dm, h0 = case
+    _check_ew(oracle_lib, gen.elementwise_inputs(bt, L, dm, h0=h0, seed=zlib.crc32(repr(case).encode()) % 100000), "random")
+
+
+@pytest.mark.parametrize("segments", [2, 5, 64])
+def test_elementwise_two_pass_forced(oracle_lib, monkeypatch, segments):
+    monkeypatch.setenv("SSS_FORCE_SEGMENTS", str(segments))
+    _check_ew(oracle_lib, gen.elementwise_inputs(2, 3001, 7, h0=True, seed=70 + segments), f"S={segments}")
+
+
+def test_elementwise_hand_worked_and_zero_decay(oracle_lib):
+    import json
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_worked_elementwise.json")))
+    f = lambda k: np.asarray(g[k], dtype=np.float32)
+    y, hl = run_elementwise(dict(x=f("x"), A=f("A"), B=f("B"), C=f("C"), h0=f("h0")))
+    assert np.array_equal(y, np.asarray(g["y"], dtype=np.float32))
+    assert np.array_equal(hl, np.asarray(g["h_last"], dtype=np.float32))
+    inp = gen.elementwise_inputs(2, 500, 9, h0=True, seed=71)
+    inp["A"][:] = 0.0
+    y, _ = run_elementwise(inp)
+    assert np.array_equal(y, (inp["C"] * (inp["B"] * inp["x"])).astype(np.float32))
+
+
+# ---------------------------------------------------------------- the configurations
+def test_config0_elementwise_small(oracle_lib):
+    cfg, inp = gen.config_inputs(0)
+    _check_ew(oracle_lib, inp, cfg["name"])
+
+
+def test_config1_selective_fp32(oracle_lib):
+    cfg, inp = gen.config_inputs(1)
+    _check_sel(oracle_lib, inp, cfg["name"])
+
+
+def test_config2_selective_bf16_full(oracle_lib):
+    cfg, inp = gen.config_inputs(2)
+    _check_sel(oracle_lib, inp, cfg["name"])
+
+
+def _sample_channels(nch, k, seed):
+    rng = np.random.default_rng(seed)
+    pick = set([0, nch - 1, nch // 2, 1, nch - 2])
+    pick |= set(rng.choice(nch, size=k, replace=False).tolist())
+    return np.array(sorted(pick), dtype=np.int64)
+
+
+@pytest.mark.timeout(600)
+def test_config3_selective_long_sampled(oracle_lib):
+    """Full-size long-sequence layer (B=1, D=5120, N=16, L=65536, bf16): every output finite;
+    sampled channels (ends, middle, random) against the oracle over the whole sequence."""
+    cfg, inp = gen.config_inputs(3)
+    note(f"[selective] {cfg['name']} inputs generated")
+    y, hl = run_selective(inp)
+    note("    GPU done")
+    assert np.all(np.isfinite(y)) and np.all(np.isfinite(hl))
+    ch = _sample_channels(cfg["dim"], 24, 3)
+    note(f"[selective] {cfg['name']} sampled channels {ch.tolist()}")
+    yr, hlr = oracle_lib.selective_scan_channels(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"],
+                                                 inp["z"], inp["h0"], channels=ch)
+    yg = y[0][:, ch].T
+    hg = hl[0][ch]
+    ey, eh = rel_err(yg, yr), rel_err(hg, hlr)
+    note(f"    err y={ey:.3e} h_last={eh:.3e}")
+    assert ey <= TOL_BF16 and eh <= TOL_BF16
+
+
+@pytest.mark.timeout(900)
+def test_config4_elementwise_large_sampled(oracle_lib):
+    """Full-size elementwise scan (8 x 32768 x 4096, fp32): finite everywhere, sampled
+    channels against the oracle over the whole sequence, A = 0 identity on a slab."""
+    cfg, inp = gen.config_inputs(4)
+    note(f"[elementwise] {cfg['name']} inputs generated")
+    y, hl = run_elementwise(inp)
+    note("    GPU done")
+    assert np.all(np.isfinite(hl))
+    nch = cfg["batch"] * cfg["dim"]
+    ch = _sample_channels(nch, 24, 4)
+    note(f"[elementwise] {cfg['name']} sampled channels {ch.tolist()}")
+    yr, hlr = oracle_lib.elementwise_scan_channels(inp["x"], inp["A"], inp["B"], inp["C"], inp["h0"], channels=ch)
+    yg = np.stack([y[c // cfg["dim"], :, c % cfg["dim"]] for c in ch])
+    ey, eh = rel_err(yg, yr), rel_err(hl.reshape(-1)[ch], hlr)
+    note(f"    err y={ey:.3e} h_last={eh:.3e}")
+    assert ey <= TOL_F32 and eh <= TOL_F32
+    assert np.all(np.isfinite(y))
