@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""Benchmark of the selective scan on one MI355X.
+
+Workload: the long-sequence Mamba-2.8B-shaped layer (batch 1, d_inner 5120, d_state 16,
+seqlen 65536; bf16 x/delta/z, fp32 A/B/C/D/h0 and state; y and h_last fp32), synthetic
+seeded inputs already resident in HBM.  A step is one selective_scan_fwd call.
+
+Prints ONE JSON line.  `value` is the achieved algorithmic HBM bandwidth (every input read
+once and every output written once, the state never counted) in GB/s.
+
+  python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+  python bench.py --copy-calibration      # plain copy of a known size, for counter scaling
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+VALU_FP32_TFLOPS = 157.3        # MI355X fp32 vector, published (FMA = 2 flops)
+WORKLOAD_INDEX = 3              # the largest selective_scan_fwd configuration
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(cfg):
+    """Each input read once, each output written once (bytes)."""
+    b, L, d, n = cfg["batch"], cfg["seqlen"], cfg["dim"], cfg["dstate"]
+    es = 2 if cfg["io"] == "bf16" else 4
+    e = b * L * d
+    tot = e * es * 2                        # x, delta
+    tot += e * es if cfg["with_z"] else 0   # z
+    tot += e * 4                            # y
+    tot += 2 * b * L * n * 4                # B, C
+    tot += d * n * 4                        # A
+    tot += d * 4 if cfg["with_D"] else 0    # D
+    tot += b * d * n * 4 if cfg["h0"] else 0
+    tot += b * d * n * 4 if cfg["h_last"] else 0
+    return tot
+
+
+def algorithmic_alu_ops(cfg):
+    """Minimal fp32 ALU work of the recurrence, in VALU-op equivalents (a transcendental
+    counts 4: it issues at a quarter of the fp32 rate).  Per element and state: exp of
+    delta*A, delta*x*B (1 mul; delta*x shared), h update (1 fma), C*h accumulation (1 fma),
+    delta*A (1 mul).  Per element: delta*x (1 mul), D*x (1 fma), silu gate (exp, rcp, 4 ops)."""
+    e = cfg["batch"] * cfg["seqlen"] * cfg["dim"]
+    n = cfg["dstate"]
+    valu = n * 4 + 1 + (1 if cfg["with_D"] else 0) + (4 if cfg["with_z"] else 0)
+    trans = n + (2 if cfg["with_z"] else 0)
+    return e * (valu + 4 * trans)
+
+
+def cpu_baseline(cfg, inp, budget_s=12.0):
+    """The fp64 oracle (never tuned) on a bounded sample of channels of the same workload,
+    all host threads; scaled to GB/s of the workload's algorithmic bytes per element."""
+    import oracle
+    oracle.build(force=False)
+    cores = oracle.max_threads()
+    nch = cfg["batch"] * cfg["dim"]
+    args = (inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], inp["h0"])
+    k = min(nch, max(cores, 1) * 2)
+    t0 = time.perf_counter()
+    oracle.selective_scan_channels(*args, channels=np.arange(k, dtype=np.int64))
+    dt = time.perf_counter() - t0
+    k2 = int(min(nch, max(k, k * budget_s / max(dt, 1e-3))))
+    k2 = max(cores, (k2 // max(cores, 1)) * max(cores, 1)) if k2 >= cores else k2
+    ch = np.linspace(0, nch - 1, k2).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.selective_scan_channels(*args, channels=ch)
+    dt = time.perf_counter() - t0
+    elems = k2 * cfg["seqlen"]
+    bpe = algorithmic_bytes(cfg) / (cfg["batch"] * cfg["seqlen"] * cfg["dim"])
+    return {"value": round(elems * bpe / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{k2} of {nch} channels x {cfg['seqlen']} steps (all {cfg['dstate']} states), fp64, "
+                      f"{dt:.2f} s wall, {elems / dt:.4g} elements/s"}
+
+
+def copy_calibration(nbytes=1 << 30, reps=5):
+    """A plain device copy of a known size (for scaling FETCH_SIZE / WRITE_SIZE)."""
+    import torch
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_each_way": nbytes, "reps": reps}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE={world}): the scan is built "
+              "and measured on a single MI355X; the multi-GPU split is a design note, not a run.", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import torch
+    import selective_state_space_20_amd as sss
+    from selective_state_space_20_amd import inputs as gen
+
+    cfg, inp = gen.config_inputs(WORKLOAD_INDEX)
+    log(f"[bench] inputs generated for {cfg['name']}")
+    dev = torch.device("cuda:0")
+
+    def td(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    t = {k: td(v) for k, v in inp.items() if k != "io"}
+    b, L, d, n = cfg["batch"], cfg["seqlen"], cfg["dim"], cfg["dstate"]
+    y = torch.empty((b, L, d), dtype=torch.float32, device=dev)
+    hl = torch.empty((b, d, n), dtype=torch.float32, device=dev)
+    ws_bytes = sss.selective_scan_fwd_workspace_size(b, L, d, n, 0)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        sss.selective_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"], out=y,
+                               out_last=hl, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} done")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    per_call_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    mean_ms = float(np.mean(per_call_ms))
+    ms_per_step = wall * 1e3 / args.steps
+    log(f"[bench] {args.steps} steps: wall {ms_per_step:.4f} ms/step, event mean {mean_ms:.4f} ms, "
+        f"min {min(per_call_ms):.4f}, max {max(per_call_ms):.4f}")
+
+    nbytes = algorithmic_bytes(cfg)
+    elems = b * L * d
+    gbs_wall = nbytes / (ms_per_step * 1e-3) / 1e9
+    gbs_call = nbytes / (mean_ms * 1e-3) / 1e9
+    alu = algorithmic_alu_ops(cfg)
+    alu_tflops = 2.0 * alu / (mean_ms * 1e-3) / 1e12       # op-equivalents x 2 flops (FMA convention)
+    out = {
+        "metric": "selective-scan achieved HBM GB/s (% of peak) and B·L·D elements/s, 1 GPU",
+        "value": round(gbs_wall, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg["name"], "batch": b, "seqlen": L, "dim": d, "dstate": n, "io_dtype": cfg["io"],
+                   "z_gate": cfg["with_z"], "D_skip": cfg["with_D"], "h0": cfg["h0"], "h_last": cfg["h_last"],
+                   "algorithmic_bytes": nbytes, "elements": elems},
+        "elements_per_s": round(elems / (ms_per_step * 1e-3), 1),
+        "pct_hbm_peak": round(100.0 * gbs_wall / HBM_PEAK_GBS, 2),
+        "roofline": {
+            "bound": "alu",
+            "achieved": round(alu_tflops, 3),
+            "peak": VALU_FP32_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(alu_tflops / VALU_FP32_TFLOPS, 4),
+            "traffic": None,
+            "kernel": "selective_scan_fwd call (sel_scan_kernel + 2 bc_transpose_kernel)",
+            "call_ms_event_mean": round(mean_ms, 5),
+            "alu_work": "fp32 VALU-op equivalents x 2 per FMA-convention flop; transcendental = 4 ops",
+            "hbm": {"achieved": round(gbs_call, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(gbs_call / HBM_PEAK_GBS, 4)},
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle on a channel sample)")
+        out["cpu_baseline"] = cpu_baseline(cfg, inp)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -60,8 +60,8 @@ typedef enum {
   SSS_OK = 0,
   SSS_ERR_NULL_ARG = -1,    /* a required pointer is NULL                             */
   SSS_ERR_BAD_DIM = -2,     /* a dimension is < 1 or a size overflows                 */
-  SSS_ERR_UNSUPPORTED = -3, /* dstate outside 1..64, unknown dtype, or a pointer not
-                               16-byte aligned                                         */
+  SSS_ERR_UNSUPPORTED = -3, /* dstate not in {1,2,4,8,16,32,64}, unknown dtype, or a
+                               pointer not 16-byte aligned                             */
   SSS_ERR_WORKSPACE = -4,   /* workspace smaller than the size query (or NULL)        */
   SSS_ERR_ALIAS = -5,       /* an output overlaps an input or another output           */
   SSS_ERR_HIP = -6          /* no usable device, or a HIP launch/runtime error         */

@@ -79,7 +79,7 @@ const char* sss_status_string(int status) {
     case SSS_OK: return "SSS_OK";
     case SSS_ERR_NULL_ARG: return "SSS_ERR_NULL_ARG: a required pointer is NULL";
     case SSS_ERR_BAD_DIM: return "SSS_ERR_BAD_DIM: a dimension is < 1 or a size is too large";
-    case SSS_ERR_UNSUPPORTED: return "SSS_ERR_UNSUPPORTED: dstate outside 1..64, unknown dtype or misaligned pointer";
+    case SSS_ERR_UNSUPPORTED: return "SSS_ERR_UNSUPPORTED: dstate not in {1,2,4,8,16,32,64}, unknown dtype or misaligned pointer";
     case SSS_ERR_WORKSPACE: return "SSS_ERR_WORKSPACE: workspace missing or smaller than the size query";
     case SSS_ERR_ALIAS: return "SSS_ERR_ALIAS: an output overlaps an input, another output or the workspace";
     case SSS_ERR_HIP: return "SSS_ERR_HIP: no usable HIP device or a launch failed";
@@ -93,7 +93,7 @@ static int sel_dims_ok(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstat
   if (!mul_ok(batch, seqlen, &t) || !mul_ok(t, dim, &e) || !mul_ok(e, 4, &t)) return SSS_ERR_BAD_DIM;
   if (!mul_ok(batch, seqlen, &t) || !mul_ok(t, dstate, &e) || !mul_ok(e, 4, &t)) return SSS_ERR_BAD_DIM;
   if (batch * ((dim + 3) / 4) > (int64_t)1 << 30) return SSS_ERR_BAD_DIM;  // grid size
-  if (dstate > 64) return SSS_ERR_UNSUPPORTED;
+  if (dstate > 64 || (dstate & (dstate - 1)) != 0) return SSS_ERR_UNSUPPORTED;
   return SSS_OK;
 }
 
@@ -137,9 +137,9 @@ int selective_scan_fwd(const void* x, const void* delta, const float* A, const f
       if (overlap(workspace, wb, in_p[i], in_b[i])) return SSS_ERR_ALIAS;
   }
   if (env_int("SSS_LOG", 0))
-    std::fprintf(stderr, "[sss] selective_scan_fwd B=%lld L=%lld D=%lld N=%lld %s: k=%d wpb=%d segments=%d seg_len=%lld ws=%zu\n",
+    std::fprintf(stderr, "[sss] selective_scan_fwd B=%lld L=%lld D=%lld N=%lld %s: segments=%d seg_len=%lld ws=%zu\n",
                  (long long)batch, (long long)seqlen, (long long)dim, (long long)dstate,
-                 io_dtype == SSS_BF16 ? "bf16" : "f32", pl.k, pl.wpb, pl.segments, (long long)pl.seg_len, pl.ws_total);
+                 io_dtype == SSS_BF16 ? "bf16" : "f32", pl.segments, (long long)pl.seg_len, pl.ws_total);
   SelArgs a{};
   a.x = x;
   a.delta = delta;

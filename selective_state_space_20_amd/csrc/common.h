@@ -40,6 +40,35 @@ __device__ __forceinline__ void wave_scan_pairs(float& a, float& b) {
   scan_level<0x143, 0xC>(a, b);  // row_bcast:31 into rows 2, 3
 }
 
+// Same scan with the lane shift fused into the arithmetic (v_fmac/v_mul with a DPP source):
+// a lane whose source is outside the pattern, or whose row is masked off, is not written,
+// which leaves it composed with the identity.  Per level: b = a * b[src] + b, then
+// a = a[src] * a.  The s_nop 1 before each DPP instruction provides the two wait states a
+// DPP read of a VGPR written by the previous VALU instruction needs on gfx9.
+__device__ __forceinline__ void wave_scan_pairs_fused(float& a, float& b) {
+  asm volatile(
+      "s_nop 1\n\tv_fmac_f32_dpp %1, %1, %0 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\tv_mul_f32_dpp %0, %0, %0 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\tv_fmac_f32_dpp %1, %1, %0 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\tv_mul_f32_dpp %0, %0, %0 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\tv_fmac_f32_dpp %1, %1, %0 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\tv_mul_f32_dpp %0, %0, %0 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\tv_fmac_f32_dpp %1, %1, %0 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\tv_mul_f32_dpp %0, %0, %0 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\tv_fmac_f32_dpp %1, %1, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
+      "s_nop 1\n\tv_mul_f32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
+      "s_nop 1\n\tv_fmac_f32_dpp %1, %1, %0 row_bcast:31 row_mask:0xc bank_mask:0xf\n\t"
+      "s_nop 1\n\tv_mul_f32_dpp %0, %0, %0 row_bcast:31 row_mask:0xc bank_mask:0xf"
+      : "+v"(a), "+v"(b));
+}
+
+// Lane j receives v from lane j-1; lane 0 receives `first`.
+__device__ __forceinline__ float wave_shift_in(float v, float first) {
+  float r;
+  asm volatile("s_nop 1\n\tv_mov_b32_dpp %0, %1 wave_shr:1 row_mask:0xf bank_mask:0xf" : "=v"(r) : "v"(v), "0"(first));
+  return r;
+}
+
 // Wave-wide inclusive sum (lane order), then the total from lane 63.
 __device__ __forceinline__ float wave_sum(float v) {
   v += dpp_or<0x111, 0xF>(0.0f, v);

@@ -6,15 +6,11 @@
 
 namespace sss {
 
-// Launch plan of the selective scan (chosen on the host, see api.cpp).
+// Launch plan of the selective scan (chosen on the host, see selective_scan.hip).
 struct SelPlan {
-  int k;             // steps per lane (time sub-chunk held in registers): 8 or 16
-  int wpb;           // waves per workgroup = channels per workgroup
-  int segments;      // time segments S (S > 1 -> two-pass: segment states, then outputs)
-  int64_t seg_len;   // steps per segment, a multiple of 64*k
-  int64_t lpad;      // seqlen rounded up to 4 (row length of the transposed B/C)
-  int vec4;          // staging with 4-channel vectors (dim % 4 == 0 and wpb % 4 == 0)
-  size_t ws_bt, ws_ct, ws_state, ws_dsum, ws_total;  // workspace offsets / total bytes
+  int segments;      // time segments S (S > 1: segment states, carry, then outputs)
+  int64_t seg_len;   // steps per segment (multiple of the load batch)
+  size_t ws_state, ws_dsum, ws_carry, ws_total;  // workspace offsets / total bytes
 };
 
 struct SelArgs {
