@@ -87,11 +87,14 @@ const char* sss_status_string(int status) {
   }
 }
 
+constexpr int64_t kMaxSelDim = (int64_t)1 << 24;
+
 static int sel_dims_ok(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
   if (batch < 1 || seqlen < 1 || dim < 1 || dstate < 1) return SSS_ERR_BAD_DIM;
   int64_t e = 0, t = 0;
   if (!mul_ok(batch, seqlen, &t) || !mul_ok(t, dim, &e) || !mul_ok(e, 4, &t)) return SSS_ERR_BAD_DIM;
   if (!mul_ok(batch, seqlen, &t) || !mul_ok(t, dstate, &e) || !mul_ok(e, 4, &t)) return SSS_ERR_BAD_DIM;
+  if (dim > kMaxSelDim) return SSS_ERR_BAD_DIM;                              // 32-bit buffer offsets
   if (batch * ((dim + 3) / 4) > (int64_t)1 << 30) return SSS_ERR_BAD_DIM;  // grid size
   if (dstate > 64 || (dstate & (dstate - 1)) != 0) return SSS_ERR_UNSUPPORTED;
   return SSS_OK;
@@ -129,6 +132,10 @@ int selective_scan_fwd(const void* x, const void* delta, const float* A, const f
   const int cus = current_device_cus();
   if (cus <= 0) return SSS_ERR_HIP;
   const SelPlan pl = plan_selective(batch, seqlen, dim, dstate, cus);
+  // threads of the widest launch: 64 per channel group (padded to whole workgroups of 4)
+  // and segment; must fit a 1-D grid
+  const int64_t wg_groups = ((dim + 63) / 64 + 3) / 4 * 4;
+  if ((double)batch * (double)wg_groups * 64.0 * (double)pl.segments > 2147483647.0) return SSS_ERR_BAD_DIM;
   if (pl.ws_total > 0) {
     if (workspace == nullptr || workspace_bytes < pl.ws_total) return SSS_ERR_WORKSPACE;
     const int64_t wb = (int64_t)pl.ws_total;

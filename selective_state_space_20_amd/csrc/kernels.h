@@ -10,7 +10,7 @@ namespace sss {
 struct SelPlan {
   int segments;      // time segments S (S > 1: segment states, carry, then outputs)
   int64_t seg_len;   // steps per segment (multiple of the load batch)
-  size_t ws_state, ws_dsum, ws_carry, ws_total;  // workspace offsets / total bytes
+  size_t ws_state, ws_dsum, ws_total;  // workspace offsets / total bytes
 };
 
 struct SelArgs {

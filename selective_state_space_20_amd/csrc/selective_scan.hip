@@ -33,8 +33,14 @@
 
 namespace sss {
 
-constexpr int kStepsPerBatch = 4;  // time steps whose x/delta/z loads are issued together
+constexpr int kStepsPerBatch = 2;  // time steps whose x/delta/z loads are issued together
 constexpr int kMinWavesPerSimd = 4; // register budget: at least this many resident waves per SIMD
+constexpr int kStreamPolicy = 2;    // buffer cache policy of streamed x/delta/z/y: non-temporal
+
+// Raw buffer descriptor (gfx9 dword3) over 2^31-1 bytes from `base`.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7FFFFFFF, 0x00020000);
+}
 
 struct SelSeg {
   int64_t batch, L, D, seg_len;
@@ -55,7 +61,6 @@ __global__ __launch_bounds__(256, kMinWavesPerSimd) void sel_seq_kernel(const vo
                                                      const float* __restrict__ carry, float* __restrict__ y,
                                                      float* __restrict__ h_last, float* __restrict__ seg_state,
                                                      float* __restrict__ seg_dsum, SelSeg g) {
-  using IO = typename std::conditional<BF16, uint16_t, float>::type;
   // Workgroup = gpb waves on adjacent channel groups and the SAME time segment, so that the
   // scalar B_t/C_t rows one wave fetches are scalar-cache hits for the others.
   const int lane = threadIdx.x & 63;
@@ -64,14 +69,17 @@ __global__ __launch_bounds__(256, kMinWavesPerSimd) void sel_seq_kernel(const vo
   lid /= (uint32_t)g.nblk;
   const int64_t b = (int64_t)(lid % (uint32_t)g.batch);
   const int s = (int)(lid / (uint32_t)g.batch);
-  const int grp = min(blk * g.gpb + (int)(threadIdx.x >> 6), g.ngroups - 1);  // surplus waves mirror the last group
+  // wave index made provably wave-uniform, so that everything derived from it (row bases,
+  // buffer descriptors) lives in SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int grp = min(blk * g.gpb + wave, g.ngroups - 1);  // surplus waves mirror the last group
   const int64_t d0 = (int64_t)grp * 64;
   // Lanes past the last channel mirror channel D-1: same inputs, same state, same outputs,
   // so every load and store can stay unconditional (duplicate stores write equal values).
   const int64_t dc = min(d0 + lane, g.D - 1);
   const int loff = (int)(dc - d0);
   const int64_t tbeg = (int64_t)s * g.seg_len;
-  const int64_t len = min(tbeg + g.seg_len, g.L) - tbeg;
+  const int len = (int)(min(tbeg + g.seg_len, g.L) - tbeg);  // < 2^30 (plan)
   const int N = NS;
 
   float a2[NS], h[NS];
@@ -90,12 +98,18 @@ __global__ __launch_bounds__(256, kMinWavesPerSimd) void sel_seq_kernel(const vo
   constexpr bool has_z = PASS == 2 && HAS_Z;
   float dsum = 0.0f;
 
-  // wave-uniform row bases of this segment (rows are D elements apart)
+  // Buffer descriptors based at this wave's first row of the segment: per-step offsets are
+  // wave-uniform (SGPR soffset), the lane offset is a constant VGPR, so no per-load VALU
+  // address arithmetic is needed.  The host keeps seg_len * D * 4 below 2^31.
+  constexpr int ES = BF16 ? 2 : 4;
   const int64_t row0 = b * g.L + tbeg;
-  const IO* xr = reinterpret_cast<const IO*>(x) + row0 * g.D + d0;
-  const IO* dr = reinterpret_cast<const IO*>(delta) + row0 * g.D + d0;
-  const IO* zr = has_z ? reinterpret_cast<const IO*>(z) + row0 * g.D + d0 : nullptr;
-  float* yr = y + row0 * g.D + d0;
+  const int rstride = (int)(g.D * ES);  // bytes between consecutive steps
+  const uint32_t vo = (uint32_t)loff * ES;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc((const char*)x + (row0 * g.D + d0) * ES);
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc((const char*)delta + (row0 * g.D + d0) * ES);
+  const __amdgpu_buffer_rsrc_t rz = make_rsrc(has_z ? (const char*)z + (row0 * g.D + d0) * ES : (const char*)x);
+  const __amdgpu_buffer_rsrc_t ry = make_rsrc(PASS == 2 ? (const char*)(y + row0 * g.D + d0) : (const char*)x);
+  const int ystride = (int)(g.D * 4);
   const float* Br = Bm + row0 * N;
   const float* Cr = Cm + row0 * N;
 
@@ -103,19 +117,18 @@ __global__ __launch_bounds__(256, kMinWavesPerSimd) void sel_seq_kernel(const vo
   // raw loaded values (bf16 bits or fp32 bits) are widened only when used, so that the
   // loads of the next batch stay in flight while the current batch is computed
   uint32_t xq[2][U], dq[2][U], zq[2][U];
-  const uint32_t lo = (uint32_t)loff;
-  auto ld = [lo](const IO* row) -> uint32_t {
-    if (BF16) return (uint32_t)__builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(row) + lo);
-    return __builtin_bit_cast(uint32_t, __builtin_nontemporal_load(reinterpret_cast<const float*>(row) + lo));
+  auto ld = [vo](__amdgpu_buffer_rsrc_t r, int soff) -> uint32_t {
+    if (BF16) return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)vo, soff, kStreamPolicy);
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)vo, soff, kStreamPolicy);
   };
   auto wid = [](uint32_t v) -> float { return BF16 ? __builtin_bit_cast(float, v << 16) : __builtin_bit_cast(float, v); };
 #define SSS_LOAD_BATCH(SLOT, T0)                                                 \
   do {                                                                           \
     _Pragma("unroll") for (int i_ = 0; i_ < U; ++i_) {                           \
-      const int64_t t_ = min((int64_t)(T0) + i_, len - 1); /* clamped, unused */ \
-      xq[SLOT][i_] = ld(xr + t_ * g.D);                                          \
-      dq[SLOT][i_] = ld(dr + t_ * g.D);                                          \
-      if (has_z) zq[SLOT][i_] = ld(zr + t_ * g.D);                               \
+      const int t_ = min((T0) + i_, len - 1); /* clamped, unused */              \
+      xq[SLOT][i_] = ld(rx, t_ * rstride);                                       \
+      dq[SLOT][i_] = ld(rd, t_ * rstride);                                       \
+      if (has_z) zq[SLOT][i_] = ld(rz, t_ * rstride);                            \
     }                                                                            \
   } while (0)
 
@@ -123,8 +136,8 @@ __global__ __launch_bounds__(256, kMinWavesPerSimd) void sel_seq_kernel(const vo
   // wave-uniform and come through scalar loads
 #define SSS_STEP(SLOT, I, T)                                                     \
   do {                                                                           \
-    const float* Bt = Br + (int64_t)(T) * N;                                     \
-    const float* Ct = Cr + (int64_t)(T) * N;                                     \
+    const float* Bt = Br + (T) * N;                                              \
+    const float* Ct = Cr + (T) * N;                                              \
     const float xv = wid(xq[SLOT][I]), dl = wid(dq[SLOT][I]);                    \
     const float dx = dl * xv;                                                    \
     float y0 = Dd * xv, y1 = 0.0f;                                               \
@@ -141,12 +154,13 @@ __global__ __launch_bounds__(256, kMinWavesPerSimd) void sel_seq_kernel(const vo
     } else {                                                                     \
       float out = y0 + y1;                                                       \
       if (has_z) out *= silu(wid(zq[SLOT][I]));                                  \
-      __builtin_nontemporal_store(out, yr + (int64_t)(T) * g.D + lo);            \
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, out), ry, (int)(loff * 4), \
+                                            (T) * ystride, kStreamPolicy);       \
     }                                                                            \
   } while (0)
 
   SSS_LOAD_BATCH(0, 0);
-  int64_t t0 = 0;
+  int t0 = 0;
   // full blocks of 2U steps: straight-line code, no per-step branches
   for (; t0 + 2 * U <= len; t0 += 2 * U) {
     SSS_LOAD_BATCH(1, t0 + U);
@@ -176,11 +190,14 @@ __global__ __launch_bounds__(256, kMinWavesPerSimd) void sel_seq_kernel(const vo
 }
 
 // ------------------------------------------------------------------ carry between segments
-// One thread per (b, n, d): carry[0] = h0, carry[s+1] = exp2(A'*dsum_s) * carry[s] + state_s.
+// One thread per (b, n, d), in place over the segment states: slot s holds the end state
+// of segment s from zero on entry and the state entering segment s on exit,
+//   carry[0] = h0,  carry[s+1] = exp2(A' * dsum_s) * carry[s] + state_s.
+// Loads of a batch of segments are issued before the serial fma chain consumes them.
+constexpr int kCarryBatch = 8;
+
 __global__ __launch_bounds__(256) void sel_carry_kernel(const float* __restrict__ A, const float* __restrict__ h0,
-                                                        const float* __restrict__ seg_state,
-                                                        const float* __restrict__ seg_dsum, float* __restrict__ carry,
-                                                        SelSeg g) {
+                                                        float* slots, const float* __restrict__ seg_dsum, SelSeg g) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t per_b = (int64_t)g.N * g.D;
   if (idx >= g.batch * per_b) return;
@@ -189,12 +206,21 @@ __global__ __launch_bounds__(256) void sel_carry_kernel(const float* __restrict_
   const int64_t n = rem / g.D, d = rem - n * g.D;
   const float a2 = fmaxf(A[d * g.N + n] * kLog2e, -kFltMax);
   float h = h0 ? h0[(b * g.D + d) * g.N + n] : 0.0f;
-  for (int s = 0; s < g.S; ++s) {
-    const int64_t o = ((int64_t)s * g.batch + b) * per_b + rem;  // [s][b][n][d]
-    carry[o] = h;
-    if (s + 1 < g.S) {
-      const float ds = seg_dsum[((int64_t)s * g.batch + b) * g.D + d];
-      h = __builtin_fmaf(fast_exp2(a2 * ds), h, seg_state[o]);
+  const int64_t sstride = g.batch * per_b, dstride = g.batch * g.D;
+  float* slot = slots + b * per_b + rem;              // [s][b][n][d]
+  const float* dsp = seg_dsum + b * g.D + d;          // [s][b][d]
+  for (int s0 = 0; s0 < g.S; s0 += kCarryBatch) {
+    float st[kCarryBatch], ds[kCarryBatch];
+#pragma unroll
+    for (int i = 0; i < kCarryBatch; ++i) {
+      const bool live = s0 + i < g.S - 1;            // segment S-1 has no end state
+      st[i] = live ? slot[(int64_t)(s0 + i) * sstride] : 0.0f;
+      ds[i] = live ? dsp[(int64_t)(s0 + i) * dstride] : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < kCarryBatch; ++i) {
+      if (s0 + i < g.S) slot[(int64_t)(s0 + i) * sstride] = h;
+      h = __builtin_fmaf(fast_exp2(a2 * ds[i]), h, st[i]);
     }
   }
 }
@@ -205,29 +231,35 @@ static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 SelPlan plan_selective(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int num_cus) {
   SelPlan pl{};
   const int64_t groups = batch * ((dim + 63) / 64);
-  // aim at ~5 resident waves per SIMD (4 SIMDs per CU), one wave per (group, segment)
-  const int64_t target = (int64_t)std::max(num_cus, 1) * 4 * env_int("SSS_WAVES_PER_SIMD", 5);
-  int64_t S = std::max<int64_t>(1, (target + groups / 2) / groups);
-  const int64_t max_seg = std::max<int64_t>(1, seqlen / (4 * kStepsPerBatch));  // segments of >= 32 steps
-  S = std::min<int64_t>(S, max_seg);
-  S = std::min<int64_t>(S, 4096);
+  const int64_t simds = (int64_t)std::max(num_cus, 1) * 4;
+  // One wave per (channel group, segment).  Splitting time costs a second pass over the
+  // inputs, so it is only worth it when the channel groups alone leave most SIMDs idle;
+  // then aim at ~20 waves per SIMD: short segments keep every SIMD busy to the end.
+  int64_t S = 1;
+  if (groups < 2 * simds) {
+    const int64_t target = simds * env_int("SSS_WAVES_PER_SIMD", 20);
+    S = std::max<int64_t>(1, (target + groups / 2) / groups);
+    S = std::min<int64_t>(S, std::max<int64_t>(1, seqlen / 32));  // segments of >= 32 steps
+    S = std::min<int64_t>(S, 4096);
+  }
   const int forced = env_int("SSS_FORCE_SEGMENTS", 0);
   if (forced > 0) S = std::min<int64_t>(forced, (seqlen + kStepsPerBatch - 1) / kStepsPerBatch);
   if (S < 1) S = 1;
+  // buffer offsets inside one segment (seg_len rows of dim fp32 values) must stay below
+  // 2^30 bytes; dim <= 2^24 is checked by the caller, so max_len >= 16 steps
+  const int64_t max_len = std::max<int64_t>(kStepsPerBatch, ((int64_t)1 << 30) / (dim * 4) / kStepsPerBatch * kStepsPerBatch);
   int64_t seg_len = (seqlen + S - 1) / S;
   seg_len = (seg_len + kStepsPerBatch - 1) / kStepsPerBatch * kStepsPerBatch;
+  seg_len = std::min(seg_len, max_len);
   S = (seqlen + seg_len - 1) / seg_len;
   pl.segments = (int)S;
   pl.seg_len = seg_len;
-  size_t off = 0;
-  const size_t st = S > 1 ? (size_t)S * batch * dstate * dim * 4 : 0;
-  pl.ws_state = off;
-  off = align_up(off + st, 256);
-  pl.ws_dsum = off;
-  off = align_up(off + (S > 1 ? (size_t)S * batch * dim * 4 : 0), 256);
-  pl.ws_carry = off;
-  off = align_up(off + st, 256);
-  pl.ws_total = off;
+  // workspace: segment states / entering states [S][batch][dstate][dim], segment sums of
+  // delta [S][batch][dim]
+  pl.ws_state = 0;
+  pl.ws_dsum = align_up(S > 1 ? (size_t)S * batch * dstate * dim * 4 : 0, 256);
+  pl.ws_total = align_up(pl.ws_dsum + (S > 1 ? (size_t)S * batch * dim * 4 : 0), 256);
+  if (S == 1) pl.ws_dsum = pl.ws_total = 0;
   return pl;
 }
 
@@ -241,12 +273,11 @@ static hipError_t run_selective(const SelArgs& a, const SelPlan& pl, hipStream_t
   g.N = NS;
   g.S = pl.segments;
   g.ngroups = (int)((a.dim + 63) / 64);
-  g.gpb = std::min(4, g.ngroups);
+  g.gpb = std::min(2, g.ngroups);
   g.nblk = (g.ngroups + g.gpb - 1) / g.gpb;
   unsigned char* ws = static_cast<unsigned char*>(a.workspace);
   float* st = pl.segments > 1 ? reinterpret_cast<float*>(ws + pl.ws_state) : nullptr;
   float* ds = pl.segments > 1 ? reinterpret_cast<float*>(ws + pl.ws_dsum) : nullptr;
-  float* cr = pl.segments > 1 ? reinterpret_cast<float*>(ws + pl.ws_carry) : nullptr;
   const int64_t per_seg = (int64_t)g.nblk * g.batch;
   const unsigned nthr_wg = 64u * (unsigned)g.gpb;
   if (pl.segments > 1) {
@@ -256,17 +287,19 @@ static hipError_t run_selective(const SelArgs& a, const SelPlan& pl, hipStream_t
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t nthr = g.batch * (int64_t)NS * g.D;
-    hipLaunchKernelGGL(sel_carry_kernel, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, stream, a.A, a.h0,
-                       (const float*)st, (const float*)ds, cr, g);
+    hipLaunchKernelGGL(sel_carry_kernel, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, stream, a.A, a.h0, st,
+                       (const float*)ds, g);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (a.z != nullptr)
     hipLaunchKernelGGL((sel_seq_kernel<NS, BF16, 2, true>), dim3((unsigned)(per_seg * pl.segments)), dim3(nthr_wg), 0,
-                       stream, a.x, a.delta, a.A, a.B, a.C, a.Dsk, a.z, a.h0, (const float*)cr, a.y, a.h_last, st, ds, g);
+                       stream, a.x, a.delta, a.A, a.B, a.C, a.Dsk, a.z, a.h0, (const float*)st, a.y, a.h_last,
+                       (float*)nullptr, (float*)nullptr, g);
   else
     hipLaunchKernelGGL((sel_seq_kernel<NS, BF16, 2, false>), dim3((unsigned)(per_seg * pl.segments)), dim3(nthr_wg), 0,
-                       stream, a.x, a.delta, a.A, a.B, a.C, a.Dsk, a.z, a.h0, (const float*)cr, a.y, a.h_last, st, ds, g);
+                       stream, a.x, a.delta, a.A, a.B, a.C, a.Dsk, a.z, a.h0, (const float*)st, a.y, a.h_last,
+                       (float*)nullptr, (float*)nullptr, g);
   return hipGetLastError();
 }
 

@@ -74,7 +74,7 @@ def test_elementwise_null_required(name):
 
 
 @pytest.mark.parametrize("kw", [dict(batch=0), dict(seqlen=0), dict(dim=-1), dict(dstate=0),
-                                dict(batch=1 << 40, seqlen=1 << 30)])
+                                dict(batch=1 << 40, seqlen=1 << 30), dict(dim=(1 << 24) + 1, seqlen=4)])
 def test_selective_bad_dims(kw):
     assert sel(**kw) == BAD_DIM
 
