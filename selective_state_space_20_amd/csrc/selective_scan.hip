@@ -34,7 +34,9 @@
 namespace sss {
 
 constexpr int kStepsPerBatch = 2;  // time steps whose x/delta/z loads are issued together
-constexpr int kMinWavesPerSimd = 4; // register budget: at least this many resident waves per SIMD
+// register budget: at least this many resident waves per SIMD (512 VGPRs / waves each);
+// 32 and 64 states need the larger budgets to stay spill-free
+constexpr int min_waves_per_simd(int ns) { return ns >= 64 ? 1 : ns >= 32 ? 3 : 4; }
 constexpr int kStreamPolicy = 2;    // buffer cache policy of streamed x/delta/z/y: non-temporal
 
 // Raw buffer descriptor (gfx9 dword3) over 2^31-1 bytes from `base`.
@@ -54,7 +56,7 @@ struct SelSeg {
 // PASS 2 (segments 0..S-1): y, and h_last from the last segment; entering state from
 //         carry[s][b][n][d] (S > 1) or h0 (S == 1).
 template <int NS, bool BF16, int PASS, bool HAS_Z>
-__global__ __launch_bounds__(256, kMinWavesPerSimd) void sel_seq_kernel(const void* __restrict__ x, const void* __restrict__ delta,
+__global__ __launch_bounds__(256, min_waves_per_simd(NS)) void sel_seq_kernel(const void* __restrict__ x, const void* __restrict__ delta,
                                                      const float* __restrict__ A, const float* __restrict__ Bm,
                                                      const float* __restrict__ Cm, const float* __restrict__ Dsk,
                                                      const void* __restrict__ z, const float* __restrict__ h0,
@@ -246,8 +248,10 @@ SelPlan plan_selective(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstat
   if (forced > 0) S = std::min<int64_t>(forced, (seqlen + kStepsPerBatch - 1) / kStepsPerBatch);
   if (S < 1) S = 1;
   // buffer offsets inside one segment (seg_len rows of dim fp32 values) must stay below
-  // 2^30 bytes; dim <= 2^24 is checked by the caller, so max_len >= 16 steps
-  const int64_t max_len = std::max<int64_t>(kStepsPerBatch, ((int64_t)1 << 30) / (dim * 4) / kStepsPerBatch * kStepsPerBatch);
+  // 2^30 bytes; dim <= 2^24 is checked by the caller, so max_len >= 16 steps (the B/C row
+  // pointers advance by dstate floats per step, also kept below 2^30 bytes)
+  const int64_t row_bytes = std::max(dim, dstate) * 4;
+  const int64_t max_len = std::max<int64_t>(kStepsPerBatch, ((int64_t)1 << 30) / row_bytes / kStepsPerBatch * kStepsPerBatch);
   int64_t seg_len = (seqlen + S - 1) / S;
   seg_len = (seg_len + kStepsPerBatch - 1) / kStepsPerBatch * kStepsPerBatch;
   seg_len = std::min(seg_len, max_len);
