@@ -9,6 +9,7 @@ Prints ONE JSON line.  `value` is the achieved algorithmic HBM bandwidth (every 
 once and every output written once, the state never counted) in GB/s.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+  python bench.py --workload 4            # another configuration (0..4); the default is 3
   python bench.py --copy-calibration      # plain copy of a known size, for counter scaling
 """
 from __future__ import annotations
@@ -51,6 +52,10 @@ def log(msg):
 
 def algorithmic_bytes(cfg):
     """Each input read once, each output written once (bytes)."""
+    if cfg["api"] == "elementwise":
+        e = cfg["batch"] * cfg["seqlen"] * cfg["dim"]
+        hb = cfg["batch"] * cfg["dim"] * 4
+        return e * 4 * 5 + (hb if cfg["h0"] else 0) + (hb if cfg.get("h_last", False) else 0)   # x, A, B, C in; y out
     b, L, d, n = cfg["batch"], cfg["seqlen"], cfg["dim"], cfg["dstate"]
     es = 2 if cfg["io"] == "bf16" else 4
     e = b * L * d
@@ -61,7 +66,7 @@ def algorithmic_bytes(cfg):
     tot += d * n * 4                        # A
     tot += d * 4 if cfg["with_D"] else 0    # D
     tot += b * d * n * 4 if cfg["h0"] else 0
-    tot += b * d * n * 4 if cfg["h_last"] else 0
+    tot += b * d * n * 4 if cfg.get("h_last", False) else 0
     return tot
 
 
@@ -71,6 +76,8 @@ def algorithmic_alu_ops(cfg):
     delta*A, delta*x*B (1 mul; delta*x shared), h update (1 fma), C*h accumulation (1 fma),
     delta*A (1 mul).  Per element: delta*x (1 mul), D*x (1 fma), silu gate (exp, rcp, 4 ops)."""
     e = cfg["batch"] * cfg["seqlen"] * cfg["dim"]
+    if cfg["api"] == "elementwise":
+        return e * 2                        # B*x (1 mul), h update (1 fma); C*h (1 mul) -> ~2-3
     n = cfg["dstate"]
     valu = n * 4 + 1 + (1 if cfg["with_D"] else 0) + (4 if cfg["with_z"] else 0)
     trans = n + (2 if cfg["with_z"] else 0)
@@ -101,21 +108,26 @@ def cpu_baseline(cfg, inp, budget_s=12.0):
     oracle.build(force=False)
     cores = oracle.max_threads()
     nch = cfg["batch"] * cfg["dim"]
-    args = (inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], inp["h0"])
+    if cfg["api"] == "elementwise":
+        args = (inp["x"], inp["A"], inp["B"], inp["C"], inp["h0"])
+        run = oracle.elementwise_scan_channels
+    else:
+        args = (inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], inp["h0"])
+        run = oracle.selective_scan_channels
     k = min(nch, max(cores, 1) * 2)
     t0 = time.perf_counter()
-    oracle.selective_scan_channels(*args, channels=np.arange(k, dtype=np.int64))
+    run(*args, channels=np.arange(k, dtype=np.int64))
     dt = time.perf_counter() - t0
     k2 = int(min(nch, max(k, k * budget_s / max(dt, 1e-3))))
     k2 = max(cores, (k2 // max(cores, 1)) * max(cores, 1)) if k2 >= cores else k2
     ch = np.linspace(0, nch - 1, k2).astype(np.int64)
     t0 = time.perf_counter()
-    oracle.selective_scan_channels(*args, channels=ch)
+    run(*args, channels=ch)
     dt = time.perf_counter() - t0
     elems = k2 * cfg["seqlen"]
     bpe = algorithmic_bytes(cfg) / (cfg["batch"] * cfg["seqlen"] * cfg["dim"])
     return {"value": round(elems * bpe / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"{k2} of {nch} channels x {cfg['seqlen']} steps (all {cfg['dstate']} states), fp64, "
+            "sample": f"{k2} of {nch} channels x {cfg['seqlen']} steps (all {cfg.get('dstate') or 1} states), fp64, "
                       f"{dt:.2f} s wall, {elems / dt:.4g} elements/s"}
 
 
@@ -137,6 +149,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--workload", type=int, default=WORKLOAD_INDEX, help="configuration index 0..4")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -151,7 +164,8 @@ def main():
     import selective_state_space_20_amd as sss
     from selective_state_space_20_amd import inputs as gen
 
-    cfg, inp = gen.config_inputs(WORKLOAD_INDEX)
+    cfg, inp = gen.config_inputs(args.workload)
+    selective = cfg["api"] == "selective"
     log(f"[bench] inputs generated for {cfg['name']}")
     dev = torch.device("cuda:0")
 
@@ -163,16 +177,25 @@ def main():
         return torch.from_numpy(a).to(dev)
 
     t = {k: td(v) for k, v in inp.items() if k != "io"}
-    b, L, d, n = cfg["batch"], cfg["seqlen"], cfg["dim"], cfg["dstate"]
+    b, L, d = cfg["batch"], cfg["seqlen"], cfg["dim"]
+    n = cfg["dstate"] if selective else 1
     y = torch.empty((b, L, d), dtype=torch.float32, device=dev)
-    hl = torch.empty((b, d, n), dtype=torch.float32, device=dev)
-    ws_bytes = sss.selective_scan_fwd_workspace_size(b, L, d, n, 0)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
+    if selective:
+        hl = torch.empty((b, d, n), dtype=torch.float32, device=dev)
+        ws_bytes = sss.selective_scan_fwd_workspace_size(b, L, d, n, 0)
+    else:
+        hl = torch.empty((b, d), dtype=torch.float32, device=dev)
+        ws_bytes = sss.elementwise_scan_workspace_size(b, L, d, 0)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 
     def step():
-        sss.selective_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"], out=y,
-                               out_last=hl, workspace=ws)
+        if selective:
+            sss.selective_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"], out=y,
+                                   out_last=hl if cfg.get("h_last", False) else None, workspace=ws)
+        else:
+            sss.elementwise_scan(t["x"], t["A"], t["B"], t["C"], t["h0"], out=y,
+                                 out_last=hl if cfg.get("h_last", False) else None, workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -199,6 +222,26 @@ def main():
     gbs_call = nbytes / (mean_ms * 1e-3) / 1e9
     alu = algorithmic_alu_ops(cfg)
     alu_tflops = 2.0 * alu / (mean_ms * 1e-3) / 1e12       # op-equivalents x 2 flops (FMA convention)
+    hbm = {"achieved": round(gbs_call, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs_call / HBM_PEAK_GBS, 4)}
+    if selective:
+        roofline = {
+            "bound": "alu",
+            "achieved": round(alu_tflops, 3),
+            "peak": VALU_FP32_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(alu_tflops / VALU_FP32_TFLOPS, 4),
+            "traffic": measured_traffic() if args.workload == WORKLOAD_INDEX else None,
+            "kernel": "one selective_scan_fwd call: sel_seq_kernel pass 1 + sel_carry_kernel + sel_seq_kernel pass 2",
+            "call_ms_event_mean": round(mean_ms, 5),
+            "alu_work": "method's minimal fp32 work per call in VALU-op equivalents (transcendental = 4), "
+                        "x2 flops per op",
+            "alu_ops_per_call": alu,
+            "source_digest": kernel_source_digest(),
+            "hbm": hbm,
+        }
+    else:
+        roofline = dict(hbm, bound="hbm", traffic=None, call_ms_event_mean=round(mean_ms, 5),
+                        kernel="one elementwise_scan call: ew_scan_kernel pass 1 (if split) + pass 2")
     out = {
         "metric": "selective-scan achieved HBM GB/s (% of peak) and B·L·D elements/s, 1 GPU",
         "value": round(gbs_wall, 2),
@@ -212,27 +255,13 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": cfg["name"], "batch": b, "seqlen": L, "dim": d, "dstate": n, "io_dtype": cfg["io"],
-                   "z_gate": cfg["with_z"], "D_skip": cfg["with_D"], "h0": cfg["h0"], "h_last": cfg["h_last"],
+        "config": {"workload": cfg["name"], "batch": b, "seqlen": L, "dim": d, "dstate": n if selective else None,
+                   "io_dtype": cfg.get("io", "f32"), "z_gate": cfg.get("with_z", False),
+                   "D_skip": cfg.get("with_D", False), "h0": cfg["h0"], "h_last": cfg.get("h_last", False),
                    "algorithmic_bytes": nbytes, "elements": elems},
         "elements_per_s": round(elems / (ms_per_step * 1e-3), 1),
         "pct_hbm_peak": round(100.0 * gbs_wall / HBM_PEAK_GBS, 2),
-        "roofline": {
-            "bound": "alu",
-            "achieved": round(alu_tflops, 3),
-            "peak": VALU_FP32_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(alu_tflops / VALU_FP32_TFLOPS, 4),
-            "traffic": measured_traffic(),
-            "kernel": "one selective_scan_fwd call: sel_seq_kernel pass 1 + sel_carry_kernel + sel_seq_kernel pass 2",
-            "call_ms_event_mean": round(mean_ms, 5),
-            "alu_work": "method's minimal fp32 work per call in VALU-op equivalents (transcendental = 4), "
-                        "x2 flops per op",
-            "alu_ops_per_call": alu,
-            "source_digest": kernel_source_digest(),
-            "hbm": {"achieved": round(gbs_call, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(gbs_call / HBM_PEAK_GBS, 4)},
-        },
+        "roofline": roofline,
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle on a channel sample)")

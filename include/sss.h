@@ -59,8 +59,7 @@ typedef enum { SSS_F32 = 0, SSS_BF16 = 1 } sss_dtype;
 typedef enum {
   SSS_OK = 0,
   SSS_ERR_NULL_ARG = -1,    /* a required pointer is NULL                             */
-  SSS_ERR_BAD_DIM = -2,     /* a dimension is < 1, a size overflows, or (selective
-                               scan) dim > 2^24                                        */
+  SSS_ERR_BAD_DIM = -2,     /* a dimension is < 1, a size overflows, or dim > 2^24    */
   SSS_ERR_UNSUPPORTED = -3, /* dstate not in {1,2,4,8,16,32,64}, unknown dtype, or a
                                pointer not 16-byte aligned                             */
   SSS_ERR_WORKSPACE = -4,   /* workspace smaller than the size query (or NULL)        */

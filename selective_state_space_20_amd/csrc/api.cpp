@@ -87,7 +87,7 @@ const char* sss_status_string(int status) {
   }
 }
 
-constexpr int64_t kMaxSelDim = (int64_t)1 << 24;
+constexpr int64_t kMaxSelDim = (int64_t)1 << 24;  // largest dim of either call
 
 static int sel_dims_ok(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
   if (batch < 1 || seqlen < 1 || dim < 1 || dstate < 1) return SSS_ERR_BAD_DIM;
@@ -172,7 +172,8 @@ static int ew_dims_ok(int64_t batch, int64_t seqlen, int64_t dim) {
   if (batch < 1 || seqlen < 1 || dim < 1) return SSS_ERR_BAD_DIM;
   int64_t e = 0, t = 0;
   if (!mul_ok(batch, seqlen, &t) || !mul_ok(t, dim, &e) || !mul_ok(e, 4, &t)) return SSS_ERR_BAD_DIM;
-  if ((batch * dim + 63) / 64 > (int64_t)1 << 30) return SSS_ERR_BAD_DIM;
+  if (dim > kMaxSelDim) return SSS_ERR_BAD_DIM;                     // 32-bit buffer offsets
+  if (batch * ((dim + 63) / 64) > (int64_t)1 << 30) return SSS_ERR_BAD_DIM;
   return SSS_OK;
 }
 
@@ -203,6 +204,8 @@ int elementwise_scan(const float* x, const float* A, const float* B, const float
   const int cus = current_device_cus();
   if (cus <= 0) return SSS_ERR_HIP;
   const EwPlan pl = plan_elementwise(batch, seqlen, dim, cus);
+  // one wave per (batch, 64-channel group, segment) must fit a 1-D grid
+  if ((double)batch * (double)((dim + 63) / 64) * (double)pl.segments > 2147483647.0 / 64) return SSS_ERR_BAD_DIM;
   if (pl.ws_total > 0) {
     if (workspace == nullptr || workspace_bytes < pl.ws_total) return SSS_ERR_WORKSPACE;
     const int64_t wb = (int64_t)pl.ws_total;
