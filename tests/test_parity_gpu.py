@@ -172,48 +172,35 @@ def test_config2_selective_bf16_full(oracle_lib):
     _check_sel(oracle_lib, inp, cfg["name"])
 
 
-def _sample_channels(nch, k, seed):
-    rng = np.random.default_rng(seed)
-    pick = set([0, nch - 1, nch // 2, 1, nch - 2])
-    pick |= set(rng.choice(nch, size=k, replace=False).tolist())
-    return np.array(sorted(pick), dtype=np.int64)
-
-
 @pytest.mark.timeout(600)
-def test_config3_selective_long_sampled(oracle_lib):
-    """Full-size long-sequence layer (B=1, D=5120, N=16, L=65536, bf16): every output finite;
-    sampled channels (ends, middle, random) against the oracle over the whole sequence."""
+def test_config3_selective_long_full(oracle_lib):
+    """Full-size long-sequence layer (B=1, D=5120, N=16, L=65536, bf16) in the launch
+    configuration the benchmark times: every output and the final state against the oracle
+    (all channels, all steps; the oracle runs the whole layer on the host threads)."""
     cfg, inp = gen.config_inputs(3)
     note(f"[selective] {cfg['name']} inputs generated")
     y, hl = run_selective(inp)
     note("    GPU done")
     assert np.all(np.isfinite(y)) and np.all(np.isfinite(hl))
-    ch = _sample_channels(cfg["dim"], 24, 3)
-    note(f"[selective] {cfg['name']} sampled channels {ch.tolist()}")
-    yr, hlr = oracle_lib.selective_scan_channels(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"],
-                                                 inp["z"], inp["h0"], channels=ch)
-    yg = y[0][:, ch].T
-    hg = hl[0][ch]
-    ey, eh = rel_err(yg, yr), rel_err(hg, hlr)
+    yr, hlr = oracle_lib.selective_scan(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                                        inp["h0"])
+    note("    oracle done")
+    ey, eh = rel_err(y, yr), rel_err(hl, hlr)
     note(f"    err y={ey:.3e} h_last={eh:.3e}")
     assert ey <= TOL_BF16 and eh <= TOL_BF16
 
 
 @pytest.mark.timeout(900)
-def test_config4_elementwise_large_sampled(oracle_lib):
-    """Full-size elementwise scan (8 x 32768 x 4096, fp32): finite everywhere, sampled
-    channels against the oracle over the whole sequence, A = 0 identity on a slab."""
+def test_config4_elementwise_large_full(oracle_lib):
+    """Full-size elementwise scan (8 x 32768 x 4096, fp32): every output against the oracle,
+    which runs the whole scan on the host threads."""
     cfg, inp = gen.config_inputs(4)
     note(f"[elementwise] {cfg['name']} inputs generated")
     y, hl = run_elementwise(inp)
     note("    GPU done")
-    assert np.all(np.isfinite(hl))
-    nch = cfg["batch"] * cfg["dim"]
-    ch = _sample_channels(nch, 24, 4)
-    note(f"[elementwise] {cfg['name']} sampled channels {ch.tolist()}")
-    yr, hlr = oracle_lib.elementwise_scan_channels(inp["x"], inp["A"], inp["B"], inp["C"], inp["h0"], channels=ch)
-    yg = np.stack([y[c // cfg["dim"], :, c % cfg["dim"]] for c in ch])
-    ey, eh = rel_err(yg, yr), rel_err(hl.reshape(-1)[ch], hlr)
+    assert np.all(np.isfinite(y)) and np.all(np.isfinite(hl))
+    yr, hlr = oracle_lib.elementwise_scan(inp["x"], inp["A"], inp["B"], inp["C"], inp["h0"])
+    note("    oracle done")
+    ey, eh = rel_err(y, yr), rel_err(hl, hlr)
     note(f"    err y={ey:.3e} h_last={eh:.3e}")
     assert ey <= TOL_F32 and eh <= TOL_F32
-    assert np.all(np.isfinite(y))
