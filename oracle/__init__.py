@@ -58,7 +58,9 @@ def _load():
         lib.oracle_elementwise_scan.argtypes = [vp] * 7 + [i64] * 3 + [i32]
         lib.oracle_elementwise_scan_channels.argtypes = [vp] * 5 + [vp, i64, vp, vp] + [i64] * 3 + [i32]
         lib.oracle_elementwise_scan_chunked.argtypes = [vp] * 7 + [i64] * 4 + [i32]
+        lib.oracle_selective_state_update.argtypes = [vp] * 10 + [i64] * 3 + [i32] * 2
         for f in ("oracle_selective_scan", "oracle_selective_scan_channels", "oracle_selective_scan_chunked",
+                  "oracle_selective_state_update",
                   "oracle_elementwise_scan", "oracle_elementwise_scan_channels",
                   "oracle_elementwise_scan_chunked", "oracle_max_threads"):
             getattr(lib, f).restype = ctypes.c_int
@@ -148,6 +150,23 @@ def selective_scan_chunked(x, delta, A, B, C, D=None, z=None, h0=None, *, chunk,
                                                int(chunk), nthreads)
     _check(rc)
     return y, hl
+
+
+def selective_state_update(x, delta, A, B, C, D=None, z=None, state=None, *, nthreads=0):
+    """One decode step.  x, delta, z: (Bt, Dm); A: (Dm, N); B, C: (Bt, N); D: (Dm,);
+    state: (Bt, Dm, N) float32.  Returns (y (Bt, Dm) float64, new state (Bt, Dm, N) float64)."""
+    x, delta, z = _io(x), _io(delta), _io(z)
+    if delta.dtype != x.dtype or (z is not None and z.dtype != x.dtype):
+        raise TypeError("x, delta and z must share one dtype")
+    A, B, C, D, state = _f32(A), _f32(B), _f32(C), _f32(D), _f32(state)
+    bt, dm = x.shape
+    n = A.shape[1]
+    y = np.empty((bt, dm), dtype=np.float64)
+    st = np.empty((bt, dm, n), dtype=np.float64)
+    rc = _load().oracle_selective_state_update(_p(x), _p(delta), _p(A), _p(B), _p(C), _p(D), _p(z), _p(state),
+                                               _p(y), _p(st), bt, dm, n, _io_code(x), nthreads)
+    _check(rc)
+    return y, st
 
 
 def elementwise_scan(x, A, B, C, h0=None, *, return_last=True, nthreads=0):

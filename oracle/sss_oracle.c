@@ -171,6 +171,45 @@ int oracle_selective_scan_channels(const void* x, const void* delta, const float
 }
 
 /*
+ * One recurrent-inference step of the selective form -- [P1] "Selective Scan thay doi
+ * inference chuoi dai nhu the nao?" (generation carries only the state from token to
+ * token) with the update and readout of "Tai sao ..." / "Selection ...":
+ *   for each (b, d, n): h = exp(Delta[b,d] * A[d,n]) * state[b,d,n] + Delta[b,d] * B[b,n] * x[b,d]
+ *   y[b,d] = (sum_n C[b,n] * h[b,d,n] + D[d] * x[b,d]) * silu(z[b,d])   (D, z optional)
+ * Layouts: x, delta, z (B, D); B, C (B, N); A (D, N); D (D); state (B, D, N) fp32 in;
+ * y (B, D) and state_out (B, D, N) in double.
+ */
+int oracle_selective_state_update(const void* x, const void* delta, const float* A, const float* Bm,
+                                  const float* Cm, const float* Dsk, const void* z, const float* state,
+                                  double* y, double* state_out, int64_t batch, int64_t Dm, int64_t N, int dtype,
+                                  int nthreads) {
+  if (!x || !delta || !A || !Bm || !Cm || !state || !y || !state_out) return OR_ERR_ARG;
+  if (batch < 1 || Dm < 1 || N < 1 || N > 4096) return OR_ERR_ARG;
+  if (dtype != OR_F32 && dtype != OR_BF16) return OR_ERR_ARG;
+  set_threads(nthreads);
+  int64_t nch = batch * Dm;
+#pragma omp parallel for schedule(static)
+  for (int64_t c = 0; c < nch; ++c) {
+    int64_t b = c / Dm, d = c % Dm;
+    double xv = load_val(x, c, dtype);
+    double dv = load_val(delta, c, dtype);
+    double acc = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+      double h = exp(dv * (double)A[d * N + n]) * (double)state[c * N + n] + dv * (double)Bm[b * N + n] * xv;
+      state_out[c * N + n] = h;
+      acc += (double)Cm[b * N + n] * h;
+    }
+    if (Dsk) acc += (double)Dsk[d] * xv;
+    if (z) {
+      double zv = load_val(z, c, dtype);
+      acc *= zv / (1.0 + exp(-zv));
+    }
+    y[c] = acc;
+  }
+  return OR_OK;
+}
+
+/*
  * Elementwise form, one channel -- [P3] "Reference solution":
  *   h = h0[b,d] (or 0); for t: h = A_t*h + B_t*x_t; y_t = C_t*h.
  * All of x, A, B, C are (B, L, D) fp32; h0, h_last (B, D).

@@ -44,6 +44,11 @@ MUTANTS = {
     "compose_wrong_order": ("  r.b = cur.a * prefix.b + cur.b;", "  r.b = prefix.a * cur.b + prefix.b;"),
     "zoh_without_A_division": ("(a != 0.0 ? expm1(dt * a) / a : dt) * (double)Bt[n]",
                                "(a != 0.0 ? expm1(dt * a) : dt) * (double)Bt[n]"),
+    "update_reads_old_state": ("      acc += (double)Cm[b * N + n] * h;",
+                               "      acc += (double)Cm[b * N + n] * (double)state[c * N + n];"),
+    "update_B_of_batch_0": ("dv * (double)Bm[b * N + n] * xv;", "dv * (double)Bm[n] * xv;"),
+    "update_decay_without_delta": ("double h = exp(dv * (double)A[d * N + n])", "double h = exp((double)A[d * N + n])"),
+    "update_dropped_skip": ("    if (Dsk) acc += (double)Dsk[d] * xv;", "    (void)Dsk;"),
 }
 
 
@@ -61,6 +66,8 @@ def _pin_calls():
         elif name == "test_M5_brute_force_unrolled":
             for io in ("f32", "bf16"):
                 calls.append((name + io, lambda o, fn=fn, io=io: fn(o, io, True, True, True)))
+        elif name == "test_U1_decode_step_is_one_step_of_the_scan":
+            calls.append((name, lambda o, fn=fn: fn(o, "f32", True, True)))
     return calls
 
 

@@ -380,3 +380,58 @@ def test_bf16_rounding_is_nearest_even():
     back = gen.bf16_bits_to_f32(bits)
     assert back[0] == 1.0 and back[1] == 1.0 and back[2] == 1.0 + 2 ** -6 and back[3] == -2.5
     assert abs(back[4] - 3.0e-3) <= 2 ** -8 * 3.0e-3   # half an ulp (7 stored mantissa bits)
+
+
+# ---------------------------------------------------------------- single-step decode update
+def _decode_inputs(bt, dm, n, io, with_D, with_z, seed):
+    rng = np.random.default_rng(seed)
+    inp = gen.selective_inputs(bt, 1, dm, n, io=io, with_D=with_D, with_z=with_z, h0=True, h0_std=1.0, seed=seed)
+    x, dl = inp["x"][:, 0], inp["delta"][:, 0]
+    z = inp["z"][:, 0] if inp["z"] is not None else None
+    state = rng.standard_normal((bt, dm, n)).astype(np.float32)
+    return inp, x, dl, z, state
+
+
+@pytest.mark.parametrize("io,with_D,with_z", [("f32", True, True), ("bf16", True, True), ("f32", False, False)])
+def test_U1_decode_step_is_one_step_of_the_scan(oracle_lib, io, with_D, with_z):
+    """P1 'Selective Scan thay doi inference ...': a generated token advances the carried
+    state by exactly one step of the recurrence, so the decode update equals the (pinned)
+    scan over a length-1 sequence started from that state, for y and the new state."""
+    inp, x, dl, z, state = _decode_inputs(3, 7, 8, io, with_D, with_z, seed=81)
+    y, st = oracle_lib.selective_state_update(x, dl, inp["A"], inp["B"][:, 0], inp["C"][:, 0], inp["D"], z, state)
+    yr, hr = oracle_lib.selective_scan(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], state)
+    assert rel_err(y, yr[:, 0]) < 1e-14 and rel_err(st, hr) < 1e-14
+
+
+def test_U2_decode_chain_reproduces_the_scan(oracle_lib):
+    """Twenty decode steps, the fp32 state handed from one to the next, reproduce the scan
+    over those twenty steps (up to the fp32 rounding of the carried state)."""
+    bt, L, dm, n = 2, 20, 5, 16
+    inp = gen.selective_inputs(bt, L, dm, n, io="f32", with_D=True, with_z=True, h0=True, h0_std=1.0, seed=82)
+    yr, hr = oracle_lib.selective_scan(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                                       inp["h0"])
+    state = inp["h0"].copy()
+    ys = []
+    for t in range(L):
+        y, st = oracle_lib.selective_state_update(inp["x"][:, t], inp["delta"][:, t], inp["A"], inp["B"][:, t],
+                                                  inp["C"][:, t], inp["D"], inp["z"][:, t], state)
+        ys.append(y)
+        state = st.astype(np.float32)
+    assert rel_err(np.stack(ys, axis=1), yr) < 1e-6 and rel_err(state, hr) < 1e-6
+
+
+def test_U3_decode_hand_worked(oracle_lib):
+    """Exact small cases.  A = 0 (no decay): h = state + Delta B x; A = -inf: h = Delta B x.
+    Delta = 1/2, x = 2, B = (1, -1), C = (1/2, 2), state = (1, 2), D = 1/4, no gate:
+      A = 0:    h = (2, 1),  y = 1 + 2 + 1/2 = 3.5
+      A = -inf: h = (1, -1), y = 1/2 - 2 + 1/2 = -1."""
+    f = lambda *v: np.asarray(v, dtype=np.float32)
+    x, dl = f(2.0)[None], f(0.5)[None]
+    B, C, D = f(1.0, -1.0)[None], f(0.5, 2.0)[None], f(0.25)
+    state = f(1.0, 2.0)[None, None]
+    y, st = oracle_lib.selective_state_update(x.reshape(1, 1), dl.reshape(1, 1), f(0.0, 0.0)[None], B, C, D, None,
+                                              state)
+    assert np.array_equal(st, [[[2.0, 1.0]]]) and y[0, 0] == 3.5
+    y, st = oracle_lib.selective_state_update(x.reshape(1, 1), dl.reshape(1, 1), f(-np.inf, -np.inf)[None], B, C,
+                                              D, None, state)
+    assert np.array_equal(st, [[[1.0, -1.0]]]) and y[0, 0] == -1.0
