@@ -10,6 +10,7 @@ once and every output written once, the state never counted) in GB/s.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
   python bench.py --workload 4            # another configuration (0..4); the default is 3
+  python bench.py --decode 64             # one decode step of 64 tokens (selective_state_update)
   python bench.py --copy-calibration      # plain copy of a known size, for counter scaling
 """
 from __future__ import annotations
@@ -142,6 +143,64 @@ def copy_calibration(nbytes=1 << 30, reps=5):
     print(json.dumps({"copy_bytes_each_way": nbytes, "reps": reps}))
 
 
+def bench_decode(batch, steps, warmup, dim=5120, dstate=16):
+    """One decode step (selective_state_update) per call on a Mamba-2.8B-shaped layer
+    (d_inner 5120, d_state 16, bf16 x/delta/z, fp32 state), `batch` tokens per step.
+    Bound by moving the state: algorithmic bytes = state read + written, x/delta/z, y, B/C,
+    A and D once each."""
+    import torch
+    import selective_state_space_20_amd as sss
+    from selective_state_space_20_amd import inputs as gen
+    inp = gen.selective_inputs(batch, 1, dim, dstate, io="bf16", with_D=True, with_z=True, h0=True, h0_std=1.0,
+                               seed=2000 + batch)
+    dev = torch.device("cuda:0")
+
+    def td(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    x, dl, z = td(inp["x"][:, 0]), td(inp["delta"][:, 0]), td(inp["z"][:, 0])
+    Bm, Cm, A, D = td(inp["B"][:, 0]), td(inp["C"][:, 0]), td(inp["A"]), td(inp["D"])
+    state = td(inp["h0"])
+    y = torch.empty((batch, dim), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        sss.selective_state_update(x, dl, A, Bm, Cm, D, z, state=state, out=y)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t_start = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    per_call = [e0.elapsed_time(e1) for e0, e1 in ev]
+    mean_ms = float(np.mean(per_call))
+    nbytes = (2 * batch * dim * dstate * 4 + 3 * batch * dim * 2 + batch * dim * 4 + 2 * batch * dstate * 4
+              + dim * dstate * 4 + dim * 4)
+    log(f"[bench] decode B={batch}: {steps} steps, wall {wall * 1e3 / steps:.4f} ms/step, event mean {mean_ms:.4f} ms, "
+        f"min {min(per_call):.4f}")
+    gbs = nbytes / (mean_ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "selective_state_update (one decode step) achieved HBM GB/s, 1 GPU", "value": round(gbs, 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(wall * 1e3 / steps, 5),
+        "higher_is_better": True, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"decode_bf16_b{batch}_D{dim}_N{dstate}", "batch": batch, "dim": dim, "dstate": dstate,
+                   "algorithmic_bytes": nbytes},
+        "tokens_per_s": round(batch / (mean_ms * 1e-3), 1),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "sel_update_kernel",
+                     "call_ms_event_mean": round(mean_ms, 5)},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -150,6 +209,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--workload", type=int, default=WORKLOAD_INDEX, help="configuration index 0..4")
+    ap.add_argument("--decode", type=int, default=0, metavar="BATCH",
+                    help="time one decode step (selective_state_update) of BATCH tokens instead")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -158,6 +219,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.decode > 0:
+        bench_decode(args.decode, args.steps, args.warmup)
         return
 
     import torch

@@ -1,7 +1,7 @@
 /*
  * sss.h -- C ABI of the MI355X (gfx950) selective-scan library, libsss.so.
  *
- * Two operations, both fully computed by hand-written HIP kernels on the device:
+ * Three operations, all fully computed by hand-written HIP kernels on the device:
  *
  *  selective_scan_fwd  -- the selective (input-dependent) state-space recurrence of
  *      "Selective Scan trong Mamba toi uu chuoi dai the nao?" (thecsnote.cc), sections
@@ -15,13 +15,16 @@
  *      delta, B and C are outside this library ("15. Selective (Data-Dependent) SSM
  *      Scan", Problem: the data-dependent parameters are given).
  *
+ *  selective_state_update -- one decode step of the same recurrence on a carried state
+ *      (in place), for token-by-token generation.
+ *
  *  elementwise_scan -- the per-channel form of "15. Selective (Data-Dependent) SSM
  *      Scan" (Reference solution): h = A_t*h + B_t*x_t, y_t = C_t*h.
  *
- * Conventions (both calls)
+ * Conventions (all calls)
  *  - Pointers are DEVICE pointers owned by the caller.  Inputs are read-only; outputs
- *    may not overlap any input (SSS_ERR_ALIAS).  Every pointer must be 16-byte aligned
- *    (SSS_ERR_UNSUPPORTED otherwise).
+ *    may not overlap any input (SSS_ERR_ALIAS); the decode step's state is the one
+ *    in/out buffer.  Every pointer must be 16-byte aligned (SSS_ERR_UNSUPPORTED otherwise).
  *  - Layout is row-major, all indices 64-bit:
  *      x, delta, z, y : (batch, seqlen, dim)        -- dim fastest
  *      B, C           : (batch, seqlen, dstate)
@@ -79,6 +82,22 @@ int selective_scan_fwd(const void* x, const void* delta, const float* A, const f
                        const float* D_skip, const void* z, const float* h0, float* y, float* h_last,
                        int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
                        void* workspace, size_t workspace_bytes, sss_stream_t stream);
+
+/* One decode step of the selective scan ("Selective Scan trong Mamba toi uu chuoi dai the
+ * nao?", section "Selective Scan thay doi inference chuoi dai nhu the nao?": generation
+ * carries only the state from token to token), for one token per batch row:
+ *   state[b,d,n] = exp(delta[b,d]*A[d,n]) * state[b,d,n] + delta[b,d]*B[b,n]*x[b,d]
+ *   y[b,d]       = (sum_n C[b,n]*state[b,d,n] + D[d]*x[b,d]) * silu(z[b,d])
+ * i.e. exactly selective_scan_fwd over a length-1 sequence with h0 = h_last = state.
+ * Layouts: x, delta, z (batch, dim) in io_dtype; B, C (batch, dstate); A (dim, dstate);
+ * D_skip (dim); state (batch, dim, dstate) float32, read and overwritten IN PLACE (the
+ * only buffer that is both input and output); y (batch, dim) float32.
+ * Required: x, delta, A, B, C, state, y.  Optional (NULL): D_skip, z.  No workspace.
+ * Errors as above; state and y may not overlap any other argument (SSS_ERR_ALIAS);
+ * batch*dim*dstate must not exceed 2^31 (SSS_ERR_BAD_DIM).  Returns an sss_status. */
+int selective_state_update(const void* x, const void* delta, const float* A, const float* B, const float* C,
+                           const float* D_skip, const void* z, float* state, float* y, int64_t batch, int64_t dim,
+                           int64_t dstate, int io_dtype, sss_stream_t stream);
 
 /* Bytes of workspace elementwise_scan needs for these sizes on `device`. */
 size_t elementwise_scan_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int device);

@@ -4,6 +4,8 @@ The computation lives in libsss.so (hand-written HIP kernels behind the C ABI of
 include/sss.h); this package is its thin Python binding:
 
   * ``selective_scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None)`` -> (y, h_last)
+  * ``selective_state_update(x, delta, A, B, C, D=None, z=None, state=...)`` -> y (one
+    decode step; ``state`` is updated in place)
   * ``elementwise_scan(x, A, B, C, h0=None)`` -> (y, h_last)
   * ``*_workspace_size``, raw-pointer variants ``*_raw`` and ``status_string``.
 
@@ -11,8 +13,10 @@ include/sss.h); this package is its thin Python binding:
 """
 from ._lib import (EXPORTED, LIB_PATH, SSSError, SSS_BF16, SSS_F32, elementwise_scan, elementwise_scan_raw,
                    elementwise_scan_workspace_size, load, selective_scan_fwd, selective_scan_fwd_raw,
-                   selective_scan_fwd_workspace_size, status_string)
+                   selective_scan_fwd_workspace_size, selective_state_update, selective_state_update_raw,
+                   status_string)
 
-__all__ = ["selective_scan_fwd", "elementwise_scan", "selective_scan_fwd_workspace_size",
+__all__ = ["selective_scan_fwd", "selective_state_update", "selective_state_update_raw", "elementwise_scan",
+           "selective_scan_fwd_workspace_size",
            "elementwise_scan_workspace_size", "selective_scan_fwd_raw", "elementwise_scan_raw", "status_string",
            "SSSError", "SSS_F32", "SSS_BF16", "LIB_PATH", "EXPORTED", "load"]

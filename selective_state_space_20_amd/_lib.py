@@ -17,8 +17,8 @@ SSS_F32, SSS_BF16 = 0, 1
 STATUS = {0: "SSS_OK", -1: "SSS_ERR_NULL_ARG", -2: "SSS_ERR_BAD_DIM", -3: "SSS_ERR_UNSUPPORTED",
           -4: "SSS_ERR_WORKSPACE", -5: "SSS_ERR_ALIAS", -6: "SSS_ERR_HIP"}
 
-EXPORTED = ("selective_scan_fwd", "selective_scan_fwd_workspace_size", "elementwise_scan",
-            "elementwise_scan_workspace_size", "sss_status_string")
+EXPORTED = ("selective_scan_fwd", "selective_scan_fwd_workspace_size", "selective_state_update",
+            "elementwise_scan", "elementwise_scan_workspace_size", "sss_status_string")
 
 
 class SSSError(RuntimeError):
@@ -42,6 +42,8 @@ def load() -> ctypes.CDLL:
         lib.selective_scan_fwd.restype = i32
         lib.selective_scan_fwd_workspace_size.argtypes = [i64] * 4 + [i32]
         lib.selective_scan_fwd_workspace_size.restype = sz
+        lib.selective_state_update.argtypes = [vp] * 9 + [i64] * 3 + [i32, vp]
+        lib.selective_state_update.restype = i32
         lib.elementwise_scan.argtypes = [vp] * 7 + [i64] * 3 + [vp, sz, vp]
         lib.elementwise_scan.restype = i32
         lib.elementwise_scan_workspace_size.argtypes = [i64] * 3 + [i32]
@@ -62,6 +64,10 @@ def selective_scan_fwd_raw(x, delta, A, B, C, D_skip, z, h0, y, h_last, batch, s
     """Direct call of the C function with integer pointers (0 = NULL)."""
     return load().selective_scan_fwd(x, delta, A, B, C, D_skip, z, h0, y, h_last, batch, seqlen, dim, dstate,
                                      io_dtype, workspace, workspace_bytes, stream)
+
+
+def selective_state_update_raw(x, delta, A, B, C, D_skip, z, state, y, batch, dim, dstate, io_dtype, stream) -> int:
+    return load().selective_state_update(x, delta, A, B, C, D_skip, z, state, y, batch, dim, dstate, io_dtype, stream)
 
 
 def elementwise_scan_raw(x, A, B, C, h0, y, h_last, batch, seqlen, dim, workspace, workspace_bytes,
@@ -135,6 +141,36 @@ def selective_scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, return_las
     if rc != 0:
         raise SSSError(rc, "selective_scan_fwd")
     return (y, hl) if return_last or out_last is not None else y
+
+
+def selective_state_update(x, delta, A, B, C, D=None, z=None, *, state, out=None, stream=None):
+    """One decode step: updates ``state`` (batch, dim, dstate) float32 in place and returns
+    y (batch, dim) float32.  x, delta, z: (batch, dim) float32 or bfloat16 (one dtype);
+    A (dim, dstate), B, C (batch, dstate), D (dim): float32."""
+    import torch
+    dev = x.device
+    batch, dim = x.shape
+    dstate = A.shape[1]
+    io = x.dtype
+    if io not in (torch.float32, torch.bfloat16):
+        raise ValueError("x must be float32 or bfloat16")
+    f32 = torch.float32
+    _need(x, "x", io, (batch, dim), dev)
+    _need(delta, "delta", io, (batch, dim), dev)
+    _need(z, "z", io, (batch, dim), dev)
+    _need(A, "A", f32, (dim, dstate), dev)
+    _need(B, "B", f32, (batch, dstate), dev)
+    _need(C, "C", f32, (batch, dstate), dev)
+    _need(D, "D", f32, (dim,), dev)
+    _need(state, "state", f32, (batch, dim, dstate), dev)
+    y = out if out is not None else torch.empty((batch, dim), dtype=f32, device=dev)
+    _need(y, "out", f32, (batch, dim), dev)
+    st = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
+    rc = selective_state_update_raw(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(state),
+                                    _ptr(y), batch, dim, dstate, SSS_BF16 if io == torch.bfloat16 else SSS_F32, st)
+    if rc != 0:
+        raise SSSError(rc, "selective_state_update")
+    return y
 
 
 def elementwise_scan(x, A, B, C, h0=None, *, return_last=True, out=None, out_last=None, workspace=None,

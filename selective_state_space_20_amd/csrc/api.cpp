@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdio>
 #include <cstdlib>
@@ -166,6 +167,48 @@ int selective_scan_fwd(const void* x, const void* delta, const float* A, const f
   a.workspace = workspace;
   hipError_t e = launch_selective(a, pl, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? SSS_OK : SSS_ERR_HIP;
+}
+
+int selective_state_update(const void* x, const void* delta, const float* A, const float* B, const float* C,
+                           const float* D_skip, const void* z, float* state, float* y, int64_t batch, int64_t dim,
+                           int64_t dstate, int io_dtype, sss_stream_t stream) {
+  if (!x || !delta || !A || !B || !C || !state || !y) return SSS_ERR_NULL_ARG;
+  if (batch < 1 || dim < 1 || dstate < 1 || dim > kMaxSelDim) return SSS_ERR_BAD_DIM;
+  int64_t e = 0, t = 0;
+  if (!mul_ok(batch, dim, &e) || !mul_ok(e, dstate, &t) || t > ((int64_t)1 << 31)) return SSS_ERR_BAD_DIM;
+  // grid: ceil(dim * lanes per channel / 256) blocks per batch row, one row after another
+  if ((double)batch * (double)((dim * std::max<int64_t>(dstate / 4, 1) + 255) / 256) > 2147483647.0)
+    return SSS_ERR_BAD_DIM;
+  if (dstate > 64 || (dstate & (dstate - 1)) != 0) return SSS_ERR_UNSUPPORTED;
+  if (io_dtype != SSS_F32 && io_dtype != SSS_BF16) return SSS_ERR_UNSUPPORTED;
+  const void* ptrs[] = {x, delta, A, B, C, D_skip, z, state, y};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return SSS_ERR_UNSUPPORTED;
+  const int64_t es = io_dtype == SSS_BF16 ? 2 : 4;
+  const int64_t st_bytes = batch * dim * dstate * 4, y_bytes = batch * dim * 4;
+  const void* in_p[] = {x, delta, A, B, C, D_skip, z};
+  const int64_t in_b[] = {e * es, e * es, dim * dstate * 4, batch * dstate * 4, batch * dstate * 4, dim * 4, e * es};
+  for (int i = 0; i < 7; ++i) {
+    if (overlap(state, st_bytes, in_p[i], in_b[i])) return SSS_ERR_ALIAS;
+    if (overlap(y, y_bytes, in_p[i], in_b[i])) return SSS_ERR_ALIAS;
+  }
+  if (overlap(y, y_bytes, state, st_bytes)) return SSS_ERR_ALIAS;
+  if (current_device_cus() <= 0) return SSS_ERR_HIP;
+  UpdArgs a{};
+  a.x = x;
+  a.delta = delta;
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.Dsk = D_skip;
+  a.z = z;
+  a.state = state;
+  a.y = y;
+  a.batch = batch;
+  a.dim = dim;
+  a.dstate = (int)dstate;
+  a.bf16 = io_dtype == SSS_BF16;
+  return launch_update(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? SSS_OK : SSS_ERR_HIP;
 }
 
 static int ew_dims_ok(int64_t batch, int64_t seqlen, int64_t dim) {

@@ -54,6 +54,23 @@ struct EwArgs {
 EwPlan plan_elementwise(int64_t batch, int64_t seqlen, int64_t dim, int num_cus);
 hipError_t launch_elementwise(const EwArgs& a, const EwPlan& plan, hipStream_t stream);
 
+struct UpdArgs {
+  const void* x;
+  const void* delta;
+  const float* A;
+  const float* B;
+  const float* C;
+  const float* Dsk;
+  const void* z;
+  float* state;
+  float* y;
+  int64_t batch, dim;
+  int dstate;
+  int bf16;
+};
+
+hipError_t launch_update(const UpdArgs& a, hipStream_t stream);
+
 int env_int(const char* name, int dflt);
 
 }  // namespace sss

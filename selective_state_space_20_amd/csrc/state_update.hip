@@ -1,0 +1,131 @@
+// state_update.hip -- gfx950 kernel for one recurrent-inference step of the selective scan.
+//
+// "Selective Scan trong Mamba toi uu chuoi dai the nao?" (section "Selective Scan thay doi
+// inference chuoi dai nhu the nao?"): when tokens are generated one at a time only the
+// state h (batch, dim, dstate) is carried, so each token costs one update of it:
+//   h[b,d,n] = exp(delta[b,d]*A[d,n]) * h[b,d,n] + delta[b,d]*B[b,n]*x[b,d]      (in place)
+//   y[b,d]   = (sum_n C[b,n]*h[b,d,n] + D[d]*x[b,d]) * silu(z[b,d])
+//
+// The step is bound by moving the state (8 bytes per state element: read and write back),
+// so the mapping follows the state's layout: lanes walk (b, d, n) in memory order, four
+// states per lane, so that every state load and store of a wave is one contiguous 1 KiB
+// piece of 16-byte vectors.  The lanes of a channel are adjacent and reduce C*h with
+// cross-lane xor shuffles; the first of them writes y.
+#include "common.h"
+#include "kernels.h"
+
+namespace sss {
+
+template <bool BF16>
+__device__ __forceinline__ float load_io(const void* p, int64_t i) {
+  if (BF16) return __builtin_bit_cast(float, (uint32_t)static_cast<const uint16_t*>(p)[i] << 16);
+  return static_cast<const float*>(p)[i];
+}
+
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+// Each lane owns PL = min(4, NS) adjacent states of one channel (a 16-byte piece of the
+// state, of A and of B/C); the LPC = NS / PL lanes of a channel are adjacent and reduce
+// C*h with xor shuffles.  Blocks never straddle a batch row: blockIdx.x = b * bpb + k.
+template <int NS, bool BF16, bool HAS_Z>
+__global__ __launch_bounds__(256) void sel_update_kernel(const void* __restrict__ x, const void* __restrict__ delta,
+                                                         const float* __restrict__ A, const float* __restrict__ Bm,
+                                                         const float* __restrict__ Cm, const float* __restrict__ Dsk,
+                                                         const void* __restrict__ z, float* __restrict__ state,
+                                                         float* __restrict__ y, int64_t batch, int dim,
+                                                         unsigned bpb /* blocks per batch row */) {
+  constexpr int PL = NS >= 4 ? 4 : NS;
+  constexpr int LPC = NS / PL;
+  const unsigned b = blockIdx.x / bpb;
+  const int li = (int)(blockIdx.x - b * bpb) * 256 + (int)threadIdx.x;  // lane index within the row
+  // Lanes past the row's end form whole channel groups (LPC divides 64); they work on the
+  // row's last channel so that every lane takes part in the shuffles, and store nothing.
+  const bool live = li < dim * LPC;
+  const int d = (live ? li : dim * LPC - 1) / LPC;  // LPC is a power of two
+  const int j = (live ? li : dim * LPC - 1) - d * LPC;
+  const int64_t c = (int64_t)b * dim + d;
+
+  const float xv = load_io<BF16>(x, c);
+  const float dv = load_io<BF16>(delta, c);
+  const float dx = dv * xv;
+  float hv[PL], av[PL], bv[PL], cv[PL];
+  if constexpr (PL == 4) {
+    const f4v s4 = *reinterpret_cast<const f4v*>(state + c * NS + j * 4);
+    const f4v a4 = *reinterpret_cast<const f4v*>(A + (int64_t)d * NS + j * 4);
+    const f4v b4 = *reinterpret_cast<const f4v*>(Bm + (int64_t)b * NS + j * 4);
+    const f4v c4 = *reinterpret_cast<const f4v*>(Cm + (int64_t)b * NS + j * 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      hv[i] = s4[i];
+      av[i] = a4[i];
+      bv[i] = b4[i];
+      cv[i] = c4[i];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      hv[i] = state[c * NS + i];
+      av[i] = A[(int64_t)d * NS + i];
+      bv[i] = Bm[(int64_t)b * NS + i];
+      cv[i] = Cm[(int64_t)b * NS + i];
+    }
+  }
+  float part = 0.0f;
+#pragma unroll
+  for (int i = 0; i < PL; ++i) {
+    const float a2 = fmaxf(av[i] * kLog2e, -kFltMax);  // -inf clamped so that 0*a2 = 0
+    hv[i] = __builtin_fmaf(fast_exp2(dv * a2), hv[i], dx * bv[i]);
+    part = __builtin_fmaf(cv[i], hv[i], part);
+  }
+  if (live) {
+    if constexpr (PL == 4) {
+      const f4v o = {hv[0], hv[1], hv[2], hv[3]};
+      *reinterpret_cast<f4v*>(state + c * NS + j * 4) = o;
+    } else {
+#pragma unroll
+      for (int i = 0; i < PL; ++i) state[c * NS + i] = hv[i];
+    }
+  }
+#pragma unroll
+  for (int off = LPC / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, LPC);
+  if (live && j == 0) {
+    float out = part;
+    if (Dsk != nullptr) out = __builtin_fmaf(Dsk[d], xv, out);
+    if (HAS_Z) out *= silu(load_io<BF16>(z, c));
+    y[c] = out;
+  }
+}
+
+template <int NS, bool BF16>
+static hipError_t run_update(const UpdArgs& a, hipStream_t stream) {
+  constexpr int LPC = NS >= 4 ? NS / 4 : 1;
+  const unsigned bpb = (unsigned)((a.dim * LPC + 255) / 256);
+  const dim3 grid((unsigned)(bpb * a.batch)), block(256);
+  if (a.z != nullptr)
+    hipLaunchKernelGGL((sel_update_kernel<NS, BF16, true>), grid, block, 0, stream, a.x, a.delta, a.A, a.B, a.C,
+                       a.Dsk, a.z, a.state, a.y, a.batch, (int)a.dim, bpb);
+  else
+    hipLaunchKernelGGL((sel_update_kernel<NS, BF16, false>), grid, block, 0, stream, a.x, a.delta, a.A, a.B, a.C,
+                       a.Dsk, a.z, a.state, a.y, a.batch, (int)a.dim, bpb);
+  return hipGetLastError();
+}
+
+template <bool BF16>
+static hipError_t dispatch_update(const UpdArgs& a, hipStream_t stream) {
+  switch (a.dstate) {
+    case 1: return run_update<1, BF16>(a, stream);
+    case 2: return run_update<2, BF16>(a, stream);
+    case 4: return run_update<4, BF16>(a, stream);
+    case 8: return run_update<8, BF16>(a, stream);
+    case 16: return run_update<16, BF16>(a, stream);
+    case 32: return run_update<32, BF16>(a, stream);
+    case 64: return run_update<64, BF16>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_update(const UpdArgs& a, hipStream_t stream) {
+  return a.bf16 ? dispatch_update<true>(a, stream) : dispatch_update<false>(a, stream);
+}
+
+}  // namespace sss

@@ -54,3 +54,15 @@ def rel_err(got, ref):
     if not np.all(np.isfinite(got)):
         return float("inf")
     return float(np.max(np.abs(got - ref)) / max(float(np.max(np.abs(ref))), 1e-30))
+
+
+def run_update(x, delta, A, B, C, D, z, state, dev="cuda:0", fill=float("nan")):
+    """One decode step on the GPU; returns (y, new state) as numpy float32."""
+    import torch
+    import selective_state_space_20_amd as sss
+    st = to_dev(np.ascontiguousarray(state, dtype=np.float32), dev).clone()
+    y = torch.full(x.shape, fill, dtype=torch.float32, device=dev)
+    sss.selective_state_update(to_dev(x, dev), to_dev(delta, dev), to_dev(A, dev), to_dev(B, dev), to_dev(C, dev),
+                               to_dev(D, dev), to_dev(z, dev), state=st, out=y)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), st.cpu().numpy()

@@ -63,6 +63,37 @@ def ew(**kw):
     return sss.elementwise_scan_raw(**a)
 
 
+def upd(**kw):
+    a = dict(x=P, delta=2 * P, A=3 * P, B=4 * P, C=5 * P, D_skip=0, z=0, state=32 * P, y=64 * P, batch=2, dim=4,
+             dstate=4, io_dtype=0, stream=0)
+    a.update(kw)
+    return sss.selective_state_update_raw(**a)
+
+
+@pytest.mark.parametrize("name", ["x", "delta", "A", "B", "C", "state", "y"])
+def test_update_null_required(name):
+    assert upd(**{name: 0}) == NULL_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(batch=0), dict(dim=0), dict(dstate=-1), dict(dim=(1 << 24) + 1),
+                                dict(batch=1 << 20, dim=1 << 12, dstate=1 << 6)])
+def test_update_bad_dims(kw):
+    assert upd(**kw) == BAD_DIM
+
+
+@pytest.mark.parametrize("kw", [dict(dstate=3), dict(dstate=128), dict(io_dtype=5), dict(state=32 * P + 4),
+                                dict(z=7 * P + 8)])
+def test_update_unsupported(kw):
+    assert upd(**kw) == UNSUPPORTED
+
+
+def test_update_alias():
+    assert upd(state=P) == ALIAS            # state over x
+    assert upd(y=5 * P) == ALIAS            # y over C
+    assert upd(y=32 * P + 16) == ALIAS      # y over state
+    assert upd(state=3 * P + 16) == ALIAS   # state over A
+
+
 @pytest.mark.parametrize("name", ["x", "delta", "A", "B", "C", "y"])
 def test_selective_null_required(name):
     assert sel(**{name: 0}) == NULL_ARG
@@ -114,3 +145,4 @@ def test_no_device_reports_hip_error():
         pytest.skip("a GPU is present; this checks the no-device path")
     assert sel() == HIP
     assert ew() == HIP
+    assert upd() == HIP

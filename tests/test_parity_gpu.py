@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 from selective_state_space_20_amd import inputs as gen
-from tests.gpu_util import TOL_BF16, TOL_F32, note, rel_err, run_elementwise, run_selective
+from tests.gpu_util import TOL_BF16, TOL_F32, note, rel_err, run_elementwise, run_selective, run_update, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -115,6 +115,85 @@ def test_selective_guard_bands():
     torch.cuda.synchronize()
     for buf in (ybuf, hbuf):
         assert torch.all(buf[:pad] == 12345.0) and torch.all(buf[-pad:] == 12345.0)
+
+
+# ---------------------------------------------------------------- decode step
+UPD_CASES = [  # (batch, dim, dstate, io, D, z)
+    (1, 1, 1, "f32", False, False),
+    (3, 37, 2, "bf16", True, True),
+    (2, 100, 4, "f32", True, False),
+    (5, 33, 8, "bf16", False, True),
+    (4, 5120, 16, "bf16", True, True),
+    (3, 77, 16, "f32", True, True),
+    (2, 65, 32, "f32", True, True),
+    (3, 21, 64, "bf16", True, True),
+]
+
+
+@pytest.mark.parametrize("case", UPD_CASES, ids=[f"B{c[0]}D{c[1]}N{c[2]}{c[3]}" for c in UPD_CASES])
+def test_update_random_shapes(oracle_lib, case):
+    bt, dm, n, io, with_D, with_z = case
+    inp = gen.selective_inputs(bt, 1, dm, n, io=io, with_D=with_D, with_z=with_z, h0=True, h0_std=1.0,
+                               seed=zlib.crc32(repr(case).encode()) % 100000)
+    x, dl = inp["x"][:, 0], inp["delta"][:, 0]
+    z = inp["z"][:, 0] if inp["z"] is not None else None
+    state = inp["h0"]
+    note(f"[update] B={bt} D={dm} N={n} io={io}")
+    y, st = run_update(x, dl, inp["A"], inp["B"][:, 0], inp["C"][:, 0], inp["D"], z, state)
+    yr, str_ = oracle_lib.selective_state_update(x, dl, inp["A"], inp["B"][:, 0], inp["C"][:, 0], inp["D"], z, state)
+    tol = TOL_BF16 if io == "bf16" else TOL_F32
+    ey, es = rel_err(y, yr), rel_err(st, str_)
+    note(f"    err y={ey:.3e} state={es:.3e}")
+    assert ey <= tol and es <= tol
+
+
+def test_update_continues_a_prefill(oracle_lib):
+    """Prefill 300 steps with selective_scan_fwd, then decode 40 tokens one at a time from its
+    h_last: outputs and final state match the oracle's scan over all 340 steps."""
+    import torch
+    import selective_state_space_20_amd as sss
+    bt, L0, K, dm, n = 2, 300, 40, 96, 16
+    inp = gen.selective_inputs(bt, L0 + K, dm, n, io="bf16", with_D=True, with_z=True, h0=True, seed=91)
+    yr, hr = oracle_lib.selective_scan(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                                       inp["h0"])
+    pre = {k: (v[:, :L0] if isinstance(v, np.ndarray) and v.ndim == 3 and v.shape[1] == L0 + K else v)
+           for k, v in inp.items()}
+    y0, h = run_selective(pre)
+    t = {k: to_dev(v, "cuda:0") for k, v in inp.items() if k != "io"}
+    state = torch.from_numpy(h).cuda()
+    ys = []
+    for k in range(K):
+        s = L0 + k
+        c = lambda a: a[:, s].contiguous()
+        ys.append(sss.selective_state_update(c(t["x"]), c(t["delta"]), t["A"], c(t["B"]), c(t["C"]), t["D"], c(t["z"]),
+                                             state=state))
+    torch.cuda.synchronize()
+    yk = torch.stack(ys, dim=1).cpu().numpy()
+    ey = rel_err(np.concatenate([y0, yk], axis=1), yr)
+    eh = rel_err(state.cpu().numpy(), hr)
+    note(f"[update] prefill+decode err y={ey:.3e} state={eh:.3e}")
+    assert ey <= TOL_BF16 and eh <= TOL_BF16
+
+
+def test_update_guard_bands():
+    """The update writes exactly the state and y: canaries around both survive."""
+    import torch
+    import selective_state_space_20_amd as sss
+    bt, dm, n = 3, 45, 16
+    inp = gen.selective_inputs(bt, 1, dm, n, io="f32", with_D=True, with_z=True, h0=True, seed=92)
+    pad = 1024
+    sbuf = torch.full((bt * dm * n + 2 * pad,), 12345.0, device="cuda:0")
+    ybuf = torch.full((bt * dm + 2 * pad,), 12345.0, device="cuda:0")
+    st = sbuf[pad:pad + bt * dm * n].view(bt, dm, n)
+    st.copy_(torch.from_numpy(inp["h0"]))
+    y = ybuf[pad:pad + bt * dm].view(bt, dm)
+    d = lambda a: to_dev(np.ascontiguousarray(a), "cuda:0")
+    sss.selective_state_update(d(inp["x"][:, 0]), d(inp["delta"][:, 0]), d(inp["A"]), d(inp["B"][:, 0]),
+                               d(inp["C"][:, 0]), d(inp["D"]), d(inp["z"][:, 0]), state=st, out=y)
+    torch.cuda.synchronize()
+    for buf in (sbuf, ybuf):
+        assert torch.all(buf[:pad] == 12345.0) and torch.all(buf[-pad:] == 12345.0)
+    assert torch.all(torch.isfinite(y)) and torch.all(torch.isfinite(st))
 
 
 # ---------------------------------------------------------------- elementwise
