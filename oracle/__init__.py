@@ -52,8 +52,8 @@ def _load():
             build(force=True)
         lib = ctypes.CDLL(_LIB_PATH)
         vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
-        lib.oracle_selective_scan.argtypes = [vp] * 10 + [i64] * 4 + [i32] * 3
-        lib.oracle_selective_scan_channels.argtypes = [vp] * 8 + [vp, i64, vp, vp] + [i64] * 4 + [i32] * 3
+        lib.oracle_selective_scan.argtypes = [vp] * 10 + [i64] * 4 + [i32] * 2 + [vp, i32, i32]
+        lib.oracle_selective_scan_channels.argtypes = [vp] * 8 + [vp, i64, vp, vp] + [i64] * 4 + [i32] * 2 + [vp, i32, i32]
         lib.oracle_selective_scan_chunked.argtypes = [vp] * 10 + [i64] * 4 + [i32] * 2 + [i64, i32]
         lib.oracle_elementwise_scan.argtypes = [vp] * 7 + [i64] * 3 + [i32]
         lib.oracle_elementwise_scan_channels.argtypes = [vp] * 5 + [vp, i64, vp, vp] + [i64] * 3 + [i32]
@@ -100,9 +100,10 @@ def _check(rc):
         raise ValueError(f"oracle rejected its arguments (status {rc})")
 
 
-def selective_scan(x, delta, A, B, C, D=None, z=None, h0=None, *, exact_zoh=False, return_last=True,
-                   nthreads=0):
-    """x, delta, z: (Bt, L, Dm); A: (Dm, N); B, C: (Bt, L, N); D: (Dm,); h0: (Bt, Dm, N).
+def selective_scan(x, delta, A, B, C, D=None, z=None, h0=None, *, exact_zoh=False, delta_bias=None,
+                   delta_softplus=False, return_last=True, nthreads=0):
+    """x, delta, z: (Bt, L, Dm); A: (Dm, N); B, C: (Bt, L, N); D: (Dm,); h0: (Bt, Dm, N);
+    delta_bias: (Dm,) added to delta, then softplus if delta_softplus.
 
     Returns (y (Bt, L, Dm) float64, h_last (Bt, Dm, N) float64 or None).
     """
@@ -110,21 +111,24 @@ def selective_scan(x, delta, A, B, C, D=None, z=None, h0=None, *, exact_zoh=Fals
     if delta.dtype != x.dtype or (z is not None and z.dtype != x.dtype):
         raise TypeError("x, delta and z must share one dtype")
     A, B, C, D, h0 = _f32(A), _f32(B), _f32(C), _f32(D), _f32(h0)
+    dbias = _f32(delta_bias)
     bt, L, dm = x.shape
     n = A.shape[1]
     y = np.empty((bt, L, dm), dtype=np.float64)
     hl = np.empty((bt, dm, n), dtype=np.float64) if return_last else None
     rc = _load().oracle_selective_scan(_p(x), _p(delta), _p(A), _p(B), _p(C), _p(D), _p(z), _p(h0), _p(y),
-                                       _p(hl), bt, L, dm, n, _io_code(x), int(bool(exact_zoh)), nthreads)
+                                       _p(hl), bt, L, dm, n, _io_code(x), int(bool(exact_zoh)), _p(dbias),
+                                       int(bool(delta_softplus)), nthreads)
     _check(rc)
     return y, hl
 
 
 def selective_scan_channels(x, delta, A, B, C, D=None, z=None, h0=None, *, channels, exact_zoh=False,
-                            nthreads=0):
+                            delta_bias=None, delta_softplus=False, nthreads=0):
     """Only the channels ``channels`` (flat b*Dm + d).  Returns y (k, L), h_last (k, N)."""
     x, delta, z = _io(x), _io(delta), _io(z)
     A, B, C, D, h0 = _f32(A), _f32(B), _f32(C), _f32(D), _f32(h0)
+    dbias = _f32(delta_bias)
     bt, L, dm = x.shape
     n = A.shape[1]
     ch = np.ascontiguousarray(channels, dtype=np.int64)
@@ -132,7 +136,8 @@ def selective_scan_channels(x, delta, A, B, C, D=None, z=None, h0=None, *, chann
     hl = np.empty((ch.size, n), dtype=np.float64)
     rc = _load().oracle_selective_scan_channels(_p(x), _p(delta), _p(A), _p(B), _p(C), _p(D), _p(z), _p(h0),
                                                 _p(ch), ch.size, _p(y), _p(hl), bt, L, dm, n, _io_code(x),
-                                                int(bool(exact_zoh)), nthreads)
+                                                int(bool(exact_zoh)), _p(dbias), int(bool(delta_softplus)),
+                                                nthreads)
     _check(rc)
     return y, hl
 

@@ -53,6 +53,18 @@ static double load_val(const void* p, int64_t i, int dtype) {
   return (double)((const float*)p)[i];
 }
 
+/* softplus(v) = log(1 + e^v), written so that neither branch overflows. */
+static double softplus(double v) { return v > 0.0 ? v + log1p(exp(-v)) : log1p(exp(v)); }
+
+/* The step size actually used: the stored delta, plus the per-channel bias if one is
+ * given, then through softplus if asked (the front end that produces delta in Mamba,
+ * [P1] "Selection pha vo convolution kernel co dinh": Delta as a function of the input). */
+static double delta_value(const void* delta, int64_t e, int dtype, const float* dbias, int64_t d, int sp) {
+  double v = load_val(delta, e, dtype);
+  if (dbias) v += (double)dbias[d];
+  return sp ? softplus(v) : v;
+}
+
 static void set_threads(int nthreads) {
 #ifdef _OPENMP
   if (nthreads > 0) omp_set_num_threads(nthreads);
@@ -78,20 +90,21 @@ int oracle_max_threads(void) {
  *   with Bbar_t[n] = Delta_t * B_t[n]                      (exact_zoh == 0)
  *     or Bbar_t[n] = expm1(Delta_t*A[d,n]) / A[d,n] * B_t[n] (exact_zoh != 0,
  *        the P1 Python example's zero-order hold; Delta_t when A[d,n] == 0).
- *   The readout uses the state after the update ([P3] step 4).
+ *   The readout uses the state after the update ([P3] step 4).  Delta_t is the stored
+ *   value, optionally plus dbias[d] and through softplus (delta_value).
  * Layouts: x, delta, z (B, L, D); B, C (B, L, N); A (D, N); D (D);
  *          h0, h_last (B, D, N).  Outputs: y_out[t * y_stride] for t < L,
  *          hl_out[n] for n < N.
  */
 static void sel_channel(const void* x, const void* delta, const float* A, const float* Bm, const float* Cm,
                         const float* Dsk, const void* z, const float* h0, int64_t b, int64_t d, int64_t L,
-                        int64_t Dm, int64_t N, int dtype, int exact_zoh, double* y_out, int64_t y_stride,
-                        double* hl_out, double* h /* scratch N */) {
+                        int64_t Dm, int64_t N, int dtype, int exact_zoh, const float* dbias, int sp,
+                        double* y_out, int64_t y_stride, double* hl_out, double* h /* scratch N */) {
   for (int64_t n = 0; n < N; ++n) h[n] = h0 ? (double)h0[(b * Dm + d) * N + n] : 0.0;
   for (int64_t t = 0; t < L; ++t) {
     int64_t e = (b * L + t) * Dm + d;
     double xt = load_val(x, e, dtype);
-    double dt = load_val(delta, e, dtype);
+    double dt = delta_value(delta, e, dtype, dbias, d, sp);
     const float* Bt = Bm + (b * L + t) * N;
     const float* Ct = Cm + (b * L + t) * N;
     double v = 0.0;
@@ -129,7 +142,7 @@ static int sel_args_ok(const void* x, const void* delta, const float* A, const f
 int oracle_selective_scan(const void* x, const void* delta, const float* A, const float* Bm, const float* Cm,
                           const float* Dsk, const void* z, const float* h0, double* y, double* h_last,
                           int64_t batch, int64_t L, int64_t Dm, int64_t N, int dtype, int exact_zoh,
-                          int nthreads) {
+                          const float* dbias, int sp, int nthreads) {
   if (!sel_args_ok(x, delta, A, Bm, Cm, batch, L, Dm, N, dtype) || !y) return OR_ERR_ARG;
   set_threads(nthreads);
   int64_t nch = batch * Dm;
@@ -139,7 +152,7 @@ int oracle_selective_scan(const void* x, const void* delta, const float* A, cons
 #pragma omp for schedule(dynamic, 1)
     for (int64_t c = 0; c < nch; ++c) {
       int64_t b = c / Dm, d = c % Dm;
-      sel_channel(x, delta, A, Bm, Cm, Dsk, z, h0, b, d, L, Dm, N, dtype, exact_zoh, y + b * L * Dm + d, Dm,
+      sel_channel(x, delta, A, Bm, Cm, Dsk, z, h0, b, d, L, Dm, N, dtype, exact_zoh, dbias, sp, y + b * L * Dm + d, Dm,
                   h_last ? h_last + (b * Dm + d) * N : 0, hbuf);
     }
   }
@@ -151,7 +164,7 @@ int oracle_selective_scan_channels(const void* x, const void* delta, const float
                                    const float* Cm, const float* Dsk, const void* z, const float* h0,
                                    const int64_t* chan, int64_t nchan, double* y_out, double* hl_out,
                                    int64_t batch, int64_t L, int64_t Dm, int64_t N, int dtype, int exact_zoh,
-                                   int nthreads) {
+                                   const float* dbias, int sp, int nthreads) {
   if (!sel_args_ok(x, delta, A, Bm, Cm, batch, L, Dm, N, dtype) || !chan || !y_out || nchan < 0)
     return OR_ERR_ARG;
   for (int64_t k = 0; k < nchan; ++k)
@@ -163,7 +176,7 @@ int oracle_selective_scan_channels(const void* x, const void* delta, const float
 #pragma omp for schedule(dynamic, 1)
     for (int64_t k = 0; k < nchan; ++k) {
       int64_t b = chan[k] / Dm, d = chan[k] % Dm;
-      sel_channel(x, delta, A, Bm, Cm, Dsk, z, h0, b, d, L, Dm, N, dtype, exact_zoh, y_out + k * L, 1,
+      sel_channel(x, delta, A, Bm, Cm, Dsk, z, h0, b, d, L, Dm, N, dtype, exact_zoh, dbias, sp, y_out + k * L, 1,
                   hl_out ? hl_out + k * N : 0, hbuf);
     }
   }

@@ -49,6 +49,9 @@ MUTANTS = {
     "update_B_of_batch_0": ("dv * (double)Bm[b * N + n] * xv;", "dv * (double)Bm[n] * xv;"),
     "update_decay_without_delta": ("double h = exp(dv * (double)A[d * N + n])", "double h = exp((double)A[d * N + n])"),
     "update_dropped_skip": ("    if (Dsk) acc += (double)Dsk[d] * xv;", "    (void)Dsk;"),
+    "front_end_bias_ignored": ("  if (dbias) v += (double)dbias[d];", "  (void)dbias;"),
+    "front_end_exp_for_softplus": ("static double softplus(double v) { return v > 0.0 ? v + log1p(exp(-v)) : log1p(exp(v)); }",
+                                   "static double softplus(double v) { return exp(v); }"),
 }
 
 
@@ -94,6 +97,7 @@ def test_unmutated_copy_passes_every_pin(tmp_path):
         call(mod)
 
 
+@pytest.mark.filterwarnings("ignore::RuntimeWarning")  # mutants may overflow; only the verdict matters
 @pytest.mark.parametrize("mutant", sorted(MUTANTS))
 def test_mutant_is_caught(tmp_path, mutant):
     old, new = MUTANTS[mutant]

@@ -435,3 +435,36 @@ def test_U3_decode_hand_worked(oracle_lib):
     y, st = oracle_lib.selective_state_update(x.reshape(1, 1), dl.reshape(1, 1), f(-np.inf, -np.inf)[None], B, C,
                                               D, None, state)
     assert np.array_equal(st, [[[1.0, -1.0]]]) and y[0, 0] == -1.0
+
+
+# ---------------------------------------------------------------- delta front end (bias + softplus)
+def test_F1_softplus_front_end_closed_form(oracle_lib):
+    """N = 1, A = 0, B = C = 1, x = 1, h0 = 0, one step: y_0 = Delta_0, so the front end is
+    read off directly: y = softplus(delta_raw + bias) (numpy's logaddexp(0, v)), and
+    y = delta_raw + bias without softplus."""
+    v = np.asarray([-30.0, -12.5, -4.6, -0.75, 0.0, 0.5, 3.0, 25.0, 80.0], dtype=np.float32)
+    bias = np.asarray([0.25], dtype=np.float32)
+    k = v.size
+    x = np.ones((k, 1, 1), np.float32)
+    dl = v.reshape(k, 1, 1)
+    A = np.zeros((1, 1), np.float32)
+    B = np.ones((k, 1, 1), np.float32)
+    y, _ = oracle_lib.selective_scan(x, dl, A, B, B, delta_bias=bias, delta_softplus=True)
+    ref = np.logaddexp(0.0, v.astype(np.float64) + 0.25)
+    assert np.allclose(y[:, 0, 0], ref, rtol=1e-14, atol=0.0)
+    y, _ = oracle_lib.selective_scan(x, dl, A, B, B, delta_bias=bias)
+    assert np.array_equal(y[:, 0, 0], v.astype(np.float64) + 0.25)
+
+
+def test_F2_front_end_equals_transformed_delta(oracle_lib):
+    """On a full random case the front end is the same as feeding the transformed step sizes
+    (computed here with numpy, rounded to fp32) to the plain oracle."""
+    inp = gen.selective_inputs(2, 300, 9, 16, io="f32", with_D=True, with_z=True, h0=True, seed=93)
+    rng = np.random.default_rng(94)
+    raw = (rng.standard_normal(inp["delta"].shape) - 3.0).astype(np.float32)
+    bias = (0.5 * rng.standard_normal(9)).astype(np.float32)
+    y, hl = oracle_lib.selective_scan(inp["x"], raw, inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], inp["h0"],
+                                      delta_bias=bias, delta_softplus=True)
+    dl = np.logaddexp(0.0, raw.astype(np.float64) + bias.astype(np.float64)).astype(np.float32)
+    yr, hr = oracle_lib.selective_scan(inp["x"], dl, inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], inp["h0"])
+    assert rel_err(y, yr) < 1e-6 and rel_err(hl, hr) < 1e-6
