@@ -99,6 +99,26 @@ int selective_state_update(const void* x, const void* delta, const float* A, con
                            const float* D_skip, const void* z, float* state, float* y, int64_t batch, int64_t dim,
                            int64_t dstate, int io_dtype, sss_stream_t stream);
 
+/* Options of selective_scan_fwd_ex (bit flags). */
+typedef enum {
+  SSS_EXACT_ZOH = 1u,      /* input term expm1(delta*A[d,n])/A[d,n] * B_t[n] * x_t, the exact
+                              zero-order hold of the Python example in "Selective Scan trong
+                              Mamba ..." (delta * B_t[n] where A[d,n] == 0), instead of the
+                              first-order delta * B_t[n] * x_t                                 */
+  SSS_DELTA_SOFTPLUS = 2u  /* step size softplus(delta (+ delta_bias[d])): the front end that
+                              turns the projected delta into a positive step                  */
+} sss_flags;
+
+/* selective_scan_fwd with options: `delta_bias` (dim) float32, nullable, is added to delta
+ * before use (and before softplus); `flags` is a combination of sss_flags (unknown bits:
+ * SSS_ERR_UNSUPPORTED).  With delta_bias == NULL and flags == 0 it is selective_scan_fwd.
+ * Same workspace size, layouts, ownership and errors as selective_scan_fwd. */
+int selective_scan_fwd_ex(const void* x, const void* delta, const float* A, const float* B, const float* C,
+                          const float* D_skip, const void* z, const float* h0, float* y, float* h_last,
+                          const float* delta_bias, unsigned flags, int64_t batch, int64_t seqlen, int64_t dim,
+                          int64_t dstate, int io_dtype, void* workspace, size_t workspace_bytes,
+                          sss_stream_t stream);
+
 /* Bytes of workspace elementwise_scan needs for these sizes on `device`. */
 size_t elementwise_scan_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int device);
 

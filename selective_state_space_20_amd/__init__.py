@@ -3,7 +3,9 @@
 The computation lives in libsss.so (hand-written HIP kernels behind the C ABI of
 include/sss.h); this package is its thin Python binding:
 
-  * ``selective_scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None)`` -> (y, h_last)
+  * ``selective_scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None)`` -> (y, h_last);
+    keywords ``delta_bias``, ``delta_softplus``, ``exact_zoh`` select the options of
+    ``selective_scan_fwd_ex``
   * ``selective_state_update(x, delta, A, B, C, D=None, z=None, state=...)`` -> y (one
     decode step; ``state`` is updated in place)
   * ``elementwise_scan(x, A, B, C, h0=None)`` -> (y, h_last)
@@ -11,7 +13,8 @@ include/sss.h); this package is its thin Python binding:
 
 ``inputs`` holds the seeded synthetic workload generators.
 """
-from ._lib import (EXPORTED, LIB_PATH, SSSError, SSS_BF16, SSS_F32, elementwise_scan, elementwise_scan_raw,
+from ._lib import (EXPORTED, LIB_PATH, SSSError, SSS_BF16, SSS_DELTA_SOFTPLUS, SSS_EXACT_ZOH, SSS_F32,
+                   elementwise_scan, elementwise_scan_raw, selective_scan_fwd_ex_raw,
                    elementwise_scan_workspace_size, load, selective_scan_fwd, selective_scan_fwd_raw,
                    selective_scan_fwd_workspace_size, selective_state_update, selective_state_update_raw,
                    status_string)
@@ -19,4 +22,4 @@ from ._lib import (EXPORTED, LIB_PATH, SSSError, SSS_BF16, SSS_F32, elementwise_
 __all__ = ["selective_scan_fwd", "selective_state_update", "selective_state_update_raw", "elementwise_scan",
            "selective_scan_fwd_workspace_size",
            "elementwise_scan_workspace_size", "selective_scan_fwd_raw", "elementwise_scan_raw", "status_string",
-           "SSSError", "SSS_F32", "SSS_BF16", "LIB_PATH", "EXPORTED", "load"]
+           "SSSError", "SSS_F32", "SSS_BF16", "SSS_EXACT_ZOH", "SSS_DELTA_SOFTPLUS", "selective_scan_fwd_ex_raw", "LIB_PATH", "EXPORTED", "load"]

@@ -17,7 +17,9 @@ SSS_F32, SSS_BF16 = 0, 1
 STATUS = {0: "SSS_OK", -1: "SSS_ERR_NULL_ARG", -2: "SSS_ERR_BAD_DIM", -3: "SSS_ERR_UNSUPPORTED",
           -4: "SSS_ERR_WORKSPACE", -5: "SSS_ERR_ALIAS", -6: "SSS_ERR_HIP"}
 
-EXPORTED = ("selective_scan_fwd", "selective_scan_fwd_workspace_size", "selective_state_update",
+SSS_EXACT_ZOH, SSS_DELTA_SOFTPLUS = 1, 2
+
+EXPORTED = ("selective_scan_fwd", "selective_scan_fwd_ex", "selective_scan_fwd_workspace_size", "selective_state_update",
             "elementwise_scan", "elementwise_scan_workspace_size", "sss_status_string")
 
 
@@ -40,6 +42,8 @@ def load() -> ctypes.CDLL:
         vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
         lib.selective_scan_fwd.argtypes = [vp] * 10 + [i64] * 4 + [i32, vp, sz, vp]
         lib.selective_scan_fwd.restype = i32
+        lib.selective_scan_fwd_ex.argtypes = [vp] * 11 + [ctypes.c_uint] + [i64] * 4 + [i32, vp, sz, vp]
+        lib.selective_scan_fwd_ex.restype = i32
         lib.selective_scan_fwd_workspace_size.argtypes = [i64] * 4 + [i32]
         lib.selective_scan_fwd_workspace_size.restype = sz
         lib.selective_state_update.argtypes = [vp] * 9 + [i64] * 3 + [i32, vp]
@@ -64,6 +68,12 @@ def selective_scan_fwd_raw(x, delta, A, B, C, D_skip, z, h0, y, h_last, batch, s
     """Direct call of the C function with integer pointers (0 = NULL)."""
     return load().selective_scan_fwd(x, delta, A, B, C, D_skip, z, h0, y, h_last, batch, seqlen, dim, dstate,
                                      io_dtype, workspace, workspace_bytes, stream)
+
+
+def selective_scan_fwd_ex_raw(x, delta, A, B, C, D_skip, z, h0, y, h_last, delta_bias, flags, batch, seqlen, dim,
+                              dstate, io_dtype, workspace, workspace_bytes, stream) -> int:
+    return load().selective_scan_fwd_ex(x, delta, A, B, C, D_skip, z, h0, y, h_last, delta_bias, flags, batch, seqlen,
+                                        dim, dstate, io_dtype, workspace, workspace_bytes, stream)
 
 
 def selective_state_update_raw(x, delta, A, B, C, D_skip, z, state, y, batch, dim, dstate, io_dtype, stream) -> int:
@@ -104,11 +114,14 @@ def _need(t, name, dtype, shape, device):
 
 
 def selective_scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, return_last=True, out=None,
-                       out_last=None, workspace=None, stream=None):
+                       out_last=None, workspace=None, stream=None, delta_bias=None, delta_softplus=False,
+                       exact_zoh=False):
     """y (batch, seqlen, dim) float32 [, h_last (batch, dim, dstate) float32].
 
     x, delta, z: float32 or bfloat16 (one dtype); A (dim, dstate), B, C (batch, seqlen,
     dstate), D (dim), h0 (batch, dim, dstate): float32.  All on one GPU, contiguous.
+    delta_bias (dim) float32 / delta_softplus / exact_zoh select selective_scan_fwd_ex's
+    options (step size softplus(delta + bias); exact zero-order-hold input term).
     """
     import torch
     dev = x.device
@@ -134,10 +147,13 @@ def selective_scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, return_las
     wsb = selective_scan_fwd_workspace_size(batch, seqlen, dim, dstate, dev.index or 0)
     if workspace is None and wsb > 0:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    _need(delta_bias, "delta_bias", f32, (dim,), dev)
     st = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
-    rc = selective_scan_fwd_raw(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y),
-                                _ptr(hl), batch, seqlen, dim, dstate, SSS_BF16 if io == torch.bfloat16 else SSS_F32,
-                                _ptr(workspace), 0 if workspace is None else workspace.numel(), st)
+    flags = (SSS_EXACT_ZOH if exact_zoh else 0) | (SSS_DELTA_SOFTPLUS if delta_softplus else 0)
+    rc = selective_scan_fwd_ex_raw(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+                                   _ptr(y), _ptr(hl), _ptr(delta_bias), flags, batch, seqlen, dim, dstate,
+                                   SSS_BF16 if io == torch.bfloat16 else SSS_F32, _ptr(workspace),
+                                   0 if workspace is None else workspace.numel(), st)
     if rc != 0:
         raise SSSError(rc, "selective_scan_fwd")
     return (y, hl) if return_last or out_last is not None else y

@@ -112,20 +112,30 @@ int selective_scan_fwd(const void* x, const void* delta, const float* A, const f
                        const float* D_skip, const void* z, const float* h0, float* y, float* h_last,
                        int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
                        void* workspace, size_t workspace_bytes, sss_stream_t stream) {
+  return selective_scan_fwd_ex(x, delta, A, B, C, D_skip, z, h0, y, h_last, nullptr, 0u, batch, seqlen, dim, dstate,
+                               io_dtype, workspace, workspace_bytes, stream);
+}
+
+int selective_scan_fwd_ex(const void* x, const void* delta, const float* A, const float* B, const float* C,
+                          const float* D_skip, const void* z, const float* h0, float* y, float* h_last,
+                          const float* delta_bias, unsigned flags, int64_t batch, int64_t seqlen, int64_t dim,
+                          int64_t dstate, int io_dtype, void* workspace, size_t workspace_bytes,
+                          sss_stream_t stream) {
   if (!x || !delta || !A || !B || !C || !y) return SSS_ERR_NULL_ARG;
   int st = sel_dims_ok(batch, seqlen, dim, dstate);
   if (st != SSS_OK) return st;
   if (io_dtype != SSS_F32 && io_dtype != SSS_BF16) return SSS_ERR_UNSUPPORTED;
-  const void* ptrs[] = {x, delta, A, B, C, D_skip, z, h0, y, h_last, workspace};
+  if ((flags & ~(unsigned)(SSS_EXACT_ZOH | SSS_DELTA_SOFTPLUS)) != 0) return SSS_ERR_UNSUPPORTED;
+  const void* ptrs[] = {x, delta, A, B, C, D_skip, z, h0, y, h_last, workspace, delta_bias};
   for (const void* p : ptrs)
     if (!aligned16(p)) return SSS_ERR_UNSUPPORTED;
   const int64_t es = io_dtype == SSS_BF16 ? 2 : 4;
   const int64_t E = batch * seqlen * dim;
   const int64_t y_bytes = E * 4, hl_bytes = batch * dim * dstate * 4;
-  const void* in_p[] = {x, delta, A, B, C, D_skip, z, h0};
+  const void* in_p[] = {x, delta, A, B, C, D_skip, z, h0, delta_bias};
   const int64_t in_b[] = {E * es, E * es, dim * dstate * 4, batch * seqlen * dstate * 4,
-                          batch * seqlen * dstate * 4, dim * 4, E * es, batch * dim * dstate * 4};
-  for (int i = 0; i < 8; ++i) {
+                          batch * seqlen * dstate * 4, dim * 4, E * es, batch * dim * dstate * 4, dim * 4};
+  for (int i = 0; i < 9; ++i) {
     if (overlap(y, y_bytes, in_p[i], in_b[i])) return SSS_ERR_ALIAS;
     if (overlap(h_last, hl_bytes, in_p[i], in_b[i])) return SSS_ERR_ALIAS;
   }
@@ -141,13 +151,13 @@ int selective_scan_fwd(const void* x, const void* delta, const float* A, const f
     if (workspace == nullptr || workspace_bytes < pl.ws_total) return SSS_ERR_WORKSPACE;
     const int64_t wb = (int64_t)pl.ws_total;
     if (overlap(workspace, wb, y, y_bytes) || overlap(workspace, wb, h_last, hl_bytes)) return SSS_ERR_ALIAS;
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 9; ++i)
       if (overlap(workspace, wb, in_p[i], in_b[i])) return SSS_ERR_ALIAS;
   }
   if (env_int("SSS_LOG", 0))
-    std::fprintf(stderr, "[sss] selective_scan_fwd B=%lld L=%lld D=%lld N=%lld %s: segments=%d seg_len=%lld ws=%zu\n",
+    std::fprintf(stderr, "[sss] selective_scan_fwd B=%lld L=%lld D=%lld N=%lld %s flags=%u: segments=%d seg_len=%lld ws=%zu\n",
                  (long long)batch, (long long)seqlen, (long long)dim, (long long)dstate,
-                 io_dtype == SSS_BF16 ? "bf16" : "f32", pl.segments, (long long)pl.seg_len, pl.ws_total);
+                 io_dtype == SSS_BF16 ? "bf16" : "f32", flags, pl.segments, (long long)pl.seg_len, pl.ws_total);
   SelArgs a{};
   a.x = x;
   a.delta = delta;
@@ -165,6 +175,9 @@ int selective_scan_fwd(const void* x, const void* delta, const float* A, const f
   a.dstate = (int)dstate;
   a.bf16 = io_dtype == SSS_BF16;
   a.workspace = workspace;
+  a.delta_bias = delta_bias;
+  a.softplus = (flags & SSS_DELTA_SOFTPLUS) != 0;
+  a.exact_zoh = (flags & SSS_EXACT_ZOH) != 0;
   hipError_t e = launch_selective(a, pl, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? SSS_OK : SSS_ERR_HIP;
 }

@@ -28,6 +28,9 @@ struct SelArgs {
   int dstate;
   int bf16;
   void* workspace;
+  const float* delta_bias;  // nullable: added to delta before use
+  int softplus;             // step size = softplus(delta (+ bias))
+  int exact_zoh;            // input term expm1(delta*A)/A * B instead of delta * B
 };
 
 SelPlan plan_selective(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int num_cus);

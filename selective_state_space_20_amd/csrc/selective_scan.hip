@@ -44,6 +44,34 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7FFFFFFF, 0x00020000);
 }
 
+constexpr int kZoh = 1, kFront = 2, kSoftplus = 4;
+
+// softplus(v) = max(v, 0) + log1p(e^-|v|); log1p through the log(u) * e / (u - 1) form so
+// that small e keeps its relative precision.
+__device__ __forceinline__ float softplus_f(float v) {
+  const float e = fast_exp2(-fabsf(v) * kLog2e);
+  const float u = 1.0f + e;
+  const float l = u == 1.0f ? e : __builtin_amdgcn_logf(u) * kLn2 * e * fast_rcp(u - 1.0f);
+  return fmaxf(v, 0.0f) + l;
+}
+
+// The step size the recurrence uses: the stored delta, or delta + bias (then softplus).
+template <int FL>
+__device__ __forceinline__ float step_size(float raw, float bias) {
+  if constexpr ((FL & kFront) == 0) return raw;
+  const float v = raw + bias;
+  if constexpr ((FL & kSoftplus) != 0) return softplus_f(v);
+  return v;
+}
+
+// e^x - 1 for x = arg * ln 2 given e2 = 2^arg: a short Taylor series where |x| < 1/16 (no
+// cancellation), else e2 - 1.
+__device__ __forceinline__ float expm1_of_log2(float arg, float e2) {
+  const float xn = arg * kLn2;
+  const float p = xn * __builtin_fmaf(xn, __builtin_fmaf(xn, __builtin_fmaf(xn, 1.0f / 24.0f, 1.0f / 6.0f), 0.5f), 1.0f);
+  return fabsf(xn) < 0.0625f ? p : e2 - 1.0f;
+}
+
 struct SelSeg {
   int64_t batch, L, D, seg_len;
   int N, S, ngroups;  // ngroups = ceil(D / 64)
@@ -55,14 +83,18 @@ struct SelSeg {
 // PASS 1 (segments 0..S-2): seg_state[s][b][n][d] = end state from zero, seg_dsum[s][b][d].
 // PASS 2 (segments 0..S-1): y, and h_last from the last segment; entering state from
 //         carry[s][b][n][d] (S > 1) or h0 (S == 1).
-template <int NS, bool BF16, int PASS, bool HAS_Z>
+// FL: bit kZoh -- exact zero-order-hold input term, expm1(delta*A)/A * B instead of
+//     delta * B; bits kFront / kSoftplus -- the step size is delta + bias[d], then (with
+//     kSoftplus) softplus of it.
+template <int NS, bool BF16, int PASS, bool HAS_Z, int FL>
 __global__ __launch_bounds__(256, min_waves_per_simd(NS)) void sel_seq_kernel(const void* __restrict__ x, const void* __restrict__ delta,
                                                      const float* __restrict__ A, const float* __restrict__ Bm,
                                                      const float* __restrict__ Cm, const float* __restrict__ Dsk,
                                                      const void* __restrict__ z, const float* __restrict__ h0,
                                                      const float* __restrict__ carry, float* __restrict__ y,
                                                      float* __restrict__ h_last, float* __restrict__ seg_state,
-                                                     float* __restrict__ seg_dsum, SelSeg g) {
+                                                     float* __restrict__ seg_dsum, const float* __restrict__ dbias,
+                                                     SelSeg g) {
   // Workgroup = gpb waves on adjacent channel groups and the SAME time segment, so that the
   // scalar B_t/C_t rows one wave fetches are scalar-cache hits for the others.
   const int lane = threadIdx.x & 63;
@@ -84,10 +116,17 @@ __global__ __launch_bounds__(256, min_waves_per_simd(NS)) void sel_seq_kernel(co
   const int len = (int)(min(tbeg + g.seg_len, g.L) - tbeg);  // < 2^30 (plan)
   const int N = NS;
 
+  constexpr bool zoh = (FL & kZoh) != 0;
   float a2[NS], h[NS];
+  float ia[zoh ? NS : 1], az[zoh ? NS : 1];  // exact hold: 1/A[n] and (A[n] == 0)
 #pragma unroll
   for (int n = 0; n < NS; ++n) {
-    a2[n] = fmaxf(A[dc * N + n] * kLog2e, -kFltMax);  // -inf clamped so that 0*a2 = 0
+    const float an = A[dc * N + n];
+    a2[n] = fmaxf(an * kLog2e, -kFltMax);  // -inf clamped so that 0*a2 = 0
+    if constexpr (zoh) {
+      ia[n] = an != 0.0f ? 1.0f / an : 0.0f;
+      az[n] = an != 0.0f ? 0.0f : 1.0f;
+    }
     if (PASS == 1) {
       h[n] = 0.0f;
     } else if (g.S > 1) {
@@ -97,6 +136,7 @@ __global__ __launch_bounds__(256, min_waves_per_simd(NS)) void sel_seq_kernel(co
     }
   }
   const float Dd = (PASS == 2 && Dsk != nullptr) ? Dsk[dc] : 0.0f;
+  const float dbv = ((FL & kFront) != 0 && dbias != nullptr) ? dbias[dc] : 0.0f;
   constexpr bool has_z = PASS == 2 && HAS_Z;
   float dsum = 0.0f;
 
@@ -140,12 +180,19 @@ __global__ __launch_bounds__(256, min_waves_per_simd(NS)) void sel_seq_kernel(co
   do {                                                                           \
     const float* Bt = Br + (T) * N;                                              \
     const float* Ct = Cr + (T) * N;                                              \
-    const float xv = wid(xq[SLOT][I]), dl = wid(dq[SLOT][I]);                    \
+    const float xv = wid(xq[SLOT][I]);                                           \
+    const float dl = step_size<FL>(wid(dq[SLOT][I]), dbv);                       \
     const float dx = dl * xv;                                                    \
     float y0 = Dd * xv, y1 = 0.0f;                                               \
     _Pragma("unroll") for (int n = 0; n < NS; ++n) {                             \
-      const float ab = fast_exp2(dl * a2[n]);                                    \
-      h[n] = __builtin_fmaf(ab, h[n], dx * Bt[n]);                               \
+      const float arg = dl * a2[n];                                              \
+      const float ab = fast_exp2(arg);                                           \
+      if constexpr (zoh) {                                                       \
+        const float cf = __builtin_fmaf(expm1_of_log2(arg, ab), ia[n], dl * az[n]); \
+        h[n] = __builtin_fmaf(ab, h[n], cf * (xv * Bt[n]));                      \
+      } else {                                                                   \
+        h[n] = __builtin_fmaf(ab, h[n], dx * Bt[n]);                             \
+      }                                                                          \
       if (PASS == 2) {                                                           \
         if (n & 1) y1 = __builtin_fmaf(Ct[n], h[n], y1);                         \
         else y0 = __builtin_fmaf(Ct[n], h[n], y0);                               \
@@ -198,7 +245,7 @@ __global__ __launch_bounds__(256, min_waves_per_simd(NS)) void sel_seq_kernel(co
 // Loads of a batch of segments are issued before the serial fma chain consumes them.
 constexpr int kCarryBatch = 8;
 
-__global__ __launch_bounds__(256) void sel_carry_kernel(const float* __restrict__ A, const float* __restrict__ h0,
+static __global__ __launch_bounds__(256) void sel_carry_kernel(const float* __restrict__ A, const float* __restrict__ h0,
                                                         float* slots, const float* __restrict__ seg_dsum, SelSeg g) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t per_b = (int64_t)g.N * g.D;
@@ -226,6 +273,80 @@ __global__ __launch_bounds__(256) void sel_carry_kernel(const float* __restrict_
     }
   }
 }
+
+template <int NS, bool BF16, int FL>
+static hipError_t run_selective(const SelArgs& a, const SelPlan& pl, hipStream_t stream) {
+  SelSeg g{};
+  g.batch = a.batch;
+  g.L = a.seqlen;
+  g.D = a.dim;
+  g.seg_len = pl.seg_len;
+  g.N = NS;
+  g.S = pl.segments;
+  g.ngroups = (int)((a.dim + 63) / 64);
+  g.gpb = std::min(2, g.ngroups);
+  g.nblk = (g.ngroups + g.gpb - 1) / g.gpb;
+  unsigned char* ws = static_cast<unsigned char*>(a.workspace);
+  float* st = pl.segments > 1 ? reinterpret_cast<float*>(ws + pl.ws_state) : nullptr;
+  float* ds = pl.segments > 1 ? reinterpret_cast<float*>(ws + pl.ws_dsum) : nullptr;
+  const int64_t per_seg = (int64_t)g.nblk * g.batch;
+  const unsigned nthr_wg = 64u * (unsigned)g.gpb;
+  if (pl.segments > 1) {
+    hipLaunchKernelGGL((sel_seq_kernel<NS, BF16, 1, false, FL>), dim3((unsigned)(per_seg * (pl.segments - 1))),
+                       dim3(nthr_wg), 0, stream, a.x, a.delta, a.A, a.B, a.C, a.Dsk, a.z, a.h0, (const float*)nullptr,
+                       a.y, a.h_last, st, ds, a.delta_bias, g);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t nthr = g.batch * (int64_t)NS * g.D;
+    hipLaunchKernelGGL(sel_carry_kernel, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, stream, a.A, a.h0, st,
+                       (const float*)ds, g);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.z != nullptr)
+    hipLaunchKernelGGL((sel_seq_kernel<NS, BF16, 2, true, FL>), dim3((unsigned)(per_seg * pl.segments)), dim3(nthr_wg),
+                       0, stream, a.x, a.delta, a.A, a.B, a.C, a.Dsk, a.z, a.h0, (const float*)st, a.y, a.h_last,
+                       (float*)nullptr, (float*)nullptr, a.delta_bias, g);
+  else
+    hipLaunchKernelGGL((sel_seq_kernel<NS, BF16, 2, false, FL>), dim3((unsigned)(per_seg * pl.segments)),
+                       dim3(nthr_wg), 0, stream, a.x, a.delta, a.A, a.B, a.C, a.Dsk, a.z, a.h0, (const float*)st, a.y,
+                       a.h_last, (float*)nullptr, (float*)nullptr, a.delta_bias, g);
+  return hipGetLastError();
+}
+
+// Front end / hold variants: plain, exact hold, delta + bias (+ softplus), and both.
+template <int NS, bool BF16>
+hipError_t run_flags(const SelArgs& a, const SelPlan& pl, hipStream_t stream) {
+  const bool front = a.delta_bias != nullptr || a.softplus;
+  const int fl = (a.exact_zoh ? kZoh : 0) | (front ? kFront : 0) | (a.softplus ? kSoftplus : 0);
+  switch (fl) {
+    case 0: return run_selective<NS, BF16, 0>(a, pl, stream);
+    case kZoh: return run_selective<NS, BF16, kZoh>(a, pl, stream);
+    case kFront: return run_selective<NS, BF16, kFront>(a, pl, stream);
+    case kFront | kSoftplus: return run_selective<NS, BF16, kFront | kSoftplus>(a, pl, stream);
+    case kZoh | kFront: return run_selective<NS, BF16, kZoh | kFront>(a, pl, stream);
+    case kZoh | kFront | kSoftplus: return run_selective<NS, BF16, kZoh | kFront | kSoftplus>(a, pl, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Explicit instances: the file is compiled once per state count (SSS_INST_NS = N) and once
+// for the host part (plan and dispatch), so that the builds of the instances run in parallel.
+#ifdef SSS_INST_NS
+template hipError_t run_flags<SSS_INST_NS, false>(const SelArgs&, const SelPlan&, hipStream_t);
+template hipError_t run_flags<SSS_INST_NS, true>(const SelArgs&, const SelPlan&, hipStream_t);
+#else
+#define SSS_EXTERN_INSTANCES(N)                                                                     \
+  extern template hipError_t run_flags<N, false>(const SelArgs&, const SelPlan&, hipStream_t);  \
+  extern template hipError_t run_flags<N, true>(const SelArgs&, const SelPlan&, hipStream_t);
+SSS_EXTERN_INSTANCES(1)
+SSS_EXTERN_INSTANCES(2)
+SSS_EXTERN_INSTANCES(4)
+SSS_EXTERN_INSTANCES(8)
+SSS_EXTERN_INSTANCES(16)
+SSS_EXTERN_INSTANCES(32)
+SSS_EXTERN_INSTANCES(64)
+#undef SSS_EXTERN_INSTANCES
 
 // ------------------------------------------------------------------ host side
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -267,56 +388,16 @@ SelPlan plan_selective(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstat
   return pl;
 }
 
-template <int NS, bool BF16>
-static hipError_t run_selective(const SelArgs& a, const SelPlan& pl, hipStream_t stream) {
-  SelSeg g{};
-  g.batch = a.batch;
-  g.L = a.seqlen;
-  g.D = a.dim;
-  g.seg_len = pl.seg_len;
-  g.N = NS;
-  g.S = pl.segments;
-  g.ngroups = (int)((a.dim + 63) / 64);
-  g.gpb = std::min(2, g.ngroups);
-  g.nblk = (g.ngroups + g.gpb - 1) / g.gpb;
-  unsigned char* ws = static_cast<unsigned char*>(a.workspace);
-  float* st = pl.segments > 1 ? reinterpret_cast<float*>(ws + pl.ws_state) : nullptr;
-  float* ds = pl.segments > 1 ? reinterpret_cast<float*>(ws + pl.ws_dsum) : nullptr;
-  const int64_t per_seg = (int64_t)g.nblk * g.batch;
-  const unsigned nthr_wg = 64u * (unsigned)g.gpb;
-  if (pl.segments > 1) {
-    hipLaunchKernelGGL((sel_seq_kernel<NS, BF16, 1, false>), dim3((unsigned)(per_seg * (pl.segments - 1))), dim3(nthr_wg), 0,
-                       stream, a.x, a.delta, a.A, a.B, a.C, a.Dsk, a.z, a.h0, (const float*)nullptr, a.y, a.h_last,
-                       st, ds, g);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int64_t nthr = g.batch * (int64_t)NS * g.D;
-    hipLaunchKernelGGL(sel_carry_kernel, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, stream, a.A, a.h0, st,
-                       (const float*)ds, g);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (a.z != nullptr)
-    hipLaunchKernelGGL((sel_seq_kernel<NS, BF16, 2, true>), dim3((unsigned)(per_seg * pl.segments)), dim3(nthr_wg), 0,
-                       stream, a.x, a.delta, a.A, a.B, a.C, a.Dsk, a.z, a.h0, (const float*)st, a.y, a.h_last,
-                       (float*)nullptr, (float*)nullptr, g);
-  else
-    hipLaunchKernelGGL((sel_seq_kernel<NS, BF16, 2, false>), dim3((unsigned)(per_seg * pl.segments)), dim3(nthr_wg), 0,
-                       stream, a.x, a.delta, a.A, a.B, a.C, a.Dsk, a.z, a.h0, (const float*)st, a.y, a.h_last,
-                       (float*)nullptr, (float*)nullptr, g);
-  return hipGetLastError();
-}
-
 template <bool BF16>
 static hipError_t dispatch_n(const SelArgs& a, const SelPlan& pl, hipStream_t stream) {
   switch (a.dstate) {
-    case 1: return run_selective<1, BF16>(a, pl, stream);
-    case 2: return run_selective<2, BF16>(a, pl, stream);
-    case 4: return run_selective<4, BF16>(a, pl, stream);
-    case 8: return run_selective<8, BF16>(a, pl, stream);
-    case 16: return run_selective<16, BF16>(a, pl, stream);
-    case 32: return run_selective<32, BF16>(a, pl, stream);
-    case 64: return run_selective<64, BF16>(a, pl, stream);
+    case 1: return run_flags<1, BF16>(a, pl, stream);
+    case 2: return run_flags<2, BF16>(a, pl, stream);
+    case 4: return run_flags<4, BF16>(a, pl, stream);
+    case 8: return run_flags<8, BF16>(a, pl, stream);
+    case 16: return run_flags<16, BF16>(a, pl, stream);
+    case 32: return run_flags<32, BF16>(a, pl, stream);
+    case 64: return run_flags<64, BF16>(a, pl, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -324,5 +405,7 @@ static hipError_t dispatch_n(const SelArgs& a, const SelPlan& pl, hipStream_t st
 hipError_t launch_selective(const SelArgs& a, const SelPlan& pl, hipStream_t stream) {
   return a.bf16 ? dispatch_n<true>(a, pl, stream) : dispatch_n<false>(a, pl, stream);
 }
+
+#endif  // SSS_INST_NS
 
 }  // namespace sss

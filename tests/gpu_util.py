@@ -22,7 +22,8 @@ def to_dev(a, dev):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
-def run_selective(inp, dev="cuda:0", return_last=True, fill=float("nan")):
+def run_selective(inp, dev="cuda:0", return_last=True, fill=float("nan"), **options):
+    """options: delta_bias (numpy), delta_softplus, exact_zoh -- selective_scan_fwd_ex."""
     import torch
     import selective_state_space_20_amd as sss
     t = {k: to_dev(v, dev) for k, v in inp.items() if k != "io"}
@@ -30,8 +31,10 @@ def run_selective(inp, dev="cuda:0", return_last=True, fill=float("nan")):
     n = inp["A"].shape[1]
     y = torch.full((bt, L, dm), fill, dtype=torch.float32, device=dev)
     hl = torch.full((bt, dm, n), fill, dtype=torch.float32, device=dev) if return_last else None
+    if options.get("delta_bias") is not None:
+        options = dict(options, delta_bias=to_dev(options["delta_bias"], dev))
     sss.selective_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"], out=y,
-                           out_last=hl, return_last=return_last)
+                           out_last=hl, return_last=return_last, **options)
     torch.cuda.synchronize()
     return y.cpu().numpy(), (hl.cpu().numpy() if hl is not None else None)
 

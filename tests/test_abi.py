@@ -63,6 +63,22 @@ def ew(**kw):
     return sss.elementwise_scan_raw(**a)
 
 
+def selx(**kw):
+    a = dict(x=P, delta=2 * P, A=3 * P, B=4 * P, C=5 * P, D_skip=0, z=0, h0=0, y=64 * P, h_last=0, delta_bias=0,
+             flags=0, batch=2, seqlen=8, dim=4, dstate=4, io_dtype=0, workspace=0, workspace_bytes=0, stream=0)
+    a.update(kw)
+    return sss.selective_scan_fwd_ex_raw(**a)
+
+
+def test_selective_ex_rejections():
+    assert selx(x=0) == NULL_ARG
+    assert selx(flags=4) == UNSUPPORTED                 # unknown option bit
+    assert selx(flags=1 << 31) == UNSUPPORTED
+    assert selx(delta_bias=6 * P + 4) == UNSUPPORTED    # misaligned bias
+    assert selx(y=6 * P, delta_bias=6 * P) == ALIAS     # y over the bias
+    assert selx(dim=0, flags=3) == BAD_DIM
+
+
 def upd(**kw):
     a = dict(x=P, delta=2 * P, A=3 * P, B=4 * P, C=5 * P, D_skip=0, z=0, state=32 * P, y=64 * P, batch=2, dim=4,
              dstate=4, io_dtype=0, stream=0)
@@ -144,5 +160,6 @@ def test_no_device_reports_hip_error():
     if torch.cuda.device_count() > 0:
         pytest.skip("a GPU is present; this checks the no-device path")
     assert sel() == HIP
+    assert selx(flags=3, delta_bias=6 * P) == HIP
     assert ew() == HIP
     assert upd() == HIP

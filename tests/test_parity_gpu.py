@@ -117,6 +117,58 @@ def test_selective_guard_bands():
         assert torch.all(buf[:pad] == 12345.0) and torch.all(buf[-pad:] == 12345.0)
 
 
+# ---------------------------------------------------------------- options: exact hold, delta front end
+OPT_CASES = [  # (batch, seqlen, dim, dstate, io, exact_zoh, bias, softplus, forced segments)
+    (2, 1000, 100, 16, "f32", True, False, False, 0),
+    (1, 3000, 40, 16, "bf16", True, False, False, 3),
+    (2, 777, 70, 8, "f32", False, True, True, 0),
+    (3, 2100, 33, 16, "bf16", False, True, True, 5),
+    (2, 500, 64, 4, "f32", False, True, False, 0),
+    (2, 1500, 50, 32, "f32", True, True, True, 2),
+    (1, 700, 20, 64, "bf16", True, True, True, 0),
+]
+
+
+@pytest.mark.parametrize("case", OPT_CASES, ids=[f"L{c[1]}D{c[2]}N{c[3]}{c[4]}z{int(c[5])}b{int(c[6])}s{int(c[7])}S{c[8]}"
+                                                  for c in OPT_CASES])
+def test_selective_options(oracle_lib, monkeypatch, case):
+    """selective_scan_fwd_ex: exact zero-order hold and the delta front end (bias, softplus),
+    alone and together, also across a forced two-pass split."""
+    bt, L, dm, n, io, zoh, with_bias, sp, segs = case
+    if segs:
+        monkeypatch.setenv("SSS_FORCE_SEGMENTS", str(segs))
+    seed = zlib.crc32(repr(case).encode()) % 100000
+    inp = gen.selective_inputs(bt, L, dm, n, io=io, with_D=True, with_z=True, h0=True, seed=seed)
+    rng = np.random.default_rng(seed + 1)
+    if sp:  # raw step sizes before softplus: spread over both tails
+        raw = rng.normal(-3.0, 2.5, size=inp["x"].shape).astype(np.float32)
+        inp["delta"] = gen.f32_to_bf16_bits(raw) if io == "bf16" else raw
+    bias = None
+    if with_bias:  # without softplus the step must stay positive, or the state grows without bound
+        bias = (0.5 * rng.standard_normal(dm) if sp else 0.01 * np.abs(rng.standard_normal(dm))).astype(np.float32)
+    note(f"[options] {case}")
+    y, hl = run_selective(inp, delta_bias=bias, delta_softplus=sp, exact_zoh=zoh)
+    yr, hr = oracle_lib.selective_scan(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                                       inp["h0"], exact_zoh=zoh, delta_bias=bias, delta_softplus=sp)
+    tol = TOL_BF16 if io == "bf16" else TOL_F32
+    ey, eh = rel_err(y, yr), rel_err(hl, hr)
+    note(f"    err y={ey:.3e} h_last={eh:.3e}")
+    assert ey <= tol and eh <= tol
+
+
+def test_selective_exact_zoh_special_values(oracle_lib):
+    """Exact hold where A = 0 (input term delta*B), A = -inf (no input term) and for tiny
+    delta*A (the series branch of expm1)."""
+    inp = gen.selective_inputs(2, 2000, 12, 16, io="f32", with_D=True, with_z=False, h0=True, seed=95)
+    inp["A"][:, :4] = 0.0
+    inp["A"][:, 4:6] = -np.inf
+    inp["delta"][:, :, 6:] *= 1e-4
+    y, hl = run_selective(inp, exact_zoh=True)
+    yr, hr = oracle_lib.selective_scan(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                                       inp["h0"], exact_zoh=True)
+    assert rel_err(y, yr) <= TOL_F32 and rel_err(hl, hr) <= TOL_F32
+
+
 # ---------------------------------------------------------------- decode step
 UPD_CASES = [  # (batch, dim, dstate, io, D, z)
     (1, 1, 1, "f32", False, False),
