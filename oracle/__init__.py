@@ -59,8 +59,9 @@ def _load():
         lib.oracle_elementwise_scan_channels.argtypes = [vp] * 5 + [vp, i64, vp, vp] + [i64] * 3 + [i32]
         lib.oracle_elementwise_scan_chunked.argtypes = [vp] * 7 + [i64] * 4 + [i32]
         lib.oracle_selective_state_update.argtypes = [vp] * 10 + [i64] * 3 + [i32] * 2
+        lib.oracle_causal_conv1d.argtypes = [vp] * 4 + [i64] * 4 + [i32] * 3
         for f in ("oracle_selective_scan", "oracle_selective_scan_channels", "oracle_selective_scan_chunked",
-                  "oracle_selective_state_update",
+                  "oracle_selective_state_update", "oracle_causal_conv1d",
                   "oracle_elementwise_scan", "oracle_elementwise_scan_channels",
                   "oracle_elementwise_scan_chunked", "oracle_max_threads"):
             getattr(lib, f).restype = ctypes.c_int
@@ -172,6 +173,18 @@ def selective_state_update(x, delta, A, B, C, D=None, z=None, state=None, *, nth
                                                _p(y), _p(st), bt, dm, n, _io_code(x), nthreads)
     _check(rc)
     return y, st
+
+
+def causal_conv1d(x, weight, bias=None, *, silu=False, nthreads=0):
+    """x: (Bt, L, Dm) float32 or bf16 bits; weight: (Dm, W); bias: (Dm,).  Returns float64 out."""
+    x = _io(x)
+    weight, bias = _f32(weight), _f32(bias)
+    bt, L, dm = x.shape
+    out = np.empty((bt, L, dm), dtype=np.float64)
+    rc = _load().oracle_causal_conv1d(_p(x), _p(weight), _p(bias), _p(out), bt, L, dm, weight.shape[1], _io_code(x),
+                                      int(bool(silu)), nthreads)
+    _check(rc)
+    return out
 
 
 def elementwise_scan(x, A, B, C, h0=None, *, return_last=True, nthreads=0):

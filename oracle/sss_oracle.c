@@ -223,6 +223,36 @@ int oracle_selective_state_update(const void* x, const void* delta, const float*
 }
 
 /*
+ * Causal depthwise convolution in front of the scan -- [P5] "5.3. Toi uu hoa Kernel Fusion
+ * cho Mamba SSM" names the causal_conv1d kernel of the Mamba block; the operation is the
+ * usual one (reading of the build): per channel d, width W,
+ *   out[b,t,d] = bias[d] + sum_{k<W} w[d,k] * x[b, t-(W-1)+k, d]   (x = 0 before t = 0)
+ * then optionally silu(out).  Layouts: x (B, L, D) in dtype; w (D, W); bias (D), nullable;
+ * out (B, L, D) double.
+ */
+int oracle_causal_conv1d(const void* x, const float* w, const float* bias, double* out, int64_t batch, int64_t L,
+                         int64_t Dm, int64_t W, int dtype, int apply_silu, int nthreads) {
+  if (!x || !w || !out || batch < 1 || L < 1 || Dm < 1 || W < 1) return OR_ERR_ARG;
+  if (dtype != OR_F32 && dtype != OR_BF16) return OR_ERR_ARG;
+  set_threads(nthreads);
+  int64_t nch = batch * Dm;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t c = 0; c < nch; ++c) {
+    int64_t b = c / Dm, d = c % Dm;
+    for (int64_t t = 0; t < L; ++t) {
+      double v = bias ? (double)bias[d] : 0.0;
+      for (int64_t k = 0; k < W; ++k) {
+        int64_t ts = t - (W - 1) + k;
+        if (ts >= 0) v += (double)w[d * W + k] * load_val(x, (b * L + ts) * Dm + d, dtype);
+      }
+      if (apply_silu) v = v / (1.0 + exp(-v));
+      out[(b * L + t) * Dm + d] = v;
+    }
+  }
+  return OR_OK;
+}
+
+/*
  * Elementwise form, one channel -- [P3] "Reference solution":
  *   h = h0[b,d] (or 0); for t: h = A_t*h + B_t*x_t; y_t = C_t*h.
  * All of x, A, B, C are (B, L, D) fp32; h0, h_last (B, D).

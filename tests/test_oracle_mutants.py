@@ -49,6 +49,8 @@ MUTANTS = {
     "update_B_of_batch_0": ("dv * (double)Bm[b * N + n] * xv;", "dv * (double)Bm[n] * xv;"),
     "update_decay_without_delta": ("double h = exp(dv * (double)A[d * N + n])", "double h = exp((double)A[d * N + n])"),
     "update_dropped_skip": ("    if (Dsk) acc += (double)Dsk[d] * xv;", "    (void)Dsk;"),
+    "conv_taps_reversed": ("if (ts >= 0) v += (double)w[d * W + k] *", "if (ts >= 0) v += (double)w[d * W + (W - 1 - k)] *"),
+    "conv_shifted_one_step": ("        int64_t ts = t - (W - 1) + k;", "        int64_t ts = t - W + k;"),
     "front_end_bias_ignored": ("  if (dbias) v += (double)dbias[d];", "  (void)dbias;"),
     "front_end_exp_for_softplus": ("static double softplus(double v) { return v > 0.0 ? v + log1p(exp(-v)) : log1p(exp(v)); }",
                                    "static double softplus(double v) { return exp(v); }"),
@@ -69,6 +71,8 @@ def _pin_calls():
         elif name == "test_M5_brute_force_unrolled":
             for io in ("f32", "bf16"):
                 calls.append((name + io, lambda o, fn=fn, io=io: fn(o, io, True, True, True)))
+        elif name == "test_C1_conv_is_numpy_convolve":
+            calls.append((name, lambda o, fn=fn: fn(o, 4)))
         elif name == "test_U1_decode_step_is_one_step_of_the_scan":
             calls.append((name, lambda o, fn=fn: fn(o, "f32", True, True)))
     return calls

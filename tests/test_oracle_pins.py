@@ -468,3 +468,30 @@ def test_F2_front_end_equals_transformed_delta(oracle_lib):
     dl = np.logaddexp(0.0, raw.astype(np.float64) + bias.astype(np.float64)).astype(np.float32)
     yr, hr = oracle_lib.selective_scan(inp["x"], dl, inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], inp["h0"])
     assert rel_err(y, yr) < 1e-6 and rel_err(hl, hr) < 1e-6
+
+
+# ---------------------------------------------------------------- causal depthwise conv1d
+@pytest.mark.parametrize("width", [1, 2, 4, 7])
+def test_C1_conv_is_numpy_convolve(oracle_lib, width):
+    """Each channel is numpy's full convolution with the reversed taps, cut to the first L
+    outputs (causal, zero history), plus the bias; silu applied after."""
+    rng = np.random.default_rng(100 + width)
+    bt, L, dm = 2, 57, 5
+    x = rng.standard_normal((bt, L, dm)).astype(np.float32)
+    w = rng.standard_normal((dm, width)).astype(np.float32)
+    bias = rng.standard_normal(dm).astype(np.float32)
+    out = oracle_lib.causal_conv1d(x, w, bias)
+    outs = oracle_lib.causal_conv1d(x, w, bias, silu=True)
+    for b in range(bt):
+        for d in range(dm):
+            ref = np.convolve(x[b, :, d].astype(np.float64), w[d, ::-1].astype(np.float64))[:L] + float(bias[d])
+            assert np.allclose(out[b, :, d], ref, rtol=1e-13, atol=1e-13)
+            assert np.allclose(outs[b, :, d], ref / (1.0 + np.exp(-ref)), rtol=1e-13, atol=1e-13)
+
+
+def test_C2_conv_hand_worked(oracle_lib):
+    """Width 3, taps (1, 2, 4) on x = (1, 10, 100): out = (4, 42, 421) exactly (zero history)."""
+    x = np.asarray([1.0, 10.0, 100.0], np.float32).reshape(1, 3, 1)
+    w = np.asarray([[1.0, 2.0, 4.0]], np.float32)
+    out = oracle_lib.causal_conv1d(x, w)
+    assert np.array_equal(out[0, :, 0], [4.0, 42.0, 421.0])
