@@ -11,6 +11,7 @@ once and every output written once, the state never counted) in GB/s.
   python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
   python bench.py --workload 4            # another configuration (0..4); the default is 3
   python bench.py --decode 64             # one decode step of 64 tokens (selective_state_update)
+  python bench.py --conv                  # the causal conv1d front end on the long layer
   python bench.py --copy-calibration      # plain copy of a known size, for counter scaling
 """
 from __future__ import annotations
@@ -201,6 +202,43 @@ def bench_decode(batch, steps, warmup, dim=5120, dstate=16):
     }), flush=True)
 
 
+def bench_conv(steps, warmup, batch=1, seqlen=65536, dim=5120, width=4):
+    """The causal depthwise conv front end (causal_conv1d_fwd, silu, bf16) on the long
+    Mamba-2.8B-shaped layer; bound by streaming x in and out once."""
+    import torch
+    import selective_state_space_20_amd as sss
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(3000)
+    x = torch.randn((batch, seqlen, dim), device=dev, generator=g).to(torch.bfloat16)
+    w = torch.randn((dim, width), device=dev, generator=g)
+    bias = torch.randn((dim,), device=dev, generator=g)
+    out = torch.empty_like(x)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(warmup):
+        sss.causal_conv1d_fwd(x, w, bias, silu=True, out=out)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        sss.causal_conv1d_fwd(x, w, bias, silu=True, out=out)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    mean_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    nbytes = 2 * batch * seqlen * dim * 2 + dim * (width + 1) * 4
+    gbs = nbytes / (mean_ms * 1e-3) / 1e9
+    log(f"[bench] conv1d {batch}x{seqlen}x{dim} W={width}: event mean {mean_ms:.4f} ms")
+    print(json.dumps({
+        "metric": "causal_conv1d_fwd achieved HBM GB/s, 1 GPU", "value": round(gbs, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(mean_ms, 5), "higher_is_better": True,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"conv1d_bf16_b{batch}_L{seqlen}_D{dim}_W{width}_silu", "algorithmic_bytes": nbytes},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "conv1d_kernel",
+                     "call_ms_event_mean": round(mean_ms, 5)},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -209,6 +247,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--workload", type=int, default=WORKLOAD_INDEX, help="configuration index 0..4")
+    ap.add_argument("--conv", action="store_true", help="time the causal conv1d front end instead")
     ap.add_argument("--decode", type=int, default=0, metavar="BATCH",
                     help="time one decode step (selective_state_update) of BATCH tokens instead")
     args = ap.parse_args()
@@ -219,6 +258,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.conv:
+        bench_conv(args.steps, args.warmup)
         return
     if args.decode > 0:
         bench_decode(args.decode, args.steps, args.warmup)

@@ -1,7 +1,7 @@
 /*
  * sss.h -- C ABI of the MI355X (gfx950) selective-scan library, libsss.so.
  *
- * Three operations, all fully computed by hand-written HIP kernels on the device:
+ * Four operations, all fully computed by hand-written HIP kernels on the device:
  *
  *  selective_scan_fwd  -- the selective (input-dependent) state-space recurrence of
  *      "Selective Scan trong Mamba toi uu chuoi dai the nao?" (thecsnote.cc), sections
@@ -17,6 +17,9 @@
  *
  *  selective_state_update -- one decode step of the same recurrence on a carried state
  *      (in place), for token-by-token generation.
+ *
+ *  causal_conv1d_fwd -- the causal depthwise convolution (+ silu) that produces the
+ *      scan's input x in the Mamba block.
  *
  *  elementwise_scan -- the per-channel form of "15. Selective (Data-Dependent) SSM
  *      Scan" (Reference solution): h = A_t*h + B_t*x_t, y_t = C_t*h.
@@ -118,6 +121,17 @@ int selective_scan_fwd_ex(const void* x, const void* delta, const float* A, cons
                           const float* delta_bias, unsigned flags, int64_t batch, int64_t seqlen, int64_t dim,
                           int64_t dstate, int io_dtype, void* workspace, size_t workspace_bytes,
                           sss_stream_t stream);
+
+/* Causal depthwise convolution that feeds the scan in the Mamba block ("Toan Canh Tien Hoa
+ * Kien Truc AI ...", section "5.3. Toi uu hoa Kernel Fusion cho Mamba SSM": the
+ * causal_conv1d kernel), per channel d with `width` taps:
+ *   out[b,t,d] = bias[d] + sum_{k<width} weight[d,k] * x[b, t-(width-1)+k, d]
+ * with x = 0 before t = 0, then silu(out) if apply_silu.  x and out (batch, seqlen, dim) in
+ * io_dtype (a bf16 out is rounded to nearest even); weight (dim, width) and bias (dim,
+ * nullable) float32.  Required: x, weight, out.  width in 1..8 (SSS_ERR_UNSUPPORTED
+ * otherwise).  out may not overlap x, weight or bias.  No workspace.  Returns an sss_status. */
+int causal_conv1d_fwd(const void* x, const float* weight, const float* bias, void* out, int64_t batch,
+                      int64_t seqlen, int64_t dim, int64_t width, int io_dtype, int apply_silu, sss_stream_t stream);
 
 /* Bytes of workspace elementwise_scan needs for these sizes on `device`. */
 size_t elementwise_scan_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int device);

@@ -8,18 +8,20 @@ include/sss.h); this package is its thin Python binding:
     ``selective_scan_fwd_ex``
   * ``selective_state_update(x, delta, A, B, C, D=None, z=None, state=...)`` -> y (one
     decode step; ``state`` is updated in place)
+  * ``causal_conv1d_fwd(x, weight, bias=None, silu=False)`` -> out (the conv front end)
   * ``elementwise_scan(x, A, B, C, h0=None)`` -> (y, h_last)
   * ``*_workspace_size``, raw-pointer variants ``*_raw`` and ``status_string``.
 
 ``inputs`` holds the seeded synthetic workload generators.
 """
 from ._lib import (EXPORTED, LIB_PATH, SSSError, SSS_BF16, SSS_DELTA_SOFTPLUS, SSS_EXACT_ZOH, SSS_F32,
-                   elementwise_scan, elementwise_scan_raw, selective_scan_fwd_ex_raw,
+                   causal_conv1d_fwd, causal_conv1d_fwd_raw, elementwise_scan, elementwise_scan_raw,
+                   selective_scan_fwd_ex_raw,
                    elementwise_scan_workspace_size, load, selective_scan_fwd, selective_scan_fwd_raw,
                    selective_scan_fwd_workspace_size, selective_state_update, selective_state_update_raw,
                    status_string)
 
-__all__ = ["selective_scan_fwd", "selective_state_update", "selective_state_update_raw", "elementwise_scan",
+__all__ = ["selective_scan_fwd", "selective_state_update", "causal_conv1d_fwd", "causal_conv1d_fwd_raw", "selective_state_update_raw", "elementwise_scan",
            "selective_scan_fwd_workspace_size",
            "elementwise_scan_workspace_size", "selective_scan_fwd_raw", "elementwise_scan_raw", "status_string",
            "SSSError", "SSS_F32", "SSS_BF16", "SSS_EXACT_ZOH", "SSS_DELTA_SOFTPLUS", "selective_scan_fwd_ex_raw", "LIB_PATH", "EXPORTED", "load"]

@@ -20,6 +20,7 @@ STATUS = {0: "SSS_OK", -1: "SSS_ERR_NULL_ARG", -2: "SSS_ERR_BAD_DIM", -3: "SSS_E
 SSS_EXACT_ZOH, SSS_DELTA_SOFTPLUS = 1, 2
 
 EXPORTED = ("selective_scan_fwd", "selective_scan_fwd_ex", "selective_scan_fwd_workspace_size", "selective_state_update",
+            "causal_conv1d_fwd",
             "elementwise_scan", "elementwise_scan_workspace_size", "sss_status_string")
 
 
@@ -48,6 +49,8 @@ def load() -> ctypes.CDLL:
         lib.selective_scan_fwd_workspace_size.restype = sz
         lib.selective_state_update.argtypes = [vp] * 9 + [i64] * 3 + [i32, vp]
         lib.selective_state_update.restype = i32
+        lib.causal_conv1d_fwd.argtypes = [vp] * 4 + [i64] * 4 + [i32, i32, vp]
+        lib.causal_conv1d_fwd.restype = i32
         lib.elementwise_scan.argtypes = [vp] * 7 + [i64] * 3 + [vp, sz, vp]
         lib.elementwise_scan.restype = i32
         lib.elementwise_scan_workspace_size.argtypes = [i64] * 3 + [i32]
@@ -74,6 +77,33 @@ def selective_scan_fwd_ex_raw(x, delta, A, B, C, D_skip, z, h0, y, h_last, delta
                               dstate, io_dtype, workspace, workspace_bytes, stream) -> int:
     return load().selective_scan_fwd_ex(x, delta, A, B, C, D_skip, z, h0, y, h_last, delta_bias, flags, batch, seqlen,
                                         dim, dstate, io_dtype, workspace, workspace_bytes, stream)
+
+
+def causal_conv1d_fwd_raw(x, weight, bias, out, batch, seqlen, dim, width, io_dtype, apply_silu, stream) -> int:
+    return load().causal_conv1d_fwd(x, weight, bias, out, batch, seqlen, dim, width, io_dtype, apply_silu, stream)
+
+
+def causal_conv1d_fwd(x, weight, bias=None, *, silu=False, out=None, stream=None):
+    """Causal depthwise convolution: out (batch, seqlen, dim) in x's dtype (float32 or
+    bfloat16); weight (dim, width), bias (dim) float32."""
+    import torch
+    dev = x.device
+    batch, seqlen, dim = x.shape
+    width = weight.shape[1]
+    io = x.dtype
+    if io not in (torch.float32, torch.bfloat16):
+        raise ValueError("x must be float32 or bfloat16")
+    _need(x, "x", io, (batch, seqlen, dim), dev)
+    _need(weight, "weight", torch.float32, (dim, width), dev)
+    _need(bias, "bias", torch.float32, (dim,), dev)
+    o = out if out is not None else torch.empty((batch, seqlen, dim), dtype=io, device=dev)
+    _need(o, "out", io, (batch, seqlen, dim), dev)
+    st = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
+    rc = causal_conv1d_fwd_raw(_ptr(x), _ptr(weight), _ptr(bias), _ptr(o), batch, seqlen, dim, width,
+                               SSS_BF16 if io == torch.bfloat16 else SSS_F32, int(bool(silu)), st)
+    if rc != 0:
+        raise SSSError(rc, "causal_conv1d_fwd")
+    return o
 
 
 def selective_state_update_raw(x, delta, A, B, C, D_skip, z, state, y, batch, dim, dstate, io_dtype, stream) -> int:

@@ -224,6 +224,39 @@ int selective_state_update(const void* x, const void* delta, const float* A, con
   return launch_update(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? SSS_OK : SSS_ERR_HIP;
 }
 
+int causal_conv1d_fwd(const void* x, const float* weight, const float* bias, void* out, int64_t batch,
+                      int64_t seqlen, int64_t dim, int64_t width, int io_dtype, int apply_silu, sss_stream_t stream) {
+  if (!x || !weight || !out) return SSS_ERR_NULL_ARG;
+  if (batch < 1 || seqlen < 1 || dim < 1 || width < 1 || dim > kMaxSelDim) return SSS_ERR_BAD_DIM;
+  int64_t e = 0, t = 0;
+  if (!mul_ok(batch, seqlen, &t) || !mul_ok(t, dim, &e) || !mul_ok(e, 4, &t)) return SSS_ERR_BAD_DIM;
+  if (width > 8) return SSS_ERR_UNSUPPORTED;
+  if (io_dtype != SSS_F32 && io_dtype != SSS_BF16) return SSS_ERR_UNSUPPORTED;
+  const void* ptrs[] = {x, weight, bias, out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return SSS_ERR_UNSUPPORTED;
+  const int64_t es = io_dtype == SSS_BF16 ? 2 : 4;
+  if (overlap(out, e * es, x, e * es) || overlap(out, e * es, weight, dim * width * 4) ||
+      overlap(out, e * es, bias, dim * 4))
+    return SSS_ERR_ALIAS;
+  const int cus = current_device_cus();
+  if (cus <= 0) return SSS_ERR_HIP;
+  const ConvPlan pl = plan_conv1d(batch, seqlen, dim, cus);
+  if ((double)batch * (double)((dim + 63) / 64) * (double)pl.segments > 2147483647.0 / 64) return SSS_ERR_BAD_DIM;
+  ConvArgs a{};
+  a.x = x;
+  a.w = weight;
+  a.bias = bias;
+  a.out = out;
+  a.batch = batch;
+  a.seqlen = seqlen;
+  a.dim = dim;
+  a.width = (int)width;
+  a.bf16 = io_dtype == SSS_BF16;
+  a.silu = apply_silu != 0;
+  return launch_conv1d(a, pl, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? SSS_OK : SSS_ERR_HIP;
+}
+
 static int ew_dims_ok(int64_t batch, int64_t seqlen, int64_t dim) {
   if (batch < 1 || seqlen < 1 || dim < 1) return SSS_ERR_BAD_DIM;
   int64_t e = 0, t = 0;

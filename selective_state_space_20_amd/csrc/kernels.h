@@ -74,6 +74,25 @@ struct UpdArgs {
 
 hipError_t launch_update(const UpdArgs& a, hipStream_t stream);
 
+struct ConvPlan {
+  int segments;
+  int64_t seg_len;
+};
+
+struct ConvArgs {
+  const void* x;
+  const float* w;
+  const float* bias;
+  void* out;
+  int64_t batch, seqlen, dim;
+  int width;
+  int bf16;
+  int silu;
+};
+
+ConvPlan plan_conv1d(int64_t batch, int64_t seqlen, int64_t dim, int num_cus);
+hipError_t launch_conv1d(const ConvArgs& a, const ConvPlan& plan, hipStream_t stream);
+
 int env_int(const char* name, int dflt);
 
 }  // namespace sss

@@ -169,6 +169,57 @@ def test_selective_exact_zoh_special_values(oracle_lib):
     assert rel_err(y, yr) <= TOL_F32 and rel_err(hl, hr) <= TOL_F32
 
 
+# ---------------------------------------------------------------- causal conv1d front end
+CONV_CASES = [  # (batch, seqlen, dim, width, io, silu, bias, forced segments)
+    (1, 1, 1, 1, "f32", False, False, 0),
+    (2, 100, 64, 4, "bf16", True, True, 0),
+    (3, 1000, 37, 4, "f32", True, True, 7),
+    (1, 5000, 130, 2, "bf16", False, True, 13),
+    (2, 333, 70, 3, "f32", False, False, 3),
+    (2, 2000, 200, 8, "bf16", True, False, 5),
+    (1, 700, 16, 5, "f32", True, True, 0),
+    (2, 640, 96, 6, "bf16", True, True, 4),
+    (1, 900, 65, 7, "f32", False, True, 2),
+]
+
+
+@pytest.mark.parametrize("case", CONV_CASES, ids=[f"B{c[0]}L{c[1]}D{c[2]}W{c[3]}{c[4]}s{int(c[5])}S{c[7]}"
+                                                  for c in CONV_CASES])
+def test_conv1d(oracle_lib, monkeypatch, case):
+    """causal_conv1d_fwd against the oracle; forced segment counts put segment boundaries
+    (where the window is reloaded from the previous segment) inside the sequence."""
+    import torch
+    import selective_state_space_20_amd as sss
+    bt, L, dm, width, io, silu, with_bias, segs = case
+    if segs:
+        monkeypatch.setenv("SSS_FORCE_SEGMENTS", str(segs))
+    rng = np.random.default_rng(zlib.crc32(repr(case).encode()) % 100000)
+    x = rng.standard_normal((bt, L, dm)).astype(np.float32)
+    if io == "bf16":
+        x = gen.f32_to_bf16_bits(x)
+    w = rng.standard_normal((dm, width)).astype(np.float32)
+    bias = rng.standard_normal(dm).astype(np.float32) if with_bias else None
+    note(f"[conv1d] {case}")
+    xd = to_dev(x, "cuda:0")
+    out = torch.full(xd.shape, float("nan"), dtype=xd.dtype, device="cuda:0")
+    sss.causal_conv1d_fwd(xd, to_dev(w, "cuda:0"), to_dev(bias, "cuda:0"), silu=silu, out=out)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    ref = oracle_lib.causal_conv1d(x, w, bias, silu=silu)
+    if io == "f32":
+        err = rel_err(got, ref)
+        note(f"    err {err:.3e}")
+        assert err <= TOL_F32
+    else:
+        # a bf16 output is a rounding decision: every element must be one of the two bf16
+        # neighbours of the exact value, i.e. within one bf16 ulp of it (plus fp32 noise)
+        assert np.all(np.isfinite(got))
+        ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
+        excess = np.abs(got - ref) - ulp - TOL_F32 * np.max(np.abs(ref))
+        note(f"    max |err| / ulp = {np.max(np.abs(got - ref) / ulp):.3f}")
+        assert np.all(excess <= 0)
+
+
 # ---------------------------------------------------------------- decode step
 UPD_CASES = [  # (batch, dim, dstate, io, D, z)
     (1, 1, 1, "f32", False, False),
