@@ -60,8 +60,9 @@ def _load():
         lib.oracle_elementwise_scan_chunked.argtypes = [vp] * 7 + [i64] * 4 + [i32]
         lib.oracle_selective_state_update.argtypes = [vp] * 10 + [i64] * 3 + [i32] * 2
         lib.oracle_causal_conv1d.argtypes = [vp] * 4 + [i64] * 4 + [i32] * 3
+        lib.oracle_selective_scan_bwd.argtypes = [vp] * 18 + [i64] * 4 + [i32] * 2
         for f in ("oracle_selective_scan", "oracle_selective_scan_channels", "oracle_selective_scan_chunked",
-                  "oracle_selective_state_update", "oracle_causal_conv1d",
+                  "oracle_selective_state_update", "oracle_causal_conv1d", "oracle_selective_scan_bwd",
                   "oracle_elementwise_scan", "oracle_elementwise_scan_channels",
                   "oracle_elementwise_scan_chunked", "oracle_max_threads"):
             getattr(lib, f).restype = ctypes.c_int
@@ -173,6 +174,29 @@ def selective_state_update(x, delta, A, B, C, D=None, z=None, state=None, *, nth
                                                _p(y), _p(st), bt, dm, n, _io_code(x), nthreads)
     _check(rc)
     return y, st
+
+
+def selective_scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, *, dy, dh_last=None, nthreads=0):
+    """Gradients of sum(dy * y) + sum(dh_last * h_last) with respect to every input.
+
+    Returns a dict of float64 arrays: dx, ddelta (Bt, L, Dm); dz (only with z); dA (Dm, N);
+    dB, dC (Bt, L, N); dD (only with D); dh0 (Bt, Dm, N)."""
+    x, delta, z = _io(x), _io(delta), _io(z)
+    A, B, C, D, h0 = _f32(A), _f32(B), _f32(C), _f32(D), _f32(h0)
+    bt, L, dm = x.shape
+    n = A.shape[1]
+    dy = np.ascontiguousarray(dy, dtype=np.float64)
+    dhl = None if dh_last is None else np.ascontiguousarray(dh_last, dtype=np.float64)
+    out = dict(dx=np.empty((bt, L, dm)), ddelta=np.empty((bt, L, dm)), dA=np.empty((dm, n)),
+               dB=np.empty((bt, L, n)), dC=np.empty((bt, L, n)), dh0=np.empty((bt, dm, n)))
+    out["dD"] = np.empty(dm) if D is not None else None
+    out["dz"] = np.empty((bt, L, dm)) if z is not None else None
+    rc = _load().oracle_selective_scan_bwd(_p(x), _p(delta), _p(A), _p(B), _p(C), _p(D), _p(z), _p(h0), _p(dy),
+                                           _p(dhl), _p(out["dx"]), _p(out["ddelta"]), _p(out["dA"]), _p(out["dB"]),
+                                           _p(out["dC"]), _p(out["dD"]), _p(out["dz"]), _p(out["dh0"]), bt, L, dm, n,
+                                           _io_code(x), nthreads)
+    _check(rc)
+    return out
 
 
 def causal_conv1d(x, weight, bias=None, *, silu=False, nthreads=0):

@@ -28,6 +28,7 @@
  *  the exact zero-order-hold B-bar of the P1 example is kept as an option).
  */
 #include <math.h>
+#include <stdlib.h>
 #include <stdint.h>
 #include <string.h>
 #ifdef _OPENMP
@@ -218,6 +219,117 @@ int oracle_selective_state_update(const void* x, const void* delta, const float*
       acc *= zv / (1.0 + exp(-zv));
     }
     y[c] = acc;
+  }
+  return OR_OK;
+}
+
+/*
+ * Gradients of the selective form (first-order input term, no delta front end) by the
+ * adjoint of the recurrence, walked backwards in time -- the training path of [P1]
+ * "Recomputation: doi mot it compute lay it memory hon" (the states are recomputed here by
+ * a forward sweep per channel, then the adjoint runs from t = L-1 down to 0):
+ *   a_t = exp(Delta_t A_n), h_t = a_t h_{t-1} + Delta_t B_t[n] x_t,
+ *   v_t = sum_n C_t[n] h_t[n] + D x_t, y_t = v_t * silu(z_t)
+ *   dv_t = dy_t * silu(z_t);  dz_t = dy_t * v_t * silu'(z_t)
+ *   lambda_t[n] = C_t[n] dv_t + a_{t+1}[n] lambda_{t+1}[n],  lambda_{L-1} += dh_last[n]
+ *   dx_t = D dv_t + sum_n lambda_t Delta_t B_t[n]
+ *   dDelta_t = sum_n lambda_t (B_t[n] x_t + A_n a_t h_{t-1})
+ *   dA_n += lambda_t Delta_t a_t h_{t-1};  dB_t[n] += lambda_t Delta_t x_t (sum over d);
+ *   dC_t[n] += dv_t h_t[n] (sum over d);  dD += dv_t x_t;  dh0 = a_0 lambda_0.
+ * dy (B, L, D) and dh_last (B, D, N, nullable) are double.  Outputs in double: dx, ddelta,
+ * dz (B, L, D; dz only with z), dA (D, N), dB, dC (B, L, N), dD (D), dh0 (B, D, N) (each
+ * nullable where its input is optional).
+ */
+int oracle_selective_scan_bwd(const void* x, const void* delta, const float* A, const float* Bm, const float* Cm,
+                              const float* Dsk, const void* z, const float* h0, const double* dy,
+                              const double* dh_last, double* dx, double* ddelta, double* dA, double* dB, double* dC,
+                              double* dD, double* dz, double* dh0, int64_t batch, int64_t L, int64_t Dm, int64_t N,
+                              int dtype, int nthreads) {
+  if (!sel_args_ok(x, delta, A, Bm, Cm, batch, L, Dm, N, dtype) || !dy || !dx || !ddelta || !dA || !dB || !dC)
+    return OR_ERR_ARG;
+  set_threads(nthreads);
+  int64_t nch = batch * Dm;
+  memset(dA, 0, sizeof(double) * Dm * N);
+  memset(dB, 0, sizeof(double) * batch * L * N);
+  memset(dC, 0, sizeof(double) * batch * L * N);
+  if (dD) memset(dD, 0, sizeof(double) * Dm);
+#pragma omp parallel
+  {
+    double* hs = (double*)malloc(sizeof(double) * (L + 1) * N);   /* h_{t-1} for t = 0..L */
+    double* vs = (double*)malloc(sizeof(double) * L);
+    double* lam = (double*)malloc(sizeof(double) * N);
+    double* lB = (double*)calloc((size_t)(batch * L * N), sizeof(double));
+    double* lC = (double*)calloc((size_t)(batch * L * N), sizeof(double));
+    double* lA = (double*)calloc((size_t)(Dm * N), sizeof(double));
+    double* lD = (double*)calloc((size_t)Dm, sizeof(double));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t c = 0; c < nch; ++c) {
+      int64_t b = c / Dm, d = c % Dm;
+      /* forward: hs[(t+1)*N + n] = h_t, hs[n] = h_{-1} */
+      for (int64_t n = 0; n < N; ++n) hs[n] = h0 ? (double)h0[c * N + n] : 0.0;
+      for (int64_t t = 0; t < L; ++t) {
+        int64_t e = (b * L + t) * Dm + d;
+        double xt = load_val(x, e, dtype), dt = load_val(delta, e, dtype);
+        double v = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+          double hn = exp(dt * (double)A[d * N + n]) * hs[t * N + n] + dt * (double)Bm[(b * L + t) * N + n] * xt;
+          hs[(t + 1) * N + n] = hn;
+          v += (double)Cm[(b * L + t) * N + n] * hn;
+        }
+        if (Dsk) v += (double)Dsk[d] * xt;
+        vs[t] = v;
+      }
+      /* adjoint, backwards in time; lam holds a_{t+1} lambda_{t+1} on entry to step t */
+      for (int64_t n = 0; n < N; ++n) lam[n] = dh_last ? dh_last[c * N + n] : 0.0;
+      for (int64_t t = L - 1; t >= 0; --t) {
+        int64_t e = (b * L + t) * Dm + d;
+        double xt = load_val(x, e, dtype), dt = load_val(delta, e, dtype);
+        double g = 1.0;
+        if (z) {
+          double zt = load_val(z, e, dtype);
+          double sg = 1.0 / (1.0 + exp(-zt));
+          g = zt * sg;
+          if (dz) dz[e] = dy[e] * vs[t] * sg * (1.0 + zt * (1.0 - sg));
+        }
+        double dv = dy[e] * g;
+        double gx = Dsk ? (double)Dsk[d] * dv : 0.0, gd = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+          double an = (double)A[d * N + n];
+          double Bn = (double)Bm[(b * L + t) * N + n], Cn = (double)Cm[(b * L + t) * N + n];
+          double at = exp(dt * an);
+          double l = Cn * dv + lam[n];                  /* lambda_t */
+          double hp = hs[t * N + n];                    /* h_{t-1} */
+          gx += l * dt * Bn;
+          gd += l * (Bn * xt + an * at * hp);
+          lA[d * N + n] += l * dt * at * hp;
+          lB[(b * L + t) * N + n] += l * dt * xt;
+          lC[(b * L + t) * N + n] += dv * hs[(t + 1) * N + n];
+          lam[n] = at * l;                              /* a_t lambda_t, for step t-1 */
+        }
+        if (Dsk) lD[d] += dv * xt;
+        dx[e] = gx;
+        ddelta[e] = gd;
+      }
+      if (dh0)
+        for (int64_t n = 0; n < N; ++n) dh0[c * N + n] = lam[n];
+    }
+#pragma omp critical
+    {
+      for (int64_t i = 0; i < batch * L * N; ++i) {
+        dB[i] += lB[i];
+        dC[i] += lC[i];
+      }
+      for (int64_t i = 0; i < Dm * N; ++i) dA[i] += lA[i];
+      if (dD)
+        for (int64_t i = 0; i < Dm; ++i) dD[i] += lD[i];
+    }
+    free(hs);
+    free(vs);
+    free(lam);
+    free(lB);
+    free(lC);
+    free(lA);
+    free(lD);
   }
   return OR_OK;
 }

@@ -51,6 +51,11 @@ MUTANTS = {
     "update_dropped_skip": ("    if (Dsk) acc += (double)Dsk[d] * xv;", "    (void)Dsk;"),
     "conv_taps_reversed": ("if (ts >= 0) v += (double)w[d * W + k] *", "if (ts >= 0) v += (double)w[d * W + (W - 1 - k)] *"),
     "conv_shifted_one_step": ("        int64_t ts = t - (W - 1) + k;", "        int64_t ts = t - W + k;"),
+    "bwd_delta_without_decay_term": ("gd += l * (Bn * xt + an * at * hp);", "gd += l * (Bn * xt);"),
+    "bwd_dA_uses_new_state": ("lA[d * N + n] += l * dt * at * hp;", "lA[d * N + n] += l * dt * at * hs[(t + 1) * N + n];"),
+    "bwd_dh_last_ignored": ("lam[n] = dh_last ? dh_last[c * N + n] : 0.0;", "lam[n] = 0.0;"),
+    "bwd_adjoint_not_decayed": ("lam[n] = at * l;", "lam[n] = l;"),
+    "bwd_silu_derivative": ("sg * (1.0 + zt * (1.0 - sg))", "sg"),
     "front_end_bias_ignored": ("  if (dbias) v += (double)dbias[d];", "  (void)dbias;"),
     "front_end_exp_for_softplus": ("static double softplus(double v) { return v > 0.0 ? v + log1p(exp(-v)) : log1p(exp(v)); }",
                                    "static double softplus(double v) { return exp(v); }"),

@@ -495,3 +495,51 @@ def test_C2_conv_hand_worked(oracle_lib):
     w = np.asarray([[1.0, 2.0, 4.0]], np.float32)
     out = oracle_lib.causal_conv1d(x, w)
     assert np.array_equal(out[0, :, 0], [4.0, 42.0, 421.0])
+
+
+# ---------------------------------------------------------------- backward (gradients)
+def _fd_check(oracle_lib, inp, dy, dhl, names, eps_rel=1e-4, seed=0):
+    """Central differences of L = sum(dy*y) + sum(dh_last*h_last) (the pinned forward oracle)
+    along a random direction per input, against the adjoint gradients.  The perturbed inputs
+    are fp32; the difference actually applied (after rounding) is what the gradient is
+    contracted with, so rounding of the perturbation does not enter the comparison."""
+    g = oracle_lib.selective_scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                                      inp["h0"], dy=dy, dh_last=dhl)
+    key = {"x": "dx", "delta": "ddelta", "A": "dA", "B": "dB", "C": "dC", "D": "dD", "z": "dz", "h0": "dh0"}
+    rng = np.random.default_rng(seed)
+
+    def loss(d):
+        y, hl = oracle_lib.selective_scan(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["h0"])
+        return float(np.sum(dy * y) + (np.sum(dhl * hl) if dhl is not None else 0.0))
+
+    for name in names:
+        p = inp[name].astype(np.float64)
+        v = rng.standard_normal(p.shape)
+        eps = eps_rel * (np.sqrt(np.mean(p * p)) + 1e-3)
+        plus, minus = dict(inp), dict(inp)
+        plus[name] = (p + eps * v).astype(np.float32)
+        minus[name] = (p - eps * v).astype(np.float32)
+        step = plus[name].astype(np.float64) - minus[name].astype(np.float64)
+        fd = loss(plus) - loss(minus)
+        an = float(np.sum(g[key[name]] * step))
+        assert abs(fd - an) <= 1e-6 * max(abs(fd), abs(an)) + 1e-13, (name, fd, an)
+
+
+def test_G1_gradients_match_finite_differences(oracle_lib):
+    """Every gradient (x, delta, A, B, C, D, z, h0, with an upstream dh_last) against central
+    differences of the forward oracle."""
+    inp = gen.selective_inputs(2, 40, 5, 4, io="f32", with_D=True, with_z=True, h0=True, h0_std=0.5, seed=201)
+    rng = np.random.default_rng(202)
+    dy = rng.standard_normal(inp["x"].shape)
+    dhl = rng.standard_normal(inp["h0"].shape)
+    _fd_check(oracle_lib, inp, dy, dhl, ["x", "delta", "A", "B", "C", "D", "z", "h0"], seed=203)
+
+
+def test_G2_gradients_without_options(oracle_lib):
+    """No D, no z, no h0, no dh_last: the remaining gradients still match."""
+    inp = gen.selective_inputs(1, 60, 3, 8, io="f32", with_D=False, with_z=False, h0=False, seed=204)
+    rng = np.random.default_rng(205)
+    dy = rng.standard_normal(inp["x"].shape)
+    _fd_check(oracle_lib, inp, dy, None, ["x", "delta", "A", "B", "C"], seed=206)
+    g = oracle_lib.selective_scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], dy=dy)
+    assert g["dD"] is None and g["dz"] is None
