@@ -12,6 +12,7 @@ once and every output written once, the state never counted) in GB/s.
   python bench.py --workload 4            # another configuration (0..4); the default is 3
   python bench.py --decode 64             # one decode step of 64 tokens (selective_state_update)
   python bench.py --conv                  # the causal conv1d front end on the long layer
+  python bench.py --backward              # selective_scan_bwd (all gradients) on the default workload
   python bench.py --copy-calibration      # plain copy of a known size, for counter scaling
 """
 from __future__ import annotations
@@ -239,6 +240,63 @@ def bench_conv(steps, warmup, batch=1, seqlen=65536, dim=5120, width=4):
     }), flush=True)
 
 
+def bench_backward(steps, warmup):
+    """selective_scan_bwd on the default workload (the long Mamba-2.8B-shaped layer, bf16,
+    gated, h0, dh_last): every gradient, states recomputed.  Algorithmic bytes: every input
+    (x, delta, z, dy, B, C, A, D, h0, dh_last) read once and every gradient written once."""
+    import torch
+    import selective_state_space_20_amd as sss
+    from selective_state_space_20_amd import inputs as gen
+    cfg, inp = gen.config_inputs(WORKLOAD_INDEX)
+    dev = torch.device("cuda:0")
+
+    def td(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    t = {k: td(v) for k, v in inp.items() if k != "io"}
+    b, L, d, n = cfg["batch"], cfg["seqlen"], cfg["dim"], cfg["dstate"]
+    g = torch.Generator(device=dev)
+    g.manual_seed(5000)
+    dy = torch.randn((b, L, d), device=dev, generator=g)
+    dhl = torch.randn((b, d, n), device=dev, generator=g)
+    ws = torch.empty(sss.selective_scan_bwd_workspace_size(b, L, d, n, 0), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        sss.selective_scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"], dy=dy,
+                               dh_last=dhl, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    mean_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    e = b * L * d
+    nbytes = e * (2 * 3 + 4) + 2 * b * L * n * 4 + d * n * 4 + d * 4 + 2 * b * d * n * 4   # inputs
+    nbytes += e * 4 * 3 + d * n * 4 + 2 * b * L * n * 4 + d * 4 + b * d * n * 4               # gradients
+    gbs = nbytes / (mean_ms * 1e-3) / 1e9
+    log(f"[bench] backward {cfg['name']}: event mean {mean_ms:.4f} ms, workspace {ws.numel() / 1e9:.2f} GB")
+    print(json.dumps({
+        "metric": "selective_scan_bwd achieved HBM GB/s and elements/s, 1 GPU", "value": round(gbs, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(mean_ms, 5), "higher_is_better": True,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "backward_" + cfg["name"], "algorithmic_bytes": nbytes, "elements": e},
+        "elements_per_s": round(e / (mean_ms * 1e-3), 1),
+        "roofline": {"bound": "alu", "achieved": None, "peak": VALU_FP32_TFLOPS, "unit": "TFLOP/s", "frac": None,
+                     "traffic": None, "kernel": "selective_scan_bwd call (7 launches)", "call_ms_event_mean": round(mean_ms, 5),
+                     "hbm": {"achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(gbs / HBM_PEAK_GBS, 4)}},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -248,6 +306,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--workload", type=int, default=WORKLOAD_INDEX, help="configuration index 0..4")
     ap.add_argument("--conv", action="store_true", help="time the causal conv1d front end instead")
+    ap.add_argument("--backward", action="store_true", help="time selective_scan_bwd on the default workload")
     ap.add_argument("--decode", type=int, default=0, metavar="BATCH",
                     help="time one decode step (selective_state_update) of BATCH tokens instead")
     args = ap.parse_args()
@@ -261,6 +320,9 @@ def main():
         return
     if args.conv:
         bench_conv(args.steps, args.warmup)
+        return
+    if args.backward:
+        bench_backward(args.steps, args.warmup)
         return
     if args.decode > 0:
         bench_decode(args.decode, args.steps, args.warmup)

@@ -1,7 +1,7 @@
 /*
  * sss.h -- C ABI of the MI355X (gfx950) selective-scan library, libsss.so.
  *
- * Four operations, all fully computed by hand-written HIP kernels on the device:
+ * Five operations, all fully computed by hand-written HIP kernels on the device:
  *
  *  selective_scan_fwd  -- the selective (input-dependent) state-space recurrence of
  *      "Selective Scan trong Mamba toi uu chuoi dai the nao?" (thecsnote.cc), sections
@@ -14,6 +14,8 @@
  *      delta arrives already passed through softplus: the projections that produce
  *      delta, B and C are outside this library ("15. Selective (Data-Dependent) SSM
  *      Scan", Problem: the data-dependent parameters are given).
+ *
+ *  selective_scan_bwd -- its gradients (training), with the states recomputed.
  *
  *  selective_state_update -- one decode step of the same recurrence on a carried state
  *      (in place), for token-by-token generation.
@@ -85,6 +87,31 @@ int selective_scan_fwd(const void* x, const void* delta, const float* A, const f
                        const float* D_skip, const void* z, const float* h0, float* y, float* h_last,
                        int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
                        void* workspace, size_t workspace_bytes, sss_stream_t stream);
+
+/* Bytes of workspace selective_scan_bwd needs for these sizes on `device`. */
+size_t selective_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int device);
+
+/* Gradients of the selective scan (plain form: first-order input term, no delta options),
+ * for training: with L = sum(dy * y) + sum(dh_last * h_last) over selective_scan_fwd's
+ * outputs, writes dL/d of every input.  The states are recomputed, not stored ("Selective
+ * Scan trong Mamba toi uu chuoi dai the nao?", section "Recomputation: doi mot it compute
+ * lay it memory hon"), and the adjoint runs backwards in time:
+ *   lambda_t = C_t dv_t + exp(delta_{t+1} A) lambda_{t+1},  dv_t = dy_t silu(z_t).
+ * Inputs as selective_scan_fwd, plus dy (batch, seqlen, dim) float32 and dh_last
+ * (batch, dim, dstate) float32 (NULL = 0).  Outputs, all float32, caller-owned:
+ *   dx, ddelta, dz (batch, seqlen, dim); dA (dim, dstate); dB, dC (batch, seqlen, dstate);
+ *   dD (dim); dh0 (batch, dim, dstate).
+ * Required: x, delta, A, B, C, dy, dx, ddelta, dA, dB, dC; dD when D_skip is given and dz
+ * when z is given (SSS_ERR_NULL_ARG otherwise); dh0 optional (gradient of the initial
+ * state, zero or h0).  Outputs may not overlap inputs, each other or the workspace.
+ * Workspace: at least selective_scan_bwd_workspace_size() bytes (never zero).  The sums
+ * over channels (dB, dC) and over time (dA, dD) are formed from per-wave / per-segment
+ * partials in a fixed order: results are deterministic.  Returns an sss_status. */
+int selective_scan_bwd(const void* x, const void* delta, const float* A, const float* B, const float* C,
+                       const float* D_skip, const void* z, const float* h0, const float* dy, const float* dh_last,
+                       float* dx, float* ddelta, float* dA, float* dB, float* dC, float* dD, float* dz, float* dh0,
+                       int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype, void* workspace,
+                       size_t workspace_bytes, sss_stream_t stream);
 
 /* One decode step of the selective scan ("Selective Scan trong Mamba toi uu chuoi dai the
  * nao?", section "Selective Scan thay doi inference chuoi dai nhu the nao?": generation

@@ -20,7 +20,7 @@ STATUS = {0: "SSS_OK", -1: "SSS_ERR_NULL_ARG", -2: "SSS_ERR_BAD_DIM", -3: "SSS_E
 SSS_EXACT_ZOH, SSS_DELTA_SOFTPLUS = 1, 2
 
 EXPORTED = ("selective_scan_fwd", "selective_scan_fwd_ex", "selective_scan_fwd_workspace_size", "selective_state_update",
-            "causal_conv1d_fwd",
+            "causal_conv1d_fwd", "selective_scan_bwd", "selective_scan_bwd_workspace_size",
             "elementwise_scan", "elementwise_scan_workspace_size", "sss_status_string")
 
 
@@ -51,6 +51,10 @@ def load() -> ctypes.CDLL:
         lib.selective_state_update.restype = i32
         lib.causal_conv1d_fwd.argtypes = [vp] * 4 + [i64] * 4 + [i32, i32, vp]
         lib.causal_conv1d_fwd.restype = i32
+        lib.selective_scan_bwd.argtypes = [vp] * 18 + [i64] * 4 + [i32, vp, sz, vp]
+        lib.selective_scan_bwd.restype = i32
+        lib.selective_scan_bwd_workspace_size.argtypes = [i64] * 4 + [i32]
+        lib.selective_scan_bwd_workspace_size.restype = sz
         lib.elementwise_scan.argtypes = [vp] * 7 + [i64] * 3 + [vp, sz, vp]
         lib.elementwise_scan.restype = i32
         lib.elementwise_scan_workspace_size.argtypes = [i64] * 3 + [i32]
@@ -77,6 +81,53 @@ def selective_scan_fwd_ex_raw(x, delta, A, B, C, D_skip, z, h0, y, h_last, delta
                               dstate, io_dtype, workspace, workspace_bytes, stream) -> int:
     return load().selective_scan_fwd_ex(x, delta, A, B, C, D_skip, z, h0, y, h_last, delta_bias, flags, batch, seqlen,
                                         dim, dstate, io_dtype, workspace, workspace_bytes, stream)
+
+
+def selective_scan_bwd_raw(x, delta, A, B, C, D_skip, z, h0, dy, dh_last, dx, ddelta, dA, dB, dC, dD, dz, dh0, batch,
+                           seqlen, dim, dstate, io_dtype, workspace, workspace_bytes, stream) -> int:
+    return load().selective_scan_bwd(x, delta, A, B, C, D_skip, z, h0, dy, dh_last, dx, ddelta, dA, dB, dC, dD, dz, dh0,
+                                     batch, seqlen, dim, dstate, io_dtype, workspace, workspace_bytes, stream)
+
+
+def selective_scan_bwd_workspace_size(batch, seqlen, dim, dstate, device=0) -> int:
+    return int(load().selective_scan_bwd_workspace_size(batch, seqlen, dim, dstate, device))
+
+
+def selective_scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, *, dy, dh_last=None, want_dh0=True,
+                       workspace=None, stream=None):
+    """Gradients of sum(dy * y) + sum(dh_last * h_last) of selective_scan_fwd (plain form).
+
+    Returns a dict of float32 tensors: dx, ddelta, dA, dB, dC, and dD (with D), dz (with z),
+    dh0 (if want_dh0)."""
+    import torch
+    dev = x.device
+    batch, seqlen, dim = x.shape
+    dstate = A.shape[1]
+    io = x.dtype
+    f32 = torch.float32
+    for t, n, dt, sh in ((x, "x", io, (batch, seqlen, dim)), (delta, "delta", io, (batch, seqlen, dim)),
+                         (z, "z", io, (batch, seqlen, dim)), (A, "A", f32, (dim, dstate)),
+                         (B, "B", f32, (batch, seqlen, dstate)), (C, "C", f32, (batch, seqlen, dstate)),
+                         (D, "D", f32, (dim,)), (h0, "h0", f32, (batch, dim, dstate)),
+                         (dy, "dy", f32, (batch, seqlen, dim)), (dh_last, "dh_last", f32, (batch, dim, dstate))):
+        _need(t, n, dt, sh, dev)
+    e = lambda *sh: torch.empty(sh, dtype=f32, device=dev)
+    g = dict(dx=e(batch, seqlen, dim), ddelta=e(batch, seqlen, dim), dA=e(dim, dstate), dB=e(batch, seqlen, dstate),
+             dC=e(batch, seqlen, dstate))
+    g["dD"] = e(dim) if D is not None else None
+    g["dz"] = e(batch, seqlen, dim) if z is not None else None
+    g["dh0"] = e(batch, dim, dstate) if want_dh0 else None
+    wsb = selective_scan_bwd_workspace_size(batch, seqlen, dim, dstate, dev.index or 0)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    st = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
+    rc = selective_scan_bwd_raw(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(dy),
+                                _ptr(dh_last), _ptr(g["dx"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]),
+                                _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["dh0"]), batch, seqlen, dim, dstate,
+                                SSS_BF16 if io == torch.bfloat16 else SSS_F32, _ptr(workspace), workspace.numel(), st)
+    if rc != 0:
+        raise SSSError(rc, "selective_scan_bwd")
+    return g
 
 
 def causal_conv1d_fwd_raw(x, weight, bias, out, batch, seqlen, dim, width, io_dtype, apply_silu, stream) -> int:

@@ -182,6 +182,81 @@ int selective_scan_fwd_ex(const void* x, const void* delta, const float* A, cons
   return e == hipSuccess ? SSS_OK : SSS_ERR_HIP;
 }
 
+size_t selective_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int device) {
+  if (sel_dims_ok(batch, seqlen, dim, dstate) != SSS_OK) return 0;
+  int cus = device_cus(device);
+  if (cus <= 0) cus = 256;
+  return plan_selective_bwd(batch, seqlen, dim, dstate, cus).ws_total;
+}
+
+int selective_scan_bwd(const void* x, const void* delta, const float* A, const float* B, const float* C,
+                       const float* D_skip, const void* z, const float* h0, const float* dy, const float* dh_last,
+                       float* dx, float* ddelta, float* dA, float* dB, float* dC, float* dD, float* dz, float* dh0,
+                       int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype, void* workspace,
+                       size_t workspace_bytes, sss_stream_t stream) {
+  if (!x || !delta || !A || !B || !C || !dy || !dx || !ddelta || !dA || !dB || !dC) return SSS_ERR_NULL_ARG;
+  if ((D_skip && !dD) || (z && !dz)) return SSS_ERR_NULL_ARG;
+  int st = sel_dims_ok(batch, seqlen, dim, dstate);
+  if (st != SSS_OK) return st;
+  if (io_dtype != SSS_F32 && io_dtype != SSS_BF16) return SSS_ERR_UNSUPPORTED;
+  const void* ptrs[] = {x, delta, A, B, C, D_skip, z, h0, dy, dh_last, dx, ddelta, dA, dB, dC, dD, dz, dh0, workspace};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return SSS_ERR_UNSUPPORTED;
+  const int64_t es = io_dtype == SSS_BF16 ? 2 : 4;
+  const int64_t E = batch * seqlen * dim, H = batch * dim * dstate * 4, BC = batch * seqlen * dstate * 4;
+  const void* in_p[] = {x, delta, A, B, C, D_skip, z, h0, dy, dh_last};
+  const int64_t in_b[] = {E * es, E * es, dim * dstate * 4, BC, BC, dim * 4, E * es, H, E * 4, H};
+  void* out_p[] = {dx, ddelta, dA, dB, dC, dD, dz, dh0};
+  const int64_t out_b[] = {E * 4, E * 4, dim * dstate * 4, BC, BC, dim * 4, E * 4, H};
+  for (int i = 0; i < 8; ++i) {
+    for (int j = 0; j < 10; ++j)
+      if (overlap(out_p[i], out_b[i], in_p[j], in_b[j])) return SSS_ERR_ALIAS;
+    for (int j = 0; j < i; ++j)
+      if (overlap(out_p[i], out_b[i], out_p[j], out_b[j])) return SSS_ERR_ALIAS;
+  }
+  const int cus = current_device_cus();
+  if (cus <= 0) return SSS_ERR_HIP;
+  const BwdPlan bp = plan_selective_bwd(batch, seqlen, dim, dstate, cus);
+  const int64_t wg_groups = (dim + 63) / 64;
+  if ((double)batch * (double)wg_groups * (double)bp.fwd.segments > 2147483647.0 / 64) return SSS_ERR_BAD_DIM;
+  if (workspace == nullptr || workspace_bytes < bp.ws_total) return SSS_ERR_WORKSPACE;
+  const int64_t wb = (int64_t)bp.ws_total;
+  for (int i = 0; i < 10; ++i)
+    if (overlap(workspace, wb, in_p[i], in_b[i])) return SSS_ERR_ALIAS;
+  for (int i = 0; i < 8; ++i)
+    if (overlap(workspace, wb, out_p[i], out_b[i])) return SSS_ERR_ALIAS;
+  if (env_int("SSS_LOG", 0))
+    std::fprintf(stderr, "[sss] selective_scan_bwd B=%lld L=%lld D=%lld N=%lld: segments=%d seg_len=%lld K=%d ws=%zu\n",
+                 (long long)batch, (long long)seqlen, (long long)dim, (long long)dstate, bp.fwd.segments,
+                 (long long)bp.fwd.seg_len, bp.K, bp.ws_total);
+  BwdArgs a{};
+  a.fwd.x = x;
+  a.fwd.delta = delta;
+  a.fwd.A = A;
+  a.fwd.B = B;
+  a.fwd.C = C;
+  a.fwd.Dsk = D_skip;
+  a.fwd.z = z;
+  a.fwd.h0 = h0;
+  a.fwd.batch = batch;
+  a.fwd.seqlen = seqlen;
+  a.fwd.dim = dim;
+  a.fwd.dstate = (int)dstate;
+  a.fwd.bf16 = io_dtype == SSS_BF16;
+  a.fwd.workspace = workspace;
+  a.dy = dy;
+  a.dh_last = dh_last;
+  a.dx = dx;
+  a.ddelta = ddelta;
+  a.dA = dA;
+  a.dB = dB;
+  a.dC = dC;
+  a.dD = dD;
+  a.dz = dz;
+  a.dh0 = dh0;
+  return launch_selective_bwd(a, bp, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? SSS_OK : SSS_ERR_HIP;
+}
+
 int selective_state_update(const void* x, const void* delta, const float* A, const float* B, const float* C,
                            const float* D_skip, const void* z, float* state, float* y, int64_t batch, int64_t dim,
                            int64_t dstate, int io_dtype, sss_stream_t stream) {

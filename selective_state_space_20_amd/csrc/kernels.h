@@ -35,6 +35,32 @@ struct SelArgs {
 
 SelPlan plan_selective(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int num_cus);
 hipError_t launch_selective(const SelArgs& a, const SelPlan& plan, hipStream_t stream);
+// pass 1 + carry only: the workspace's state slots hold the state entering each segment
+hipError_t launch_segment_states(const SelArgs& a, const SelPlan& plan, hipStream_t stream);
+
+// Backward pass of the selective scan (selective_bwd.hip).
+struct BwdPlan {
+  SelPlan fwd;     // segments of the forward pass (its workspace comes first)
+  int K, nsub;     // checkpoint spacing and checkpoints per segment
+  size_t off_mu, off_ckpt, off_bc, off_pa, off_pd, ws_total;
+};
+
+struct BwdArgs {
+  SelArgs fwd;  // forward inputs (y / h_last unused)
+  const float* dy;
+  const float* dh_last;
+  float* dx;
+  float* ddelta;
+  float* dA;
+  float* dB;
+  float* dC;
+  float* dD;
+  float* dz;
+  float* dh0;
+};
+
+BwdPlan plan_selective_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int num_cus);
+hipError_t launch_selective_bwd(const BwdArgs& a, const BwdPlan& plan, hipStream_t stream);
 
 struct EwPlan {
   int segments;

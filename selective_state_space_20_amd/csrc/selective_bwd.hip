@@ -1,0 +1,462 @@
+// selective_bwd.hip -- gfx950 kernels for the gradients of the selective scan.
+//
+// Training needs the gradients of the scan's inputs.  "Selective Scan trong Mamba toi uu
+// chuoi dai the nao?" (section "Recomputation: doi mot it compute lay it memory hon"):
+// the states are not kept from the forward pass but recomputed.  With
+//   a_t = exp(delta_t A_n), h_t = a_t h_{t-1} + delta_t B_t[n] x_t,
+//   y_t = (sum_n C_t[n] h_t[n] + D x_t) silu(z_t),
+// the adjoint lambda_t = dL/dh_t runs backwards in time with the same affine structure,
+//   lambda_t = C_t dv_t + a_{t+1} lambda_{t+1},   dv_t = dy_t silu(z_t),
+// and every gradient is a per-step product of lambda_t with forward quantities:
+//   dx_t = D dv_t + sum_n lambda_t delta_t B_t,  ddelta_t = sum_n lambda_t (B_t x_t + A a_t h_{t-1}),
+//   dA_n = sum lambda_t delta_t a_t h_{t-1},     dB_t[n] = sum_d lambda_t delta_t x_t,
+//   dC_t[n] = sum_d dv_t h_t,  dD = sum dv_t x_t,  dz_t = dy_t v_t silu'(z_t),  dh0 = a_0 lambda_0.
+//
+// Mapping (lanes = 64 adjacent channels, time split into the forward pass's segments):
+//   1. forward pass 1 + carry (selective_scan.hip): the state entering every segment;
+//   2. sel_bwd_local: each segment's adjoint folded backwards from zero, mu = a (mu + C dv);
+//   3. sel_bwd_carry: the adjoint entering every segment from its right end (from dh_last);
+//   4. sel_bwd_kernel: per segment, a forward sweep stores the state every K steps; then the
+//      K-step sub-chunks are taken in reverse order: their states are re-formed in
+//      registers from the checkpoint and the adjoint walks them backwards, writing dx,
+//      ddelta, dz and per-wave partial sums of dB/dC (a cross-lane reduce-scatter over the
+//      64 channels) and per-segment partials of dA/dD;
+//   5. small kernels add the partials up.
+#include "common.h"
+#include "kernels.h"
+
+#include <algorithm>
+
+namespace sss {
+
+struct BwdSeg {
+  int64_t batch, L, D, seg_len;
+  int S, ngroups, nsub, K;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t bwd_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7FFFFFFF, 0x00020000);
+}
+
+template <bool BF16>
+__device__ __forceinline__ float ld_io(__amdgpu_buffer_rsrc_t r, int vo, int so) {
+  if (BF16) return __builtin_bit_cast(float, (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, vo, so, 0) << 16);
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, vo, so, 0));
+}
+
+__device__ __forceinline__ float ld_f32(__amdgpu_buffer_rsrc_t r, int vo, int so) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, vo, so, 0));
+}
+
+__device__ __forceinline__ void st_f32(float v, __amdgpu_buffer_rsrc_t r, int vo, int so) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, vo, so, 2);
+}
+
+// silu'(z) = s (1 + z (1 - s)), s = sigmoid(z)
+__device__ __forceinline__ float sigmoid_f(float z) { return fast_rcp(1.0f + fast_exp2(-z * kLog2e)); }
+
+constexpr int bwd_k(int ns) { return ns >= 64 ? 1 : ns >= 32 ? 2 : ns >= 16 ? 4 : ns >= 8 ? 8 : 16; }
+constexpr int bwd_min_waves(int ns) { return ns >= 32 ? 1 : 2; }
+
+// Common prologue: (wave, batch, segment) of this workgroup and the lane's channel.
+struct BwdLane {
+  int lane, grp, s;
+  int64_t b, d0, dc, tbeg;
+  int loff, len;
+  bool real;  // false for lanes mirroring channel D-1 past the end
+};
+
+__device__ __forceinline__ BwdLane bwd_lane(const BwdSeg& g, int seg_offset) {
+  BwdLane r;
+  r.lane = threadIdx.x & 63;
+  uint32_t lid = xcd_remap(blockIdx.x, gridDim.x);
+  r.grp = (int)(lid % (uint32_t)g.ngroups);
+  lid /= (uint32_t)g.ngroups;
+  r.b = (int64_t)(lid % (uint32_t)g.batch);
+  r.s = (int)(lid / (uint32_t)g.batch) + seg_offset;
+  r.d0 = (int64_t)r.grp * 64;
+  r.real = r.d0 + r.lane < g.D;
+  r.dc = min(r.d0 + r.lane, g.D - 1);
+  r.loff = (int)(r.dc - r.d0);
+  r.tbeg = (int64_t)r.s * g.seg_len;
+  r.len = (int)(min(r.tbeg + g.seg_len, g.L) - r.tbeg);
+  return r;
+}
+
+// ------------------------------------------------------------------ 2. reverse-local fold
+// Segments 1..S-1: mu_loc[s][b][n][d] = adjoint at the segment's first step from a zero
+// adjoint at its end, mu = a_t (mu + C_t dv_t) walked from the last step down; also the
+// segment's delta sum (the forward pass 1 has none for the last segment).
+template <int NS, bool BF16, bool HAS_Z>
+__global__ __launch_bounds__(64) void sel_bwd_local(const void* __restrict__ delta, const float* __restrict__ A,
+                                                    const float* __restrict__ Cm, const void* __restrict__ z,
+                                                    const float* __restrict__ dy, float* __restrict__ mu_loc,
+                                                    float* __restrict__ seg_dsum, BwdSeg g) {
+  const BwdLane q = bwd_lane(g, 1);
+  constexpr int ES = BF16 ? 2 : 4;
+  float a2[NS], mu[NS];
+#pragma unroll
+  for (int n = 0; n < NS; ++n) {
+    a2[n] = fmaxf(A[q.dc * NS + n] * kLog2e, -kFltMax);
+    mu[n] = 0.0f;
+  }
+  const int64_t row0 = (q.b * g.L + q.tbeg) * g.D + q.d0;
+  const __amdgpu_buffer_rsrc_t rd = bwd_rsrc((const char*)delta + row0 * ES);
+  const __amdgpu_buffer_rsrc_t rz = bwd_rsrc(HAS_Z ? (const char*)z + row0 * ES : (const char*)delta);
+  const __amdgpu_buffer_rsrc_t rg = bwd_rsrc(dy + row0);
+  const int rs = (int)(g.D * ES), rs4 = (int)(g.D * 4);
+  const float* Cr = Cm + (q.b * g.L + q.tbeg) * NS;
+  float dsum = 0.0f;
+  for (int t = q.len - 1; t >= 0; --t) {
+    const float dl = ld_io<BF16>(rd, q.loff * ES, t * rs);
+    dsum += dl;
+    float dv = ld_f32(rg, q.loff * 4, t * rs4);
+    if (HAS_Z) {
+      const float zv = ld_io<BF16>(rz, q.loff * ES, t * rs);
+      dv *= zv * sigmoid_f(zv);
+    }
+    const float* Ct = Cr + t * NS;
+#pragma unroll
+    for (int n = 0; n < NS; ++n) mu[n] = fast_exp2(dl * a2[n]) * __builtin_fmaf(Ct[n], dv, mu[n]);
+  }
+#pragma unroll
+  for (int n = 0; n < NS; ++n) mu_loc[(((int64_t)q.s * g.batch + q.b) * NS + n) * g.D + q.dc] = mu[n];
+  seg_dsum[((int64_t)q.s * g.batch + q.b) * g.D + q.dc] = dsum;
+}
+
+// ------------------------------------------------------------------ 3. reverse carry
+// One thread per (b, n, d), in place: slot[s] := adjoint entering segment s from its right
+// end (dh_last for the last segment), then mu_{s-1} = exp2(A' sum delta_s) mu_s + mu_loc[s].
+__global__ __launch_bounds__(256) void sel_bwd_carry(const float* __restrict__ A, const float* __restrict__ dh_last,
+                                                     float* slots, const float* __restrict__ seg_dsum, int64_t batch,
+                                                     int64_t D, int N, int S) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_b = (int64_t)N * D;
+  if (idx >= batch * per_b) return;
+  const int64_t b = idx / per_b, rem = idx - b * per_b;
+  const int64_t n = rem / D, d = rem - n * D;
+  const float a2 = fmaxf(A[d * N + n] * kLog2e, -kFltMax);
+  float cur = dh_last ? dh_last[(b * D + d) * N + n] : 0.0f;
+  const int64_t sstride = batch * per_b, dstride = batch * D;
+  float* slot = slots + b * per_b + rem;
+  const float* dsp = seg_dsum + b * D + d;
+  for (int s1 = S - 1; s1 >= 0; s1 -= 8) {
+    float lo[8], ds[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int s = s1 - i;
+      const bool live = s >= 1;  // segment 0 has no local fold
+      lo[i] = live ? slot[(int64_t)s * sstride] : 0.0f;
+      ds[i] = live ? dsp[(int64_t)s * dstride] : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int s = s1 - i;
+      if (s >= 0) slot[(int64_t)s * sstride] = cur;
+      cur = __builtin_fmaf(fast_exp2(a2 * ds[i]), cur, lo[i]);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ cross-lane reduce-scatter
+// V values per lane -> after the xor levels 32, 16, ..., 1 each lane holds V >> min(6, log2 V)
+// values, each summed over all 64 lanes; value index = (lane >> (6 - levels)) * keep + i.
+// Level LV halves the CNT live values (lanes with the level's bit set keep the upper half,
+// the others the lower half) until one is left, then keeps adding the partner's value.
+template <int LV, int CNT, int V>
+__device__ __forceinline__ void reduce_scatter_level(float (&p)[V], int lane) {
+  if constexpr (LV < 6) {
+    constexpr int dist = 32 >> LV;
+    const bool hi = (lane & dist) != 0;
+    if constexpr (CNT > 1) {
+      constexpr int half = CNT / 2;
+#pragma unroll
+      for (int i = 0; i < half; ++i) {
+        const float send = hi ? p[i] : p[half + i];
+        const float keep = hi ? p[half + i] : p[i];
+        p[i] = keep + __shfl_xor(send, dist);
+      }
+      reduce_scatter_level<LV + 1, half, V>(p, lane);
+    } else {
+      p[0] += __shfl_xor(p[0], dist);
+      reduce_scatter_level<LV + 1, 1, V>(p, lane);
+    }
+  }
+}
+
+template <int V>
+__device__ __forceinline__ void reduce_scatter(float (&p)[V], int lane) {
+  reduce_scatter_level<0, V, V>(p, lane);
+}
+
+constexpr int ilog2c(int v) { return v <= 1 ? 0 : 1 + ilog2c(v / 2); }
+
+// ------------------------------------------------------------------ 4. main backward pass
+template <int NS, bool BF16, bool HAS_Z>
+__global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
+    const void* __restrict__ x, const void* __restrict__ delta, const float* __restrict__ A,
+    const float* __restrict__ Bm, const float* __restrict__ Cm, const float* __restrict__ Dsk,
+    const void* __restrict__ z, const float* __restrict__ h0, const float* __restrict__ dy,
+    const float* __restrict__ dh_last, const float* __restrict__ seg_in, const float* __restrict__ mu_right,
+    float* __restrict__ ckpt, float* __restrict__ dx, float* __restrict__ ddelta, float* __restrict__ dz,
+    float* __restrict__ part_bc, float* __restrict__ part_a, float* __restrict__ part_d, float* __restrict__ dh0,
+    BwdSeg g) {
+  constexpr int K = bwd_k(NS);
+  constexpr int ES = BF16 ? 2 : 4;
+  constexpr int V = 2 * NS;
+  constexpr int LV = ilog2c(V) < 6 ? ilog2c(V) : 6;
+  constexpr int KEEP = V >> LV;
+  const BwdLane q = bwd_lane(g, 0);
+  const int64_t chl = (q.b * g.D + q.dc) * NS;  // (b, d) row of h0 / dh_last / dh0
+
+  float a2[NS], h[NS], mu[NS], dacc[NS];
+#pragma unroll
+  for (int n = 0; n < NS; ++n) {
+    a2[n] = fmaxf(A[q.dc * NS + n] * kLog2e, -kFltMax);
+    const int64_t so = (((int64_t)q.s * g.batch + q.b) * NS + n) * g.D + q.dc;
+    h[n] = g.S > 1 ? seg_in[so] : (h0 ? h0[chl + n] : 0.0f);
+    mu[n] = g.S > 1 ? mu_right[so] : (dh_last ? dh_last[chl + n] : 0.0f);
+    dacc[n] = 0.0f;
+  }
+  const float Dd = Dsk ? Dsk[q.dc] : 0.0f;
+  float ddacc = 0.0f;
+
+  const int64_t row0 = (q.b * g.L + q.tbeg) * g.D + q.d0;
+  const __amdgpu_buffer_rsrc_t rx = bwd_rsrc((const char*)x + row0 * ES);
+  const __amdgpu_buffer_rsrc_t rd = bwd_rsrc((const char*)delta + row0 * ES);
+  const __amdgpu_buffer_rsrc_t rz = bwd_rsrc(HAS_Z ? (const char*)z + row0 * ES : (const char*)x);
+  const __amdgpu_buffer_rsrc_t rg = bwd_rsrc(dy + row0);
+  const __amdgpu_buffer_rsrc_t rdx = bwd_rsrc(dx + row0);
+  const __amdgpu_buffer_rsrc_t rdd = bwd_rsrc(ddelta + row0);
+  const __amdgpu_buffer_rsrc_t rdz = bwd_rsrc(HAS_Z ? dz + row0 : dx + row0);
+  const int rs = (int)(g.D * ES), rs4 = (int)(g.D * 4);
+  const int vo = q.loff * ES, vo4 = q.loff * 4;
+  const float* Br = Bm + (q.b * g.L + q.tbeg) * NS;
+  const float* Cr = Cm + (q.b * g.L + q.tbeg) * NS;
+  // checkpoint j of this segment: [s * nsub + j][b][n][d]
+  auto ck = [&](int j, int n) -> int64_t {
+    return ((((int64_t)q.s * g.nsub + j) * g.batch + q.b) * NS + n) * g.D + q.dc;
+  };
+
+  // forward sweep: the state before every K-th step
+  for (int t = 0; t < q.len; ++t) {
+    if (t % K == 0) {
+#pragma unroll
+      for (int n = 0; n < NS; ++n) ckpt[ck(t / K, n)] = h[n];
+    }
+    const float xv = ld_io<BF16>(rx, vo, t * rs), dl = ld_io<BF16>(rd, vo, t * rs);
+    const float dxv = dl * xv;
+    const float* Bt = Br + t * NS;
+#pragma unroll
+    for (int n = 0; n < NS; ++n) h[n] = __builtin_fmaf(fast_exp2(dl * a2[n]), h[n], dxv * Bt[n]);
+  }
+
+  // sub-chunks in reverse order
+  for (int j = (q.len - 1) / K; j >= 0; --j) {
+    const int tb = j * K;
+    const int k = min(K, q.len - tb);
+    float hs[K + 1][NS], xs[K], ds[K];
+#pragma unroll
+    for (int n = 0; n < NS; ++n) hs[0][n] = ckpt[ck(j, n)];
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      if (i < k) {
+        const int t = tb + i;
+        xs[i] = ld_io<BF16>(rx, vo, t * rs);
+        ds[i] = ld_io<BF16>(rd, vo, t * rs);
+        const float dxv = ds[i] * xs[i];
+        const float* Bt = Br + t * NS;
+#pragma unroll
+        for (int n = 0; n < NS; ++n) hs[i + 1][n] = __builtin_fmaf(fast_exp2(ds[i] * a2[n]), hs[i][n], dxv * Bt[n]);
+      }
+    }
+#pragma unroll
+    for (int i = K - 1; i >= 0; --i) {
+      if (i < k) {
+        const int t = tb + i;
+        const float xv = xs[i], dl = ds[i];
+        const float* Bt = Br + t * NS;
+        const float* Ct = Cr + t * NS;
+        float gy = ld_f32(rg, vo4, t * rs4);
+        float dv = gy;
+        float zv = 0.0f, sg = 0.0f;
+        if (HAS_Z) {
+          zv = ld_io<BF16>(rz, vo, t * rs);
+          sg = sigmoid_f(zv);
+          dv = gy * zv * sg;
+        }
+        float vsum = Dd * xv, gx = Dd * dv, gd = 0.0f;
+        float pr[V];
+#pragma unroll
+        for (int n = 0; n < NS; ++n) {
+          vsum = __builtin_fmaf(Ct[n], hs[i + 1][n], vsum);
+          const float a = fast_exp2(dl * a2[n]);
+          const float lam = __builtin_fmaf(Ct[n], dv, mu[n]);
+          const float lb = lam * Bt[n];
+          const float ah = a * hs[i][n];
+          gx = __builtin_fmaf(lb, dl, gx);
+          gd = __builtin_fmaf(lb, xv, __builtin_fmaf(lam * (a2[n] * kLn2), ah, gd));
+          dacc[n] = __builtin_fmaf(lam * dl, ah, dacc[n]);
+          pr[n] = q.real ? lam * dl * xv : 0.0f;            // dB_t[n], this channel
+          pr[NS + n] = q.real ? dv * hs[i + 1][n] : 0.0f;   // dC_t[n], this channel
+          mu[n] = a * lam;
+        }
+        ddacc = __builtin_fmaf(dv, xv, ddacc);
+        st_f32(gx, rdx, vo4, t * rs4);
+        st_f32(gd, rdd, vo4, t * rs4);
+        if (HAS_Z) st_f32(gy * vsum * sg * __builtin_fmaf(zv, 1.0f - sg, 1.0f), rdz, vo4, t * rs4);
+        reduce_scatter<V>(pr, q.lane);
+        // lanes holding distinct sums write them: this wave's partial over its 64 channels
+        if ((q.lane & ((1 << (6 - LV)) - 1)) == 0) {
+          float* dst = part_bc + (((int64_t)q.grp * g.batch + q.b) * g.L + q.tbeg + t) * V + (q.lane >> (6 - LV)) * KEEP;
+#pragma unroll
+          for (int e = 0; e < KEEP; ++e) dst[e] = pr[e];
+        }
+      }
+    }
+  }
+
+#pragma unroll
+  for (int n = 0; n < NS; ++n) part_a[(((int64_t)q.s * g.batch + q.b) * NS + n) * g.D + q.dc] = dacc[n];
+  part_d[((int64_t)q.s * g.batch + q.b) * g.D + q.dc] = ddacc;
+  if (q.s == 0 && dh0 != nullptr) {
+#pragma unroll
+    for (int n = 0; n < NS; ++n) dh0[chl + n] = mu[n];
+  }
+}
+
+// ------------------------------------------------------------------ 5. partial sums
+// dB[b][t][n] = sum_grp part[grp][b][t][n], dC from the second half of each row.
+__global__ __launch_bounds__(256) void bwd_reduce_bc(const float* __restrict__ part, float* __restrict__ dB,
+                                                     float* __restrict__ dC, int64_t rows /* batch * L */, int N,
+                                                     int ngroups) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t V = 2 * (int64_t)N;
+  if (idx >= rows * V) return;
+  float acc = 0.0f;
+  for (int gidx = 0; gidx < ngroups; ++gidx) acc += part[(int64_t)gidx * rows * V + idx];
+  const int64_t r = idx / V, j = idx - r * V;
+  if (j < N) dB[r * N + j] = acc;
+  else dC[r * N + (j - N)] = acc;
+}
+
+// dA[d][n] = sum_{s,b} part_a[s][b][n][d]; dD[d] = sum_{s,b} part_d[s][b][d].
+__global__ __launch_bounds__(256) void bwd_reduce_ad(const float* __restrict__ part_a,
+                                                     const float* __restrict__ part_d, float* __restrict__ dA,
+                                                     float* __restrict__ dD, int64_t sb /* S * batch */, int N,
+                                                     int64_t D) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // n * D + d
+  if (idx >= (int64_t)N * D) return;
+  const int64_t n = idx / D, d = idx - n * D;
+  float acc = 0.0f;
+  for (int64_t i = 0; i < sb; ++i) acc += part_a[i * N * D + idx];
+  dA[d * N + n] = acc;
+  if (n == 0 && dD != nullptr) {
+    float ad = 0.0f;
+    for (int64_t i = 0; i < sb; ++i) ad += part_d[i * D + d];
+    dD[d] = ad;
+  }
+}
+
+// ------------------------------------------------------------------ host side
+static size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+BwdPlan plan_selective_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int num_cus) {
+  BwdPlan bp{};
+  bp.fwd = plan_selective(batch, seqlen, dim, dstate, num_cus);
+  const int64_t S = bp.fwd.segments;
+  const int K = bwd_k((int)dstate);
+  bp.K = K;
+  bp.nsub = (int)((bp.fwd.seg_len + K - 1) / K);
+  const int64_t ngroups = (dim + 63) / 64;
+  size_t off = align256(bp.fwd.ws_total);
+  bp.off_mu = off;
+  off = align256(off + (S > 1 ? (size_t)S * batch * dstate * dim * 4 : 0));
+  bp.off_ckpt = off;
+  off = align256(off + (size_t)S * bp.nsub * batch * dstate * dim * 4);
+  bp.off_bc = off;
+  off = align256(off + (size_t)ngroups * batch * seqlen * 2 * dstate * 4);
+  bp.off_pa = off;
+  off = align256(off + (size_t)S * batch * dstate * dim * 4);
+  bp.off_pd = off;
+  off = align256(off + (size_t)S * batch * dim * 4);
+  bp.ws_total = off;
+  return bp;
+}
+
+template <int NS, bool BF16>
+static hipError_t run_bwd(const BwdArgs& a, const BwdPlan& bp, hipStream_t stream) {
+  unsigned char* ws = static_cast<unsigned char*>(a.fwd.workspace);
+  const int S = bp.fwd.segments;
+  BwdSeg g{};
+  g.batch = a.fwd.batch;
+  g.L = a.fwd.seqlen;
+  g.D = a.fwd.dim;
+  g.seg_len = bp.fwd.seg_len;
+  g.S = S;
+  g.ngroups = (int)((a.fwd.dim + 63) / 64);
+  g.nsub = bp.nsub;
+  g.K = bp.K;
+  float* st = reinterpret_cast<float*>(ws + bp.fwd.ws_state);
+  float* dsum = reinterpret_cast<float*>(ws + bp.fwd.ws_dsum);
+  float* mu = reinterpret_cast<float*>(ws + bp.off_mu);
+  float* ckpt = reinterpret_cast<float*>(ws + bp.off_ckpt);
+  float* pbc = reinterpret_cast<float*>(ws + bp.off_bc);
+  float* pa = reinterpret_cast<float*>(ws + bp.off_pa);
+  float* pd = reinterpret_cast<float*>(ws + bp.off_pd);
+  const int64_t per_seg = (int64_t)g.ngroups * g.batch;
+  hipError_t e;
+  if (S > 1) {
+    if (a.fwd.z != nullptr)
+      hipLaunchKernelGGL((sel_bwd_local<NS, BF16, true>), dim3((unsigned)(per_seg * (S - 1))), dim3(64), 0, stream,
+                         a.fwd.delta, a.fwd.A, a.fwd.C, a.fwd.z, a.dy, mu, dsum, g);
+    else
+      hipLaunchKernelGGL((sel_bwd_local<NS, BF16, false>), dim3((unsigned)(per_seg * (S - 1))), dim3(64), 0, stream,
+                         a.fwd.delta, a.fwd.A, a.fwd.C, a.fwd.z, a.dy, mu, dsum, g);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t nthr = g.batch * (int64_t)NS * g.D;
+    hipLaunchKernelGGL(sel_bwd_carry, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, stream, a.fwd.A, a.dh_last,
+                       mu, (const float*)dsum, g.batch, g.D, NS, S);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const dim3 grid((unsigned)(per_seg * S)), block(64);
+  if (a.fwd.z != nullptr)
+    hipLaunchKernelGGL((sel_bwd_kernel<NS, BF16, true>), grid, block, 0, stream, a.fwd.x, a.fwd.delta, a.fwd.A,
+                       a.fwd.B, a.fwd.C, a.fwd.Dsk, a.fwd.z, a.fwd.h0, a.dy, a.dh_last, (const float*)st,
+                       (const float*)mu, ckpt, a.dx, a.ddelta, a.dz, pbc, pa, pd, a.dh0, g);
+  else
+    hipLaunchKernelGGL((sel_bwd_kernel<NS, BF16, false>), grid, block, 0, stream, a.fwd.x, a.fwd.delta, a.fwd.A,
+                       a.fwd.B, a.fwd.C, a.fwd.Dsk, a.fwd.z, a.fwd.h0, a.dy, a.dh_last, (const float*)st,
+                       (const float*)mu, ckpt, a.dx, a.ddelta, a.dz, pbc, pa, pd, a.dh0, g);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t rows = g.batch * g.L;
+  hipLaunchKernelGGL(bwd_reduce_bc, dim3((unsigned)((rows * 2 * NS + 255) / 256)), dim3(256), 0, stream,
+                     (const float*)pbc, a.dB, a.dC, rows, NS, g.ngroups);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_reduce_ad, dim3((unsigned)(((int64_t)NS * g.D + 255) / 256)), dim3(256), 0, stream,
+                     (const float*)pa, (const float*)pd, a.dA, a.dD, (int64_t)S * g.batch, NS, g.D);
+  return hipGetLastError();
+}
+
+template <bool BF16>
+static hipError_t dispatch_bwd(const BwdArgs& a, const BwdPlan& bp, hipStream_t stream) {
+  switch (a.fwd.dstate) {
+    case 1: return run_bwd<1, BF16>(a, bp, stream);
+    case 2: return run_bwd<2, BF16>(a, bp, stream);
+    case 4: return run_bwd<4, BF16>(a, bp, stream);
+    case 8: return run_bwd<8, BF16>(a, bp, stream);
+    case 16: return run_bwd<16, BF16>(a, bp, stream);
+    case 32: return run_bwd<32, BF16>(a, bp, stream);
+    case 64: return run_bwd<64, BF16>(a, bp, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_selective_bwd(const BwdArgs& a, const BwdPlan& bp, hipStream_t stream) {
+  // 1. the state entering every segment (pass 1 + carry of the forward scan)
+  hipError_t e = launch_segment_states(a.fwd, bp.fwd, stream);
+  if (e != hipSuccess) return e;
+  return a.fwd.bf16 ? dispatch_bwd<true>(a, bp, stream) : dispatch_bwd<false>(a, bp, stream);
+}
+
+}  // namespace sss

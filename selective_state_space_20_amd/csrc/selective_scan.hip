@@ -274,44 +274,63 @@ static __global__ __launch_bounds__(256) void sel_carry_kernel(const float* __re
   }
 }
 
-template <int NS, bool BF16, int FL>
-static hipError_t run_selective(const SelArgs& a, const SelPlan& pl, hipStream_t stream) {
+static SelSeg make_seg(const SelArgs& a, const SelPlan& pl, int ns) {
   SelSeg g{};
   g.batch = a.batch;
   g.L = a.seqlen;
   g.D = a.dim;
   g.seg_len = pl.seg_len;
-  g.N = NS;
+  g.N = ns;
   g.S = pl.segments;
   g.ngroups = (int)((a.dim + 63) / 64);
   g.gpb = std::min(2, g.ngroups);
   g.nblk = (g.ngroups + g.gpb - 1) / g.gpb;
+  return g;
+}
+
+// Pass 1 and the carry: the workspace's state slots end up holding the state entering
+// every segment (S > 1; nothing to do for a single segment).
+template <int NS, bool BF16, int FL>
+static hipError_t run_states(const SelArgs& a, const SelPlan& pl, hipStream_t stream) {
+  if (pl.segments <= 1) return hipSuccess;
+  const SelSeg g = make_seg(a, pl, NS);
   unsigned char* ws = static_cast<unsigned char*>(a.workspace);
-  float* st = pl.segments > 1 ? reinterpret_cast<float*>(ws + pl.ws_state) : nullptr;
-  float* ds = pl.segments > 1 ? reinterpret_cast<float*>(ws + pl.ws_dsum) : nullptr;
+  float* st = reinterpret_cast<float*>(ws + pl.ws_state);
+  float* ds = reinterpret_cast<float*>(ws + pl.ws_dsum);
   const int64_t per_seg = (int64_t)g.nblk * g.batch;
-  const unsigned nthr_wg = 64u * (unsigned)g.gpb;
-  if (pl.segments > 1) {
-    hipLaunchKernelGGL((sel_seq_kernel<NS, BF16, 1, false, FL>), dim3((unsigned)(per_seg * (pl.segments - 1))),
-                       dim3(nthr_wg), 0, stream, a.x, a.delta, a.A, a.B, a.C, a.Dsk, a.z, a.h0, (const float*)nullptr,
-                       a.y, a.h_last, st, ds, a.delta_bias, g);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int64_t nthr = g.batch * (int64_t)NS * g.D;
-    hipLaunchKernelGGL(sel_carry_kernel, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, stream, a.A, a.h0, st,
-                       (const float*)ds, g);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (a.z != nullptr)
-    hipLaunchKernelGGL((sel_seq_kernel<NS, BF16, 2, true, FL>), dim3((unsigned)(per_seg * pl.segments)), dim3(nthr_wg),
-                       0, stream, a.x, a.delta, a.A, a.B, a.C, a.Dsk, a.z, a.h0, (const float*)st, a.y, a.h_last,
-                       (float*)nullptr, (float*)nullptr, a.delta_bias, g);
-  else
-    hipLaunchKernelGGL((sel_seq_kernel<NS, BF16, 2, false, FL>), dim3((unsigned)(per_seg * pl.segments)),
-                       dim3(nthr_wg), 0, stream, a.x, a.delta, a.A, a.B, a.C, a.Dsk, a.z, a.h0, (const float*)st, a.y,
-                       a.h_last, (float*)nullptr, (float*)nullptr, a.delta_bias, g);
+  hipLaunchKernelGGL((sel_seq_kernel<NS, BF16, 1, false, FL>), dim3((unsigned)(per_seg * (pl.segments - 1))),
+                     dim3(64u * (unsigned)g.gpb), 0, stream, a.x, a.delta, a.A, a.B, a.C, a.Dsk, a.z, a.h0,
+                     (const float*)nullptr, a.y, a.h_last, st, ds, a.delta_bias, g);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t nthr = g.batch * (int64_t)NS * g.D;
+  hipLaunchKernelGGL(sel_carry_kernel, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, stream, a.A, a.h0, st,
+                     (const float*)ds, g);
   return hipGetLastError();
+}
+
+template <int NS, bool BF16, int FL>
+static hipError_t run_selective(const SelArgs& a, const SelPlan& pl, hipStream_t stream) {
+  hipError_t e = run_states<NS, BF16, FL>(a, pl, stream);
+  if (e != hipSuccess) return e;
+  const SelSeg g = make_seg(a, pl, NS);
+  unsigned char* ws = static_cast<unsigned char*>(a.workspace);
+  const float* st = pl.segments > 1 ? reinterpret_cast<const float*>(ws + pl.ws_state) : nullptr;
+  const int64_t per_seg = (int64_t)g.nblk * g.batch;
+  const dim3 grid((unsigned)(per_seg * pl.segments)), block(64u * (unsigned)g.gpb);
+  if (a.z != nullptr)
+    hipLaunchKernelGGL((sel_seq_kernel<NS, BF16, 2, true, FL>), grid, block, 0, stream, a.x, a.delta, a.A, a.B, a.C,
+                       a.Dsk, a.z, a.h0, st, a.y, a.h_last, (float*)nullptr, (float*)nullptr, a.delta_bias, g);
+  else
+    hipLaunchKernelGGL((sel_seq_kernel<NS, BF16, 2, false, FL>), grid, block, 0, stream, a.x, a.delta, a.A, a.B,
+                       a.C, a.Dsk, a.z, a.h0, st, a.y, a.h_last, (float*)nullptr, (float*)nullptr, a.delta_bias, g);
+  return hipGetLastError();
+}
+
+// Segment entering states of the plain form (no options), for the backward pass.
+template <int NS, bool BF16>
+hipError_t run_segment_states(const SelArgs& a, const SelPlan& pl, hipStream_t stream) {
+  return run_states<NS, BF16, 0>(a, pl, stream);
 }
 
 // Front end / hold variants: plain, exact hold, delta + bias (+ softplus), and both.
@@ -335,10 +354,14 @@ hipError_t run_flags(const SelArgs& a, const SelPlan& pl, hipStream_t stream) {
 #ifdef SSS_INST_NS
 template hipError_t run_flags<SSS_INST_NS, false>(const SelArgs&, const SelPlan&, hipStream_t);
 template hipError_t run_flags<SSS_INST_NS, true>(const SelArgs&, const SelPlan&, hipStream_t);
+template hipError_t run_segment_states<SSS_INST_NS, false>(const SelArgs&, const SelPlan&, hipStream_t);
+template hipError_t run_segment_states<SSS_INST_NS, true>(const SelArgs&, const SelPlan&, hipStream_t);
 #else
-#define SSS_EXTERN_INSTANCES(N)                                                                     \
-  extern template hipError_t run_flags<N, false>(const SelArgs&, const SelPlan&, hipStream_t);  \
-  extern template hipError_t run_flags<N, true>(const SelArgs&, const SelPlan&, hipStream_t);
+#define SSS_EXTERN_INSTANCES(N)                                                                        \
+  extern template hipError_t run_flags<N, false>(const SelArgs&, const SelPlan&, hipStream_t);           \
+  extern template hipError_t run_flags<N, true>(const SelArgs&, const SelPlan&, hipStream_t);            \
+  extern template hipError_t run_segment_states<N, false>(const SelArgs&, const SelPlan&, hipStream_t);  \
+  extern template hipError_t run_segment_states<N, true>(const SelArgs&, const SelPlan&, hipStream_t);
 SSS_EXTERN_INSTANCES(1)
 SSS_EXTERN_INSTANCES(2)
 SSS_EXTERN_INSTANCES(4)
@@ -404,6 +427,24 @@ static hipError_t dispatch_n(const SelArgs& a, const SelPlan& pl, hipStream_t st
 
 hipError_t launch_selective(const SelArgs& a, const SelPlan& pl, hipStream_t stream) {
   return a.bf16 ? dispatch_n<true>(a, pl, stream) : dispatch_n<false>(a, pl, stream);
+}
+
+template <bool BF16>
+static hipError_t dispatch_states(const SelArgs& a, const SelPlan& pl, hipStream_t stream) {
+  switch (a.dstate) {
+    case 1: return run_segment_states<1, BF16>(a, pl, stream);
+    case 2: return run_segment_states<2, BF16>(a, pl, stream);
+    case 4: return run_segment_states<4, BF16>(a, pl, stream);
+    case 8: return run_segment_states<8, BF16>(a, pl, stream);
+    case 16: return run_segment_states<16, BF16>(a, pl, stream);
+    case 32: return run_segment_states<32, BF16>(a, pl, stream);
+    case 64: return run_segment_states<64, BF16>(a, pl, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_segment_states(const SelArgs& a, const SelPlan& pl, hipStream_t stream) {
+  return a.bf16 ? dispatch_states<true>(a, pl, stream) : dispatch_states<false>(a, pl, stream);
 }
 
 #endif  // SSS_INST_NS

@@ -79,6 +79,27 @@ def test_selective_ex_rejections():
     assert selx(dim=0, flags=3) == BAD_DIM
 
 
+def bwd(**kw):
+    a = dict(x=P, delta=2 * P, A=3 * P, B=4 * P, C=5 * P, D_skip=0, z=0, h0=0, dy=6 * P, dh_last=0, dx=64 * P,
+             ddelta=65 * P, dA=66 * P, dB=67 * P, dC=68 * P, dD=0, dz=0, dh0=0, batch=2, seqlen=8, dim=4, dstate=4,
+             io_dtype=0, workspace=80 * P, workspace_bytes=1 << 30, stream=0)
+    a.update(kw)
+    return sss.selective_scan_bwd_raw(**a)
+
+
+def test_backward_rejections():
+    assert bwd(dy=0) == NULL_ARG
+    assert bwd(dC=0) == NULL_ARG
+    assert bwd(D_skip=7 * P) == NULL_ARG          # D given without dD
+    assert bwd(z=7 * P) == NULL_ARG               # z given without dz
+    assert bwd(dstate=3) == UNSUPPORTED
+    assert bwd(dx=P) == ALIAS                     # dx over x
+    assert bwd(dB=65 * P + 16) == ALIAS           # dB over ddelta
+    assert bwd(dx=6 * P) == ALIAS                 # dx over dy
+    assert bwd(seqlen=0) == BAD_DIM
+    assert sss.selective_scan_bwd_workspace_size(1, 1000, 64, 16) > sss.selective_scan_fwd_workspace_size(1, 1000, 64, 16)
+
+
 def upd(**kw):
     a = dict(x=P, delta=2 * P, A=3 * P, B=4 * P, C=5 * P, D_skip=0, z=0, state=32 * P, y=64 * P, batch=2, dim=4,
              dstate=4, io_dtype=0, stream=0)
@@ -163,3 +184,4 @@ def test_no_device_reports_hip_error():
     assert selx(flags=3, delta_bias=6 * P) == HIP
     assert ew() == HIP
     assert upd() == HIP
+    assert bwd() == HIP

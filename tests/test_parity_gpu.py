@@ -169,6 +169,78 @@ def test_selective_exact_zoh_special_values(oracle_lib):
     assert rel_err(y, yr) <= TOL_F32 and rel_err(hl, hr) <= TOL_F32
 
 
+# ---------------------------------------------------------------- backward (gradients)
+BWD_CASES = [  # (batch, seqlen, dim, dstate, io, z, D, h0, dh_last, forced segments)
+    (1, 1, 1, 1, "f32", False, False, False, False, 0),
+    (2, 300, 33, 16, "f32", True, True, True, True, 0),
+    (2, 1000, 70, 16, "f32", True, True, True, True, 3),
+    (1, 2000, 64, 16, "bf16", True, True, True, True, 0),
+    (3, 513, 20, 8, "bf16", False, True, False, True, 7),
+    (2, 777, 40, 4, "f32", True, False, True, False, 2),
+    (1, 400, 100, 2, "f32", True, True, True, True, 5),
+    (2, 300, 24, 32, "f32", True, True, True, True, 3),
+    (1, 200, 16, 64, "bf16", True, True, True, True, 2),
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=[f"B{c[0]}L{c[1]}D{c[2]}N{c[3]}{c[4]}S{c[9]}" for c in BWD_CASES])
+def test_backward(oracle_lib, monkeypatch, case):
+    """selective_scan_bwd against the oracle's adjoint gradients (itself pinned by finite
+    differences), every gradient tensor, across single- and multi-segment plans."""
+    import torch
+    import selective_state_space_20_amd as sss
+    bt, L, dm, n, io, with_z, with_D, with_h0, with_dhl, segs = case
+    if segs:
+        monkeypatch.setenv("SSS_FORCE_SEGMENTS", str(segs))
+    seed = zlib.crc32(repr(case).encode()) % 100000
+    inp = gen.selective_inputs(bt, L, dm, n, io=io, with_z=with_z, with_D=with_D, h0=with_h0, seed=seed)
+    rng = np.random.default_rng(seed + 7)
+    dy = rng.standard_normal((bt, L, dm)).astype(np.float32)
+    dhl = rng.standard_normal((bt, dm, n)).astype(np.float32) if with_dhl else None
+    note(f"[backward] {case}")
+    t = {k: to_dev(v, "cuda:0") for k, v in inp.items() if k != "io"}
+    g = sss.selective_scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"],
+                               dy=to_dev(dy, "cuda:0"), dh_last=to_dev(dhl, "cuda:0"))
+    torch.cuda.synchronize()
+    r = oracle_lib.selective_scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                                      inp["h0"], dy=dy, dh_last=dhl)
+    tol = TOL_BF16 if io == "bf16" else TOL_F32
+    errs = {}
+    for k in ("dx", "ddelta", "dA", "dB", "dC", "dD", "dz", "dh0"):
+        if r[k] is None:
+            assert g[k] is None
+            continue
+        errs[k] = rel_err(g[k].cpu().numpy(), r[k])
+    note("    " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    assert all(v <= tol for v in errs.values()), errs
+
+
+@pytest.mark.timeout(600)
+def test_backward_long_layer_full():
+    """Gradients of the full-size long layer (B=1, D=5120, N=16, L=65536, bf16, gated, h0,
+    dh_last) against the oracle, every element of every gradient tensor."""
+    import torch
+    import oracle
+    import selective_state_space_20_amd as sss
+    cfg, inp = gen.config_inputs(3)
+    rng = np.random.default_rng(4003)
+    dy = rng.standard_normal(inp["x"].shape, dtype=np.float32)
+    dhl = rng.standard_normal(inp["h0"].shape, dtype=np.float32)
+    note(f"[backward] {cfg['name']} inputs generated")
+    t = {k: to_dev(v, "cuda:0") for k, v in inp.items() if k != "io"}
+    g = sss.selective_scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"],
+                               dy=to_dev(dy, "cuda:0"), dh_last=to_dev(dhl, "cuda:0"))
+    torch.cuda.synchronize()
+    g = {k: (v.cpu().numpy() if v is not None else None) for k, v in g.items()}
+    note("    GPU done")
+    r = oracle.selective_scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], inp["h0"],
+                                  dy=dy, dh_last=dhl)
+    note("    oracle done")
+    errs = {k: rel_err(g[k], r[k]) for k in ("dx", "ddelta", "dA", "dB", "dC", "dD", "dz", "dh0")}
+    note("    " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    assert all(v <= TOL_BF16 for v in errs.values()), errs
+
+
 # ---------------------------------------------------------------- causal conv1d front end
 CONV_CASES = [  # (batch, seqlen, dim, width, io, silu, bias, forced segments)
     (1, 1, 1, 1, "f32", False, False, 0),
