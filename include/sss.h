@@ -104,6 +104,7 @@ size_t selective_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t 
  * Required: x, delta, A, B, C, dy, dx, ddelta, dA, dB, dC; dD when D_skip is given and dz
  * when z is given (SSS_ERR_NULL_ARG otherwise); dh0 optional (gradient of the initial
  * state, zero or h0).  Outputs may not overlap inputs, each other or the workspace.
+ * dim * dstate * 4 must stay below 2^31 (SSS_ERR_BAD_DIM).
  * Workspace: at least selective_scan_bwd_workspace_size() bytes (never zero).  The sums
  * over channels (dB, dC) and over time (dA, dD) are formed from per-wave / per-segment
  * partials in a fixed order: results are deterministic.  Returns an sss_status. */

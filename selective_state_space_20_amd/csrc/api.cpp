@@ -198,6 +198,7 @@ int selective_scan_bwd(const void* x, const void* delta, const float* A, const f
   if ((D_skip && !dD) || (z && !dz)) return SSS_ERR_NULL_ARG;
   int st = sel_dims_ok(batch, seqlen, dim, dstate);
   if (st != SSS_OK) return st;
+  if (dim * dstate * 4 >= ((int64_t)1 << 31)) return SSS_ERR_BAD_DIM;  // checkpoint rows: 32-bit offsets
   if (io_dtype != SSS_F32 && io_dtype != SSS_BF16) return SSS_ERR_UNSUPPORTED;
   const void* ptrs[] = {x, delta, A, B, C, D_skip, z, h0, dy, dh_last, dx, ddelta, dA, dB, dC, dD, dz, dh0, workspace};
   for (const void* p : ptrs)

@@ -37,6 +37,10 @@ SelPlan plan_selective(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstat
 hipError_t launch_selective(const SelArgs& a, const SelPlan& plan, hipStream_t stream);
 // pass 1 + carry only: the workspace's state slots hold the state entering each segment
 hipError_t launch_segment_states(const SelArgs& a, const SelPlan& plan, hipStream_t stream);
+// after launch_segment_states: the state before every 2^kshift-th step of every segment,
+// into ckpt[s * nsub + j][batch][dstate][dim]
+hipError_t launch_checkpoints(const SelArgs& a, const SelPlan& plan, float* ckpt, int kshift, int nsub,
+                              hipStream_t stream);
 
 // Backward pass of the selective scan (selective_bwd.hip).
 struct BwdPlan {

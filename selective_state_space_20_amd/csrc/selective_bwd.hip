@@ -16,9 +16,9 @@
 //   1. forward pass 1 + carry (selective_scan.hip): the state entering every segment;
 //   2. sel_bwd_local: each segment's adjoint folded backwards from zero, mu = a (mu + C dv);
 //   3. sel_bwd_carry: the adjoint entering every segment from its right end (from dh_last);
-//   4. sel_bwd_kernel: per segment, a forward sweep stores the state every K steps; then the
-//      K-step sub-chunks are taken in reverse order: their states are re-formed in
-//      registers from the checkpoint and the adjoint walks them backwards, writing dx,
+//   4. the forward scan's checkpoint pass stores the state before every K-th step; then
+//      sel_bwd_kernel takes each segment's K-step sub-chunks in reverse order: their states
+//      are re-formed in registers from the checkpoint and the adjoint walks them backwards, writing dx,
 //      ddelta, dz and per-wave partial sums of dB/dC (a cross-lane reduce-scatter over the
 //      64 channels) and per-segment partials of dA/dD;
 //   5. small kernels add the partials up.
@@ -55,7 +55,10 @@ __device__ __forceinline__ void st_f32(float v, __amdgpu_buffer_rsrc_t r, int vo
 // silu'(z) = s (1 + z (1 - s)), s = sigmoid(z)
 __device__ __forceinline__ float sigmoid_f(float z) { return fast_rcp(1.0f + fast_exp2(-z * kLog2e)); }
 
-constexpr int bwd_k(int ns) { return ns >= 64 ? 1 : ns >= 32 ? 2 : ns >= 16 ? 4 : ns >= 8 ? 8 : 16; }
+// checkpoint spacing K: the K+1 states of a sub-chunk live in registers next to the adjoint
+// (measured on the 1 x 65536 x 5120 N=16 layer: K=2 11.7 ms; K=4 spills or, with a 512-VGPR
+// budget, runs one wave per SIMD: 17 ms)
+constexpr int bwd_k(int ns) { return ns >= 64 ? 1 : ns >= 16 ? 2 : ns >= 8 ? 4 : 8; }
 constexpr int bwd_min_waves(int ns) { return ns >= 32 ? 1 : 2; }
 
 // Common prologue: (wave, batch, segment) of this workgroup and the lane's channel.
@@ -192,30 +195,32 @@ __device__ __forceinline__ void reduce_scatter(float (&p)[V], int lane) {
 constexpr int ilog2c(int v) { return v <= 1 ? 0 : 1 + ilog2c(v / 2); }
 
 // ------------------------------------------------------------------ 4. main backward pass
+// Checkpoints (the state before every K-th step, from the forward scan's PASS 3) are taken
+// in reverse order; for each K-step sub-chunk the states are re-formed in registers and the
+// adjoint walks the sub-chunk backwards.  (Prefetching the next sub-chunk into a second
+// register slot pushed the kernel into scratch spills; two resident waves per SIMD hide
+// the loads instead.)
 template <int NS, bool BF16, bool HAS_Z>
 __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
     const void* __restrict__ x, const void* __restrict__ delta, const float* __restrict__ A,
     const float* __restrict__ Bm, const float* __restrict__ Cm, const float* __restrict__ Dsk,
-    const void* __restrict__ z, const float* __restrict__ h0, const float* __restrict__ dy,
-    const float* __restrict__ dh_last, const float* __restrict__ seg_in, const float* __restrict__ mu_right,
-    float* __restrict__ ckpt, float* __restrict__ dx, float* __restrict__ ddelta, float* __restrict__ dz,
-    float* __restrict__ part_bc, float* __restrict__ part_a, float* __restrict__ part_d, float* __restrict__ dh0,
-    BwdSeg g) {
+    const void* __restrict__ z, const float* __restrict__ dy, const float* __restrict__ dh_last,
+    const float* __restrict__ mu_right, const float* __restrict__ ckpt, float* __restrict__ dx,
+    float* __restrict__ ddelta, float* __restrict__ dz, float* __restrict__ part_bc, float* __restrict__ part_a,
+    float* __restrict__ part_d, float* __restrict__ dh0, BwdSeg g) {
   constexpr int K = bwd_k(NS);
   constexpr int ES = BF16 ? 2 : 4;
-  constexpr int V = 2 * NS;
-  constexpr int LV = ilog2c(V) < 6 ? ilog2c(V) : 6;
-  constexpr int KEEP = V >> LV;
+  constexpr int LV = ilog2c(NS) < 6 ? ilog2c(NS) : 6;  // reduce-scatter levels for NS values
+  constexpr int KEEP = NS >> LV;
   const BwdLane q = bwd_lane(g, 0);
-  const int64_t chl = (q.b * g.D + q.dc) * NS;  // (b, d) row of h0 / dh_last / dh0
+  const int64_t chl = (q.b * g.D + q.dc) * NS;  // (b, d) row of dh_last / dh0
 
-  float a2[NS], h[NS], mu[NS], dacc[NS];
+  float a2[NS], mu[NS], dacc[NS];
 #pragma unroll
   for (int n = 0; n < NS; ++n) {
     a2[n] = fmaxf(A[q.dc * NS + n] * kLog2e, -kFltMax);
-    const int64_t so = (((int64_t)q.s * g.batch + q.b) * NS + n) * g.D + q.dc;
-    h[n] = g.S > 1 ? seg_in[so] : (h0 ? h0[chl + n] : 0.0f);
-    mu[n] = g.S > 1 ? mu_right[so] : (dh_last ? dh_last[chl + n] : 0.0f);
+    mu[n] = g.S > 1 ? mu_right[(((int64_t)q.s * g.batch + q.b) * NS + n) * g.D + q.dc]
+                    : (dh_last ? dh_last[chl + n] : 0.0f);
     dacc[n] = 0.0f;
   }
   const float Dd = Dsk ? Dsk[q.dc] : 0.0f;
@@ -229,92 +234,99 @@ __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
   const __amdgpu_buffer_rsrc_t rdx = bwd_rsrc(dx + row0);
   const __amdgpu_buffer_rsrc_t rdd = bwd_rsrc(ddelta + row0);
   const __amdgpu_buffer_rsrc_t rdz = bwd_rsrc(HAS_Z ? dz + row0 : dx + row0);
+  // checkpoint j of this (segment, batch row): [s * nsub + j][b][n][d]; one descriptor per
+  // checkpoint (offsets n * D * 4 < 2^31: the caller keeps dim * dstate * 4 below 2^31)
+  auto ck_rsrc = [&](int j) {
+    return bwd_rsrc(ckpt + ((((int64_t)q.s * g.nsub + j) * g.batch + q.b) * NS) * g.D + q.d0);
+  };
   const int rs = (int)(g.D * ES), rs4 = (int)(g.D * 4);
   const int vo = q.loff * ES, vo4 = q.loff * 4;
   const float* Br = Bm + (q.b * g.L + q.tbeg) * NS;
   const float* Cr = Cm + (q.b * g.L + q.tbeg) * NS;
-  // checkpoint j of this segment: [s * nsub + j][b][n][d]
-  auto ck = [&](int j, int n) -> int64_t {
-    return ((((int64_t)q.s * g.nsub + j) * g.batch + q.b) * NS + n) * g.D + q.dc;
-  };
+  const int last = (q.len - 1) / K;
 
-  // forward sweep: the state before every K-th step
-  for (int t = 0; t < q.len; ++t) {
-    if (t % K == 0) {
-#pragma unroll
-      for (int n = 0; n < NS; ++n) ckpt[ck(t / K, n)] = h[n];
-    }
-    const float xv = ld_io<BF16>(rx, vo, t * rs), dl = ld_io<BF16>(rd, vo, t * rs);
-    const float dxv = dl * xv;
-    const float* Bt = Br + t * NS;
-#pragma unroll
-    for (int n = 0; n < NS; ++n) h[n] = __builtin_fmaf(fast_exp2(dl * a2[n]), h[n], dxv * Bt[n]);
-  }
+  float xs[1][K], ds[1][K], gs[1][K], zs[1][K];
+#define BWD_LOAD(SLOT, J)                                                                  \
+  do {                                                                                     \
+    _Pragma("unroll") for (int i = 0; i < K; ++i) {                                        \
+      const int t_ = min((J) * K + i, q.len - 1); /* clamped: tail values are not used */  \
+      xs[SLOT][i] = ld_io<BF16>(rx, vo, t_ * rs);                                          \
+      ds[SLOT][i] = ld_io<BF16>(rd, vo, t_ * rs);                                          \
+      gs[SLOT][i] = ld_f32(rg, vo4, t_ * rs4);                                             \
+      if (HAS_Z) zs[SLOT][i] = ld_io<BF16>(rz, vo, t_ * rs);                               \
+    }                                                                                      \
+  } while (0)
 
-  // sub-chunks in reverse order
-  for (int j = (q.len - 1) / K; j >= 0; --j) {
-    const int tb = j * K;
-    const int k = min(K, q.len - tb);
-    float hs[K + 1][NS], xs[K], ds[K];
-#pragma unroll
-    for (int n = 0; n < NS; ++n) hs[0][n] = ckpt[ck(j, n)];
-#pragma unroll
-    for (int i = 0; i < K; ++i) {
-      if (i < k) {
-        const int t = tb + i;
-        xs[i] = ld_io<BF16>(rx, vo, t * rs);
-        ds[i] = ld_io<BF16>(rd, vo, t * rs);
-        const float dxv = ds[i] * xs[i];
-        const float* Bt = Br + t * NS;
-#pragma unroll
-        for (int n = 0; n < NS; ++n) hs[i + 1][n] = __builtin_fmaf(fast_exp2(ds[i] * a2[n]), hs[i][n], dxv * Bt[n]);
-      }
-    }
-#pragma unroll
-    for (int i = K - 1; i >= 0; --i) {
-      if (i < k) {
-        const int t = tb + i;
-        const float xv = xs[i], dl = ds[i];
-        const float* Bt = Br + t * NS;
-        const float* Ct = Cr + t * NS;
-        float gy = ld_f32(rg, vo4, t * rs4);
-        float dv = gy;
-        float zv = 0.0f, sg = 0.0f;
-        if (HAS_Z) {
-          zv = ld_io<BF16>(rz, vo, t * rs);
-          sg = sigmoid_f(zv);
-          dv = gy * zv * sg;
-        }
-        float vsum = Dd * xv, gx = Dd * dv, gd = 0.0f;
-        float pr[V];
-#pragma unroll
-        for (int n = 0; n < NS; ++n) {
-          vsum = __builtin_fmaf(Ct[n], hs[i + 1][n], vsum);
-          const float a = fast_exp2(dl * a2[n]);
-          const float lam = __builtin_fmaf(Ct[n], dv, mu[n]);
-          const float lb = lam * Bt[n];
-          const float ah = a * hs[i][n];
-          gx = __builtin_fmaf(lb, dl, gx);
-          gd = __builtin_fmaf(lb, xv, __builtin_fmaf(lam * (a2[n] * kLn2), ah, gd));
-          dacc[n] = __builtin_fmaf(lam * dl, ah, dacc[n]);
-          pr[n] = q.real ? lam * dl * xv : 0.0f;            // dB_t[n], this channel
-          pr[NS + n] = q.real ? dv * hs[i + 1][n] : 0.0f;   // dC_t[n], this channel
-          mu[n] = a * lam;
-        }
-        ddacc = __builtin_fmaf(dv, xv, ddacc);
-        st_f32(gx, rdx, vo4, t * rs4);
-        st_f32(gd, rdd, vo4, t * rs4);
-        if (HAS_Z) st_f32(gy * vsum * sg * __builtin_fmaf(zv, 1.0f - sg, 1.0f), rdz, vo4, t * rs4);
-        reduce_scatter<V>(pr, q.lane);
-        // lanes holding distinct sums write them: this wave's partial over its 64 channels
-        if ((q.lane & ((1 << (6 - LV)) - 1)) == 0) {
-          float* dst = part_bc + (((int64_t)q.grp * g.batch + q.b) * g.L + q.tbeg + t) * V + (q.lane >> (6 - LV)) * KEEP;
-#pragma unroll
-          for (int e = 0; e < KEEP; ++e) dst[e] = pr[e];
-        }
-      }
-    }
+#define BWD_CHUNK(SLOT, J)                                                                 \
+  do {                                                                                     \
+    const int tb = (J) * K;                                                                \
+    const int k = min(K, q.len - tb);                                                      \
+    float hs[K + 1][NS];                                                                   \
+    const __amdgpu_buffer_rsrc_t rc_ = ck_rsrc(J);                                         \
+    _Pragma("unroll") for (int n = 0; n < NS; ++n) hs[0][n] = ld_f32(rc_, vo4, n * rs4);   \
+    _Pragma("unroll") for (int i = 0; i < K; ++i) {                                        \
+      if (i < k) {                                                                         \
+        const float* Bt = Br + (tb + i) * NS;                                              \
+        const float dxv = ds[SLOT][i] * xs[SLOT][i];                                       \
+        _Pragma("unroll") for (int n = 0; n < NS; ++n)                                     \
+          hs[i + 1][n] = __builtin_fmaf(fast_exp2(ds[SLOT][i] * a2[n]), hs[i][n], dxv * Bt[n]); \
+      }                                                                                    \
+    }                                                                                      \
+    _Pragma("unroll") for (int i = K - 1; i >= 0; --i) {                                   \
+      if (i < k) {                                                                         \
+        const int t = tb + i;                                                              \
+        const float xv = xs[SLOT][i], dl = ds[SLOT][i], gy = gs[SLOT][i];                  \
+        const float* Bt = Br + t * NS;                                                     \
+        const float* Ct = Cr + t * NS;                                                     \
+        float dv = gy, zv = 0.0f, sg = 0.0f;                                               \
+        if (HAS_Z) {                                                                       \
+          zv = zs[SLOT][i];                                                                \
+          sg = sigmoid_f(zv);                                                              \
+          dv = gy * zv * sg;                                                               \
+        }                                                                                  \
+        /* dC_t: this wave's 64 channels summed, one state per lane group */               \
+        float vsum = Dd * xv;                                                              \
+        float pc[NS];                                                                      \
+        _Pragma("unroll") for (int n = 0; n < NS; ++n) {                                   \
+          vsum = __builtin_fmaf(Ct[n], hs[i + 1][n], vsum);                                \
+          pc[n] = q.real ? dv * hs[i + 1][n] : 0.0f;                                       \
+        }                                                                                  \
+        reduce_scatter<NS>(pc, q.lane);                                                    \
+        float* rowp = part_bc + (((int64_t)q.grp * g.batch + q.b) * g.L + q.tbeg + t) * (2 * NS); \
+        if ((q.lane & ((1 << (6 - LV)) - 1)) == 0) {                                       \
+          _Pragma("unroll") for (int e = 0; e < KEEP; ++e) rowp[NS + (q.lane >> (6 - LV)) * KEEP + e] = pc[e]; \
+        }                                                                                  \
+        float gx = Dd * dv, gd = 0.0f;                                                     \
+        float pb[NS];                                                                      \
+        _Pragma("unroll") for (int n = 0; n < NS; ++n) {                                   \
+          const float a = fast_exp2(dl * a2[n]);                                           \
+          const float lam = __builtin_fmaf(Ct[n], dv, mu[n]);                              \
+          const float lb = lam * Bt[n];                                                    \
+          const float ah = a * hs[i][n];                                                   \
+          gx = __builtin_fmaf(lb, dl, gx);                                                 \
+          gd = __builtin_fmaf(lb, xv, __builtin_fmaf(lam * (a2[n] * kLn2), ah, gd));       \
+          dacc[n] = __builtin_fmaf(lam * dl, ah, dacc[n]);                                 \
+          pb[n] = q.real ? lam * dl * xv : 0.0f;                                           \
+          mu[n] = a * lam;                                                                 \
+        }                                                                                  \
+        ddacc = __builtin_fmaf(dv, xv, ddacc);                                             \
+        st_f32(gx, rdx, vo4, t * rs4);                                                     \
+        st_f32(gd, rdd, vo4, t * rs4);                                                     \
+        if (HAS_Z) st_f32(gy * vsum * sg * __builtin_fmaf(zv, 1.0f - sg, 1.0f), rdz, vo4, t * rs4); \
+        reduce_scatter<NS>(pb, q.lane);                                                    \
+        if ((q.lane & ((1 << (6 - LV)) - 1)) == 0) {                                       \
+          _Pragma("unroll") for (int e = 0; e < KEEP; ++e) rowp[(q.lane >> (6 - LV)) * KEEP + e] = pb[e]; \
+        }                                                                                  \
+      }                                                                                    \
+    }                                                                                      \
+  } while (0)
+
+  for (int j = last; j >= 0; --j) {
+    BWD_LOAD(0, j);
+    BWD_CHUNK(0, j);
   }
+#undef BWD_LOAD
+#undef BWD_CHUNK
 
 #pragma unroll
   for (int n = 0; n < NS; ++n) part_a[(((int64_t)q.s * g.batch + q.b) * NS + n) * g.D + q.dc] = dacc[n];
@@ -397,7 +409,6 @@ static hipError_t run_bwd(const BwdArgs& a, const BwdPlan& bp, hipStream_t strea
   g.ngroups = (int)((a.fwd.dim + 63) / 64);
   g.nsub = bp.nsub;
   g.K = bp.K;
-  float* st = reinterpret_cast<float*>(ws + bp.fwd.ws_state);
   float* dsum = reinterpret_cast<float*>(ws + bp.fwd.ws_dsum);
   float* mu = reinterpret_cast<float*>(ws + bp.off_mu);
   float* ckpt = reinterpret_cast<float*>(ws + bp.off_ckpt);
@@ -422,12 +433,12 @@ static hipError_t run_bwd(const BwdArgs& a, const BwdPlan& bp, hipStream_t strea
   const dim3 grid((unsigned)(per_seg * S)), block(64);
   if (a.fwd.z != nullptr)
     hipLaunchKernelGGL((sel_bwd_kernel<NS, BF16, true>), grid, block, 0, stream, a.fwd.x, a.fwd.delta, a.fwd.A,
-                       a.fwd.B, a.fwd.C, a.fwd.Dsk, a.fwd.z, a.fwd.h0, a.dy, a.dh_last, (const float*)st,
-                       (const float*)mu, ckpt, a.dx, a.ddelta, a.dz, pbc, pa, pd, a.dh0, g);
+                       a.fwd.B, a.fwd.C, a.fwd.Dsk, a.fwd.z, a.dy, a.dh_last, (const float*)mu, (const float*)ckpt,
+                       a.dx, a.ddelta, a.dz, pbc, pa, pd, a.dh0, g);
   else
     hipLaunchKernelGGL((sel_bwd_kernel<NS, BF16, false>), grid, block, 0, stream, a.fwd.x, a.fwd.delta, a.fwd.A,
-                       a.fwd.B, a.fwd.C, a.fwd.Dsk, a.fwd.z, a.fwd.h0, a.dy, a.dh_last, (const float*)st,
-                       (const float*)mu, ckpt, a.dx, a.ddelta, a.dz, pbc, pa, pd, a.dh0, g);
+                       a.fwd.B, a.fwd.C, a.fwd.Dsk, a.fwd.z, a.dy, a.dh_last, (const float*)mu, (const float*)ckpt,
+                       a.dx, a.ddelta, a.dz, pbc, pa, pd, a.dh0, g);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t rows = g.batch * g.L;
   hipLaunchKernelGGL(bwd_reduce_bc, dim3((unsigned)((rows * 2 * NS + 255) / 256)), dim3(256), 0, stream,
@@ -453,8 +464,12 @@ static hipError_t dispatch_bwd(const BwdArgs& a, const BwdPlan& bp, hipStream_t 
 }
 
 hipError_t launch_selective_bwd(const BwdArgs& a, const BwdPlan& bp, hipStream_t stream) {
-  // 1. the state entering every segment (pass 1 + carry of the forward scan)
+  // 1. the state entering every segment (pass 1 + carry of the forward scan), then the
+  //    state before every K-th step (its checkpoint pass)
   hipError_t e = launch_segment_states(a.fwd, bp.fwd, stream);
+  if (e != hipSuccess) return e;
+  unsigned char* ws = static_cast<unsigned char*>(a.fwd.workspace);
+  e = launch_checkpoints(a.fwd, bp.fwd, reinterpret_cast<float*>(ws + bp.off_ckpt), ilog2c(bp.K), bp.nsub, stream);
   if (e != hipSuccess) return e;
   return a.fwd.bf16 ? dispatch_bwd<true>(a, bp, stream) : dispatch_bwd<false>(a, bp, stream);
 }

@@ -77,12 +77,15 @@ struct SelSeg {
   int N, S, ngroups;  // ngroups = ceil(D / 64)
   int gpb;            // channel groups (waves) per workgroup, all on the same segment
   int nblk;           // workgroups per (batch, segment) = ceil(ngroups / gpb)
+  int kshift, nsub;   // PASS 3: a checkpoint every 2^kshift steps, nsub per segment
 };
 
 // ------------------------------------------------------------------ pass 1 / pass 2
 // PASS 1 (segments 0..S-2): seg_state[s][b][n][d] = end state from zero, seg_dsum[s][b][d].
 // PASS 2 (segments 0..S-1): y, and h_last from the last segment; entering state from
 //         carry[s][b][n][d] (S > 1) or h0 (S == 1).
+// PASS 3 (segments 0..S-1, for the backward pass): from the same entering state, the state
+//         before every 2^kshift-th step into seg_state[s * nsub + j][b][n][d].
 // FL: bit kZoh -- exact zero-order-hold input term, expm1(delta*A)/A * B instead of
 //     delta * B; bits kFront / kSoftplus -- the step size is delta + bias[d], then (with
 //     kSoftplus) softplus of it.
@@ -136,6 +139,7 @@ __global__ __launch_bounds__(256, min_waves_per_simd(NS)) void sel_seq_kernel(co
     }
   }
   const float Dd = (PASS == 2 && Dsk != nullptr) ? Dsk[dc] : 0.0f;
+  const int kmask = (1 << g.kshift) - 1;
   const float dbv = ((FL & kFront) != 0 && dbias != nullptr) ? dbias[dc] : 0.0f;
   constexpr bool has_z = PASS == 2 && HAS_Z;
   float dsum = 0.0f;
@@ -180,6 +184,10 @@ __global__ __launch_bounds__(256, min_waves_per_simd(NS)) void sel_seq_kernel(co
   do {                                                                           \
     const float* Bt = Br + (T) * N;                                              \
     const float* Ct = Cr + (T) * N;                                              \
+    if (PASS == 3 && ((T) & kmask) == 0) {                                       \
+      _Pragma("unroll") for (int n = 0; n < NS; ++n)                             \
+        seg_state[((((int64_t)s * g.nsub + ((T) >> g.kshift)) * g.batch + b) * N + n) * g.D + dc] = h[n]; \
+    }                                                                            \
     const float xv = wid(xq[SLOT][I]);                                           \
     const float dl = step_size<FL>(wid(dq[SLOT][I]), dbv);                       \
     const float dx = dl * xv;                                                    \
@@ -200,7 +208,7 @@ __global__ __launch_bounds__(256, min_waves_per_simd(NS)) void sel_seq_kernel(co
     }                                                                            \
     if (PASS == 1) {                                                             \
       dsum += dl;                                                                \
-    } else {                                                                     \
+    } else if (PASS == 2) {                                                      \
       float out = y0 + y1;                                                       \
       if (has_z) out *= silu(wid(zq[SLOT][I]));                                  \
       __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, out), ry, (int)(loff * 4), \
@@ -232,7 +240,7 @@ __global__ __launch_bounds__(256, min_waves_per_simd(NS)) void sel_seq_kernel(co
     if (lane == 0 || d0 + lane < g.D) seg_dsum[((int64_t)s * g.batch + b) * g.D + dc] = dsum;
 #pragma unroll
     for (int n = 0; n < NS; ++n) seg_state[(((int64_t)s * g.batch + b) * N + n) * g.D + dc] = h[n];
-  } else if (h_last != nullptr && s == g.S - 1) {
+  } else if (PASS == 2 && h_last != nullptr && s == g.S - 1) {
 #pragma unroll
     for (int n = 0; n < NS; ++n) h_last[(b * g.D + dc) * N + n] = h[n];
   }
@@ -333,6 +341,23 @@ hipError_t run_segment_states(const SelArgs& a, const SelPlan& pl, hipStream_t s
   return run_states<NS, BF16, 0>(a, pl, stream);
 }
 
+// Checkpoints for the backward pass (after run_segment_states): the state before every
+// 2^kshift-th step of every segment, into ckpt[s * nsub + j][b][n][d].
+template <int NS, bool BF16>
+hipError_t run_checkpoints(const SelArgs& a, const SelPlan& pl, float* ckpt, int kshift, int nsub,
+                           hipStream_t stream) {
+  SelSeg g = make_seg(a, pl, NS);
+  g.kshift = kshift;
+  g.nsub = nsub;
+  unsigned char* ws = static_cast<unsigned char*>(a.workspace);
+  const float* st = pl.segments > 1 ? reinterpret_cast<const float*>(ws + pl.ws_state) : nullptr;
+  const int64_t per_seg = (int64_t)g.nblk * g.batch;
+  hipLaunchKernelGGL((sel_seq_kernel<NS, BF16, 3, false, 0>), dim3((unsigned)(per_seg * pl.segments)),
+                     dim3(64u * (unsigned)g.gpb), 0, stream, a.x, a.delta, a.A, a.B, a.C, a.Dsk, a.z, a.h0, st,
+                     (float*)nullptr, (float*)nullptr, ckpt, (float*)nullptr, (const float*)nullptr, g);
+  return hipGetLastError();
+}
+
 // Front end / hold variants: plain, exact hold, delta + bias (+ softplus), and both.
 template <int NS, bool BF16>
 hipError_t run_flags(const SelArgs& a, const SelPlan& pl, hipStream_t stream) {
@@ -356,12 +381,16 @@ template hipError_t run_flags<SSS_INST_NS, false>(const SelArgs&, const SelPlan&
 template hipError_t run_flags<SSS_INST_NS, true>(const SelArgs&, const SelPlan&, hipStream_t);
 template hipError_t run_segment_states<SSS_INST_NS, false>(const SelArgs&, const SelPlan&, hipStream_t);
 template hipError_t run_segment_states<SSS_INST_NS, true>(const SelArgs&, const SelPlan&, hipStream_t);
+template hipError_t run_checkpoints<SSS_INST_NS, false>(const SelArgs&, const SelPlan&, float*, int, int, hipStream_t);
+template hipError_t run_checkpoints<SSS_INST_NS, true>(const SelArgs&, const SelPlan&, float*, int, int, hipStream_t);
 #else
 #define SSS_EXTERN_INSTANCES(N)                                                                        \
   extern template hipError_t run_flags<N, false>(const SelArgs&, const SelPlan&, hipStream_t);           \
   extern template hipError_t run_flags<N, true>(const SelArgs&, const SelPlan&, hipStream_t);            \
   extern template hipError_t run_segment_states<N, false>(const SelArgs&, const SelPlan&, hipStream_t);  \
-  extern template hipError_t run_segment_states<N, true>(const SelArgs&, const SelPlan&, hipStream_t);
+  extern template hipError_t run_segment_states<N, true>(const SelArgs&, const SelPlan&, hipStream_t);            \
+  extern template hipError_t run_checkpoints<N, false>(const SelArgs&, const SelPlan&, float*, int, int, hipStream_t); \
+  extern template hipError_t run_checkpoints<N, true>(const SelArgs&, const SelPlan&, float*, int, int, hipStream_t);
 SSS_EXTERN_INSTANCES(1)
 SSS_EXTERN_INSTANCES(2)
 SSS_EXTERN_INSTANCES(4)
@@ -445,6 +474,27 @@ static hipError_t dispatch_states(const SelArgs& a, const SelPlan& pl, hipStream
 
 hipError_t launch_segment_states(const SelArgs& a, const SelPlan& pl, hipStream_t stream) {
   return a.bf16 ? dispatch_states<true>(a, pl, stream) : dispatch_states<false>(a, pl, stream);
+}
+
+template <bool BF16>
+static hipError_t dispatch_ckpt(const SelArgs& a, const SelPlan& pl, float* ckpt, int kshift, int nsub,
+                                hipStream_t stream) {
+  switch (a.dstate) {
+    case 1: return run_checkpoints<1, BF16>(a, pl, ckpt, kshift, nsub, stream);
+    case 2: return run_checkpoints<2, BF16>(a, pl, ckpt, kshift, nsub, stream);
+    case 4: return run_checkpoints<4, BF16>(a, pl, ckpt, kshift, nsub, stream);
+    case 8: return run_checkpoints<8, BF16>(a, pl, ckpt, kshift, nsub, stream);
+    case 16: return run_checkpoints<16, BF16>(a, pl, ckpt, kshift, nsub, stream);
+    case 32: return run_checkpoints<32, BF16>(a, pl, ckpt, kshift, nsub, stream);
+    case 64: return run_checkpoints<64, BF16>(a, pl, ckpt, kshift, nsub, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_checkpoints(const SelArgs& a, const SelPlan& pl, float* ckpt, int kshift, int nsub,
+                              hipStream_t stream) {
+  return a.bf16 ? dispatch_ckpt<true>(a, pl, ckpt, kshift, nsub, stream)
+                : dispatch_ckpt<false>(a, pl, ckpt, kshift, nsub, stream);
 }
 
 #endif  // SSS_INST_NS
