@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+FLUSH_BYTES = 1 << 30           # written between timed calls to evict the 256 MB last-level cache
 VALU_FP32_TFLOPS = 157.3        # MI355X fp32 vector, published (FMA = 2 flops)
 WORKLOAD_INDEX = 3              # the largest selective_scan_fwd configuration
 
@@ -37,12 +38,10 @@ WORKLOAD_INDEX = 3              # the largest selective_scan_fwd configuration
 # dispatches), each scaled by what the same counter reads for a plain 1 GiB device copy
 # (`bench.py --copy-calibration`).  Valid only for the kernel sources they were taken on:
 # reported as null once those files change.
-# (Removing unused helpers from common.h after the runs left the generated code identical;
-# the digest below is of the cleaned sources.)
 PMC_TRAFFIC = {
-    "sources": "3a027dbe26b653a9",      # kernel_source_digest() of the profiled sources
-    "fetch_kib": 659055.0 + 46576.8 + 1034310.0,   # pass 1 + carry + pass 2, mean of 3 calls
-    "fetch_scale": 1048576.0 / 524300.0,           # 1 GiB copy reads as 524300 KiB
+    "sources": "67f71078c95cc102",      # kernel_source_digest() of the profiled sources
+    "fetch_kib": 659040.0 + 46571.8 + 1034300.0,   # pass 1 + carry + pass 2, mean of 3 calls
+    "fetch_scale": 1048576.0 / 524301.0,           # 1 GiB copy reads as 524301 KiB
     "write_kib": 86700.0 + 81920.0 + 1311040.0,
     "write_scale": 1048576.0 / 1048576.0,          # 1 GiB copy writes as 1048576 KiB
 }
@@ -84,7 +83,21 @@ def algorithmic_alu_ops(cfg):
     n = cfg["dstate"]
     valu = n * 4 + 1 + (1 if cfg["with_D"] else 0) + (4 if cfg["with_z"] else 0)
     trans = n + (2 if cfg["with_z"] else 0)
+    if cfg.get("delta_softplus"):     # bias add, softplus = max + log1p(e^-|v|): exp, log, rcp, 6 ops
+        valu += 7
+        trans += 3
+    if cfg.get("exact_zoh"):          # per state: (2^arg - 1) * (1/A) from the same exp, 2 ops
+        valu += 2 * n
     return e * (valu + 4 * trans)
+
+
+def backward_alu_ops(b, L, d, n):
+    """Minimal fp32 ALU work of the gradients (gated, D skip), in VALU-op equivalents.  Per
+    element and state: the recomputed forward step (exp, delta*A, delta*x*B, h fma = 7), the
+    adjoint lambda = a*lambda' + C*dv (2), dC += dv*h and dB += lambda*delta*x (2), and the
+    delta/A terms lambda*a*h_prev into dA and ddelta with B*lambda into dx/ddelta (5).  Per
+    element: dv = dy*silu(z) and dz (exp, rcp + 9 ops), dD, dx and ddelta (5)."""
+    return b * L * d * (n * 16 + 4 * 2 + 14)
 
 
 def kernel_source_digest():
@@ -117,6 +130,10 @@ def cpu_baseline(cfg, inp, budget_s=12.0):
     else:
         args = (inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], inp["h0"])
         run = oracle.selective_scan_channels
+    if cfg["api"] != "elementwise" and (cfg.get("delta_softplus") or cfg.get("exact_zoh")):
+        plain = run
+        run = lambda *a, channels: plain(*a, channels=channels, delta_softplus=bool(cfg.get("delta_softplus")),
+                                         exact_zoh=bool(cfg.get("exact_zoh")))
     k = min(nch, max(cores, 1) * 2)
     t0 = time.perf_counter()
     run(*args, channels=np.arange(k, dtype=np.int64))
@@ -145,7 +162,7 @@ def copy_calibration(nbytes=1 << 30, reps=5):
     print(json.dumps({"copy_bytes_each_way": nbytes, "reps": reps}))
 
 
-def bench_decode(batch, steps, warmup, dim=5120, dstate=16):
+def bench_decode(batch, steps, warmup, dim=5120, dstate=16, flush=True):
     """One decode step (selective_state_update) per call on a Mamba-2.8B-shaped layer
     (d_inner 5120, d_state 16, bf16 x/delta/z, fp32 state), `batch` tokens per step.
     Bound by moving the state: algorithmic bytes = state read + written, x/delta/z, y, B/C,
@@ -172,12 +189,17 @@ def bench_decode(batch, steps, warmup, dim=5120, dstate=16):
     def step():
         sss.selective_state_update(x, dl, A, Bm, Cm, D, z, state=state, out=y)
 
+    # The state of a few hundred tokens fits in the 256 MB last-level cache: without a flush
+    # between calls, repeated steps would be timed out of that cache instead of HBM.
+    scrub = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev) if flush else None
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t_start = time.perf_counter()
     for e0, e1 in ev:
+        if scrub is not None:
+            scrub.zero_()
         e0.record(stream)
         step()
         e1.record(stream)
@@ -188,14 +210,15 @@ def bench_decode(batch, steps, warmup, dim=5120, dstate=16):
     nbytes = (2 * batch * dim * dstate * 4 + 3 * batch * dim * 2 + batch * dim * 4 + 2 * batch * dstate * 4
               + dim * dstate * 4 + dim * 4)
     log(f"[bench] decode B={batch}: {steps} steps, wall {wall * 1e3 / steps:.4f} ms/step, event mean {mean_ms:.4f} ms, "
-        f"min {min(per_call):.4f}")
+        f"min {min(per_call):.4f}, caches flushed between calls: {flush}")
     gbs = nbytes / (mean_ms * 1e-3) / 1e9
     print(json.dumps({
         "metric": "selective_state_update (one decode step) achieved HBM GB/s, 1 GPU", "value": round(gbs, 2),
-        "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(wall * 1e3 / steps, 5),
+        "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(mean_ms if flush else wall * 1e3 / steps, 5),
         "higher_is_better": True, "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"decode_bf16_b{batch}_D{dim}_N{dstate}", "batch": batch, "dim": dim, "dstate": dstate,
-                   "algorithmic_bytes": nbytes},
+                   "algorithmic_bytes": nbytes, "caches_flushed_between_calls": flush},
         "tokens_per_s": round(batch / (mean_ms * 1e-3), 1),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "sel_update_kernel",
@@ -283,6 +306,8 @@ def bench_backward(steps, warmup):
     nbytes = e * (2 * 3 + 4) + 2 * b * L * n * 4 + d * n * 4 + d * 4 + 2 * b * d * n * 4   # inputs
     nbytes += e * 4 * 3 + d * n * 4 + 2 * b * L * n * 4 + d * 4 + b * d * n * 4               # gradients
     gbs = nbytes / (mean_ms * 1e-3) / 1e9
+    alu = backward_alu_ops(b, L, d, n)
+    alu_tflops = 2.0 * alu / (mean_ms * 1e-3) / 1e12
     log(f"[bench] backward {cfg['name']}: event mean {mean_ms:.4f} ms, workspace {ws.numel() / 1e9:.2f} GB")
     print(json.dumps({
         "metric": "selective_scan_bwd achieved HBM GB/s and elements/s, 1 GPU", "value": round(gbs, 2), "unit": "GB/s",
@@ -290,8 +315,10 @@ def bench_backward(steps, warmup):
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": "backward_" + cfg["name"], "algorithmic_bytes": nbytes, "elements": e},
         "elements_per_s": round(e / (mean_ms * 1e-3), 1),
-        "roofline": {"bound": "alu", "achieved": None, "peak": VALU_FP32_TFLOPS, "unit": "TFLOP/s", "frac": None,
-                     "traffic": None, "kernel": "selective_scan_bwd call (7 launches)", "call_ms_event_mean": round(mean_ms, 5),
+        "roofline": {"bound": "alu", "achieved": round(alu_tflops, 3), "peak": VALU_FP32_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(alu_tflops / VALU_FP32_TFLOPS, 4), "traffic": None,
+                     "kernel": "one selective_scan_bwd call (8 launches)", "call_ms_event_mean": round(mean_ms, 5),
+                     "alu_ops_per_call": alu,
                      "hbm": {"achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": round(gbs / HBM_PEAK_GBS, 4)}},
     }), flush=True)
@@ -309,6 +336,10 @@ def main():
     ap.add_argument("--backward", action="store_true", help="time selective_scan_bwd on the default workload")
     ap.add_argument("--decode", type=int, default=0, metavar="BATCH",
                     help="time one decode step (selective_state_update) of BATCH tokens instead")
+    ap.add_argument("--no-flush", action="store_true", help="decode: do not evict the caches between calls")
+    ap.add_argument("--delta-softplus", action="store_true",
+                    help="selective: time the softplus front end (the stored delta taken as the raw step)")
+    ap.add_argument("--exact-zoh", action="store_true", help="selective: time the exact zero-order-hold option")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -325,7 +356,7 @@ def main():
         bench_backward(args.steps, args.warmup)
         return
     if args.decode > 0:
-        bench_decode(args.decode, args.steps, args.warmup)
+        bench_decode(args.decode, args.steps, args.warmup, flush=not args.no_flush)
         return
 
     import torch
@@ -334,6 +365,12 @@ def main():
 
     cfg, inp = gen.config_inputs(args.workload)
     selective = cfg["api"] == "selective"
+    if selective:
+        cfg = dict(cfg, delta_softplus=args.delta_softplus, exact_zoh=args.exact_zoh)
+        if args.delta_softplus or args.exact_zoh:
+            cfg["name"] += ("_softplus" if args.delta_softplus else "") + ("_exactzoh" if args.exact_zoh else "")
+    elif args.delta_softplus or args.exact_zoh:
+        sys.exit("--delta-softplus / --exact-zoh apply to the selective configurations only")
     log(f"[bench] inputs generated for {cfg['name']}")
     dev = torch.device("cuda:0")
 
@@ -360,7 +397,8 @@ def main():
     def step():
         if selective:
             sss.selective_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"], out=y,
-                                   out_last=hl if cfg.get("h_last", False) else None, workspace=ws)
+                                   out_last=hl if cfg.get("h_last", False) else None, workspace=ws,
+                                   delta_softplus=args.delta_softplus, exact_zoh=args.exact_zoh)
         else:
             sss.elementwise_scan(t["x"], t["A"], t["B"], t["C"], t["h0"], out=y,
                                  out_last=hl if cfg.get("h_last", False) else None, workspace=ws)
@@ -398,7 +436,8 @@ def main():
             "peak": VALU_FP32_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(alu_tflops / VALU_FP32_TFLOPS, 4),
-            "traffic": measured_traffic() if args.workload == WORKLOAD_INDEX else None,
+            "traffic": (measured_traffic() if args.workload == WORKLOAD_INDEX and not (args.delta_softplus or args.exact_zoh)
+                        else None),
             "kernel": "one selective_scan_fwd call: sel_seq_kernel pass 1 + sel_carry_kernel + sel_seq_kernel pass 2",
             "call_ms_event_mean": round(mean_ms, 5),
             "alu_work": "method's minimal fp32 work per call in VALU-op equivalents (transcendental = 4), "
