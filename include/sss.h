@@ -46,7 +46,9 @@
  *  - The library allocates no device memory and keeps no state between calls other
  *    than a per-device cache of the compute-unit count.  Calls are thread-safe.
  *  - Environment: SSS_FORCE_SEGMENTS=<S> forces the number of time segments (the
- *    two-pass split) for testing; SSS_LOG=1 prints the chosen launch plan to stderr.
+ *    two-pass split) for testing; SSS_LOG=1 prints the chosen launch plan to stderr;
+ *    SSS_WAVES_PER_SIMD / SSS_CONV_WAVES_PER_CU override the occupancy targets the
+ *    selective-scan and convolution plans aim at (tuning only).
  */
 #ifndef SSS_H_
 #define SSS_H_

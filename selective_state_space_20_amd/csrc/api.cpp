@@ -317,11 +317,11 @@ int causal_conv1d_fwd(const void* x, const float* weight, const float* bias, voi
     return SSS_ERR_ALIAS;
   const int cus = current_device_cus();
   if (cus <= 0) return SSS_ERR_HIP;
-  const ConvPlan pl = plan_conv1d(batch, seqlen, dim, cus);
+  const ConvPlan pl = plan_conv1d(batch, seqlen, dim, io_dtype == SSS_BF16, cus);
   if (env_int("SSS_LOG", 0))
-    std::fprintf(stderr, "[sss] causal_conv1d_fwd B=%lld L=%lld D=%lld W=%lld: segments=%d seg_len=%lld cus=%d\n",
+    std::fprintf(stderr, "[sss] causal_conv1d_fwd B=%lld L=%lld D=%lld W=%lld: segments=%d seg_len=%lld cpl=%d\n",
                  (long long)batch, (long long)seqlen, (long long)dim, (long long)width, pl.segments,
-                 (long long)pl.seg_len, cus);
+                 (long long)pl.seg_len, pl.cpl);
   if ((double)batch * (double)((dim + 63) / 64) * (double)pl.segments > 2147483647.0 / 64) return SSS_ERR_BAD_DIM;
   ConvArgs a{};
   a.x = x;

@@ -107,6 +107,7 @@ hipError_t launch_update(const UpdArgs& a, hipStream_t stream);
 struct ConvPlan {
   int segments;
   int64_t seg_len;
+  int cpl;  // channels per lane (adjacent), 1 or 8 bytes' worth
 };
 
 struct ConvArgs {
@@ -120,7 +121,7 @@ struct ConvArgs {
   int silu;
 };
 
-ConvPlan plan_conv1d(int64_t batch, int64_t seqlen, int64_t dim, int num_cus);
+ConvPlan plan_conv1d(int64_t batch, int64_t seqlen, int64_t dim, bool bf16, int num_cus);
 hipError_t launch_conv1d(const ConvArgs& a, const ConvPlan& plan, hipStream_t stream);
 
 int env_int(const char* name, int dflt);

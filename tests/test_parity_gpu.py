@@ -252,6 +252,10 @@ CONV_CASES = [  # (batch, seqlen, dim, width, io, silu, bias, forced segments)
     (1, 700, 16, 5, "f32", True, True, 0),
     (2, 640, 96, 6, "bf16", True, True, 4),
     (1, 900, 65, 7, "f32", False, True, 2),
+    (1, 40, 4, 4, "bf16", True, True, 3),       # one lane of 4 channels, 61 mirrored lanes
+    (2, 300, 2, 3, "f32", True, True, 0),       # one lane of 2 channels
+    (1, 3000, 5120, 4, "bf16", True, True, 0),  # the long layer's width, 4 channels per lane
+    (2, 1500, 1538, 4, "f32", True, True, 5),   # 2 channels per lane, ragged last wave
 ]
 
 
@@ -278,6 +282,10 @@ def test_conv1d(oracle_lib, monkeypatch, case):
     torch.cuda.synchronize()
     got = out.float().cpu().numpy()
     ref = oracle_lib.causal_conv1d(x, w, bias, silu=silu)
+    _conv_check(got, ref, io)
+
+
+def _conv_check(got, ref, io):
     if io == "f32":
         err = rel_err(got, ref)
         note(f"    err {err:.3e}")
@@ -290,6 +298,27 @@ def test_conv1d(oracle_lib, monkeypatch, case):
         excess = np.abs(got - ref) - ulp - TOL_F32 * np.max(np.abs(ref))
         note(f"    max |err| / ulp = {np.max(np.abs(got - ref) / ulp):.3f}")
         assert np.all(excess <= 0)
+
+
+@pytest.mark.timeout(600)
+def test_conv1d_long_layer_full(oracle_lib):
+    """The front end at the long layer's full size (1 x 65536 x 5120 bf16, width 4, bias,
+    silu) in the launch configuration the benchmark times, every output element."""
+    import torch
+    import selective_state_space_20_amd as sss
+    rng = np.random.default_rng(4100)
+    x = gen.f32_to_bf16_bits(rng.standard_normal((1, 65536, 5120), dtype=np.float32))
+    w = (0.5 * rng.standard_normal((5120, 4))).astype(np.float32)
+    bias = rng.standard_normal(5120).astype(np.float32)
+    note("[conv1d] long layer inputs generated")
+    xd = to_dev(x, "cuda:0")
+    out = torch.empty(xd.shape, dtype=xd.dtype, device="cuda:0")
+    sss.causal_conv1d_fwd(xd, to_dev(w, "cuda:0"), to_dev(bias, "cuda:0"), silu=True, out=out)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    del out, xd
+    ref = oracle_lib.causal_conv1d(x, w, bias, silu=True)
+    _conv_check(got, ref, "bf16")
 
 
 # ---------------------------------------------------------------- decode step
