@@ -48,7 +48,8 @@
  *  - Environment: SSS_FORCE_SEGMENTS=<S> forces the number of time segments (the
  *    two-pass split) for testing; SSS_LOG=1 prints the chosen launch plan to stderr;
  *    SSS_WAVES_PER_SIMD / SSS_CONV_WAVES_PER_CU override the occupancy targets the
- *    selective-scan and convolution plans aim at (tuning only).
+ *    selective-scan and convolution plans aim at, SSS_EW_CPL (1, 2 or 4) the channels per
+ *    lane of the elementwise scan (tuning only).
  */
 #ifndef SSS_H_
 #define SSS_H_

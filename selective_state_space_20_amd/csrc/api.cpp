@@ -383,8 +383,9 @@ int elementwise_scan(const float* x, const float* A, const float* B, const float
       if (overlap(workspace, wb, in_p[i], in_b[i])) return SSS_ERR_ALIAS;
   }
   if (env_int("SSS_LOG", 0))
-    std::fprintf(stderr, "[sss] elementwise_scan B=%lld L=%lld D=%lld: segments=%d seg_len=%lld ws=%zu\n",
-                 (long long)batch, (long long)seqlen, (long long)dim, pl.segments, (long long)pl.seg_len, pl.ws_total);
+    std::fprintf(stderr, "[sss] elementwise_scan B=%lld L=%lld D=%lld: segments=%d seg_len=%lld cpl=%d ws=%zu\n",
+                 (long long)batch, (long long)seqlen, (long long)dim, pl.segments, (long long)pl.seg_len, pl.cpl,
+                 pl.ws_total);
   EwArgs a{};
   a.x = x;
   a.A = A;

@@ -70,6 +70,7 @@ struct EwPlan {
   int segments;
   int64_t seg_len;
   size_t ws_total;
+  int cpl;  // adjacent channels per lane (1, 2 or 4)
 };
 
 struct EwArgs {

@@ -411,7 +411,7 @@ def _check_ew(oracle_lib, inp, tag):
 
 
 EW_CASES = [(1, 1, 1, False), (2, 6, 4, False), (2, 64, 4, False), (3, 1000, 65, True), (1, 5000, 3, True),
-            (4, 333, 130, True)]
+            (4, 333, 130, True), (2, 777, 200, True), (1, 3000, 4096, True), (3, 129, 1028, False)]
 
 
 @pytest.mark.parametrize("case", EW_CASES, ids=[f"B{c[0]}L{c[1]}D{c[2]}" for c in EW_CASES])
@@ -424,6 +424,7 @@ def test_elementwise_random_shapes(oracle_lib, case):
 def test_elementwise_two_pass_forced(oracle_lib, monkeypatch, segments):
     monkeypatch.setenv("SSS_FORCE_SEGMENTS", str(segments))
     _check_ew(oracle_lib, gen.elementwise_inputs(2, 3001, 7, h0=True, seed=70 + segments), f"S={segments}")
+    _check_ew(oracle_lib, gen.elementwise_inputs(2, 3001, 520, h0=True, seed=90 + segments), f"S={segments} D=520")
 
 
 def test_elementwise_hand_worked_and_zero_decay(oracle_lib):
