@@ -13,6 +13,8 @@ What each function computes (pages cited by title and section):
     discrete recurrence h_t = Abar_t h_{t-1} + Bbar_t x_t, y_t = C_t h_t with
     input-dependent Delta, B, C; Abar = exp(Delta*A); Bbar = Delta*B (or the page's
     exact zero-order hold, ``exact_zoh=True``); plus D*x and the silu(z) gate.
+    ``layout="bdl"`` takes the channel-major arrays (time fastest) of the same operands and
+    is the same definition on their transpose.
   * ``elementwise_scan`` -- "15. Selective (Data-Dependent) SSM Scan", reference solution.
   * ``*_chunked`` -- the same results by pairs (a, b) composed with
     (a2,b2)(x)(a1,b1) = (a2 a1, a2 b1 + b2), identity (1, 0): section "Scan bien
@@ -102,13 +104,28 @@ def _check(rc):
         raise ValueError(f"oracle rejected its arguments (status {rc})")
 
 
+def _to_time_major(x, delta, z, B, C):
+    """Channel-major operands -- x, delta, z (Bt, Dm, L) and B, C (Bt, N, L), time fastest --
+    as the time-major arrays the stepwise definition below indexes (a transpose only)."""
+    tr = lambda a: None if a is None else np.ascontiguousarray(np.asarray(a).transpose(0, 2, 1))
+    return tr(x), tr(delta), tr(z), tr(B), tr(C)
+
+
 def selective_scan(x, delta, A, B, C, D=None, z=None, h0=None, *, exact_zoh=False, delta_bias=None,
-                   delta_softplus=False, return_last=True, nthreads=0):
+                   delta_softplus=False, return_last=True, layout="bld", nthreads=0):
     """x, delta, z: (Bt, L, Dm); A: (Dm, N); B, C: (Bt, L, N); D: (Dm,); h0: (Bt, Dm, N);
-    delta_bias: (Dm,) added to delta, then softplus if delta_softplus.
+    delta_bias: (Dm,) added to delta, then softplus if delta_softplus.  With
+    layout="bdl" x, delta, z are (Bt, Dm, L), B, C are (Bt, N, L) and y is (Bt, Dm, L).
 
     Returns (y (Bt, L, Dm) float64, h_last (Bt, Dm, N) float64 or None).
     """
+    if layout == "bdl":
+        x, delta, z, B, C = _to_time_major(x, delta, z, B, C)
+        y, hl = selective_scan(x, delta, A, B, C, D, z, h0, exact_zoh=exact_zoh, delta_bias=delta_bias,
+                               delta_softplus=delta_softplus, return_last=return_last, nthreads=nthreads)
+        return np.ascontiguousarray(y.transpose(0, 2, 1)), hl
+    if layout != "bld":
+        raise ValueError(f"layout must be 'bld' or 'bdl', got {layout!r}")
     x, delta, z = _io(x), _io(delta), _io(z)
     if delta.dtype != x.dtype or (z is not None and z.dtype != x.dtype):
         raise TypeError("x, delta and z must share one dtype")
@@ -126,8 +143,12 @@ def selective_scan(x, delta, A, B, C, D=None, z=None, h0=None, *, exact_zoh=Fals
 
 
 def selective_scan_channels(x, delta, A, B, C, D=None, z=None, h0=None, *, channels, exact_zoh=False,
-                            delta_bias=None, delta_softplus=False, nthreads=0):
+                            delta_bias=None, delta_softplus=False, layout="bld", nthreads=0):
     """Only the channels ``channels`` (flat b*Dm + d).  Returns y (k, L), h_last (k, N)."""
+    if layout == "bdl":
+        x, delta, z, B, C = _to_time_major(x, delta, z, B, C)
+    elif layout != "bld":
+        raise ValueError(f"layout must be 'bld' or 'bdl', got {layout!r}")
     x, delta, z = _io(x), _io(delta), _io(z)
     A, B, C, D, h0 = _f32(A), _f32(B), _f32(C), _f32(D), _f32(h0)
     dbias = _f32(delta_bias)

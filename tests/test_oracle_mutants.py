@@ -80,6 +80,8 @@ def _pin_calls():
             calls.append((name, lambda o, fn=fn: fn(o, 4)))
         elif name == "test_U1_decode_step_is_one_step_of_the_scan":
             calls.append((name, lambda o, fn=fn: fn(o, "f32", True, True)))
+        elif name == "test_L1_channel_major_running_sum":
+            calls.append((name, lambda o, fn=fn: fn(o, "f32")))
     return calls
 
 
@@ -118,3 +120,31 @@ def test_mutant_is_caught(tmp_path, mutant):
         except Exception:       # an assertion, or a ValueError from an impossible result
             caught.append(name)
     assert caught, f"no pin detects the planted mistake '{mutant}'"
+
+
+def _reshape_not_transpose(which):
+    """The channel-major adapter with one operand group reshaped instead of transposed."""
+    import numpy as np
+
+    def adapter(x, delta, z, B, C):
+        tr = lambda a: None if a is None else np.ascontiguousarray(np.asarray(a).transpose(0, 2, 1))
+        rs = lambda a: None if a is None else np.ascontiguousarray(np.asarray(a)).reshape(a.shape[0], a.shape[2], a.shape[1])
+        f_io = rs if which == "io" else tr
+        f_bc = rs if which == "bc" else tr
+        return f_io(x), f_io(delta), f_io(z), f_bc(B), f_bc(C)
+    return adapter
+
+
+@pytest.mark.parametrize("which", ["io", "bc"])
+def test_layout_mutant_is_caught(tmp_path, which):
+    """A reshape in place of the transpose in the channel-major entry (of x/delta/z, or of
+    B/C) fails a pin."""
+    mod = _mutant_module(tmp_path, "layout_" + which, "int oracle_max_threads(void)", "int oracle_max_threads(void)")
+    mod._to_time_major = _reshape_not_transpose(which)
+    caught = []
+    for name, call in _pin_calls():
+        try:
+            call(mod)
+        except Exception:
+            caught.append(name)
+    assert caught, f"no pin detects a reshaped {which} operand"

@@ -543,3 +543,50 @@ def test_G2_gradients_without_options(oracle_lib):
     _fd_check(oracle_lib, inp, dy, None, ["x", "delta", "A", "B", "C"], seed=206)
     g = oracle_lib.selective_scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], dy=dy)
     assert g["dD"] is None and g["dz"] is None
+
+
+# ---------------------------------------------------------------- channel-major (B,D,L) layout
+def _bdl(a):
+    return None if a is None else np.ascontiguousarray(np.asarray(a).transpose(0, 2, 1))
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_L1_channel_major_running_sum(oracle_lib, io):
+    """Channel-major operands (x, delta (B,D,L); B, C (B,N,L)) with A = 0: no decay, so
+    y[b,d,t] = sum_n C[b,n,t] * sum_{j<=t} delta[b,d,j] x[b,d,j] B[b,n,j] -- a cumulative
+    sum along the last axis and a contraction over n, indexed in the channel-major layout
+    itself (B and C differ per state and step, so a swapped axis anywhere shows)."""
+    rng = np.random.default_rng(31)
+    bt, dm, L, n = 2, 5, 23, 3
+    x = rng.standard_normal((bt, dm, L)).astype(np.float32)
+    dl = rng.uniform(0.1, 1.0, (bt, dm, L)).astype(np.float32)
+    Bm = rng.standard_normal((bt, n, L)).astype(np.float32)
+    Cm = rng.standard_normal((bt, n, L)).astype(np.float32)
+    if io == "bf16":
+        x, dl = gen.f32_to_bf16_bits(x), gen.f32_to_bf16_bits(dl)
+    A = np.zeros((dm, n), dtype=np.float32)
+    y, _ = oracle_lib.selective_scan(x, dl, A, Bm, Cm, layout="bdl")
+    xv, dv = widen(x), widen(dl)
+    s = np.cumsum((dv * xv)[:, :, None, :] * Bm.astype(np.float64)[:, None, :, :], axis=3)   # (b, d, n, t)
+    ref = np.sum(Cm.astype(np.float64)[:, None, :, :] * s, axis=2)
+    assert y.shape == (bt, dm, L)
+    assert rel_err(y, ref) < 1e-12
+
+
+def test_L2_channel_major_is_the_same_scan(oracle_lib):
+    """Every option through the channel-major entry equals the time-major one on the same
+    values, element for element (the layout moves data, not arithmetic)."""
+    inp = gen.selective_inputs(2, 40, 6, 4, io="bf16", with_D=True, with_z=True, h0=True, seed=32)
+    bias = np.linspace(-0.5, 0.5, 6).astype(np.float32)
+    ref, hr = oracle_lib.selective_scan(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                                        inp["h0"], exact_zoh=True, delta_bias=bias, delta_softplus=True)
+    y, hl = oracle_lib.selective_scan(_bdl(inp["x"]), _bdl(inp["delta"]), inp["A"], _bdl(inp["B"]), _bdl(inp["C"]),
+                                      inp["D"], _bdl(inp["z"]), inp["h0"], exact_zoh=True, delta_bias=bias,
+                                      delta_softplus=True, layout="bdl")
+    assert np.array_equal(y, _bdl(ref)) and np.array_equal(hl, hr)
+    yc, hc = oracle_lib.selective_scan_channels(_bdl(inp["x"]), _bdl(inp["delta"]), inp["A"], _bdl(inp["B"]),
+                                                _bdl(inp["C"]), inp["D"], _bdl(inp["z"]), inp["h0"],
+                                                channels=np.array([0, 7, 11]), exact_zoh=True, delta_bias=bias,
+                                                delta_softplus=True, layout="bdl")
+    flat = _bdl(ref).reshape(12, 40)
+    assert np.array_equal(yc, flat[[0, 7, 11]])
