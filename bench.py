@@ -130,10 +130,10 @@ def cpu_baseline(cfg, inp, budget_s=12.0):
     else:
         args = (inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], inp["h0"])
         run = oracle.selective_scan_channels
-    if cfg["api"] != "elementwise" and (cfg.get("delta_softplus") or cfg.get("exact_zoh")):
+    if cfg["api"] != "elementwise":
         plain = run
         run = lambda *a, channels: plain(*a, channels=channels, delta_softplus=bool(cfg.get("delta_softplus")),
-                                         exact_zoh=bool(cfg.get("exact_zoh")))
+                                         exact_zoh=bool(cfg.get("exact_zoh")), layout=cfg.get("layout", "bld"))
     k = min(nch, max(cores, 1) * 2)
     t0 = time.perf_counter()
     run(*args, channels=np.arange(k, dtype=np.int64))
@@ -340,6 +340,8 @@ def main():
     ap.add_argument("--delta-softplus", action="store_true",
                     help="selective: time the softplus front end (the stored delta taken as the raw step)")
     ap.add_argument("--exact-zoh", action="store_true", help="selective: time the exact zero-order-hold option")
+    ap.add_argument("--layout", choices=("bld", "bdl"), default="bld",
+                    help="selective: operand layout (bdl = channel-major x/delta/z/y and B/C)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -365,12 +367,17 @@ def main():
 
     cfg, inp = gen.config_inputs(args.workload)
     selective = cfg["api"] == "selective"
+    bdl = args.layout == "bdl"
     if selective:
-        cfg = dict(cfg, delta_softplus=args.delta_softplus, exact_zoh=args.exact_zoh)
-        if args.delta_softplus or args.exact_zoh:
-            cfg["name"] += ("_softplus" if args.delta_softplus else "") + ("_exactzoh" if args.exact_zoh else "")
-    elif args.delta_softplus or args.exact_zoh:
-        sys.exit("--delta-softplus / --exact-zoh apply to the selective configurations only")
+        cfg = dict(cfg, delta_softplus=args.delta_softplus, exact_zoh=args.exact_zoh, layout=args.layout)
+        cfg["name"] += (("_softplus" if args.delta_softplus else "") + ("_exactzoh" if args.exact_zoh else "")
+                        + ("_bdl" if bdl else ""))
+        if bdl:  # the same values, channel-major
+            for k in ("x", "delta", "z", "B", "C"):
+                if inp.get(k) is not None:
+                    inp[k] = np.ascontiguousarray(inp[k].transpose(0, 2, 1))
+    elif args.delta_softplus or args.exact_zoh or bdl:
+        sys.exit("--delta-softplus / --exact-zoh / --layout apply to the selective configurations only")
     log(f"[bench] inputs generated for {cfg['name']}")
     dev = torch.device("cuda:0")
 
@@ -384,11 +391,13 @@ def main():
     t = {k: td(v) for k, v in inp.items() if k != "io"}
     b, L, d = cfg["batch"], cfg["seqlen"], cfg["dim"]
     n = cfg["dstate"] if selective else 1
-    y = torch.empty((b, L, d), dtype=torch.float32, device=dev)
+    y = torch.empty((b, d, L) if bdl else (b, L, d), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     if selective:
         hl = torch.empty((b, d, n), dtype=torch.float32, device=dev)
-        ws_bytes = sss.selective_scan_fwd_workspace_size(b, L, d, n, 0)
+        flags = ((sss.SSS_EXACT_ZOH if args.exact_zoh else 0) | (sss.SSS_DELTA_SOFTPLUS if args.delta_softplus else 0)
+                 | (sss.SSS_LAYOUT_BDL if bdl else 0))
+        ws_bytes = sss.selective_scan_fwd_ex_workspace_size(b, L, d, n, flags, 0)
     else:
         hl = torch.empty((b, d), dtype=torch.float32, device=dev)
         ws_bytes = sss.elementwise_scan_workspace_size(b, L, d, 0)
@@ -398,7 +407,7 @@ def main():
         if selective:
             sss.selective_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"], out=y,
                                    out_last=hl if cfg.get("h_last", False) else None, workspace=ws,
-                                   delta_softplus=args.delta_softplus, exact_zoh=args.exact_zoh)
+                                   delta_softplus=args.delta_softplus, exact_zoh=args.exact_zoh, layout=args.layout)
         else:
             sss.elementwise_scan(t["x"], t["A"], t["B"], t["C"], t["h0"], out=y,
                                  out_last=hl if cfg.get("h_last", False) else None, workspace=ws)
@@ -436,8 +445,8 @@ def main():
             "peak": VALU_FP32_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(alu_tflops / VALU_FP32_TFLOPS, 4),
-            "traffic": (measured_traffic() if args.workload == WORKLOAD_INDEX and not (args.delta_softplus or args.exact_zoh)
-                        else None),
+            "traffic": (measured_traffic() if args.workload == WORKLOAD_INDEX
+                        and not (args.delta_softplus or args.exact_zoh or bdl) else None),
             "kernel": "one selective_scan_fwd call: sel_seq_kernel pass 1 + sel_carry_kernel + sel_seq_kernel pass 2",
             "call_ms_event_mean": round(mean_ms, 5),
             "alu_work": "method's minimal fp32 work per call in VALU-op equivalents (transcendental = 4), "

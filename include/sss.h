@@ -139,14 +139,25 @@ typedef enum {
                               zero-order hold of the Python example in "Selective Scan trong
                               Mamba ..." (delta * B_t[n] where A[d,n] == 0), instead of the
                               first-order delta * B_t[n] * x_t                                 */
-  SSS_DELTA_SOFTPLUS = 2u  /* step size softplus(delta (+ delta_bias[d])): the front end that
+  SSS_DELTA_SOFTPLUS = 2u, /* step size softplus(delta (+ delta_bias[d])): the front end that
                               turns the projected delta into a positive step                  */
+  SSS_LAYOUT_BDL = 4u      /* channel-major operands, time fastest: x, delta, z, y are
+                              (batch, dim, seqlen) and B, C are (batch, dstate, seqlen); A,
+                              D_skip, h0, h_last and delta_bias keep their layouts.  seqlen
+                              must stay below 2^23 (SSS_ERR_BAD_DIM).  Rows of a multiple of 8
+                              (bf16) / 4 (fp32) steps stream as 16-byte pieces per lane      */
 } sss_flags;
+
+/* Bytes of workspace selective_scan_fwd_ex needs for these sizes and flags on `device` (0 on
+ * invalid sizes or flags).  SSS_LAYOUT_BDL adds time-major copies of B and C. */
+size_t selective_scan_fwd_ex_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                                            unsigned flags, int device);
 
 /* selective_scan_fwd with options: `delta_bias` (dim) float32, nullable, is added to delta
  * before use (and before softplus); `flags` is a combination of sss_flags (unknown bits:
  * SSS_ERR_UNSUPPORTED).  With delta_bias == NULL and flags == 0 it is selective_scan_fwd.
- * Same workspace size, layouts, ownership and errors as selective_scan_fwd. */
+ * Workspace: at least selective_scan_fwd_ex_workspace_size() bytes for the same flags.
+ * Layouts as selective_scan_fwd unless SSS_LAYOUT_BDL; ownership and errors the same. */
 int selective_scan_fwd_ex(const void* x, const void* delta, const float* A, const float* B, const float* C,
                           const float* D_skip, const void* z, const float* h0, float* y, float* h_last,
                           const float* delta_bias, unsigned flags, int64_t batch, int64_t seqlen, int64_t dim,

@@ -17,9 +17,10 @@ SSS_F32, SSS_BF16 = 0, 1
 STATUS = {0: "SSS_OK", -1: "SSS_ERR_NULL_ARG", -2: "SSS_ERR_BAD_DIM", -3: "SSS_ERR_UNSUPPORTED",
           -4: "SSS_ERR_WORKSPACE", -5: "SSS_ERR_ALIAS", -6: "SSS_ERR_HIP"}
 
-SSS_EXACT_ZOH, SSS_DELTA_SOFTPLUS = 1, 2
+SSS_EXACT_ZOH, SSS_DELTA_SOFTPLUS, SSS_LAYOUT_BDL = 1, 2, 4
 
-EXPORTED = ("selective_scan_fwd", "selective_scan_fwd_ex", "selective_scan_fwd_workspace_size", "selective_state_update",
+EXPORTED = ("selective_scan_fwd", "selective_scan_fwd_ex", "selective_scan_fwd_workspace_size",
+            "selective_scan_fwd_ex_workspace_size", "selective_state_update",
             "causal_conv1d_fwd", "selective_scan_bwd", "selective_scan_bwd_workspace_size",
             "elementwise_scan", "elementwise_scan_workspace_size", "sss_status_string")
 
@@ -47,6 +48,8 @@ def load() -> ctypes.CDLL:
         lib.selective_scan_fwd_ex.restype = i32
         lib.selective_scan_fwd_workspace_size.argtypes = [i64] * 4 + [i32]
         lib.selective_scan_fwd_workspace_size.restype = sz
+        lib.selective_scan_fwd_ex_workspace_size.argtypes = [i64] * 4 + [ctypes.c_uint, i32]
+        lib.selective_scan_fwd_ex_workspace_size.restype = sz
         lib.selective_state_update.argtypes = [vp] * 9 + [i64] * 3 + [i32, vp]
         lib.selective_state_update.restype = i32
         lib.causal_conv1d_fwd.argtypes = [vp] * 4 + [i64] * 4 + [i32, i32, vp]
@@ -167,6 +170,10 @@ def elementwise_scan_raw(x, A, B, C, h0, y, h_last, batch, seqlen, dim, workspac
                                    stream)
 
 
+def selective_scan_fwd_ex_workspace_size(batch, seqlen, dim, dstate, flags=0, device=0) -> int:
+    return int(load().selective_scan_fwd_ex_workspace_size(batch, seqlen, dim, dstate, flags, device))
+
+
 def selective_scan_fwd_workspace_size(batch, seqlen, dim, dstate, device=0) -> int:
     return int(load().selective_scan_fwd_workspace_size(batch, seqlen, dim, dstate, device))
 
@@ -196,41 +203,51 @@ def _need(t, name, dtype, shape, device):
 
 def selective_scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, return_last=True, out=None,
                        out_last=None, workspace=None, stream=None, delta_bias=None, delta_softplus=False,
-                       exact_zoh=False):
+                       exact_zoh=False, layout="bld"):
     """y (batch, seqlen, dim) float32 [, h_last (batch, dim, dstate) float32].
 
     x, delta, z: float32 or bfloat16 (one dtype); A (dim, dstate), B, C (batch, seqlen,
     dstate), D (dim), h0 (batch, dim, dstate): float32.  All on one GPU, contiguous.
     delta_bias (dim) float32 / delta_softplus / exact_zoh select selective_scan_fwd_ex's
     options (step size softplus(delta + bias); exact zero-order-hold input term).
+    layout="bdl": x, delta, z and y are (batch, dim, seqlen), B and C (batch, dstate, seqlen).
     """
     import torch
+    if layout not in ("bld", "bdl"):
+        raise ValueError(f"layout must be 'bld' or 'bdl', got {layout!r}")
+    bdl = layout == "bdl"
     dev = x.device
-    batch, seqlen, dim = x.shape
+    if bdl:
+        batch, dim, seqlen = x.shape
+    else:
+        batch, seqlen, dim = x.shape
     dstate = A.shape[1]
     io = x.dtype
     if io not in (torch.float32, torch.bfloat16):
         raise ValueError("x must be float32 or bfloat16")
     f32 = torch.float32
-    _need(x, "x", io, (batch, seqlen, dim), dev)
-    _need(delta, "delta", io, (batch, seqlen, dim), dev)
-    _need(z, "z", io, (batch, seqlen, dim), dev)
+    io_shape = (batch, dim, seqlen) if bdl else (batch, seqlen, dim)
+    bc_shape = (batch, dstate, seqlen) if bdl else (batch, seqlen, dstate)
+    _need(x, "x", io, io_shape, dev)
+    _need(delta, "delta", io, io_shape, dev)
+    _need(z, "z", io, io_shape, dev)
     _need(A, "A", f32, (dim, dstate), dev)
-    _need(B, "B", f32, (batch, seqlen, dstate), dev)
-    _need(C, "C", f32, (batch, seqlen, dstate), dev)
+    _need(B, "B", f32, bc_shape, dev)
+    _need(C, "C", f32, bc_shape, dev)
     _need(D, "D", f32, (dim,), dev)
     _need(h0, "h0", f32, (batch, dim, dstate), dev)
-    y = out if out is not None else torch.empty((batch, seqlen, dim), dtype=f32, device=dev)
+    y = out if out is not None else torch.empty(io_shape, dtype=f32, device=dev)
     hl = out_last if out_last is not None else (
         torch.empty((batch, dim, dstate), dtype=f32, device=dev) if return_last else None)
-    _need(y, "out", f32, (batch, seqlen, dim), dev)
+    _need(y, "out", f32, io_shape, dev)
     _need(hl, "out_last", f32, (batch, dim, dstate), dev)
-    wsb = selective_scan_fwd_workspace_size(batch, seqlen, dim, dstate, dev.index or 0)
+    flags = ((SSS_EXACT_ZOH if exact_zoh else 0) | (SSS_DELTA_SOFTPLUS if delta_softplus else 0)
+             | (SSS_LAYOUT_BDL if bdl else 0))
+    wsb = selective_scan_fwd_ex_workspace_size(batch, seqlen, dim, dstate, flags, dev.index or 0)
     if workspace is None and wsb > 0:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
     _need(delta_bias, "delta_bias", f32, (dim,), dev)
     st = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
-    flags = (SSS_EXACT_ZOH if exact_zoh else 0) | (SSS_DELTA_SOFTPLUS if delta_softplus else 0)
     rc = selective_scan_fwd_ex_raw(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
                                    _ptr(y), _ptr(hl), _ptr(delta_bias), flags, batch, seqlen, dim, dstate,
                                    SSS_BF16 if io == torch.bfloat16 else SSS_F32, _ptr(workspace),

@@ -102,10 +102,22 @@ static int sel_dims_ok(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstat
 }
 
 size_t selective_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int device) {
-  if (sel_dims_ok(batch, seqlen, dim, dstate) != SSS_OK) return 0;
+  return selective_scan_fwd_ex_workspace_size(batch, seqlen, dim, dstate, 0u, device);
+}
+
+static constexpr unsigned kKnownFlags = SSS_EXACT_ZOH | SSS_DELTA_SOFTPLUS | SSS_LAYOUT_BDL;
+// channel-major rows: a lane's row offset (up to 64 rows of seqlen fp32 values) stays a
+// 32-bit buffer offset
+static constexpr int64_t kMaxBdlSeqlen = ((int64_t)1 << 23) - 1;
+
+size_t selective_scan_fwd_ex_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                                            unsigned flags, int device) {
+  if (sel_dims_ok(batch, seqlen, dim, dstate) != SSS_OK || (flags & ~kKnownFlags) != 0) return 0;
+  const bool bdl = (flags & SSS_LAYOUT_BDL) != 0;
+  if (bdl && seqlen > kMaxBdlSeqlen) return 0;
   int cus = device_cus(device);
   if (cus <= 0) cus = 256;
-  return plan_selective(batch, seqlen, dim, dstate, cus).ws_total;
+  return plan_selective(batch, seqlen, dim, dstate, cus, bdl).ws_total;
 }
 
 int selective_scan_fwd(const void* x, const void* delta, const float* A, const float* B, const float* C,
@@ -125,7 +137,9 @@ int selective_scan_fwd_ex(const void* x, const void* delta, const float* A, cons
   int st = sel_dims_ok(batch, seqlen, dim, dstate);
   if (st != SSS_OK) return st;
   if (io_dtype != SSS_F32 && io_dtype != SSS_BF16) return SSS_ERR_UNSUPPORTED;
-  if ((flags & ~(unsigned)(SSS_EXACT_ZOH | SSS_DELTA_SOFTPLUS)) != 0) return SSS_ERR_UNSUPPORTED;
+  if ((flags & ~kKnownFlags) != 0) return SSS_ERR_UNSUPPORTED;
+  const bool bdl = (flags & SSS_LAYOUT_BDL) != 0;
+  if (bdl && seqlen > kMaxBdlSeqlen) return SSS_ERR_BAD_DIM;
   const void* ptrs[] = {x, delta, A, B, C, D_skip, z, h0, y, h_last, workspace, delta_bias};
   for (const void* p : ptrs)
     if (!aligned16(p)) return SSS_ERR_UNSUPPORTED;
@@ -142,7 +156,7 @@ int selective_scan_fwd_ex(const void* x, const void* delta, const float* A, cons
   if (overlap(y, y_bytes, h_last, hl_bytes)) return SSS_ERR_ALIAS;
   const int cus = current_device_cus();
   if (cus <= 0) return SSS_ERR_HIP;
-  const SelPlan pl = plan_selective(batch, seqlen, dim, dstate, cus);
+  const SelPlan pl = plan_selective(batch, seqlen, dim, dstate, cus, bdl);
   // threads of the widest launch: 64 per channel group (padded to whole workgroups of 4)
   // and segment; must fit a 1-D grid
   const int64_t wg_groups = ((dim + 63) / 64 + 3) / 4 * 4;
@@ -178,6 +192,7 @@ int selective_scan_fwd_ex(const void* x, const void* delta, const float* A, cons
   a.delta_bias = delta_bias;
   a.softplus = (flags & SSS_DELTA_SOFTPLUS) != 0;
   a.exact_zoh = (flags & SSS_EXACT_ZOH) != 0;
+  a.bdl = bdl;
   hipError_t e = launch_selective(a, pl, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? SSS_OK : SSS_ERR_HIP;
 }

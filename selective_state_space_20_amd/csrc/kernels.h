@@ -10,7 +10,7 @@ namespace sss {
 struct SelPlan {
   int segments;      // time segments S (S > 1: segment states, carry, then outputs)
   int64_t seg_len;   // steps per segment (multiple of the load batch)
-  size_t ws_state, ws_dsum, ws_total;  // workspace offsets / total bytes
+  size_t ws_state, ws_dsum, ws_bc, ws_total;  // workspace offsets / total bytes
 };
 
 struct SelArgs {
@@ -31,9 +31,10 @@ struct SelArgs {
   const float* delta_bias;  // nullable: added to delta before use
   int softplus;             // step size = softplus(delta (+ bias))
   int exact_zoh;            // input term expm1(delta*A)/A * B instead of delta * B
+  int bdl;                  // x/delta/z/y (batch, dim, seqlen), B/C (batch, dstate, seqlen)
 };
 
-SelPlan plan_selective(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int num_cus);
+SelPlan plan_selective(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int num_cus, bool bdl = false);
 hipError_t launch_selective(const SelArgs& a, const SelPlan& plan, hipStream_t stream);
 // pass 1 + carry only: the workspace's state slots hold the state entering each segment
 hipError_t launch_segment_states(const SelArgs& a, const SelPlan& plan, hipStream_t stream);

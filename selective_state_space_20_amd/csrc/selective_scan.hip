@@ -39,12 +39,19 @@ constexpr int kStepsPerBatch = 2;  // time steps whose x/delta/z loads are issue
 constexpr int min_waves_per_simd(int ns) { return ns >= 64 ? 1 : ns >= 32 ? 3 : 4; }
 constexpr int kStreamPolicy = 2;    // buffer cache policy of streamed x/delta/z/y: non-temporal
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// bit casts through by-value arguments: __builtin_bit_cast applied directly to an element of
+// an ext_vector (v.y, v.z, ...) has been compiled as a cast of element 0
+__device__ __forceinline__ float u32_as_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t f32_as_u32(float f) { return __builtin_bit_cast(uint32_t, f); }
+
 // Raw buffer descriptor (gfx9 dword3) over 2^31-1 bytes from `base`.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7FFFFFFF, 0x00020000);
 }
 
-constexpr int kZoh = 1, kFront = 2, kSoftplus = 4;
+constexpr int kZoh = 1, kFront = 2, kSoftplus = 4, kBdl = 8;
 
 // softplus(v) = max(v, 0) + log1p(e^-|v|); log1p through the log(u) * e / (u - 1) form so
 // that small e keeps its relative precision.
@@ -78,6 +85,7 @@ struct SelSeg {
   int gpb;            // channel groups (waves) per workgroup, all on the same segment
   int nblk;           // workgroups per (batch, segment) = ceil(ngroups / gpb)
   int kshift, nsub;   // PASS 3: a checkpoint every 2^kshift steps, nsub per segment
+  int vec;            // channel-major layout: rows are 16-byte aligned (16-byte row pieces)
 };
 
 // ------------------------------------------------------------------ pass 1 / pass 2
@@ -88,7 +96,10 @@ struct SelSeg {
 //         before every 2^kshift-th step into seg_state[s * nsub + j][b][n][d].
 // FL: bit kZoh -- exact zero-order-hold input term, expm1(delta*A)/A * B instead of
 //     delta * B; bits kFront / kSoftplus -- the step size is delta + bias[d], then (with
-//     kSoftplus) softplus of it.
+//     kSoftplus) softplus of it; bit kBdl -- x/delta/z/y channel-major (batch, dim, seqlen)
+//     instead of (batch, seqlen, dim): each lane then walks its own row, loading 16 bytes
+//     (8 bf16 / 4 fp32 steps) and storing 4 fp32 outputs per access where the rows are
+//     16-byte aligned (g.vec), else one step per access.  B/C arrive time-major either way.
 template <int NS, bool BF16, int PASS, bool HAS_Z, int FL>
 __global__ __launch_bounds__(256, min_waves_per_simd(NS)) void sel_seq_kernel(const void* __restrict__ x, const void* __restrict__ delta,
                                                      const float* __restrict__ A, const float* __restrict__ Bm,
@@ -144,37 +155,87 @@ __global__ __launch_bounds__(256, min_waves_per_simd(NS)) void sel_seq_kernel(co
   constexpr bool has_z = PASS == 2 && HAS_Z;
   float dsum = 0.0f;
 
-  // Buffer descriptors based at this wave's first row of the segment: per-step offsets are
-  // wave-uniform (SGPR soffset), the lane offset is a constant VGPR, so no per-load VALU
-  // address arithmetic is needed.  The host keeps seg_len * D * 4 below 2^31.
+  // Buffer descriptors based at this wave's first element of the segment: per-step offsets
+  // are wave-uniform (SGPR soffset), the lane offset is a constant VGPR, so no per-load VALU
+  // address arithmetic is needed.  Time-major rows: lanes are adjacent in memory and a step
+  // moves by a row (the host keeps seg_len * D * 4 below 2^31); channel-major rows: each
+  // lane starts its own row and a step moves by one element (the host keeps 64 * L * 4
+  // below 2^31).
+  constexpr bool bdl = (FL & kBdl) != 0;
   constexpr int ES = BF16 ? 2 : 4;
+  const bool vec = bdl && g.vec != 0;
   const int64_t row0 = b * g.L + tbeg;
-  const int rstride = (int)(g.D * ES);  // bytes between consecutive steps
-  const uint32_t vo = (uint32_t)loff * ES;
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc((const char*)x + (row0 * g.D + d0) * ES);
-  const __amdgpu_buffer_rsrc_t rd = make_rsrc((const char*)delta + (row0 * g.D + d0) * ES);
-  const __amdgpu_buffer_rsrc_t rz = make_rsrc(has_z ? (const char*)z + (row0 * g.D + d0) * ES : (const char*)x);
-  const __amdgpu_buffer_rsrc_t ry = make_rsrc(PASS == 2 ? (const char*)(y + row0 * g.D + d0) : (const char*)x);
-  const int ystride = (int)(g.D * 4);
+  const int64_t ebase = bdl ? (b * g.D + d0) * g.L + tbeg : row0 * g.D + d0;  // element offset
+  const int rstride = bdl ? ES : (int)(g.D * ES);  // bytes between consecutive steps
+  const uint32_t vo = bdl ? (uint32_t)(loff * g.L * ES) : (uint32_t)loff * ES;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc((const char*)x + ebase * ES);
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc((const char*)delta + ebase * ES);
+  const __amdgpu_buffer_rsrc_t rz = make_rsrc(has_z ? (const char*)z + ebase * ES : (const char*)x);
+  const __amdgpu_buffer_rsrc_t ry = make_rsrc(PASS == 2 ? (const char*)(y + ebase) : (const char*)x);
+  const int ystride = bdl ? 4 : (int)(g.D * 4);
+  const uint32_t yvo = bdl ? (uint32_t)(loff * g.L * 4) : (uint32_t)loff * 4;
+  // channel-major output goes through the caches so that the row pieces of consecutive
+  // stores merge into whole lines before they reach HBM
+  constexpr int kYPolicy = bdl ? 0 : kStreamPolicy;
+  constexpr int kInPolicy = bdl ? 0 : kStreamPolicy;
   const float* Br = Bm + row0 * N;
   const float* Cr = Cm + row0 * N;
 
-  constexpr int U = kStepsPerBatch;
+  // steps per load batch: 2 time-major steps, or one 16-byte piece of a channel-major row
+  constexpr int U = bdl ? 16 / ES : kStepsPerBatch;
+  constexpr int QW = bdl ? 4 : U;  // raw dwords per tensor and batch
   // raw loaded values (bf16 bits or fp32 bits) are widened only when used, so that the
   // loads of the next batch stay in flight while the current batch is computed
-  uint32_t xq[2][U], dq[2][U], zq[2][U];
+  uint32_t xq[2][QW], dq[2][QW], zq[2][QW];
+  float yb[bdl ? U : 1];  // channel-major: outputs of the batch, stored together
   auto ld = [vo](__amdgpu_buffer_rsrc_t r, int soff) -> uint32_t {
-    if (BF16) return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)vo, soff, kStreamPolicy);
-    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)vo, soff, kStreamPolicy);
+    if (BF16) return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)vo, soff, kInPolicy);
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)vo, soff, kInPolicy);
+  };
+  // one 16-byte piece of the lane's row
+  auto ld4 = [&](uint32_t (&q)[QW], __amdgpu_buffer_rsrc_t r, int soff) {
+    if constexpr (QW == 4) {
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)vo, soff, kInPolicy);
+      q[0] = v.x;
+      q[1] = v.y;
+      q[2] = v.z;
+      q[3] = v.w;
+    }
   };
   auto wid = [](uint32_t v) -> float { return BF16 ? __builtin_bit_cast(float, v << 16) : __builtin_bit_cast(float, v); };
+  // step I of a batch
+  auto val = [&](const uint32_t (&q)[QW], int i) -> float {
+    if constexpr (!bdl) return wid(q[i]);
+    if constexpr (BF16) return u32_as_f32((i & 1) ? (q[i >> 1] & 0xFFFF0000u) : (q[i >> 1] << 16));
+    return u32_as_f32(q[i]);
+  };
+  // channel-major, unaligned rows: one step per access, packed like a 16-byte piece
+  auto ld_steps = [&](uint32_t (&q)[QW], __amdgpu_buffer_rsrc_t r, int t0) {
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      const uint32_t v = ld(r, min(t0 + i, len - 1) * ES);
+      if (BF16) q[i >> 1] = (i & 1) ? (q[i >> 1] | (v << 16)) : v;
+      else q[i] = v;
+    }
+  };
 #define SSS_LOAD_BATCH(SLOT, T0)                                                 \
   do {                                                                           \
-    _Pragma("unroll") for (int i_ = 0; i_ < U; ++i_) {                           \
-      const int t_ = min((T0) + i_, len - 1); /* clamped, unused */              \
-      xq[SLOT][i_] = ld(rx, t_ * rstride);                                       \
-      dq[SLOT][i_] = ld(rd, t_ * rstride);                                       \
-      if (has_z) zq[SLOT][i_] = ld(rz, t_ * rstride);                            \
+    if constexpr (!bdl) {                                                        \
+      _Pragma("unroll") for (int i_ = 0; i_ < U; ++i_) {                         \
+        const int t_ = min((T0) + i_, len - 1); /* clamped, unused */            \
+        xq[SLOT][i_] = ld(rx, t_ * rstride);                                     \
+        dq[SLOT][i_] = ld(rd, t_ * rstride);                                     \
+        if (has_z) zq[SLOT][i_] = ld(rz, t_ * rstride);                          \
+      }                                                                          \
+    } else if (vec) { /* len is a multiple of U: the clamp stays aligned */      \
+      const int so_ = min((T0), len - U) * ES;                                   \
+      ld4(xq[SLOT], rx, so_);                                                    \
+      ld4(dq[SLOT], rd, so_);                                                    \
+      if (has_z) ld4(zq[SLOT], rz, so_);                                         \
+    } else {                                                                     \
+      ld_steps(xq[SLOT], rx, (T0));                                              \
+      ld_steps(dq[SLOT], rd, (T0));                                              \
+      if (has_z) ld_steps(zq[SLOT], rz, (T0));                                   \
     }                                                                            \
   } while (0)
 
@@ -188,8 +249,8 @@ __global__ __launch_bounds__(256, min_waves_per_simd(NS)) void sel_seq_kernel(co
       _Pragma("unroll") for (int n = 0; n < NS; ++n)                             \
         seg_state[((((int64_t)s * g.nsub + ((T) >> g.kshift)) * g.batch + b) * N + n) * g.D + dc] = h[n]; \
     }                                                                            \
-    const float xv = wid(xq[SLOT][I]);                                           \
-    const float dl = step_size<FL>(wid(dq[SLOT][I]), dbv);                       \
+    const float xv = val(xq[SLOT], I);                                           \
+    const float dl = step_size<FL>(val(dq[SLOT], I), dbv);                       \
     const float dx = dl * xv;                                                    \
     float y0 = Dd * xv, y1 = 0.0f;                                               \
     _Pragma("unroll") for (int n = 0; n < NS; ++n) {                             \
@@ -210,9 +271,31 @@ __global__ __launch_bounds__(256, min_waves_per_simd(NS)) void sel_seq_kernel(co
       dsum += dl;                                                                \
     } else if (PASS == 2) {                                                      \
       float out = y0 + y1;                                                       \
-      if (has_z) out *= silu(wid(zq[SLOT][I]));                                  \
-      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, out), ry, (int)(loff * 4), \
-                                            (T) * ystride, kStreamPolicy);       \
+      if (has_z) out *= silu(val(zq[SLOT], I));                                  \
+      if constexpr (bdl) {                                                       \
+        yb[(I)] = out;                                                           \
+      } else {                                                                   \
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, out), ry, (int)yvo, \
+                                              (T) * ystride, kYPolicy);          \
+      }                                                                          \
+    }                                                                            \
+  } while (0)
+
+  // channel-major: the batch's outputs, steps T0 .. T0+CNT-1
+#define SSS_STORE_BATCH(T0, CNT)                                                 \
+  do {                                                                           \
+    if constexpr (bdl && PASS == 2) {                                            \
+      if (vec) {                                                                 \
+        _Pragma("unroll") for (int j_ = 0; j_ < U; j_ += 4) {                    \
+          const u32x4 o_ = {f32_as_u32(yb[j_]), f32_as_u32(yb[j_ + 1]), f32_as_u32(yb[j_ + 2]), \
+                            f32_as_u32(yb[j_ + 3])};                             \
+          __builtin_amdgcn_raw_buffer_store_b128(o_, ry, (int)yvo, ((T0) + j_) * 4, kYPolicy); \
+        }                                                                        \
+      } else {                                                                   \
+        _Pragma("unroll") for (int j_ = 0; j_ < U; ++j_)                         \
+          if (j_ < (CNT))                                                        \
+            __builtin_amdgcn_raw_buffer_store_b32(f32_as_u32(yb[j_]), ry, (int)yvo, ((T0) + j_) * 4, kYPolicy); \
+      }                                                                          \
     }                                                                            \
   } while (0)
 
@@ -223,18 +306,29 @@ __global__ __launch_bounds__(256, min_waves_per_simd(NS)) void sel_seq_kernel(co
     SSS_LOAD_BATCH(1, t0 + U);
 #pragma unroll
     for (int i = 0; i < U; ++i) SSS_STEP(0, i, t0 + i);
+    SSS_STORE_BATCH(t0, U);
     SSS_LOAD_BATCH(0, t0 + 2 * U);
 #pragma unroll
     for (int i = 0; i < U; ++i) SSS_STEP(1, i, t0 + U + i);
+    SSS_STORE_BATCH(t0 + U, U);
   }
   // ragged tail (< 2U steps): slot 0 already holds steps t0 .. t0+U-1
   if (t0 < len) {
     SSS_LOAD_BATCH(1, t0 + U);
-    for (int i = 0; i < U && t0 + i < len; ++i) SSS_STEP(0, i, t0 + i);
-    for (int i = 0; i < U && t0 + U + i < len; ++i) SSS_STEP(1, i, t0 + U + i);
+#pragma unroll
+    for (int i = 0; i < U; ++i)
+      if (t0 + i < len) SSS_STEP(0, i, t0 + i);
+    SSS_STORE_BATCH(t0, min(U, len - t0));
+    if (t0 + U < len) {
+#pragma unroll
+      for (int i = 0; i < U; ++i)
+        if (t0 + U + i < len) SSS_STEP(1, i, t0 + U + i);
+      SSS_STORE_BATCH(t0 + U, len - t0 - U);
+    }
   }
 #undef SSS_LOAD_BATCH
 #undef SSS_STEP
+#undef SSS_STORE_BATCH
 
   if (PASS == 1) {
     if (lane == 0 || d0 + lane < g.D) seg_dsum[((int64_t)s * g.batch + b) * g.D + dc] = dsum;
@@ -293,7 +387,33 @@ static SelSeg make_seg(const SelArgs& a, const SelPlan& pl, int ns) {
   g.ngroups = (int)((a.dim + 63) / 64);
   g.gpb = std::min(2, g.ngroups);
   g.nblk = (g.ngroups + g.gpb - 1) / g.gpb;
+  const int64_t piece = a.bf16 ? 8 : 4;  // steps per 16-byte piece of a channel-major row
+  g.vec = a.bdl && a.seqlen % piece == 0 && pl.seg_len % piece == 0;
   return g;
+}
+
+// B and C from channel-major (batch, dstate, seqlen) to the time-major rows the scan kernels
+// read with scalar loads: one workgroup per (batch, 64 steps, tensor) through an LDS tile,
+// reading 256-byte row pieces and writing one contiguous 64 * dstate block.
+static __global__ __launch_bounds__(256) void bc_rows_kernel(const float* __restrict__ B, const float* __restrict__ C,
+                                                      float* __restrict__ Bt, float* __restrict__ Ct, int64_t batch,
+                                                      int64_t L, int N) {
+  __shared__ float tile[64][65];
+  const float* src = blockIdx.y == 0 ? B : C;
+  float* dst = blockIdx.y == 0 ? Bt : Ct;
+  const int64_t tiles = (L + 63) / 64;
+  const int64_t b = (int64_t)blockIdx.x / tiles;
+  const int64_t t0 = ((int64_t)blockIdx.x - b * tiles) * 64;
+  const int cnt = (int)std::min<int64_t>(64, L - t0);
+  for (int i = threadIdx.x; i < N * 64; i += 256) {
+    const int n = i >> 6, tt = i & 63;
+    if (tt < cnt) tile[n][tt] = src[(b * N + n) * L + t0 + tt];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < cnt * N; i += 256) {
+    const int tt = i / N, n = i - tt * N;
+    dst[(b * L + t0) * N + i] = tile[n][tt];
+  }
 }
 
 // Pass 1 and the carry: the workspace's state slots end up holding the state entering
@@ -358,20 +478,39 @@ hipError_t run_checkpoints(const SelArgs& a, const SelPlan& pl, float* ckpt, int
   return hipGetLastError();
 }
 
-// Front end / hold variants: plain, exact hold, delta + bias (+ softplus), and both.
-template <int NS, bool BF16>
-hipError_t run_flags(const SelArgs& a, const SelPlan& pl, hipStream_t stream) {
+// Front end / hold variants: plain, exact hold, delta + bias (+ softplus), and both; each in
+// the time-major and the channel-major layout.
+template <int NS, bool BF16, int LAY>
+static hipError_t run_options(const SelArgs& a, const SelPlan& pl, hipStream_t stream) {
   const bool front = a.delta_bias != nullptr || a.softplus;
   const int fl = (a.exact_zoh ? kZoh : 0) | (front ? kFront : 0) | (a.softplus ? kSoftplus : 0);
   switch (fl) {
-    case 0: return run_selective<NS, BF16, 0>(a, pl, stream);
-    case kZoh: return run_selective<NS, BF16, kZoh>(a, pl, stream);
-    case kFront: return run_selective<NS, BF16, kFront>(a, pl, stream);
-    case kFront | kSoftplus: return run_selective<NS, BF16, kFront | kSoftplus>(a, pl, stream);
-    case kZoh | kFront: return run_selective<NS, BF16, kZoh | kFront>(a, pl, stream);
-    case kZoh | kFront | kSoftplus: return run_selective<NS, BF16, kZoh | kFront | kSoftplus>(a, pl, stream);
+    case 0: return run_selective<NS, BF16, LAY>(a, pl, stream);
+    case kZoh: return run_selective<NS, BF16, LAY | kZoh>(a, pl, stream);
+    case kFront: return run_selective<NS, BF16, LAY | kFront>(a, pl, stream);
+    case kFront | kSoftplus: return run_selective<NS, BF16, LAY | kFront | kSoftplus>(a, pl, stream);
+    case kZoh | kFront: return run_selective<NS, BF16, LAY | kZoh | kFront>(a, pl, stream);
+    case kZoh | kFront | kSoftplus: return run_selective<NS, BF16, LAY | kZoh | kFront | kSoftplus>(a, pl, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+template <int NS, bool BF16>
+hipError_t run_flags(const SelArgs& a, const SelPlan& pl, hipStream_t stream) {
+  if (!a.bdl) return run_options<NS, BF16, 0>(a, pl, stream);
+  // channel-major B/C become time-major rows in the workspace first
+  unsigned char* ws = static_cast<unsigned char*>(a.workspace);
+  float* bt = reinterpret_cast<float*>(ws + pl.ws_bc);
+  float* ct = bt + a.batch * a.seqlen * NS;
+  const int64_t tiles = (a.seqlen + 63) / 64;
+  hipLaunchKernelGGL(bc_rows_kernel, dim3((unsigned)(a.batch * tiles), 2), dim3(256), 0, stream, a.B, a.C, bt, ct,
+                     a.batch, a.seqlen, NS);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  SelArgs r = a;
+  r.B = bt;
+  r.C = ct;
+  return run_options<NS, BF16, kBdl>(r, pl, stream);
 }
 
 // Explicit instances: the file is compiled once per state count (SSS_INST_NS = N) and once
@@ -403,8 +542,10 @@ SSS_EXTERN_INSTANCES(64)
 // ------------------------------------------------------------------ host side
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-SelPlan plan_selective(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int num_cus) {
+SelPlan plan_selective(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int num_cus, bool bdl) {
   SelPlan pl{};
+  // segments start on whole load batches: 2 steps, or 8 for the channel-major 16-byte pieces
+  const int64_t unit = bdl ? 8 : kStepsPerBatch;
   const int64_t groups = batch * ((dim + 63) / 64);
   const int64_t simds = (int64_t)std::max(num_cus, 1) * 4;
   // One wave per (channel group, segment).  Splitting time costs a second pass over the
@@ -418,25 +559,28 @@ SelPlan plan_selective(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstat
     S = std::min<int64_t>(S, 4096);
   }
   const int forced = env_int("SSS_FORCE_SEGMENTS", 0);
-  if (forced > 0) S = std::min<int64_t>(forced, (seqlen + kStepsPerBatch - 1) / kStepsPerBatch);
+  if (forced > 0) S = std::min<int64_t>(forced, (seqlen + unit - 1) / unit);
   if (S < 1) S = 1;
   // buffer offsets inside one segment (seg_len rows of dim fp32 values) must stay below
   // 2^30 bytes; dim <= 2^24 is checked by the caller, so max_len >= 16 steps (the B/C row
   // pointers advance by dstate floats per step, also kept below 2^30 bytes)
   const int64_t row_bytes = std::max(dim, dstate) * 4;
-  const int64_t max_len = std::max<int64_t>(kStepsPerBatch, ((int64_t)1 << 30) / row_bytes / kStepsPerBatch * kStepsPerBatch);
+  const int64_t max_len = std::max<int64_t>(unit, ((int64_t)1 << 30) / row_bytes / unit * unit);
   int64_t seg_len = (seqlen + S - 1) / S;
-  seg_len = (seg_len + kStepsPerBatch - 1) / kStepsPerBatch * kStepsPerBatch;
+  seg_len = (seg_len + unit - 1) / unit * unit;
   seg_len = std::min(seg_len, max_len);
   S = (seqlen + seg_len - 1) / seg_len;
   pl.segments = (int)S;
   pl.seg_len = seg_len;
   // workspace: segment states / entering states [S][batch][dstate][dim], segment sums of
-  // delta [S][batch][dim]
+  // delta [S][batch][dim]; channel-major calls add time-major copies of B and C
+  const size_t st_bytes = S > 1 ? align_up((size_t)S * batch * dstate * dim * 4, 256) : 0;
+  const size_t ds_bytes = S > 1 ? align_up((size_t)S * batch * dim * 4, 256) : 0;
+  const size_t bc_bytes = bdl ? align_up((size_t)2 * batch * seqlen * dstate * 4, 256) : 0;
   pl.ws_state = 0;
-  pl.ws_dsum = align_up(S > 1 ? (size_t)S * batch * dstate * dim * 4 : 0, 256);
-  pl.ws_total = align_up(pl.ws_dsum + (S > 1 ? (size_t)S * batch * dim * 4 : 0), 256);
-  if (S == 1) pl.ws_dsum = pl.ws_total = 0;
+  pl.ws_dsum = st_bytes;
+  pl.ws_bc = st_bytes + ds_bytes;
+  pl.ws_total = st_bytes + ds_bytes + bc_bytes;
   return pl;
 }
 

@@ -22,14 +22,29 @@ def to_dev(a, dev):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
+def to_channel_major(inp):
+    """The (B,L,D) / (B,L,N) operands of a seeded input set as (B,D,L) / (B,N,L) arrays."""
+    out = dict(inp)
+    for k in ("x", "delta", "z", "B", "C"):
+        if inp.get(k) is not None:
+            out[k] = np.ascontiguousarray(inp[k].transpose(0, 2, 1))
+    return out
+
+
 def run_selective(inp, dev="cuda:0", return_last=True, fill=float("nan"), **options):
-    """options: delta_bias (numpy), delta_softplus, exact_zoh -- selective_scan_fwd_ex."""
+    """options: delta_bias (numpy), delta_softplus, exact_zoh, layout -- selective_scan_fwd_ex.
+    With layout="bdl" the input arrays are channel-major and so is the returned y."""
     import torch
     import selective_state_space_20_amd as sss
     t = {k: to_dev(v, dev) for k, v in inp.items() if k != "io"}
-    bt, L, dm = inp["x"].shape
+    if options.get("layout", "bld") == "bdl":
+        bt, dm, L = inp["x"].shape
+        yshape = (bt, dm, L)
+    else:
+        bt, L, dm = inp["x"].shape
+        yshape = (bt, L, dm)
     n = inp["A"].shape[1]
-    y = torch.full((bt, L, dm), fill, dtype=torch.float32, device=dev)
+    y = torch.full(yshape, fill, dtype=torch.float32, device=dev)
     hl = torch.full((bt, dm, n), fill, dtype=torch.float32, device=dev) if return_last else None
     if options.get("delta_bias") is not None:
         options = dict(options, delta_bias=to_dev(options["delta_bias"], dev))

@@ -72,8 +72,9 @@ def selx(**kw):
 
 def test_selective_ex_rejections():
     assert selx(x=0) == NULL_ARG
-    assert selx(flags=4) == UNSUPPORTED                 # unknown option bit
+    assert selx(flags=8) == UNSUPPORTED                 # unknown option bit
     assert selx(flags=1 << 31) == UNSUPPORTED
+    assert selx(flags=4, seqlen=1 << 23) == BAD_DIM     # channel-major rows past 32-bit offsets
     assert selx(delta_bias=6 * P + 4) == UNSUPPORTED    # misaligned bias
     assert selx(y=6 * P, delta_bias=6 * P) == ALIAS     # y over the bias
     assert selx(dim=0, flags=3) == BAD_DIM
@@ -169,6 +170,12 @@ def test_alias_detected_before_any_device_work():
 
 def test_workspace_query_is_sane():
     assert sss.selective_scan_fwd_workspace_size(0, 8, 4, 4) == 0
+    # the channel-major layout adds time-major copies of B and C; unknown flags give 0
+    plain = sss.selective_scan_fwd_ex_workspace_size(2, 4096, 4096, 16, 0)
+    assert plain == sss.selective_scan_fwd_workspace_size(2, 4096, 4096, 16)
+    assert sss.selective_scan_fwd_ex_workspace_size(2, 4096, 4096, 16, 4) >= plain + 2 * 2 * 4096 * 16 * 4
+    assert sss.selective_scan_fwd_ex_workspace_size(2, 4096, 4096, 16, 8) == 0
+    assert sss.selective_scan_fwd_ex_workspace_size(2, 1 << 23, 64, 16, 4) == 0
     a = sss.selective_scan_fwd_workspace_size(1, 1000, 64, 16)
     b = sss.selective_scan_fwd_workspace_size(1, 100000, 64, 16)
     assert 0 < a <= b and a % 256 == 0 and b % 256 == 0
@@ -182,6 +189,7 @@ def test_no_device_reports_hip_error():
         pytest.skip("a GPU is present; this checks the no-device path")
     assert sel() == HIP
     assert selx(flags=3, delta_bias=6 * P) == HIP
+    assert selx(flags=4, workspace=80 * P, workspace_bytes=1 << 20) == HIP
     assert ew() == HIP
     assert upd() == HIP
     assert bwd() == HIP
