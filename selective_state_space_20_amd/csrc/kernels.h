@@ -39,7 +39,7 @@ hipError_t launch_selective(const SelArgs& a, const SelPlan& plan, hipStream_t s
 // pass 1 + carry only: the workspace's state slots hold the state entering each segment
 hipError_t launch_segment_states(const SelArgs& a, const SelPlan& plan, hipStream_t stream);
 // after launch_segment_states: the state before every 2^kshift-th step of every segment,
-// into ckpt[s * nsub + j][batch][dstate][dim]
+// into ckpt[s][batch][channel group][j][dstate][64 lanes] (ceil(dim / 64) groups)
 hipError_t launch_checkpoints(const SelArgs& a, const SelPlan& plan, float* ckpt, int kshift, int nsub,
                               hipStream_t stream);
 

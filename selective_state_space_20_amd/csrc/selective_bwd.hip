@@ -162,26 +162,47 @@ __global__ __launch_bounds__(256) void sel_bwd_carry(const float* __restrict__ A
 }
 
 // ------------------------------------------------------------------ cross-lane reduce-scatter
-// V values per lane -> after the xor levels 32, 16, ..., 1 each lane holds V >> min(6, log2 V)
-// values, each summed over all 64 lanes; value index = (lane >> (6 - levels)) * keep + i.
-// Level LV halves the CNT live values (lanes with the level's bit set keep the upper half,
-// the others the lower half) until one is left, then keeps adding the partner's value.
+// V values per lane -> after the levels 32, 16, 8, 4, 2, 1 (lane bit of the level) each lane
+// holds V >> min(6, log2 V) values, each summed over all 64 lanes; value index =
+// (lane >> (6 - levels)) * keep + i.  Level LV halves the CNT live values: lanes with the
+// level's bit set keep the upper half, the others the lower half, and each adds its partner's
+// copy of the half it keeps; once one value is left the levels just add the partner's value.
+// Partners: v_permlane32_swap / v_permlane16_swap exchange the halves of two registers across
+// 32 / 16 lanes in one instruction (lane bits 5 and 4); within a row of 16 lanes DPP
+// row_mirror, row_half_mirror and the quad permutations pair lanes that differ in bit 3, 2,
+// 1 and 0 and agree on every higher bit -- the same pairs of value sets as an xor exchange.
+__device__ __forceinline__ uint32_t bwd_u32(float f) { return __builtin_bit_cast(uint32_t, f); }
+__device__ __forceinline__ float bwd_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+// a: the value lanes without the level's bit keep, b: the value lanes with it keep
+template <int LV>
+__device__ __forceinline__ float pair_sum(float a, float b, bool hi) {
+  if constexpr (LV == 0 || LV == 1) {
+    // the upper lanes of the first register trade places with the lower lanes of the second:
+    // afterwards every lane holds its own kept value and its partner's copy of it
+    const auto r = LV == 0 ? __builtin_amdgcn_permlane32_swap(bwd_u32(a), bwd_u32(b), false, false)
+                           : __builtin_amdgcn_permlane16_swap(bwd_u32(a), bwd_u32(b), false, false);
+    const uint32_t r0 = r[0], r1 = r[1];  // elements copied out before the casts
+    return bwd_f32(r0) + bwd_f32(r1);
+  } else {
+    constexpr int ctrl = LV == 2 ? 0x140 : LV == 3 ? 0x141 : LV == 4 ? 0x4E : 0xB1;
+    const float keep = hi ? b : a;
+    const float send = hi ? a : b;
+    return keep + bwd_f32((uint32_t)__builtin_amdgcn_mov_dpp((int)bwd_u32(send), ctrl, 0xF, 0xF, false));
+  }
+}
+
 template <int LV, int CNT, int V>
 __device__ __forceinline__ void reduce_scatter_level(float (&p)[V], int lane) {
   if constexpr (LV < 6) {
-    constexpr int dist = 32 >> LV;
-    const bool hi = (lane & dist) != 0;
+    const bool hi = (lane & (32 >> LV)) != 0;
     if constexpr (CNT > 1) {
       constexpr int half = CNT / 2;
 #pragma unroll
-      for (int i = 0; i < half; ++i) {
-        const float send = hi ? p[i] : p[half + i];
-        const float keep = hi ? p[half + i] : p[i];
-        p[i] = keep + __shfl_xor(send, dist);
-      }
+      for (int i = 0; i < half; ++i) p[i] = pair_sum<LV>(p[i], p[half + i], hi);
       reduce_scatter_level<LV + 1, half, V>(p, lane);
     } else {
-      p[0] += __shfl_xor(p[0], dist);
+      p[0] = pair_sum<LV>(p[0], p[0], hi);
       reduce_scatter_level<LV + 1, 1, V>(p, lane);
     }
   }
@@ -210,15 +231,20 @@ __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
     float* __restrict__ part_d, float* __restrict__ dh0, BwdSeg g) {
   constexpr int K = bwd_k(NS);
   constexpr int ES = BF16 ? 2 : 4;
-  constexpr int LV = ilog2c(NS) < 6 ? ilog2c(NS) : 6;  // reduce-scatter levels for NS values
-  constexpr int KEEP = NS >> LV;
+  // dB and dC partials of one step go through one reduce-scatter of 2 NS values; from 32
+  // states on through two of NS (fewer live registers)
+  constexpr bool kMerged = NS <= 16;
+  constexpr int NV = kMerged ? 2 * NS : NS;            // values per reduce-scatter
+  constexpr int LV = ilog2c(NV) < 6 ? ilog2c(NV) : 6;  // its levels
+  constexpr int KEEP = NV >> LV;
   const BwdLane q = bwd_lane(g, 0);
   const int64_t chl = (q.b * g.D + q.dc) * NS;  // (b, d) row of dh_last / dh0
 
-  float a2[NS], mu[NS], dacc[NS];
+  float a2[NS], a1[NS], mu[NS], dacc[NS];  // A' = A log2 e (for exp2), A itself (clamped)
 #pragma unroll
   for (int n = 0; n < NS; ++n) {
     a2[n] = fmaxf(A[q.dc * NS + n] * kLog2e, -kFltMax);
+    a1[n] = a2[n] * kLn2;
     mu[n] = g.S > 1 ? mu_right[(((int64_t)q.s * g.batch + q.b) * NS + n) * g.D + q.dc]
                     : (dh_last ? dh_last[chl + n] : 0.0f);
     dacc[n] = 0.0f;
@@ -234,10 +260,9 @@ __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
   const __amdgpu_buffer_rsrc_t rdx = bwd_rsrc(dx + row0);
   const __amdgpu_buffer_rsrc_t rdd = bwd_rsrc(ddelta + row0);
   const __amdgpu_buffer_rsrc_t rdz = bwd_rsrc(HAS_Z ? dz + row0 : dx + row0);
-  // checkpoint j of this (segment, batch row): [s * nsub + j][b][n][d]; one descriptor per
-  // checkpoint (offsets n * D * 4 < 2^31: the caller keeps dim * dstate * 4 below 2^31)
+  // checkpoint j of this wave: [s][b][grp][j][n][lane], one contiguous 256-byte row per state
   auto ck_rsrc = [&](int j) {
-    return bwd_rsrc(ckpt + ((((int64_t)q.s * g.nsub + j) * g.batch + q.b) * NS) * g.D + q.d0);
+    return bwd_rsrc(ckpt + ((((int64_t)q.s * g.batch + q.b) * g.ngroups + q.grp) * g.nsub + j) * NS * 64);
   };
   const int rs = (int)(g.D * ES), rs4 = (int)(g.D * 4);
   const int vo = q.loff * ES, vo4 = q.loff * 4;
@@ -261,15 +286,17 @@ __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
   do {                                                                                     \
     const int tb = (J) * K;                                                                \
     const int k = min(K, q.len - tb);                                                      \
-    float hs[K + 1][NS];                                                                   \
+    float hs[K + 1][NS], ea[K][NS]; /* states and decays of the sub-chunk */               \
     const __amdgpu_buffer_rsrc_t rc_ = ck_rsrc(J);                                         \
-    _Pragma("unroll") for (int n = 0; n < NS; ++n) hs[0][n] = ld_f32(rc_, vo4, n * rs4);   \
+    _Pragma("unroll") for (int n = 0; n < NS; ++n) hs[0][n] = ld_f32(rc_, q.lane * 4, n * 256); \
     _Pragma("unroll") for (int i = 0; i < K; ++i) {                                        \
       if (i < k) {                                                                         \
         const float* Bt = Br + (tb + i) * NS;                                              \
         const float dxv = ds[SLOT][i] * xs[SLOT][i];                                       \
-        _Pragma("unroll") for (int n = 0; n < NS; ++n)                                     \
-          hs[i + 1][n] = __builtin_fmaf(fast_exp2(ds[SLOT][i] * a2[n]), hs[i][n], dxv * Bt[n]); \
+        _Pragma("unroll") for (int n = 0; n < NS; ++n) {                                   \
+          ea[i][n] = fast_exp2(ds[SLOT][i] * a2[n]);                                       \
+          hs[i + 1][n] = __builtin_fmaf(ea[i][n], hs[i][n], dxv * Bt[n]);                  \
+        }                                                                                  \
       }                                                                                    \
     }                                                                                      \
     _Pragma("unroll") for (int i = K - 1; i >= 0; --i) {                                   \
@@ -284,38 +311,45 @@ __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
           sg = sigmoid_f(zv);                                                              \
           dv = gy * zv * sg;                                                               \
         }                                                                                  \
-        /* dC_t: this wave's 64 channels summed, one state per lane group */               \
+        /* pv: this step's dB (first NS) and dC (last NS) partials of the lane's channel;  \
+           lanes mirroring channel D-1 contribute zero */                                   \
+        const float dvm = q.real ? dv : 0.0f;                                              \
+        const float dxm = q.real ? dl * xv : 0.0f;                                         \
         float vsum = Dd * xv;                                                              \
-        float pc[NS];                                                                      \
+        float* rowp = part_bc + (((int64_t)q.grp * g.batch + q.b) * g.L + q.tbeg + t) * (2 * NS); \
+        const bool writer = (q.lane & ((1 << (6 - LV)) - 1)) == 0;                         \
+        const int widx = (q.lane >> (6 - LV)) * KEEP;                                      \
+        float pv[kMerged ? 2 * NS : NS], pc[kMerged ? 1 : NS];                             \
         _Pragma("unroll") for (int n = 0; n < NS; ++n) {                                   \
           vsum = __builtin_fmaf(Ct[n], hs[i + 1][n], vsum);                                \
-          pc[n] = q.real ? dv * hs[i + 1][n] : 0.0f;                                       \
+          if constexpr (kMerged) pv[NS + n] = dvm * hs[i + 1][n];                          \
+          else pc[n] = dvm * hs[i + 1][n];                                                 \
         }                                                                                  \
-        reduce_scatter<NS>(pc, q.lane);                                                    \
-        float* rowp = part_bc + (((int64_t)q.grp * g.batch + q.b) * g.L + q.tbeg + t) * (2 * NS); \
-        if ((q.lane & ((1 << (6 - LV)) - 1)) == 0) {                                       \
-          _Pragma("unroll") for (int e = 0; e < KEEP; ++e) rowp[NS + (q.lane >> (6 - LV)) * KEEP + e] = pc[e]; \
+        if constexpr (!kMerged) {                                                          \
+          reduce_scatter<NV>(pc, q.lane);                                                  \
+          if (writer) {                                                                    \
+            _Pragma("unroll") for (int e = 0; e < KEEP; ++e) rowp[NS + widx + e] = pc[e];  \
+          }                                                                                \
         }                                                                                  \
         float gx = Dd * dv, gd = 0.0f;                                                     \
-        float pb[NS];                                                                      \
         _Pragma("unroll") for (int n = 0; n < NS; ++n) {                                   \
-          const float a = fast_exp2(dl * a2[n]);                                           \
+          const float a = ea[i][n];                                                        \
           const float lam = __builtin_fmaf(Ct[n], dv, mu[n]);                              \
           const float lb = lam * Bt[n];                                                    \
           const float ah = a * hs[i][n];                                                   \
           gx = __builtin_fmaf(lb, dl, gx);                                                 \
-          gd = __builtin_fmaf(lb, xv, __builtin_fmaf(lam * (a2[n] * kLn2), ah, gd));       \
+          gd = __builtin_fmaf(lb, xv, __builtin_fmaf(lam * a1[n], ah, gd));                \
           dacc[n] = __builtin_fmaf(lam * dl, ah, dacc[n]);                                 \
-          pb[n] = q.real ? lam * dl * xv : 0.0f;                                           \
+          pv[n] = lam * dxm;                                                               \
           mu[n] = a * lam;                                                                 \
         }                                                                                  \
         ddacc = __builtin_fmaf(dv, xv, ddacc);                                             \
         st_f32(gx, rdx, vo4, t * rs4);                                                     \
         st_f32(gd, rdd, vo4, t * rs4);                                                     \
         if (HAS_Z) st_f32(gy * vsum * sg * __builtin_fmaf(zv, 1.0f - sg, 1.0f), rdz, vo4, t * rs4); \
-        reduce_scatter<NS>(pb, q.lane);                                                    \
-        if ((q.lane & ((1 << (6 - LV)) - 1)) == 0) {                                       \
-          _Pragma("unroll") for (int e = 0; e < KEEP; ++e) rowp[(q.lane >> (6 - LV)) * KEEP + e] = pb[e]; \
+        reduce_scatter<kMerged ? 2 * NS : NS>(pv, q.lane);                                 \
+        if (writer) {                                                                      \
+          _Pragma("unroll") for (int e = 0; e < KEEP; ++e) rowp[widx + e] = pv[e];         \
         }                                                                                  \
       }                                                                                    \
     }                                                                                      \
@@ -385,7 +419,7 @@ BwdPlan plan_selective_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t d
   bp.off_mu = off;
   off = align256(off + (S > 1 ? (size_t)S * batch * dstate * dim * 4 : 0));
   bp.off_ckpt = off;
-  off = align256(off + (size_t)S * bp.nsub * batch * dstate * dim * 4);
+  off = align256(off + (size_t)S * bp.nsub * batch * dstate * ((dim + 63) / 64) * 64 * 4);
   bp.off_bc = off;
   off = align256(off + (size_t)ngroups * batch * seqlen * 2 * dstate * 4);
   bp.off_pa = off;

@@ -93,7 +93,8 @@ struct SelSeg {
 // PASS 2 (segments 0..S-1): y, and h_last from the last segment; entering state from
 //         carry[s][b][n][d] (S > 1) or h0 (S == 1).
 // PASS 3 (segments 0..S-1, for the backward pass): from the same entering state, the state
-//         before every 2^kshift-th step into seg_state[s * nsub + j][b][n][d].
+//         before every 2^kshift-th step into seg_state[s][b][grp][j][n][lane] (each wave's
+//         checkpoints are one contiguous stream of 256-byte rows).
 // FL: bit kZoh -- exact zero-order-hold input term, expm1(delta*A)/A * B instead of
 //     delta * B; bits kFront / kSoftplus -- the step size is delta + bias[d], then (with
 //     kSoftplus) softplus of it; bit kBdl -- x/delta/z/y channel-major (batch, dim, seqlen)
@@ -246,8 +247,11 @@ __global__ __launch_bounds__(256, min_waves_per_simd(NS)) void sel_seq_kernel(co
     const float* Bt = Br + (T) * N;                                              \
     const float* Ct = Cr + (T) * N;                                              \
     if (PASS == 3 && ((T) & kmask) == 0) {                                       \
+      /* checkpoint j = T >> kshift: [s][b][grp][j][n][lane] */                 \
+      const __amdgpu_buffer_rsrc_t rk_ = make_rsrc(                              \
+          seg_state + ((((int64_t)s * g.batch + b) * g.ngroups + grp) * g.nsub + ((T) >> g.kshift)) * N * 64); \
       _Pragma("unroll") for (int n = 0; n < NS; ++n)                             \
-        seg_state[((((int64_t)s * g.nsub + ((T) >> g.kshift)) * g.batch + b) * N + n) * g.D + dc] = h[n]; \
+        __builtin_amdgcn_raw_buffer_store_b32(f32_as_u32(h[n]), rk_, lane * 4, n * 256, kStreamPolicy); \
     }                                                                            \
     const float xv = val(xq[SLOT], I);                                           \
     const float dl = step_size<FL>(val(dq[SLOT], I), dbv);                       \
@@ -462,7 +466,7 @@ hipError_t run_segment_states(const SelArgs& a, const SelPlan& pl, hipStream_t s
 }
 
 // Checkpoints for the backward pass (after run_segment_states): the state before every
-// 2^kshift-th step of every segment, into ckpt[s * nsub + j][b][n][d].
+// 2^kshift-th step of every segment, into ckpt[s][b][grp][j][n][lane].
 template <int NS, bool BF16>
 hipError_t run_checkpoints(const SelArgs& a, const SelPlan& pl, float* ckpt, int kshift, int nsub,
                            hipStream_t stream) {
