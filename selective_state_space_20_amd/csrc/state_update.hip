@@ -7,10 +7,11 @@
 //   y[b,d]   = (sum_n C[b,n]*h[b,d,n] + D[d]*x[b,d]) * silu(z[b,d])
 //
 // The step is bound by moving the state (8 bytes per state element: read and write back),
-// so the mapping follows the state's layout: lanes walk (b, d, n) in memory order, four
-// states per lane, so that every state load and store of a wave is one contiguous 1 KiB
-// piece of 16-byte vectors.  The lanes of a channel are adjacent and reduce C*h with
-// cross-lane xor shuffles; the first of them writes y.
+// so the mapping follows the state's layout: lanes walk (d, n) of a batch row in memory
+// order, four states per lane, so that every state load and store of a wave is one
+// contiguous 1 KiB piece of 16-byte vectors, and each thread carries four batch rows whose
+// loads are all in flight together.  The lanes of a channel are adjacent and reduce C*h
+// with cross-lane xor shuffles; the first of them writes y.
 #include "common.h"
 #include "kernels.h"
 
@@ -25,87 +26,107 @@ __device__ __forceinline__ float load_io(const void* p, int64_t i) {
 typedef float f4v __attribute__((ext_vector_type(4)));
 
 // Each lane owns PL = min(4, NS) adjacent states of one channel (a 16-byte piece of the
-// state, of A and of B/C); the LPC = NS / PL lanes of a channel are adjacent and reduce
-// C*h with xor shuffles.  Blocks never straddle a batch row: blockIdx.x = b * bpb + k.
-template <int NS, bool BF16, bool HAS_Z>
+// state, of A and of B/C) for R batch rows; the LPC = NS / PL lanes of a channel are
+// adjacent and reduce C*h with xor shuffles.  All R rows' loads are issued before any of
+// them is used, so that a wave keeps R KiB of state in flight (one KiB per row and wave).
+// blockIdx.x = row group * bpb + k; rows past the batch load the last row and store nothing.
+template <int NS, bool BF16, bool HAS_Z, int R>
 __global__ __launch_bounds__(256) void sel_update_kernel(const void* __restrict__ x, const void* __restrict__ delta,
                                                          const float* __restrict__ A, const float* __restrict__ Bm,
                                                          const float* __restrict__ Cm, const float* __restrict__ Dsk,
                                                          const void* __restrict__ z, float* __restrict__ state,
                                                          float* __restrict__ y, int64_t batch, int dim,
-                                                         unsigned bpb /* blocks per batch row */) {
+                                                         unsigned bpb /* blocks per row group */) {
   constexpr int PL = NS >= 4 ? 4 : NS;
   constexpr int LPC = NS / PL;
-  const unsigned b = blockIdx.x / bpb;
-  const int li = (int)(blockIdx.x - b * bpb) * 256 + (int)threadIdx.x;  // lane index within the row
+  const unsigned rg = blockIdx.x / bpb;
+  const int li = (int)(blockIdx.x - rg * bpb) * 256 + (int)threadIdx.x;  // lane index within a row
   // Lanes past the row's end form whole channel groups (LPC divides 64); they work on the
   // row's last channel so that every lane takes part in the shuffles, and store nothing.
   const bool live = li < dim * LPC;
   const int d = (live ? li : dim * LPC - 1) / LPC;  // LPC is a power of two
   const int j = (live ? li : dim * LPC - 1) - d * LPC;
-  const int64_t c = (int64_t)b * dim + d;
 
-  const float xv = load_io<BF16>(x, c);
-  const float dv = load_io<BF16>(delta, c);
-  const float dx = dv * xv;
-  float hv[PL], av[PL], bv[PL], cv[PL];
+  float av[PL];
   if constexpr (PL == 4) {
-    const f4v s4 = *reinterpret_cast<const f4v*>(state + c * NS + j * 4);
     const f4v a4 = *reinterpret_cast<const f4v*>(A + (int64_t)d * NS + j * 4);
-    const f4v b4 = *reinterpret_cast<const f4v*>(Bm + (int64_t)b * NS + j * 4);
-    const f4v c4 = *reinterpret_cast<const f4v*>(Cm + (int64_t)b * NS + j * 4);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      hv[i] = s4[i];
-      av[i] = a4[i];
-      bv[i] = b4[i];
-      cv[i] = c4[i];
-    }
+    for (int i = 0; i < 4; ++i) av[i] = fmaxf(a4[i] * kLog2e, -kFltMax);  // -inf clamped: 0*a2 = 0
   } else {
 #pragma unroll
-    for (int i = 0; i < PL; ++i) {
-      hv[i] = state[c * NS + i];
-      av[i] = A[(int64_t)d * NS + i];
-      bv[i] = Bm[(int64_t)b * NS + i];
-      cv[i] = Cm[(int64_t)b * NS + i];
-    }
+    for (int i = 0; i < PL; ++i) av[i] = fmaxf(A[(int64_t)d * NS + i] * kLog2e, -kFltMax);
   }
-  float part = 0.0f;
+  const float dd = Dsk != nullptr ? Dsk[d] : 0.0f;
+
+  float hv[R][PL], bv[R][PL], cv[R][PL], xv[R], dv[R], zv[R];
 #pragma unroll
-  for (int i = 0; i < PL; ++i) {
-    const float a2 = fmaxf(av[i] * kLog2e, -kFltMax);  // -inf clamped so that 0*a2 = 0
-    hv[i] = __builtin_fmaf(fast_exp2(dv * a2), hv[i], dx * bv[i]);
-    part = __builtin_fmaf(cv[i], hv[i], part);
-  }
-  if (live) {
+  for (int r = 0; r < R; ++r) {
+    const int64_t b = min((int64_t)rg * R + r, batch - 1);
+    const int64_t c = b * dim + d;
+    xv[r] = load_io<BF16>(x, c);
+    dv[r] = load_io<BF16>(delta, c);
+    zv[r] = HAS_Z ? load_io<BF16>(z, c) : 0.0f;
     if constexpr (PL == 4) {
-      const f4v o = {hv[0], hv[1], hv[2], hv[3]};
-      *reinterpret_cast<f4v*>(state + c * NS + j * 4) = o;
+      const f4v s4 = *reinterpret_cast<const f4v*>(state + c * NS + j * 4);
+      const f4v b4 = *reinterpret_cast<const f4v*>(Bm + b * NS + j * 4);
+      const f4v c4 = *reinterpret_cast<const f4v*>(Cm + b * NS + j * 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        hv[r][i] = s4[i];
+        bv[r][i] = b4[i];
+        cv[r][i] = c4[i];
+      }
     } else {
 #pragma unroll
-      for (int i = 0; i < PL; ++i) state[c * NS + i] = hv[i];
+      for (int i = 0; i < PL; ++i) {
+        hv[r][i] = state[c * NS + i];
+        bv[r][i] = Bm[b * NS + i];
+        cv[r][i] = Cm[b * NS + i];
+      }
     }
   }
 #pragma unroll
-  for (int off = LPC / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, LPC);
-  if (live && j == 0) {
-    float out = part;
-    if (Dsk != nullptr) out = __builtin_fmaf(Dsk[d], xv, out);
-    if (HAS_Z) out *= silu(load_io<BF16>(z, c));
-    y[c] = out;
+  for (int r = 0; r < R; ++r) {
+    const int64_t b = (int64_t)rg * R + r;
+    const bool row = b < batch;
+    const int64_t c = b * dim + d;
+    const float dx = dv[r] * xv[r];
+    float part = 0.0f;
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      hv[r][i] = __builtin_fmaf(fast_exp2(dv[r] * av[i]), hv[r][i], dx * bv[r][i]);
+      part = __builtin_fmaf(cv[r][i], hv[r][i], part);
+    }
+    if (live && row) {
+      if constexpr (PL == 4) {
+        const f4v o = {hv[r][0], hv[r][1], hv[r][2], hv[r][3]};
+        *reinterpret_cast<f4v*>(state + c * NS + j * 4) = o;
+      } else {
+#pragma unroll
+        for (int i = 0; i < PL; ++i) state[c * NS + i] = hv[r][i];
+      }
+    }
+#pragma unroll
+    for (int off = LPC / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, LPC);
+    if (live && row && j == 0) {
+      float out = __builtin_fmaf(dd, xv[r], part);
+      if (HAS_Z) out *= silu(zv[r]);
+      y[c] = out;
+    }
   }
 }
 
 template <int NS, bool BF16>
 static hipError_t run_update(const UpdArgs& a, hipStream_t stream) {
   constexpr int LPC = NS >= 4 ? NS / 4 : 1;
+  constexpr int R = 4;  // batch rows per thread
   const unsigned bpb = (unsigned)((a.dim * LPC + 255) / 256);
-  const dim3 grid((unsigned)(bpb * a.batch)), block(256);
+  const dim3 grid((unsigned)(bpb * ((a.batch + R - 1) / R))), block(256);
   if (a.z != nullptr)
-    hipLaunchKernelGGL((sel_update_kernel<NS, BF16, true>), grid, block, 0, stream, a.x, a.delta, a.A, a.B, a.C,
+    hipLaunchKernelGGL((sel_update_kernel<NS, BF16, true, R>), grid, block, 0, stream, a.x, a.delta, a.A, a.B, a.C,
                        a.Dsk, a.z, a.state, a.y, a.batch, (int)a.dim, bpb);
   else
-    hipLaunchKernelGGL((sel_update_kernel<NS, BF16, false>), grid, block, 0, stream, a.x, a.delta, a.A, a.B, a.C,
+    hipLaunchKernelGGL((sel_update_kernel<NS, BF16, false, R>), grid, block, 0, stream, a.x, a.delta, a.A, a.B, a.C,
                        a.Dsk, a.z, a.state, a.y, a.batch, (int)a.dim, bpb);
   return hipGetLastError();
 }
