@@ -33,19 +33,28 @@ FLUSH_BYTES = 1 << 30           # written between timed calls to evict the 256 M
 VALU_FP32_TFLOPS = 157.3        # MI355X fp32 vector, published (FMA = 2 flops)
 WORKLOAD_INDEX = 3              # the largest selective_scan_fwd configuration
 
-# HBM traffic of one selective_scan_fwd call on the workload above, from two rocprofv3 --pmc
-# runs of this script (FETCH_SIZE, then WRITE_SIZE; KiB summed over the call's three
-# dispatches), each scaled by what the same counter reads for a plain 1 GiB device copy
-# (`bench.py --copy-calibration`).  Valid only for the kernel sources they were taken on:
-# reported as null once those files change.
+# HBM traffic per call, from two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
+# WRITE_SIZE; KiB per dispatch summed over a call's dispatches), each scaled by what the same
+# counter reads for a plain 1 GiB device copy (`bench.py --copy-calibration`: FETCH_SIZE
+# reads 524301.4 KiB, WRITE_SIZE 1048576 KiB).  Valid only for the kernel sources they were
+# taken on: reported as null once those files change.
+COPY_FETCH_SCALE = 1048576.0 / 524301.4
+COPY_WRITE_SCALE = 1048576.0 / 1048576.0
+CSRC = "selective_state_space_20_amd/csrc/"
 PMC_TRAFFIC = {
-    "sources": "67f71078c95cc102",      # kernel_source_digest() of the profiled sources
-    "fetch_kib": 659040.0 + 46571.8 + 1034300.0,   # pass 1 + carry + pass 2, mean of 3 calls
-    "fetch_scale": 1048576.0 / 524301.0,           # 1 GiB copy reads as 524301 KiB
-    "write_kib": 86700.0 + 81920.0 + 1311040.0,
-    "write_scale": 1048576.0 / 1048576.0,          # 1 GiB copy writes as 1048576 KiB
+    # default workload: sel_seq_kernel pass 1 + sel_carry_kernel + pass 2
+    "selective": {"sources": (CSRC + "selective_scan.hip", CSRC + "common.h"), "digest": "bef473faa493b746",
+                  "fetch_kib": 659038.1 + 46577.1 + 1034743.8, "write_kib": 86700.0 + 81920.0 + 1311040.0},
+    # 8 x 32768 x 4096 fp32
+    "elementwise": {"sources": (CSRC + "elementwise_scan.hip", CSRC + "common.h"), "digest": "4b0239623ce7466b",
+                    "fetch_kib": 8388744.2, "write_kib": 4194432.0},
+    # 256 tokens x 5120 x 16
+    "decode": {"sources": (CSRC + "state_update.hip", CSRC + "common.h"), "digest": "a48994a23866d68b",
+               "fetch_kib": 45119.9, "write_kib": 87040.4},
+    # 1 x 65536 x 5120 bf16, width 4
+    "conv": {"sources": (CSRC + "conv1d.hip", CSRC + "common.h"), "digest": "0525304aa8e7045b",
+             "fetch_kib": 328260.8, "write_kib": 655360.3},
 }
-PMC_SOURCES = ("selective_state_space_20_amd/csrc/selective_scan.hip", "selective_state_space_20_amd/csrc/common.h")
 
 
 def log(msg):
@@ -100,21 +109,21 @@ def backward_alu_ops(b, L, d, n):
     return b * L * d * (n * 16 + 4 * 2 + 14)
 
 
-def kernel_source_digest():
+def kernel_source_digest(kind="selective"):
     import hashlib
     h = hashlib.sha256()
-    for rel in PMC_SOURCES:
+    for rel in PMC_TRAFFIC[kind]["sources"]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
+def measured_traffic(kind="selective"):
     """Calibrated HBM bytes per call, or None when not measured on the current sources."""
-    if PMC_TRAFFIC is None or PMC_TRAFFIC["sources"] != kernel_source_digest():
+    t = PMC_TRAFFIC.get(kind)
+    if t is None or t["digest"] != kernel_source_digest(kind):
         return None
-    t = PMC_TRAFFIC
-    return int(t["fetch_kib"] * 1024 * t["fetch_scale"] + t["write_kib"] * 1024 * t["write_scale"])
+    return int(t["fetch_kib"] * 1024 * COPY_FETCH_SCALE + t["write_kib"] * 1024 * COPY_WRITE_SCALE)
 
 
 def cpu_baseline(cfg, inp, budget_s=12.0):
@@ -221,7 +230,9 @@ def bench_decode(batch, steps, warmup, dim=5120, dstate=16, flush=True):
                    "algorithmic_bytes": nbytes, "caches_flushed_between_calls": flush},
         "tokens_per_s": round(batch / (mean_ms * 1e-3), 1),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "sel_update_kernel",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("decode") if (batch, dim, dstate) == (256, 5120, 16) else None,
+                     "kernel": "sel_update_kernel",
                      "call_ms_event_mean": round(mean_ms, 5)},
     }), flush=True)
 
@@ -258,7 +269,7 @@ def bench_conv(steps, warmup, batch=1, seqlen=65536, dim=5120, width=4):
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"conv1d_bf16_b{batch}_L{seqlen}_D{dim}_W{width}_silu", "algorithmic_bytes": nbytes},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "conv1d_kernel",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("conv"), "kernel": "conv1d_kernel",
                      "call_ms_event_mean": round(mean_ms, 5)},
     }), flush=True)
 
@@ -452,11 +463,12 @@ def main():
             "alu_work": "method's minimal fp32 work per call in VALU-op equivalents (transcendental = 4), "
                         "x2 flops per op",
             "alu_ops_per_call": alu,
-            "source_digest": kernel_source_digest(),
+            "source_digest": kernel_source_digest("selective"),
             "hbm": hbm,
         }
     else:
-        roofline = dict(hbm, bound="hbm", traffic=None, call_ms_event_mean=round(mean_ms, 5),
+        roofline = dict(hbm, bound="hbm", traffic=measured_traffic("elementwise") if args.workload == 4 else None,
+                        call_ms_event_mean=round(mean_ms, 5),
                         kernel="one elementwise_scan call: ew_scan_kernel pass 1 (if split) + pass 2")
     out = {
         "metric": "selective-scan achieved HBM GB/s (% of peak) and B·L·D elements/s, 1 GPU",
