@@ -37,7 +37,17 @@ constexpr int kStepsPerBatch = 2;  // time steps whose x/delta/z loads are issue
 // register budget: at least this many resident waves per SIMD (512 VGPRs / waves each);
 // 32 and 64 states need the larger budgets to stay spill-free
 constexpr int min_waves_per_simd(int ns) { return ns >= 64 ? 1 : ns >= 32 ? 3 : 4; }
+// Options that hold more per lane get larger register budgets: the exact hold keeps 1/A and
+// (A == 0) per state (2 waves per SIMD from 32 states on); channel-major tiles keep the next
+// tile in flight and a tile of outputs in registers (3 waves per SIMD at 16 states with no
+// other option, else 2).  (fl: bit 0 exact hold, bit 1 delta front end, bit 3 channel-major.)
+constexpr int min_waves_of(int ns, int fl) {
+  const int base = min_waves_per_simd(ns);
+  const int cap = (fl & 8) ? (((fl & 3) != 0 || ns != 16) ? 2 : 3) : ((fl & 1) && ns >= 32) ? 2 : 4;
+  return base < cap ? base : cap;
+}
 constexpr int kStreamPolicy = 2;    // buffer cache policy of streamed x/delta/z/y: non-temporal
+constexpr int kTileBytes = 64;      // channel-major tiles: bytes of each row per tile
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -85,7 +95,8 @@ struct SelSeg {
   int gpb;            // channel groups (waves) per workgroup, all on the same segment
   int nblk;           // workgroups per (batch, segment) = ceil(ngroups / gpb)
   int kshift, nsub;   // PASS 3: a checkpoint every 2^kshift steps, nsub per segment
-  int vec;            // channel-major layout: rows are 16-byte aligned (16-byte row pieces)
+  int vec;            // channel-major layout: 0 one step per access, 1 16-byte row pieces per
+                      // lane, 2 whole tiles staged through LDS (see kTileBytes)
 };
 
 // ------------------------------------------------------------------ pass 1 / pass 2
@@ -102,7 +113,7 @@ struct SelSeg {
 //     (8 bf16 / 4 fp32 steps) and storing 4 fp32 outputs per access where the rows are
 //     16-byte aligned (g.vec), else one step per access.  B/C arrive time-major either way.
 template <int NS, bool BF16, int PASS, bool HAS_Z, int FL>
-__global__ __launch_bounds__(256, min_waves_per_simd(NS)) void sel_seq_kernel(const void* __restrict__ x, const void* __restrict__ delta,
+__global__ __launch_bounds__(256, min_waves_of(NS, FL)) void sel_seq_kernel(const void* __restrict__ x, const void* __restrict__ delta,
                                                      const float* __restrict__ A, const float* __restrict__ Bm,
                                                      const float* __restrict__ Cm, const float* __restrict__ Dsk,
                                                      const void* __restrict__ z, const float* __restrict__ h0,
@@ -164,7 +175,10 @@ __global__ __launch_bounds__(256, min_waves_per_simd(NS)) void sel_seq_kernel(co
   // below 2^31).
   constexpr bool bdl = (FL & kBdl) != 0;
   constexpr int ES = BF16 ? 2 : 4;
-  const bool vec = bdl && g.vec != 0;
+  const bool vec = bdl && g.vec == 1;
+  // tiles only up to 16 states (the tile in flight needs 48 more registers); the host agrees
+  constexpr bool kTiles = bdl && NS <= 16;
+  const bool tiled = kTiles && g.vec == 2;
   const int64_t row0 = b * g.L + tbeg;
   const int64_t ebase = bdl ? (b * g.D + d0) * g.L + tbeg : row0 * g.D + d0;  // element offset
   const int rstride = bdl ? ES : (int)(g.D * ES);  // bytes between consecutive steps
@@ -185,10 +199,14 @@ __global__ __launch_bounds__(256, min_waves_per_simd(NS)) void sel_seq_kernel(co
   // steps per load batch: 2 time-major steps, or one 16-byte piece of a channel-major row
   constexpr int U = bdl ? 16 / ES : kStepsPerBatch;
   constexpr int QW = bdl ? 4 : U;  // raw dwords per tensor and batch
+  constexpr int TT = kTileBytes / ES;  // channel-major tile: steps per tile
   // raw loaded values (bf16 bits or fp32 bits) are widened only when used, so that the
   // loads of the next batch stay in flight while the current batch is computed
   uint32_t xq[2][QW], dq[2][QW], zq[2][QW];
-  float yb[bdl ? U : 1];  // channel-major: outputs of the batch, stored together
+  // channel-major: outputs stored together -- a batch, or a whole tile (a full row piece
+  // of y per lane, written by consecutive stores) when tiles are used
+  constexpr int YT = kTileBytes / ES;  // tiled: y steps per store group (a whole tile)
+  float yb[bdl ? (NS <= 16 ? YT : U) : 1];
   auto ld = [vo](__amdgpu_buffer_rsrc_t r, int soff) -> uint32_t {
     if (BF16) return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)vo, soff, kInPolicy);
     return __builtin_amdgcn_raw_buffer_load_b32(r, (int)vo, soff, kInPolicy);
@@ -219,6 +237,67 @@ __global__ __launch_bounds__(256, min_waves_per_simd(NS)) void sel_seq_kernel(co
       else q[i] = v;
     }
   };
+  // Channel-major rows whose length is a multiple of the tile: the wave's 64 rows are
+  // staged kTileBytes at a time.  Each load instruction takes 16 rows x kTileBytes (four
+  // lanes per row, so rows are read in whole 64-byte pieces), the pieces go to this wave's
+  // LDS tile, and each lane then reads its own row 16 bytes per batch.  The next tile's
+  // loads are in flight (gq) while the current tile is computed.  LDS rows are 64 bytes
+  // with the 16-byte chunks xor-swizzled by row, so that the lanes' 16-byte reads of one
+  // batch fall in distinct banks.
+  constexpr int kNT = has_z ? 3 : 2;  // tensors staged: x, delta (, z)
+  constexpr int kPieces = 4;          // 16-byte pieces per lane, tensor and tile
+  extern __shared__ uint32_t sss_lds[];  // [wave][tensor][64 rows][16 dwords]
+  uint32_t* const ltile = sss_lds + wave * (kNT * 64 * 16);
+  uint32_t gq[kNT][kPieces][4];
+  uint32_t gvo[kPieces];  // lane's byte offset of piece i: row 16 i + lane / 4, chunk lane % 4
+  int gchunk[kPieces];    // LDS dword offset of that piece within a tensor tile
+#pragma unroll
+  for (int i = 0; i < kPieces; ++i) {
+    const int r = 16 * i + (lane >> 2), c = lane & 3;
+    const int rr = (int)(min(d0 + r, g.D - 1) - d0);  // rows past D-1 repeat the last row
+    gvo[i] = (uint32_t)(rr * g.L * ES + c * 16);
+    gchunk[i] = r * 16 + ((c ^ ((r >> 1) & 3)) * 4);
+  }
+  const int lrow = loff * 16;
+  const int lswz = (loff >> 1) & 3;
+  auto tile_load = [&](int t0) {  // tile starting at segment step t0 (clamped into the segment)
+    const int so = min(t0, len - TT) * ES;
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+      const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)gvo[i], so, kStreamPolicy);
+      const u32x4 bq = __builtin_amdgcn_raw_buffer_load_b128(rd, (int)gvo[i], so, kStreamPolicy);
+      gq[0][i][0] = a.x; gq[0][i][1] = a.y; gq[0][i][2] = a.z; gq[0][i][3] = a.w;
+      gq[1][i][0] = bq.x; gq[1][i][1] = bq.y; gq[1][i][2] = bq.z; gq[1][i][3] = bq.w;
+      if constexpr (kNT == 3) {
+        const u32x4 c = __builtin_amdgcn_raw_buffer_load_b128(rz, (int)gvo[i], so, kStreamPolicy);
+        gq[2][i][0] = c.x; gq[2][i][1] = c.y; gq[2][i][2] = c.z; gq[2][i][3] = c.w;
+      }
+    }
+  };
+  auto tile_store = [&]() {  // the tile in flight -> this wave's LDS tile
+#pragma unroll
+    for (int t = 0; t < kNT; ++t) {
+#pragma unroll
+      for (int i = 0; i < kPieces; ++i) {
+        const u32x4 v = {gq[t][i][0], gq[t][i][1], gq[t][i][2], gq[t][i][3]};
+        *reinterpret_cast<u32x4*>(ltile + t * (64 * 16) + gchunk[i]) = v;
+      }
+    }
+  };
+  auto tile_read = [&](uint32_t (&q)[QW], int t, int kb) {  // batch kb of the lane's row
+    if constexpr (QW == 4) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ltile + t * (64 * 16) + lrow + ((kb ^ lswz) * 4));
+      q[0] = v.x;
+      q[1] = v.y;
+      q[2] = v.z;
+      q[3] = v.w;
+    }
+  };
+  if (tiled) {
+    tile_load(0);
+    tile_store();
+    tile_load(TT);
+  }
 #define SSS_LOAD_BATCH(SLOT, T0)                                                 \
   do {                                                                           \
     if constexpr (!bdl) {                                                        \
@@ -242,7 +321,7 @@ __global__ __launch_bounds__(256, min_waves_per_simd(NS)) void sel_seq_kernel(co
 
   // one step at segment-relative time T from register slot (SLOT, I); B_t / C_t rows are
   // wave-uniform and come through scalar loads
-#define SSS_STEP(SLOT, I, T)                                                     \
+#define SSS_STEP_Y(SLOT, I, T, YI)                                               \
   do {                                                                           \
     const float* Bt = Br + (T) * N;                                              \
     const float* Ct = Cr + (T) * N;                                              \
@@ -277,7 +356,7 @@ __global__ __launch_bounds__(256, min_waves_per_simd(NS)) void sel_seq_kernel(co
       float out = y0 + y1;                                                       \
       if (has_z) out *= silu(val(zq[SLOT], I));                                  \
       if constexpr (bdl) {                                                       \
-        yb[(I)] = out;                                                           \
+        yb[(YI)] = out;                                                          \
       } else {                                                                   \
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, out), ry, (int)yvo, \
                                               (T) * ystride, kYPolicy);          \
@@ -285,11 +364,13 @@ __global__ __launch_bounds__(256, min_waves_per_simd(NS)) void sel_seq_kernel(co
     }                                                                            \
   } while (0)
 
+#define SSS_STEP(SLOT, I, T) SSS_STEP_Y(SLOT, I, T, I)
+
   // channel-major: the batch's outputs, steps T0 .. T0+CNT-1
 #define SSS_STORE_BATCH(T0, CNT)                                                 \
   do {                                                                           \
     if constexpr (bdl && PASS == 2) {                                            \
-      if (vec) {                                                                 \
+      if (vec || tiled) {                                                        \
         _Pragma("unroll") for (int j_ = 0; j_ < U; j_ += 4) {                    \
           const u32x4 o_ = {f32_as_u32(yb[j_]), f32_as_u32(yb[j_ + 1]), f32_as_u32(yb[j_ + 2]), \
                             f32_as_u32(yb[j_ + 3])};                             \
@@ -303,8 +384,55 @@ __global__ __launch_bounds__(256, min_waves_per_simd(NS)) void sel_seq_kernel(co
     }                                                                            \
   } while (0)
 
-  SSS_LOAD_BATCH(0, 0);
   int t0 = 0;
+  if constexpr (kTiles) {
+    // Channel-major tiles (len is a multiple of the tile): one tile per iteration, its
+    // batches read from LDS one ahead; before the last batch the next tile (in flight since
+    // the previous iteration) is stored to LDS and the one after it loaded.  y is kept for
+    // the whole tile and written as one row piece per lane (a full 128-byte line in bf16).
+    constexpr int kB = TT / U;  // batches per tile: 4
+    static_assert(kB == 4 && YT == TT, "tile layout");
+    if (tiled) {
+      tile_read(xq[0], 0, 0);
+      tile_read(dq[0], 1, 0);
+      if constexpr (has_z) tile_read(zq[0], 2, 0);
+    }
+#define SSS_TILE_READ(SLOT, KB)                                                  \
+  do {                                                                           \
+    tile_read(xq[SLOT], 0, KB);                                                  \
+    tile_read(dq[SLOT], 1, KB);                                                  \
+    if constexpr (has_z) tile_read(zq[SLOT], 2, KB);                             \
+  } while (0)
+#define SSS_Y_GROUP(TY)                                                          \
+  do {                                                                           \
+    if constexpr (PASS == 2) {                                                   \
+      _Pragma("unroll") for (int j = 0; j < YT; j += 4) {                        \
+        const u32x4 o = {f32_as_u32(yb[j]), f32_as_u32(yb[j + 1]), f32_as_u32(yb[j + 2]), f32_as_u32(yb[j + 3])}; \
+        __builtin_amdgcn_raw_buffer_store_b128(o, ry, (int)yvo, ((TY) + j) * 4, kYPolicy); \
+      }                                                                          \
+    }                                                                            \
+  } while (0)
+    for (; tiled && t0 < len; t0 += TT) {
+      SSS_TILE_READ(1, 1);
+#pragma unroll
+      for (int i = 0; i < U; ++i) SSS_STEP_Y(0, i, t0 + i, i);
+      SSS_TILE_READ(0, 2);
+#pragma unroll
+      for (int i = 0; i < U; ++i) SSS_STEP_Y(1, i, t0 + U + i, U + i);
+      SSS_TILE_READ(1, 3);
+#pragma unroll
+      for (int i = 0; i < U; ++i) SSS_STEP_Y(0, i, t0 + 2 * U + i, 2 * U + i);
+      tile_store();            // the next tile, loaded during the previous iteration
+      tile_load(t0 + 2 * TT);  // the one after it (clamped into the segment)
+      SSS_TILE_READ(0, 0);
+#pragma unroll
+      for (int i = 0; i < U; ++i) SSS_STEP_Y(1, i, t0 + 3 * U + i, 3 * U + i);
+      SSS_Y_GROUP(t0);         // the tile's outputs: one row piece per lane
+    }
+#undef SSS_TILE_READ
+#undef SSS_Y_GROUP
+  }
+  if (!tiled) SSS_LOAD_BATCH(0, 0);
   // full blocks of 2U steps: straight-line code, no per-step branches
   for (; t0 + 2 * U <= len; t0 += 2 * U) {
     SSS_LOAD_BATCH(1, t0 + U);
@@ -332,6 +460,7 @@ __global__ __launch_bounds__(256, min_waves_per_simd(NS)) void sel_seq_kernel(co
   }
 #undef SSS_LOAD_BATCH
 #undef SSS_STEP
+#undef SSS_STEP_Y
 #undef SSS_STORE_BATCH
 
   if (PASS == 1) {
@@ -392,7 +521,10 @@ static SelSeg make_seg(const SelArgs& a, const SelPlan& pl, int ns) {
   g.gpb = std::min(2, g.ngroups);
   g.nblk = (g.ngroups + g.gpb - 1) / g.gpb;
   const int64_t piece = a.bf16 ? 8 : 4;  // steps per 16-byte piece of a channel-major row
-  g.vec = a.bdl && a.seqlen % piece == 0 && pl.seg_len % piece == 0;
+  const int64_t tile = kTileBytes / (a.bf16 ? 2 : 4);
+  g.vec = !a.bdl ? 0
+          : (ns <= 16 && a.seqlen % tile == 0 && pl.seg_len % tile == 0) ? 2
+          : (a.seqlen % piece == 0 && pl.seg_len % piece == 0) ? 1 : 0;
   return g;
 }
 
@@ -430,8 +562,9 @@ static hipError_t run_states(const SelArgs& a, const SelPlan& pl, hipStream_t st
   float* st = reinterpret_cast<float*>(ws + pl.ws_state);
   float* ds = reinterpret_cast<float*>(ws + pl.ws_dsum);
   const int64_t per_seg = (int64_t)g.nblk * g.batch;
+  const size_t lds1 = g.vec == 2 ? (size_t)g.gpb * 2 * 64 * kTileBytes : 0;  // x, delta tiles
   hipLaunchKernelGGL((sel_seq_kernel<NS, BF16, 1, false, FL>), dim3((unsigned)(per_seg * (pl.segments - 1))),
-                     dim3(64u * (unsigned)g.gpb), 0, stream, a.x, a.delta, a.A, a.B, a.C, a.Dsk, a.z, a.h0,
+                     dim3(64u * (unsigned)g.gpb), lds1, stream, a.x, a.delta, a.A, a.B, a.C, a.Dsk, a.z, a.h0,
                      (const float*)nullptr, a.y, a.h_last, st, ds, a.delta_bias, g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -450,11 +583,12 @@ static hipError_t run_selective(const SelArgs& a, const SelPlan& pl, hipStream_t
   const float* st = pl.segments > 1 ? reinterpret_cast<const float*>(ws + pl.ws_state) : nullptr;
   const int64_t per_seg = (int64_t)g.nblk * g.batch;
   const dim3 grid((unsigned)(per_seg * pl.segments)), block(64u * (unsigned)g.gpb);
+  const size_t lds2 = g.vec == 2 ? (size_t)g.gpb * (a.z != nullptr ? 3 : 2) * 64 * kTileBytes : 0;
   if (a.z != nullptr)
-    hipLaunchKernelGGL((sel_seq_kernel<NS, BF16, 2, true, FL>), grid, block, 0, stream, a.x, a.delta, a.A, a.B, a.C,
+    hipLaunchKernelGGL((sel_seq_kernel<NS, BF16, 2, true, FL>), grid, block, lds2, stream, a.x, a.delta, a.A, a.B, a.C,
                        a.Dsk, a.z, a.h0, st, a.y, a.h_last, (float*)nullptr, (float*)nullptr, a.delta_bias, g);
   else
-    hipLaunchKernelGGL((sel_seq_kernel<NS, BF16, 2, false, FL>), grid, block, 0, stream, a.x, a.delta, a.A, a.B,
+    hipLaunchKernelGGL((sel_seq_kernel<NS, BF16, 2, false, FL>), grid, block, lds2, stream, a.x, a.delta, a.A, a.B,
                        a.C, a.Dsk, a.z, a.h0, st, a.y, a.h_last, (float*)nullptr, (float*)nullptr, a.delta_bias, g);
   return hipGetLastError();
 }
@@ -548,8 +682,8 @@ static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 SelPlan plan_selective(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int num_cus, bool bdl) {
   SelPlan pl{};
-  // segments start on whole load batches: 2 steps, or 8 for the channel-major 16-byte pieces
-  const int64_t unit = bdl ? 8 : kStepsPerBatch;
+  // segments start on whole load batches: 2 steps, or whole channel-major tiles (32 steps)
+  const int64_t unit = bdl ? 32 : kStepsPerBatch;
   const int64_t groups = batch * ((dim + 63) / 64);
   const int64_t simds = (int64_t)std::max(num_cus, 1) * 4;
   // One wave per (channel group, segment).  Splitting time costs a second pass over the
