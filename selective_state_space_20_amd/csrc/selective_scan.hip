@@ -387,11 +387,19 @@ __global__ __launch_bounds__(256, min_waves_of(NS, FL)) void sel_seq_kernel(cons
   int t0 = 0;
   if constexpr (kTiles) {
     // Channel-major tiles (len is a multiple of the tile): one tile per iteration, its
-    // batches read from LDS one ahead; before the last batch the next tile (in flight since
-    // the previous iteration) is stored to LDS and the one after it loaded.  y is kept for
-    // the whole tile and written as one row piece per lane (a full 128-byte line in bf16).
+    // batches read from LDS one ahead; the next tile (in flight since the previous
+    // iteration) is stored to LDS once the current one is consumed, and the one after it
+    // loaded.  y is kept for the whole tile (a 128-byte line of each row in bf16, half a
+    // line in fp32) and leaves through the consumed LDS tile: each lane writes its row,
+    // then every store instruction takes whole row pieces (YC lanes per row, 64 / YC rows),
+    // so that each line is written by one instruction instead of a 16-byte piece at a time
+    // by YC of them.  LDS y rows hold YC 16-byte chunks, xor-swizzled by row so that both
+    // the row-wise writes and the piece-wise reads fall in distinct banks.
     constexpr int kB = TT / U;  // batches per tile: 4
     static_assert(kB == 4 && YT == TT, "tile layout");
+    constexpr int YC = YT / 4;                 // 16-byte chunks of y per row and tile: 8 or 4
+    constexpr int YRS = 16 / YC;               // rows per 256 bytes of LDS: 2 or 4
+    static_assert(YC <= 4 * kNT, "the y tile fits in the input tile");
     if (tiled) {
       tile_read(xq[0], 0, 0);
       tile_read(dq[0], 1, 0);
@@ -403,15 +411,30 @@ __global__ __launch_bounds__(256, min_waves_of(NS, FL)) void sel_seq_kernel(cons
     tile_read(dq[SLOT], 1, KB);                                                  \
     if constexpr (has_z) tile_read(zq[SLOT], 2, KB);                             \
   } while (0)
-#define SSS_Y_GROUP(TY)                                                          \
-  do {                                                                           \
-    if constexpr (PASS == 2) {                                                   \
-      _Pragma("unroll") for (int j = 0; j < YT; j += 4) {                        \
-        const u32x4 o = {f32_as_u32(yb[j]), f32_as_u32(yb[j + 1]), f32_as_u32(yb[j + 2]), f32_as_u32(yb[j + 3])}; \
-        __builtin_amdgcn_raw_buffer_store_b128(o, ry, (int)yvo, ((TY) + j) * 4, kYPolicy); \
-      }                                                                          \
-    }                                                                            \
-  } while (0)
+    // the tile's outputs (steps TY .. TY+YT-1) through the consumed LDS tile
+    auto y_tile = [&](int ty) {
+      if constexpr (PASS == 2) {
+        uint32_t* const ly = ltile;
+        const int wrow = lane * (YC * 4);
+        const int wswz = (lane / YRS) & (YC - 1);
+#pragma unroll
+        for (int c = 0; c < YC; ++c) {
+          const u32x4 o = {f32_as_u32(yb[4 * c]), f32_as_u32(yb[4 * c + 1]), f32_as_u32(yb[4 * c + 2]),
+                           f32_as_u32(yb[4 * c + 3])};
+          *reinterpret_cast<u32x4*>(ly + wrow + ((c ^ wswz) * 4)) = o;
+        }
+        const int pc = lane % YC;  // the lane's chunk of each row piece it stores
+#pragma unroll
+        for (int k = 0; k < YC; ++k) {
+          const int r = k * (64 / YC) + lane / YC;  // row of this store
+          const u32x4 o = *reinterpret_cast<const u32x4*>(ly + r * (YC * 4) + ((pc ^ ((r / YRS) & (YC - 1))) * 4));
+          // rows past the last channel hold channel D-1's values: store them there again
+          const int rr = (int)min((int64_t)r, g.D - 1 - d0);
+          __builtin_amdgcn_raw_buffer_store_b128(o, ry, (int)((uint32_t)rr * (uint32_t)g.L * 4u + pc * 16), ty * 4,
+                                                 kYPolicy);
+        }
+      }
+    };
     for (; tiled && t0 < len; t0 += TT) {
       SSS_TILE_READ(1, 1);
 #pragma unroll
@@ -422,15 +445,22 @@ __global__ __launch_bounds__(256, min_waves_of(NS, FL)) void sel_seq_kernel(cons
       SSS_TILE_READ(1, 3);
 #pragma unroll
       for (int i = 0; i < U; ++i) SSS_STEP_Y(0, i, t0 + 2 * U + i, 2 * U + i);
-      tile_store();            // the next tile, loaded during the previous iteration
-      tile_load(t0 + 2 * TT);  // the one after it (clamped into the segment)
-      SSS_TILE_READ(0, 0);
+      if constexpr (PASS == 2) {
 #pragma unroll
-      for (int i = 0; i < U; ++i) SSS_STEP_Y(1, i, t0 + 3 * U + i, 3 * U + i);
-      SSS_Y_GROUP(t0);         // the tile's outputs: one row piece per lane
+        for (int i = 0; i < U; ++i) SSS_STEP_Y(1, i, t0 + 3 * U + i, 3 * U + i);
+        y_tile(t0);              // the LDS tile is consumed: stage y through it
+        tile_store();            // the next tile, loaded during the previous iteration
+        tile_load(t0 + 2 * TT);  // the one after it (clamped into the segment)
+        SSS_TILE_READ(0, 0);
+      } else {
+        tile_store();
+        tile_load(t0 + 2 * TT);
+        SSS_TILE_READ(0, 0);
+#pragma unroll
+        for (int i = 0; i < U; ++i) SSS_STEP_Y(1, i, t0 + 3 * U + i, 3 * U + i);
+      }
     }
 #undef SSS_TILE_READ
-#undef SSS_Y_GROUP
   }
   if (!tiled) SSS_LOAD_BATCH(0, 0);
   // full blocks of 2U steps: straight-line code, no per-step branches
