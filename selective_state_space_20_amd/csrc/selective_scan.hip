@@ -321,10 +321,10 @@ __global__ __launch_bounds__(256, min_waves_of(NS, FL)) void sel_seq_kernel(cons
 
   // one step at segment-relative time T from register slot (SLOT, I); B_t / C_t rows are
   // wave-uniform and come through scalar loads
-#define SSS_STEP_Y(SLOT, I, T, YI)                                               \
+#define SSS_STEP_BC(SLOT, I, T, YI, BT, CT)                                      \
   do {                                                                           \
-    const float* Bt = Br + (T) * N;                                              \
-    const float* Ct = Cr + (T) * N;                                              \
+    const float* Bt = (BT);                                                      \
+    const float* Ct = (CT);                                                      \
     if (PASS == 3 && ((T) & kmask) == 0) {                                       \
       /* checkpoint j = T >> kshift: [s][b][grp][j][n][lane] */                 \
       const __amdgpu_buffer_rsrc_t rk_ = make_rsrc(                              \
@@ -364,6 +364,7 @@ __global__ __launch_bounds__(256, min_waves_of(NS, FL)) void sel_seq_kernel(cons
     }                                                                            \
   } while (0)
 
+#define SSS_STEP_Y(SLOT, I, T, YI) SSS_STEP_BC(SLOT, I, T, YI, Br + (T) * N, Cr + (T) * N)
 #define SSS_STEP(SLOT, I, T) SSS_STEP_Y(SLOT, I, T, I)
 
   // channel-major: the batch's outputs, steps T0 .. T0+CNT-1
@@ -435,19 +436,50 @@ __global__ __launch_bounds__(256, min_waves_of(NS, FL)) void sel_seq_kernel(cons
         }
       }
     };
+    // Pass 2 takes its B_t / C_t rows one step ahead: each step first waits for its own rows
+    // (and for the LDS reads issued a step earlier), then issues the next step's row loads and
+    // the batch's LDS read, so that the scalar loads have a whole step to arrive instead of
+    // the few instructions the compiler leaves between a load and its first use.  (With
+    // three resident waves per SIMD, the fewest of any forward kernel, those waits were
+    // not hidden.)
+    float bq[2][NS], cq[2][NS];
+    auto bc_load = [&](int slot, int t) {
+      const float* bp = Br + t * N;
+      const float* cp = Cr + t * N;
+#pragma unroll
+      for (int n = 0; n < NS; ++n) {
+        bq[slot][n] = bp[n];
+        if constexpr (PASS == 2) cq[slot][n] = cp[n];
+      }
+    };
+#define SSS_TSTEP(SLOT, I, T, YI, ACTION)                                        \
+  do {                                                                           \
+    if constexpr (PASS == 2) {                                                   \
+      __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0) */                       \
+      __builtin_amdgcn_sched_barrier(0);                                         \
+      bc_load(((YI) & 1) ^ 1, min((T) + 1, len - 1));                            \
+      ACTION;                                                                    \
+      __builtin_amdgcn_sched_barrier(0);                                         \
+      SSS_STEP_BC(SLOT, I, T, YI, bq[(YI) & 1], cq[(YI) & 1]);                   \
+    } else {                                                                     \
+      ACTION;                                                                    \
+      SSS_STEP_Y(SLOT, I, T, YI);                                                \
+    }                                                                            \
+  } while (0)
+    if (PASS == 2 && tiled) bc_load(0, 0);
     for (; tiled && t0 < len; t0 += TT) {
-      SSS_TILE_READ(1, 1);
+      SSS_TSTEP(0, 0, t0, 0, SSS_TILE_READ(1, 1));
 #pragma unroll
-      for (int i = 0; i < U; ++i) SSS_STEP_Y(0, i, t0 + i, i);
-      SSS_TILE_READ(0, 2);
+      for (int i = 1; i < U; ++i) SSS_TSTEP(0, i, t0 + i, i, );
+      SSS_TSTEP(1, 0, t0 + U, U, SSS_TILE_READ(0, 2));
 #pragma unroll
-      for (int i = 0; i < U; ++i) SSS_STEP_Y(1, i, t0 + U + i, U + i);
-      SSS_TILE_READ(1, 3);
+      for (int i = 1; i < U; ++i) SSS_TSTEP(1, i, t0 + U + i, U + i, );
+      SSS_TSTEP(0, 0, t0 + 2 * U, 2 * U, SSS_TILE_READ(1, 3));
 #pragma unroll
-      for (int i = 0; i < U; ++i) SSS_STEP_Y(0, i, t0 + 2 * U + i, 2 * U + i);
+      for (int i = 1; i < U; ++i) SSS_TSTEP(0, i, t0 + 2 * U + i, 2 * U + i, );
       if constexpr (PASS == 2) {
 #pragma unroll
-        for (int i = 0; i < U; ++i) SSS_STEP_Y(1, i, t0 + 3 * U + i, 3 * U + i);
+        for (int i = 0; i < U; ++i) SSS_TSTEP(1, i, t0 + 3 * U + i, 3 * U + i, );
         y_tile(t0);              // the LDS tile is consumed: stage y through it
         tile_store();            // the next tile, loaded during the previous iteration
         tile_load(t0 + 2 * TT);  // the one after it (clamped into the segment)
@@ -457,9 +489,10 @@ __global__ __launch_bounds__(256, min_waves_of(NS, FL)) void sel_seq_kernel(cons
         tile_load(t0 + 2 * TT);
         SSS_TILE_READ(0, 0);
 #pragma unroll
-        for (int i = 0; i < U; ++i) SSS_STEP_Y(1, i, t0 + 3 * U + i, 3 * U + i);
+        for (int i = 0; i < U; ++i) SSS_TSTEP(1, i, t0 + 3 * U + i, 3 * U + i, );
       }
     }
+#undef SSS_TSTEP
 #undef SSS_TILE_READ
   }
   if (!tiled) SSS_LOAD_BATCH(0, 0);
@@ -491,6 +524,7 @@ __global__ __launch_bounds__(256, min_waves_of(NS, FL)) void sel_seq_kernel(cons
 #undef SSS_LOAD_BATCH
 #undef SSS_STEP
 #undef SSS_STEP_Y
+#undef SSS_STEP_BC
 #undef SSS_STORE_BATCH
 
   if (PASS == 1) {
