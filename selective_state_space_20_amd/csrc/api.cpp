@@ -168,10 +168,6 @@ int selective_scan_fwd_ex(const void* x, const void* delta, const float* A, cons
     for (int i = 0; i < 9; ++i)
       if (overlap(workspace, wb, in_p[i], in_b[i])) return SSS_ERR_ALIAS;
   }
-  if (env_int("SSS_LOG", 0))
-    std::fprintf(stderr, "[sss] selective_scan_fwd B=%lld L=%lld D=%lld N=%lld %s flags=%u: segments=%d seg_len=%lld ws=%zu\n",
-                 (long long)batch, (long long)seqlen, (long long)dim, (long long)dstate,
-                 io_dtype == SSS_BF16 ? "bf16" : "f32", flags, pl.segments, (long long)pl.seg_len, pl.ws_total);
   SelArgs a{};
   a.x = x;
   a.delta = delta;
@@ -193,6 +189,15 @@ int selective_scan_fwd_ex(const void* x, const void* delta, const float* A, cons
   a.softplus = (flags & SSS_DELTA_SOFTPLUS) != 0;
   a.exact_zoh = (flags & SSS_EXACT_ZOH) != 0;
   a.bdl = bdl;
+  if (env_int("SSS_LOG", 0)) {
+    static const char* const kRows[] = {"time-major", "step", "piece", "tile"};
+    std::fprintf(stderr,
+                 "[sss] selective_scan_fwd B=%lld L=%lld D=%lld N=%lld %s flags=%u: segments=%d seg_len=%lld rows=%s "
+                 "ws=%zu\n",
+                 (long long)batch, (long long)seqlen, (long long)dim, (long long)dstate,
+                 io_dtype == SSS_BF16 ? "bf16" : "f32", flags, pl.segments, (long long)pl.seg_len,
+                 kRows[selective_row_mode(a, pl)], pl.ws_total);
+  }
   hipError_t e = launch_selective(a, pl, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? SSS_OK : SSS_ERR_HIP;
 }

@@ -36,6 +36,9 @@ struct SelArgs {
 
 SelPlan plan_selective(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int num_cus, bool bdl = false);
 hipError_t launch_selective(const SelArgs& a, const SelPlan& plan, hipStream_t stream);
+// how the forward kernels walk the rows: 0 time-major; channel-major 1 one step per access,
+// 2 16-byte pieces per lane, 3 tiles staged through LDS
+int selective_row_mode(const SelArgs& a, const SelPlan& plan);
 // pass 1 + carry only: the workspace's state slots hold the state entering each segment
 hipError_t launch_segment_states(const SelArgs& a, const SelPlan& plan, hipStream_t stream);
 // after launch_segment_states: the state before every 2^kshift-th step of every segment,

@@ -584,13 +584,10 @@ static SelSeg make_seg(const SelArgs& a, const SelPlan& pl, int ns) {
   g.ngroups = (int)((a.dim + 63) / 64);
   g.gpb = std::min(2, g.ngroups);
   g.nblk = (g.ngroups + g.gpb - 1) / g.gpb;
-  const int64_t piece = a.bf16 ? 8 : 4;  // steps per 16-byte piece of a channel-major row
-  const int64_t tile = kTileBytes / (a.bf16 ? 2 : 4);
-  g.vec = !a.bdl ? 0
-          : (ns <= 16 && a.seqlen % tile == 0 && pl.seg_len % tile == 0) ? 2
-          : (a.seqlen % piece == 0 && pl.seg_len % piece == 0) ? 1 : 0;
+  g.vec = selective_row_mode(a, pl) - 1;
   return g;
 }
+
 
 // B and C from channel-major (batch, dstate, seqlen) to the time-major rows the scan kernels
 // read with scalar loads: one workgroup per (batch, 64 steps, tensor) through an LDS tile,
@@ -725,6 +722,13 @@ template hipError_t run_segment_states<SSS_INST_NS, true>(const SelArgs&, const 
 template hipError_t run_checkpoints<SSS_INST_NS, false>(const SelArgs&, const SelPlan&, float*, int, int, hipStream_t);
 template hipError_t run_checkpoints<SSS_INST_NS, true>(const SelArgs&, const SelPlan&, float*, int, int, hipStream_t);
 #else
+int selective_row_mode(const SelArgs& a, const SelPlan& pl) {
+  if (!a.bdl) return 0;
+  const int64_t piece = a.bf16 ? 8 : 4;  // steps per 16-byte piece of a channel-major row
+  const int64_t tile = kTileBytes / (a.bf16 ? 2 : 4);
+  if (a.dstate <= 16 && a.seqlen % tile == 0 && pl.seg_len % tile == 0) return 3;
+  return (a.seqlen % piece == 0 && pl.seg_len % piece == 0) ? 2 : 1;
+}
 #define SSS_EXTERN_INSTANCES(N)                                                                        \
   extern template hipError_t run_flags<N, false>(const SelArgs&, const SelPlan&, hipStream_t);           \
   extern template hipError_t run_flags<N, true>(const SelArgs&, const SelPlan&, hipStream_t);            \

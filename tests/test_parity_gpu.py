@@ -5,6 +5,7 @@ for bf16 inputs with fp32 state, per output tensor (y and h_last separately).
 Outputs are pre-filled with NaN so that an element the kernels never write fails.
 """
 import os
+import re
 import zlib
 
 import numpy as np
@@ -181,15 +182,35 @@ BDL_CASES = [  # (batch, seqlen, dim, dstate, io, z, D, h0, forced segments, opt
     (1, 2048, 130, 32, "bf16", True, True, True, 0, {"delta_softplus": True}),
     (2, 512, 24, 64, "f32", True, True, True, 2, {"exact_zoh": True}),
     (1, 3000, 16, 2, "bf16", True, True, False, 7, {"exact_zoh": True, "delta_softplus": True}),
+    # rows a multiple of the 64-byte tile: staged through LDS (the "_rows" entry is the row
+    # access the library must report choosing)
+    (2, 4096, 100, 16, "bf16", True, True, True, 4, {"_rows": "tile"}),   # ragged last channel group
+    (1, 2048, 70, 16, "f32", True, True, True, 2, {"_rows": "tile"}),     # fp32: half-line y pieces
+    (2, 1024, 64, 8, "bf16", False, True, False, 0, {"_rows": "tile"}),   # no gate: two staged tensors
+    (1, 2048, 96, 16, "bf16", True, True, True, 2, {"delta_softplus": True, "_rows": "tile"}),
+    (1, 1024, 40, 4, "f32", True, False, True, 4, {"exact_zoh": True, "_rows": "tile"}),
 ]
 
 
-@pytest.mark.parametrize("case", BDL_CASES, ids=[f"B{c[0]}L{c[1]}D{c[2]}N{c[3]}{c[4]}S{c[8]}" + "".join(sorted(c[9]))
+def _rows_logged(text):
+    """(seg_len, row access) from the library's SSS_LOG line of a forward call."""
+    m = re.search(r"\[sss\] selective_scan_fwd .* seg_len=(\d+) rows=(\S+)", text)
+    assert m, f"no plan line in: {text!r}"
+    return int(m.group(1)), m.group(2)
+
+
+@pytest.mark.parametrize("case", BDL_CASES, ids=[f"B{c[0]}L{c[1]}D{c[2]}N{c[3]}{c[4]}S{c[8]}" +
+                                                 "".join(sorted(k for k in c[9] if not k.startswith("_")))
                                                  for c in BDL_CASES])
-def test_selective_channel_major(oracle_lib, monkeypatch, case):
+def test_selective_channel_major(oracle_lib, monkeypatch, capfd, case):
     """layout="bdl": x/delta/z/y (B,D,L), B/C (B,N,L), against the oracle's channel-major entry
-    on the same arrays, over aligned and unaligned rows, splits and options."""
+    on the same arrays, over aligned and unaligned rows, splits and options; the row access the
+    library reports follows its rule (LDS tiles for rows and segments that are whole 64-byte
+    tiles at up to 16 states, else 16-byte pieces where they divide, else one step at a time)."""
     bt, L, dm, n, io, with_z, with_D, with_h0, segs, opts = case
+    opts = dict(opts)
+    want_rows = opts.pop("_rows", None)
+    monkeypatch.setenv("SSS_LOG", "1")
     if segs:
         monkeypatch.setenv("SSS_FORCE_SEGMENTS", str(segs))
     seed = zlib.crc32(repr(case).encode()) % 100000
@@ -199,7 +220,14 @@ def test_selective_channel_major(oracle_lib, monkeypatch, case):
         bias = (0.3 * np.random.default_rng(seed).standard_normal(dm)).astype(np.float32)
     cm = to_channel_major(inp)
     note(f"[channel-major] {case}")
+    capfd.readouterr()
     y, hl = run_selective(cm, layout="bdl", delta_bias=bias, **opts)
+    seg_len, rows = _rows_logged(capfd.readouterr().err)
+    tile, piece = (32, 8) if io == "bf16" else (16, 4)
+    rule = ("tile" if n <= 16 and L % tile == 0 and seg_len % tile == 0 else
+            "piece" if L % piece == 0 and seg_len % piece == 0 else "step")
+    note(f"    rows={rows} seg_len={seg_len}")
+    assert rows == rule and (want_rows is None or rows == want_rows)
     yr, hr = oracle_lib.selective_scan(cm["x"], cm["delta"], cm["A"], cm["B"], cm["C"], cm["D"], cm["z"], cm["h0"],
                                        layout="bdl", delta_bias=bias, **opts)
     tol = TOL_BF16 if io == "bf16" else TOL_F32
