@@ -183,9 +183,12 @@ __global__ __launch_bounds__(256, min_waves_of(NS, FL)) void sel_seq_kernel(cons
   const int64_t ebase = bdl ? (b * g.D + d0) * g.L + tbeg : row0 * g.D + d0;  // element offset
   const int rstride = bdl ? ES : (int)(g.D * ES);  // bytes between consecutive steps
   const uint32_t vo = bdl ? (uint32_t)(loff * g.L * ES) : (uint32_t)loff * ES;
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc((const char*)x + ebase * ES);
-  const __amdgpu_buffer_rsrc_t rd = make_rsrc((const char*)delta + ebase * ES);
-  const __amdgpu_buffer_rsrc_t rz = make_rsrc(has_z ? (const char*)z + ebase * ES : (const char*)x);
+  const char* const xb = (const char*)x + ebase * ES;
+  const char* const db = (const char*)delta + ebase * ES;
+  const char* const zb = has_z ? (const char*)z + ebase * ES : (const char*)x;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(xb);
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(db);
+  const __amdgpu_buffer_rsrc_t rz = make_rsrc(zb);
   const __amdgpu_buffer_rsrc_t ry = make_rsrc(PASS == 2 ? (const char*)(y + ebase) : (const char*)x);
   const int ystride = bdl ? 4 : (int)(g.D * 4);
   const uint32_t yvo = bdl ? (uint32_t)(loff * g.L * 4) : (uint32_t)loff * 4;
@@ -260,16 +263,25 @@ __global__ __launch_bounds__(256, min_waves_of(NS, FL)) void sel_seq_kernel(cons
   }
   const int lrow = loff * 16;
   const int lswz = (loff >> 1) & 3;
-  auto tile_load = [&](int t0) {  // tile starting at segment step t0 (clamped into the segment)
-    const int so = min(t0, len - TT) * ES;
+  // tile starting at segment step t0.  The loop stays branch-free: the two loads past the
+  // segment's end (their tiles are never read) go through descriptors of zero bytes, so the
+  // hardware's range check returns zeros without touching memory.
+  auto tile_load = [&](int t0) {
+    const bool inside = t0 < len;  // wave-uniform
+    const int so = inside ? t0 * ES : 0;
+    const int nrec = inside ? 0x7FFFFFFF : 0;
+    const __amdgpu_buffer_rsrc_t tx = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(xb), 0, nrec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t td = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(db), 0, nrec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t tz = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(zb), 0, nrec, 0x00020000);
 #pragma unroll
     for (int i = 0; i < kPieces; ++i) {
-      const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)gvo[i], so, kStreamPolicy);
-      const u32x4 bq = __builtin_amdgcn_raw_buffer_load_b128(rd, (int)gvo[i], so, kStreamPolicy);
+      const int vo_ = (int)gvo[i];
+      const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(tx, vo_, so, kStreamPolicy);
+      const u32x4 bq = __builtin_amdgcn_raw_buffer_load_b128(td, vo_, so, kStreamPolicy);
       gq[0][i][0] = a.x; gq[0][i][1] = a.y; gq[0][i][2] = a.z; gq[0][i][3] = a.w;
       gq[1][i][0] = bq.x; gq[1][i][1] = bq.y; gq[1][i][2] = bq.z; gq[1][i][3] = bq.w;
       if constexpr (kNT == 3) {
-        const u32x4 c = __builtin_amdgcn_raw_buffer_load_b128(rz, (int)gvo[i], so, kStreamPolicy);
+        const u32x4 c = __builtin_amdgcn_raw_buffer_load_b128(tz, vo_, so, kStreamPolicy);
         gq[2][i][0] = c.x; gq[2][i][1] = c.y; gq[2][i][2] = c.z; gq[2][i][3] = c.w;
       }
     }
@@ -482,7 +494,7 @@ __global__ __launch_bounds__(256, min_waves_of(NS, FL)) void sel_seq_kernel(cons
         for (int i = 0; i < U; ++i) SSS_TSTEP(1, i, t0 + 3 * U + i, 3 * U + i, );
         y_tile(t0);              // the LDS tile is consumed: stage y through it
         tile_store();            // the next tile, loaded during the previous iteration
-        tile_load(t0 + 2 * TT);  // the one after it (clamped into the segment)
+        tile_load(t0 + 2 * TT);  // the one after it
         SSS_TILE_READ(0, 0);
       } else {
         tile_store();
