@@ -379,8 +379,18 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc(const float* __restrict__ p
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t V = 2 * (int64_t)N;
   if (idx >= rows * V) return;
+  // the same sequential order, with a batch of loads in flight ahead of the adds
+  constexpr int kAhead = 8;
   float acc = 0.0f;
-  for (int gidx = 0; gidx < ngroups; ++gidx) acc += part[(int64_t)gidx * rows * V + idx];
+  int gidx = 0;
+  for (; gidx + kAhead <= ngroups; gidx += kAhead) {
+    float v[kAhead];
+#pragma unroll
+    for (int k = 0; k < kAhead; ++k) v[k] = part[(int64_t)(gidx + k) * rows * V + idx];
+#pragma unroll
+    for (int k = 0; k < kAhead; ++k) acc += v[k];
+  }
+  for (; gidx < ngroups; ++gidx) acc += part[(int64_t)gidx * rows * V + idx];
   const int64_t r = idx / V, j = idx - r * V;
   if (j < N) dB[r * N + j] = acc;
   else dC[r * N + (j - N)] = acc;
@@ -394,12 +404,30 @@ __global__ __launch_bounds__(256) void bwd_reduce_ad(const float* __restrict__ p
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // n * D + d
   if (idx >= (int64_t)N * D) return;
   const int64_t n = idx / D, d = idx - n * D;
+  // the same sequential order, with a batch of loads in flight ahead of the adds
+  constexpr int kAhead = 16;
   float acc = 0.0f;
-  for (int64_t i = 0; i < sb; ++i) acc += part_a[i * N * D + idx];
+  int64_t i = 0;
+  for (; i + kAhead <= sb; i += kAhead) {
+    float v[kAhead];
+#pragma unroll
+    for (int k = 0; k < kAhead; ++k) v[k] = part_a[(i + k) * N * D + idx];
+#pragma unroll
+    for (int k = 0; k < kAhead; ++k) acc += v[k];
+  }
+  for (; i < sb; ++i) acc += part_a[i * N * D + idx];
   dA[d * N + n] = acc;
   if (n == 0 && dD != nullptr) {
     float ad = 0.0f;
-    for (int64_t i = 0; i < sb; ++i) ad += part_d[i * D + d];
+    int64_t j = 0;
+    for (; j + kAhead <= sb; j += kAhead) {
+      float v[kAhead];
+#pragma unroll
+      for (int k = 0; k < kAhead; ++k) v[k] = part_d[(j + k) * D + d];
+#pragma unroll
+      for (int k = 0; k < kAhead; ++k) ad += v[k];
+    }
+    for (; j < sb; ++j) ad += part_d[j * D + d];
     dD[d] = ad;
   }
 }
