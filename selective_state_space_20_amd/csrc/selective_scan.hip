@@ -37,8 +37,8 @@ constexpr int kStepsPerBatch = 2;  // time steps whose x/delta/z loads are issue
 // register budget: at least this many resident waves per SIMD (512 VGPRs / waves each);
 // 32 and 64 states need the larger budgets to stay spill-free
 constexpr int min_waves_per_simd(int ns) { return ns >= 64 ? 1 : ns >= 32 ? 3 : 4; }
-// Options that hold more per lane get larger register budgets: the exact hold keeps 1/A and
-// (A == 0) per state (2 waves per SIMD from 32 states on); channel-major tiles keep the next
+// Options that hold more per lane get larger register budgets: the exact hold keeps 1/A per
+// state (2 waves per SIMD from 32 states on); channel-major tiles keep the next
 // tile in flight and a tile of outputs in registers (3 waves per SIMD at 16 states with no
 // other option, else 2).  (fl: bit 0 exact hold, bit 1 delta front end, bit 3 channel-major.)
 constexpr int min_waves_of(int ns, int fl) {
@@ -81,12 +81,16 @@ __device__ __forceinline__ float step_size(float raw, float bias) {
   return v;
 }
 
-// e^x - 1 for x = arg * ln 2 given e2 = 2^arg: a short Taylor series where |x| < 1/16 (no
-// cancellation), else e2 - 1.
-__device__ __forceinline__ float expm1_of_log2(float arg, float e2) {
-  const float xn = arg * kLn2;
-  const float p = xn * __builtin_fmaf(xn, __builtin_fmaf(xn, __builtin_fmaf(xn, 1.0f / 24.0f, 1.0f / 6.0f), 0.5f), 1.0f);
-  return fabsf(xn) < 0.0625f ? p : e2 - 1.0f;
+// Exact zero-order hold: the input coefficient expm1(u) / A with u = delta * A = arg * ln 2
+// (arg = delta * A * log2 e, e2 = 2^arg).  Where |u| < 1/16 it is delta * (1 + u/2 + u^2/6 +
+// u^3/24), the series of expm1(u) / u written in arg (no cancellation, and A = 0 gives delta);
+// elsewhere (e2 - 1) / A with ia = 1/A.
+constexpr float kZ1 = kLn2 / 2.0f, kZ2 = kLn2 * kLn2 / 6.0f, kZ3 = kLn2 * kLn2 * kLn2 / 24.0f;
+constexpr float kZArg = 0.0625f / kLn2;  // |u| < 1/16 in terms of arg
+__device__ __forceinline__ float zoh_coef(float arg, float e2, float dl, float ia) {
+  const float q = __builtin_fmaf(arg, __builtin_fmaf(arg, __builtin_fmaf(arg, kZ3, kZ2), kZ1), 1.0f);
+  const float big = __builtin_fmaf(e2, ia, -ia);
+  return fabsf(arg) < kZArg ? dl * q : big;
 }
 
 struct SelSeg {
@@ -144,15 +148,12 @@ __global__ __launch_bounds__(256, min_waves_of(NS, FL)) void sel_seq_kernel(cons
 
   constexpr bool zoh = (FL & kZoh) != 0;
   float a2[NS], h[NS];
-  float ia[zoh ? NS : 1], az[zoh ? NS : 1];  // exact hold: 1/A[n] and (A[n] == 0)
+  float ia[zoh ? NS : 1];  // exact hold: 1/A[n] (A = 0 takes the series, which needs none)
 #pragma unroll
   for (int n = 0; n < NS; ++n) {
     const float an = A[dc * N + n];
     a2[n] = fmaxf(an * kLog2e, -kFltMax);  // -inf clamped so that 0*a2 = 0
-    if constexpr (zoh) {
-      ia[n] = an != 0.0f ? 1.0f / an : 0.0f;
-      az[n] = an != 0.0f ? 0.0f : 1.0f;
-    }
+    if constexpr (zoh) ia[n] = an != 0.0f ? 1.0f / an : 0.0f;
     if (PASS == 1) {
       h[n] = 0.0f;
     } else if (g.S > 1) {
@@ -355,7 +356,7 @@ __global__ __launch_bounds__(256, min_waves_of(NS, FL)) void sel_seq_kernel(cons
       const float arg = dl * a2[n];                                              \
       const float ab = fast_exp2(arg);                                           \
       if constexpr (zoh) {                                                       \
-        const float cf = __builtin_fmaf(expm1_of_log2(arg, ab), ia[n], dl * az[n]); \
+        const float cf = zoh_coef(arg, ab, dl, ia[n]);                          \
         h[n] = __builtin_fmaf(ab, h[n], cf * (xv * Bt[n]));                      \
       } else {                                                                   \
         h[n] = __builtin_fmaf(ab, h[n], dx * Bt[n]);                             \
