@@ -52,6 +52,14 @@ __device__ __forceinline__ void st_f32(float v, __amdgpu_buffer_rsrc_t r, int vo
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, vo, so, 2);
 }
 
+// a h_t = h_{t+1} - (delta x)_t B_t, the input term rounded exactly as the forward step
+// rounded it (not fused), so that a zero a h_t comes back as zero
+__device__ __forceinline__ float minus_input(float h_next, float dx, float b) {
+#pragma clang fp contract(off)
+  const float p = dx * b;
+  return h_next - p;
+}
+
 // silu'(z) = s (1 + z (1 - s)), s = sigmoid(z)
 __device__ __forceinline__ float sigmoid_f(float z) { return fast_rcp(1.0f + fast_exp2(-z * kLog2e)); }
 
@@ -59,7 +67,9 @@ __device__ __forceinline__ float sigmoid_f(float z) { return fast_rcp(1.0f + fas
 // (measured on the 1 x 65536 x 5120 N=16 layer: K=2 11.7 ms; K=4 spills or, with a 512-VGPR
 // budget, runs one wave per SIMD: 17 ms)
 constexpr int bwd_k(int ns) { return ns >= 64 ? 1 : ns >= 16 ? 2 : ns >= 8 ? 4 : 8; }
-constexpr int bwd_min_waves(int ns) { return ns >= 32 ? 1 : 2; }
+// resident waves per SIMD of the main kernel: three at 16 states (168 VGPRs; 2 waves ran it
+// at 5.1-5.2 ms on that layer, 3 at 4.6 ms)
+constexpr int bwd_min_waves(int ns) { return ns >= 32 ? 1 : ns >= 16 ? 3 : 2; }
 
 // Common prologue: (wave, batch, segment) of this workgroup and the lane's channel.
 struct BwdLane {
@@ -231,20 +241,19 @@ __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
     float* __restrict__ part_d, float* __restrict__ dh0, BwdSeg g) {
   constexpr int K = bwd_k(NS);
   constexpr int ES = BF16 ? 2 : 4;
-  // dB and dC partials of one step go through one reduce-scatter of 2 NS values; from 32
+  // dB and dC partials of one step go through one reduce-scatter of 2 NS values; from 16
   // states on through two of NS (fewer live registers)
-  constexpr bool kMerged = NS <= 16;
+  constexpr bool kMerged = NS < 16;
   constexpr int NV = kMerged ? 2 * NS : NS;            // values per reduce-scatter
   constexpr int LV = ilog2c(NV) < 6 ? ilog2c(NV) : 6;  // its levels
   constexpr int KEEP = NV >> LV;
   const BwdLane q = bwd_lane(g, 0);
   const int64_t chl = (q.b * g.D + q.dc) * NS;  // (b, d) row of dh_last / dh0
 
-  float a2[NS], a1[NS], mu[NS], dacc[NS];  // A' = A log2 e (for exp2), A itself (clamped)
+  float a2[NS], mu[NS], dacc[NS];  // A' = A log2 e (for exp2; A itself is A' ln 2), clamped
 #pragma unroll
   for (int n = 0; n < NS; ++n) {
     a2[n] = fmaxf(A[q.dc * NS + n] * kLog2e, -kFltMax);
-    a1[n] = a2[n] * kLn2;
     mu[n] = g.S > 1 ? mu_right[(((int64_t)q.s * g.batch + q.b) * NS + n) * g.D + q.dc]
                     : (dh_last ? dh_last[chl + n] : 0.0f);
     dacc[n] = 0.0f;
@@ -331,21 +340,24 @@ __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
             _Pragma("unroll") for (int e = 0; e < KEEP; ++e) rowp[NS + widx + e] = pc[e];  \
           }                                                                                \
         }                                                                                  \
-        float gx = Dd * dv, gd = 0.0f;                                                     \
+        float gx = Dd * dv, gd = 0.0f, ga = 0.0f; /* ga: the A term of gd over ln 2 */     \
+        const float dxi = dl * xv;                                                         \
         _Pragma("unroll") for (int n = 0; n < NS; ++n) {                                   \
           const float a = ea[i][n];                                                        \
           const float lam = __builtin_fmaf(Ct[n], dv, mu[n]);                              \
           const float lb = lam * Bt[n];                                                    \
-          const float ah = a * hs[i][n];                                                   \
+          /* a h_t from the state after the step (h_t itself is not kept) */              \
+          const float ah = minus_input(hs[i + 1][n], dxi, Bt[n]);                          \
           gx = __builtin_fmaf(lb, dl, gx);                                                 \
-          gd = __builtin_fmaf(lb, xv, __builtin_fmaf(lam * a1[n], ah, gd));                \
+          gd = __builtin_fmaf(lb, xv, gd);                                                 \
+          ga = __builtin_fmaf(lam * ah, a2[n], ga); /* ah = 0 keeps A = -inf finite */     \
           dacc[n] = __builtin_fmaf(lam * dl, ah, dacc[n]);                                 \
           pv[n] = lam * dxm;                                                               \
           mu[n] = a * lam;                                                                 \
         }                                                                                  \
         ddacc = __builtin_fmaf(dv, xv, ddacc);                                             \
         st_f32(gx, rdx, vo4, t * rs4);                                                     \
-        st_f32(gd, rdd, vo4, t * rs4);                                                     \
+        st_f32(__builtin_fmaf(ga, kLn2, gd), rdd, vo4, t * rs4);                           \
         if (HAS_Z) st_f32(gy * vsum * sg * __builtin_fmaf(zv, 1.0f - sg, 1.0f), rdz, vo4, t * rs4); \
         reduce_scatter<kMerged ? 2 * NS : NS>(pv, q.lane);                                 \
         if (writer) {                                                                      \
