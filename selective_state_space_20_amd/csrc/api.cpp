@@ -247,9 +247,11 @@ int selective_scan_bwd(const void* x, const void* delta, const float* A, const f
   for (int i = 0; i < 8; ++i)
     if (overlap(workspace, wb, out_p[i], out_b[i])) return SSS_ERR_ALIAS;
   if (env_int("SSS_LOG", 0))
-    std::fprintf(stderr, "[sss] selective_scan_bwd B=%lld L=%lld D=%lld N=%lld: segments=%d seg_len=%lld K=%d ws=%zu\n",
+    std::fprintf(stderr,
+                 "[sss] selective_scan_bwd B=%lld L=%lld D=%lld N=%lld: segments=%d seg_len=%lld K=%d checkpoint every %d "
+                 "ws=%zu\n",
                  (long long)batch, (long long)seqlen, (long long)dim, (long long)dstate, bp.fwd.segments,
-                 (long long)bp.fwd.seg_len, bp.K, bp.ws_total);
+                 (long long)bp.fwd.seg_len, bp.K, bp.KC, bp.ws_total);
   BwdArgs a{};
   a.fwd.x = x;
   a.fwd.delta = delta;

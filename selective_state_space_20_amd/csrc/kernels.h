@@ -49,7 +49,8 @@ hipError_t launch_checkpoints(const SelArgs& a, const SelPlan& plan, float* ckpt
 // Backward pass of the selective scan (selective_bwd.hip).
 struct BwdPlan {
   SelPlan fwd;     // segments of the forward pass (its workspace comes first)
-  int K, nsub;     // checkpoint spacing and checkpoints per segment
+  int K, KC, nsub; // steps per sub-chunk, checkpoint spacing (a multiple of K), checkpoints
+                   // per segment
   size_t off_mu, off_ckpt, off_bc, off_pa, off_pd, ws_total;
 };
 

@@ -67,6 +67,10 @@ __device__ __forceinline__ float sigmoid_f(float z) { return fast_rcp(1.0f + fas
 // (measured on the 1 x 65536 x 5120 N=16 layer: K=2 11.7 ms; K=4 spills or, with a 512-VGPR
 // budget, runs one wave per SIMD: 17 ms)
 constexpr int bwd_k(int ns) { return ns >= 64 ? 1 : ns >= 16 ? 2 : ns >= 8 ? 4 : 8; }
+// sub-chunks per checkpoint: at 16 states a checkpoint every 2K steps, the odd sub-chunks
+// advancing it by K steps first (half the checkpoint bytes written and read, for K more
+// forward steps per 2K)
+constexpr int bwd_r(int ns) { return ns == 16 ? 2 : 1; }
 // resident waves per SIMD of the main kernel: three at 16 states (168 VGPRs; 2 waves ran it
 // at 5.1-5.2 ms on that layer, 3 at 4.6 ms)
 constexpr int bwd_min_waves(int ns) { return ns >= 32 ? 1 : ns >= 16 ? 3 : 2; }
@@ -240,6 +244,7 @@ __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
     float* __restrict__ ddelta, float* __restrict__ dz, float* __restrict__ part_bc, float* __restrict__ part_a,
     float* __restrict__ part_d, float* __restrict__ dh0, BwdSeg g) {
   constexpr int K = bwd_k(NS);
+  constexpr int R = bwd_r(NS);
   constexpr int ES = BF16 ? 2 : 4;
   // dB and dC partials of one step go through one reduce-scatter of 2 NS values; from 16
   // states on through two of NS (fewer live registers)
@@ -296,8 +301,18 @@ __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
     const int tb = (J) * K;                                                                \
     const int k = min(K, q.len - tb);                                                      \
     float hs[K + 1][NS], ea[K][NS]; /* states and decays of the sub-chunk */               \
-    const __amdgpu_buffer_rsrc_t rc_ = ck_rsrc(J);                                         \
+    const __amdgpu_buffer_rsrc_t rc_ = ck_rsrc((J) / R);                                   \
     _Pragma("unroll") for (int n = 0; n < NS; ++n) hs[0][n] = ld_f32(rc_, q.lane * 4, n * 256); \
+    if (R == 2 && ((J) & 1)) { /* the checkpoint is K steps before the sub-chunk */        \
+      _Pragma("unroll") for (int i = 0; i < K; ++i) {                                      \
+        const int ta = ((J) - 1) * K + i;                                                  \
+        const float dla = ld_io<BF16>(rd, vo, ta * rs);                                    \
+        const float dxa = dla * ld_io<BF16>(rx, vo, ta * rs);                              \
+        const float* Ba = Br + ta * NS;                                                    \
+        _Pragma("unroll") for (int n = 0; n < NS; ++n)                                     \
+          hs[0][n] = __builtin_fmaf(fast_exp2(dla * a2[n]), hs[0][n], dxa * Ba[n]);        \
+      }                                                                                    \
+    }                                                                                      \
     _Pragma("unroll") for (int i = 0; i < K; ++i) {                                        \
       if (i < k) {                                                                         \
         const float* Bt = Br + (tb + i) * NS;                                              \
@@ -453,7 +468,8 @@ BwdPlan plan_selective_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t d
   const int64_t S = bp.fwd.segments;
   const int K = bwd_k((int)dstate);
   bp.K = K;
-  bp.nsub = (int)((bp.fwd.seg_len + K - 1) / K);
+  bp.KC = K * bwd_r((int)dstate);
+  bp.nsub = (int)((bp.fwd.seg_len + bp.KC - 1) / bp.KC);
   const int64_t ngroups = (dim + 63) / 64;
   size_t off = align256(bp.fwd.ws_total);
   bp.off_mu = off;
@@ -543,7 +559,7 @@ hipError_t launch_selective_bwd(const BwdArgs& a, const BwdPlan& bp, hipStream_t
   hipError_t e = launch_segment_states(a.fwd, bp.fwd, stream);
   if (e != hipSuccess) return e;
   unsigned char* ws = static_cast<unsigned char*>(a.fwd.workspace);
-  e = launch_checkpoints(a.fwd, bp.fwd, reinterpret_cast<float*>(ws + bp.off_ckpt), ilog2c(bp.K), bp.nsub, stream);
+  e = launch_checkpoints(a.fwd, bp.fwd, reinterpret_cast<float*>(ws + bp.off_ckpt), ilog2c(bp.KC), bp.nsub, stream);
   if (e != hipSuccess) return e;
   return a.fwd.bf16 ? dispatch_bwd<true>(a, bp, stream) : dispatch_bwd<false>(a, bp, stream);
 }
