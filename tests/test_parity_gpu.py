@@ -265,6 +265,11 @@ BWD_CASES = [  # (batch, seqlen, dim, dstate, io, z, D, h0, dh_last, forced segm
     (1, 400, 100, 2, "f32", True, True, True, True, 5),
     (2, 300, 24, 32, "f32", True, True, True, True, 3),
     (1, 200, 16, 64, "bf16", True, True, True, True, 2),
+    # 16 states keep a checkpoint every four steps: segments whose last two-step sub-chunk is
+    # odd-numbered and one step long, and lengths of every residue mod 4
+    (1, 665, 40, 16, "bf16", True, True, True, True, 2),
+    (2, 1001, 24, 16, "f32", True, False, True, True, 3),
+    (1, 7, 70, 16, "f32", True, True, True, True, 0),
 ]
 
 
