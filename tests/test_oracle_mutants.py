@@ -108,7 +108,7 @@ def test_unmutated_copy_passes_every_pin(tmp_path):
         call(mod)
 
 
-@pytest.mark.filterwarnings("ignore::RuntimeWarning")  # mutants may overflow; only the verdict matters
+@pytest.mark.filterwarnings("ignore::RuntimeWarning")  # mutants may overflow; only the outcome matters
 @pytest.mark.parametrize("mutant", sorted(MUTANTS))
 def test_mutant_is_caught(tmp_path, mutant):
     old, new = MUTANTS[mutant]
