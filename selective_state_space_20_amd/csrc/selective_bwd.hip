@@ -306,8 +306,8 @@ __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
     if (R == 2 && ((J) & 1)) { /* the checkpoint is K steps before the sub-chunk */        \
       _Pragma("unroll") for (int i = 0; i < K; ++i) {                                      \
         const int ta = ((J) - 1) * K + i;                                                  \
-        const float dla = ld_io<BF16>(rd, vo, ta * rs);                                    \
-        const float dxa = dla * ld_io<BF16>(rx, vo, ta * rs);                              \
+        const float dla = da[i];                                                           \
+        const float dxa = dla * xa[i];                                                     \
         const float* Ba = Br + ta * NS;                                                    \
         _Pragma("unroll") for (int n = 0; n < NS; ++n)                                     \
           hs[0][n] = __builtin_fmaf(fast_exp2(dla * a2[n]), hs[0][n], dxa * Ba[n]);        \
@@ -383,6 +383,17 @@ __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
   } while (0)
 
   for (int j = last; j >= 0; --j) {
+    // inputs of the sub-chunk before, for the checkpoint advance of odd sub-chunks: loaded
+    // with the others (unconditionally, clamped) so that they are in flight together
+    float xa[K], da[K];
+    if constexpr (R == 2) {
+#pragma unroll
+      for (int i = 0; i < K; ++i) {
+        const int ta = max((j - 1) * K + i, 0);
+        xa[i] = ld_io<BF16>(rx, vo, ta * rs);
+        da[i] = ld_io<BF16>(rd, vo, ta * rs);
+      }
+    }
     BWD_LOAD(0, j);
     BWD_CHUNK(0, j);
   }
