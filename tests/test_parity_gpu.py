@@ -189,6 +189,7 @@ BDL_CASES = [  # (batch, seqlen, dim, dstate, io, z, D, h0, forced segments, opt
     (2, 1024, 64, 8, "bf16", False, True, False, 0, {"_rows": "tile"}),   # no gate: two staged tensors
     (1, 2048, 96, 16, "bf16", True, True, True, 2, {"delta_softplus": True, "_rows": "tile"}),
     (1, 1024, 40, 4, "f32", True, False, True, 4, {"exact_zoh": True, "_rows": "tile"}),
+    (1, 1024, 100, 8, "bf16", True, True, True, 3, {"exact_zoh": True, "delta_softplus": True, "_rows": "tile"}),
 ]
 
 
