@@ -355,21 +355,24 @@ __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
             _Pragma("unroll") for (int e = 0; e < KEEP; ++e) rowp[NS + widx + e] = pc[e];  \
           }                                                                                \
         }                                                                                  \
-        float gx = Dd * dv, gd = 0.0f, ga = 0.0f; /* ga: the A term of gd over ln 2 */     \
+        /* slb = sum_n lam_n B_t[n] (dx takes it times delta, ddelta times x); ga: the A   \
+           term of ddelta over ln 2 */                                                     \
+        float slb = 0.0f, ga = 0.0f;                                                       \
         const float dxi = dl * xv;                                                         \
         _Pragma("unroll") for (int n = 0; n < NS; ++n) {                                   \
           const float a = ea[i][n];                                                        \
           const float lam = __builtin_fmaf(Ct[n], dv, mu[n]);                              \
-          const float lb = lam * Bt[n];                                                    \
+          slb = __builtin_fmaf(lam, Bt[n], slb);                                           \
           /* a h_t from the state after the step (h_t itself is not kept) */              \
           const float ah = minus_input(hs[i + 1][n], dxi, Bt[n]);                          \
-          gx = __builtin_fmaf(lb, dl, gx);                                                 \
-          gd = __builtin_fmaf(lb, xv, gd);                                                 \
-          ga = __builtin_fmaf(lam * ah, a2[n], ga); /* ah = 0 keeps A = -inf finite */     \
-          dacc[n] = __builtin_fmaf(lam * dl, ah, dacc[n]);                                 \
+          const float lah = lam * ah;                                                      \
+          ga = __builtin_fmaf(lah, a2[n], ga); /* ah = 0 keeps A = -inf finite */          \
+          dacc[n] = __builtin_fmaf(lah, dl, dacc[n]);                                      \
           pv[n] = lam * dxm;                                                               \
           mu[n] = a * lam;                                                                 \
         }                                                                                  \
+        const float gx = __builtin_fmaf(slb, dl, Dd * dv);                                 \
+        const float gd = slb * xv;                                                         \
         ddacc = __builtin_fmaf(dv, xv, ddacc);                                             \
         st_f32(gx, rdx, vo4, t * rs4);                                                     \
         st_f32(__builtin_fmaf(ga, kLn2, gd), rdd, vo4, t * rs4);                           \
