@@ -363,8 +363,9 @@ __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
           const float a = ea[i][n];                                                        \
           const float lam = __builtin_fmaf(Ct[n], dv, mu[n]);                              \
           slb = __builtin_fmaf(lam, Bt[n], slb);                                           \
-          /* a h_t from the state after the step (h_t itself is not kept) */              \
-          const float ah = minus_input(hs[i + 1][n], dxi, Bt[n]);                          \
+          /* a h_t: the sub-chunk's first state is not kept, so the first step forms it    \
+             from the state after the step; the others have h_t in registers */            \
+          const float ah = i > 0 ? a * hs[i > 0 ? i : 1][n] : minus_input(hs[i + 1][n], dxi, Bt[n]); \
           const float lah = lam * ah;                                                      \
           ga = __builtin_fmaf(lah, a2[n], ga); /* ah = 0 keeps A = -inf finite */          \
           dacc[n] = __builtin_fmaf(lah, dl, dacc[n]);                                      \
