@@ -246,8 +246,8 @@ __global__ __launch_bounds__(256, min_waves_of(NS, FL)) void sel_seq_kernel(cons
   // lanes per row, so rows are read in whole 64-byte pieces), the pieces go to this wave's
   // LDS tile, and each lane then reads its own row 16 bytes per batch.  The next tile's
   // loads are in flight (gq) while the current tile is computed.  LDS rows are 64 bytes
-  // with the 16-byte chunks xor-swizzled by row, so that the lanes' 16-byte reads of one
-  // batch fall in distinct banks.
+  // with the 16-byte chunks xor-swizzled by row (by row / 4: four rows share one 256-byte
+  // bank line), so that the lanes' 16-byte reads of one batch fall in distinct banks.
   constexpr int kNT = has_z ? 3 : 2;  // tensors staged: x, delta (, z)
   constexpr int kPieces = 4;          // 16-byte pieces per lane, tensor and tile
   extern __shared__ uint32_t sss_lds[];  // [wave][tensor][64 rows][16 dwords]
@@ -260,10 +260,10 @@ __global__ __launch_bounds__(256, min_waves_of(NS, FL)) void sel_seq_kernel(cons
     const int r = 16 * i + (lane >> 2), c = lane & 3;
     const int rr = (int)(min(d0 + r, g.D - 1) - d0);  // rows past D-1 repeat the last row
     gvo[i] = (uint32_t)(rr * g.L * ES + c * 16);
-    gchunk[i] = r * 16 + ((c ^ ((r >> 1) & 3)) * 4);
+    gchunk[i] = r * 16 + ((c ^ ((r >> 2) & 3)) * 4);
   }
   const int lrow = loff * 16;
-  const int lswz = (loff >> 1) & 3;
+  const int lswz = (loff >> 2) & 3;
   // tile starting at segment step t0.  The loop stays branch-free: the two loads past the
   // segment's end (their tiles are never read) go through descriptors of zero bytes, so the
   // hardware's range check returns zeros without touching memory.
