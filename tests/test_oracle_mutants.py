@@ -44,6 +44,10 @@ MUTANTS = {
     "compose_wrong_order": ("  r.b = cur.a * prefix.b + cur.b;", "  r.b = prefix.a * cur.b + prefix.b;"),
     "zoh_without_A_division": ("(a != 0.0 ? expm1(dt * a) / a : dt) * (double)Bt[n]",
                                "(a != 0.0 ? expm1(dt * a) : dt) * (double)Bt[n]"),
+    "zoh_zero_at_A_zero": ("(a != 0.0 ? expm1(dt * a) / a : dt) * (double)Bt[n]",
+                           "(a != 0.0 ? expm1(dt * a) / a : 0.0) * (double)Bt[n]"),
+    "zoh_zero_at_A_zero_chunked": ("p.b = (exact_zoh ? (a != 0.0 ? expm1(dt * a) / a : dt) : dt) * Bn * xt;",
+                                   "p.b = (exact_zoh ? (a != 0.0 ? expm1(dt * a) / a : 0.0) : dt) * Bn * xt;"),
     "update_reads_old_state": ("      acc += (double)Cm[b * N + n] * h;",
                                "      acc += (double)Cm[b * N + n] * (double)state[c * N + n];"),
     "update_B_of_batch_0": ("dv * (double)Bm[b * N + n] * xv;", "dv * (double)Bm[n] * xv;"),

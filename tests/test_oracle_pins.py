@@ -324,21 +324,15 @@ def test_M9_gate_and_skip_wiring(oracle_lib):
     assert np.all(hl == 0.0)
 
 
-def test_M10_p1_example_exact_zoh(oracle_lib):
-    """P1 Python example replayed (setup in tests/golden/p1_example_setup.json): with the
-    exact zero-order hold, every state h_t[k] (read out with C = e_k) from the stepwise
-    oracle equals the prefix fold of pairs and the brute-force unrolled sum."""
-    g = _gold("p1_example_setup.json")
-    L, N = g["seqlen"], g["dstate"]
-    rng = np.random.default_rng(g["seed"])
-    x = rng.normal(size=L)
-    A = -np.exp(np.linspace(g["A_linspace"][0], g["A_linspace"][1], N))
-    B = rng.normal(size=(L, N))
-    delta = np.logaddexp(0.0, rng.normal(size=(L, 1)))
-    xs = x.astype(np.float32)[None, :, None]
-    ds = delta.astype(np.float32)[None, :, :]
-    As = A.astype(np.float32)[None, :]
-    Bs = B.astype(np.float32)[None]
+def test_M10_exact_zoh_sequential_equals_pairs(oracle_lib):
+    """The zero-order-hold input term of P1 ('Vi du Python: vi sao recurrence co the viet duoi
+    dang scan?': Abar = exp(Delta*A), Bbar = expm1(Delta*A)/A * B) on one channel of the
+    repository's own seeded Mamba-form inputs (8 steps, 4 states): every state h_t[k] (read
+    out with C = e_k) from the stepwise oracle equals the fold of composed pairs and the
+    brute-force unrolled sum, and the exact hold differs from the first-order Delta*B term."""
+    L, N = 8, 4
+    inp = gen.selective_inputs(1, L, 1, N, io="f32", with_D=False, seed=8)
+    xs, ds, As, Bs = inp["x"], inp["delta"], inp["A"], inp["B"]
     states = np.zeros((L, N))
     for k in range(N):
         Ck = np.zeros((1, L, N), np.float32)
@@ -348,11 +342,56 @@ def test_M10_p1_example_exact_zoh(oracle_lib):
         ref = brute_force_selective(xs, ds, As, Bs, Ck, exact_zoh=True)
         assert rel_err(yk, ref) < 1e-13 and rel_err(yc, ref) < 1e-13
         states[:, k] = yk[0, :, 0]
-    # the exact hold differs from the first-order Delta*B term (the reading used on the GPU path)
-    y_euler, _ = oracle_lib.selective_scan(xs, ds, As, Bs, np.ones((1, L, N), np.float32))
-    y_zoh, _ = oracle_lib.selective_scan(xs, ds, As, Bs, np.ones((1, L, N), np.float32), exact_zoh=True)
+    # the exact hold differs from the first-order Delta*B term (the reading used by default)
+    ones = np.ones((1, L, N), np.float32)
+    y_euler, _ = oracle_lib.selective_scan(xs, ds, As, Bs, ones)
+    y_zoh, _ = oracle_lib.selective_scan(xs, ds, As, Bs, ones, exact_zoh=True)
     assert rel_err(y_euler, y_zoh) > 1e-3
     assert np.allclose(states.sum(axis=1), y_zoh[0, :, 0], rtol=1e-13, atol=1e-13)
+
+
+def test_Z1_exact_hold_hand_worked_limits(oracle_lib):
+    """Exact hold at A = 0 (the input coefficient's limit is Delta, a running sum of
+    Delta*B*x) and at A = -1e30 (memoryless, vanishing input term): hand-derived values
+    (tests/golden/hand_worked_exact_hold.json), in both the stepwise and the chunked mode."""
+    g = _gold("hand_worked_exact_hold.json")
+    args = (_f32(g["x"]), _f32(g["delta"]), _f32(g["A"]), _f32(g["B"]), _f32(g["C"]))
+    y, hl = oracle_lib.selective_scan(*args, D=_f32(g["D"]), h0=_f32(g["h0"]), exact_zoh=True)
+    yc, hc = oracle_lib.selective_scan_chunked(*args, D=_f32(g["D"]), h0=_f32(g["h0"]), chunk=2, exact_zoh=True)
+    for yy, hh in ((y, hl), (yc, hc)):
+        assert np.array_equal(yy, np.asarray(g["y"], np.float64))
+        assert hh[0, 0, 0] == g["h_last_state0"]
+        assert abs(hh[0, 0, 1]) < g["h_last_state1_bound"]
+
+
+def test_Z2_exact_hold_is_continuous_at_A_zero(oracle_lib):
+    """expm1(u)/u -> 1 as u -> 0, so the exact hold with |A| = 1e-6 must agree with its
+    A = 0 value to O(|Delta*A| * L) and with M2's closed form (h0 plus the running sum of
+    Delta*B*x, read out with C), while |A| = 1 must not (the decay is visible)."""
+    L, N = 48, 4
+    inp = gen.selective_inputs(2, L, 3, N, io="f32", with_D=True, with_z=True, h0=True, seed=77)
+    x, dl, B, C = inp["x"], inp["delta"], inp["B"], inp["C"]
+
+    def run(a):
+        A = np.full((3, N), a, np.float32)
+        return oracle_lib.selective_scan(x, dl, A, B, C, inp["D"], inp["z"], inp["h0"], exact_zoh=True)
+
+    y0, h0l = run(0.0)
+    ys, hsl = run(-1e-6)
+    y1, _ = run(-1.0)
+    # closed form at A = 0: h_t = h0 + sum_{j<=t} Delta_j B_j x_j
+    xd, dd = x.astype(np.float64), dl.astype(np.float64)
+    h = inp["h0"].astype(np.float64)[:, None, :, :] + np.cumsum(
+        (dd * xd)[..., None] * B.astype(np.float64)[:, :, None, :], axis=1)        # (b, L, d, n)
+    v = np.einsum("bldn,bln->bld", h, C.astype(np.float64)) + inp["D"].astype(np.float64) * xd
+    z = inp["z"].astype(np.float64)
+    closed = v * silu(z)
+    assert rel_err(y0, closed) < 1e-13
+    assert rel_err(h0l, h[:, -1]) < 1e-13
+    # continuity: |Delta*A| <= ~0.1 * 1e-6 per step, L = 48 steps
+    assert 0.0 < rel_err(ys, y0) < 1e-5
+    assert rel_err(hsl, h0l) < 1e-5
+    assert rel_err(y1, y0) > 1e-3
 
 
 def test_channels_subset_matches_full(oracle_lib):
