@@ -107,6 +107,7 @@ def selective_scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, *, dy, dh_las
     batch, seqlen, dim = x.shape
     dstate = A.shape[1]
     io = x.dtype
+    io_code = _io_dtype(x)
     f32 = torch.float32
     for t, n, dt, sh in ((x, "x", io, (batch, seqlen, dim)), (delta, "delta", io, (batch, seqlen, dim)),
                          (z, "z", io, (batch, seqlen, dim)), (A, "A", f32, (dim, dstate)),
@@ -114,6 +115,7 @@ def selective_scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, *, dy, dh_las
                          (D, "D", f32, (dim,)), (h0, "h0", f32, (batch, dim, dstate)),
                          (dy, "dy", f32, (batch, seqlen, dim)), (dh_last, "dh_last", f32, (batch, dim, dstate))):
         _need(t, n, dt, sh, dev)
+    _on_device(dev, x=x, delta=delta, z=z, A=A, B=B, C=C, D=D, h0=h0, dy=dy, dh_last=dh_last)
     e = lambda *sh: torch.empty(sh, dtype=f32, device=dev)
     g = dict(dx=e(batch, seqlen, dim), ddelta=e(batch, seqlen, dim), dA=e(dim, dstate), dB=e(batch, seqlen, dstate),
              dC=e(batch, seqlen, dstate))
@@ -123,11 +125,12 @@ def selective_scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, *, dy, dh_las
     wsb = selective_scan_bwd_workspace_size(batch, seqlen, dim, dstate, dev.index or 0)
     if workspace is None:
         workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    wsp, wsn = _workspace(workspace, dev)
     st = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
     rc = selective_scan_bwd_raw(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(dy),
                                 _ptr(dh_last), _ptr(g["dx"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]),
                                 _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["dh0"]), batch, seqlen, dim, dstate,
-                                SSS_BF16 if io == torch.bfloat16 else SSS_F32, _ptr(workspace), workspace.numel(), st)
+                                io_code, wsp, wsn, st)
     if rc != 0:
         raise SSSError(rc, "selective_scan_bwd")
     return g
@@ -145,16 +148,16 @@ def causal_conv1d_fwd(x, weight, bias=None, *, silu=False, out=None, stream=None
     batch, seqlen, dim = x.shape
     width = weight.shape[1]
     io = x.dtype
-    if io not in (torch.float32, torch.bfloat16):
-        raise ValueError("x must be float32 or bfloat16")
+    io_code = _io_dtype(x)
     _need(x, "x", io, (batch, seqlen, dim), dev)
     _need(weight, "weight", torch.float32, (dim, width), dev)
     _need(bias, "bias", torch.float32, (dim,), dev)
     o = out if out is not None else torch.empty((batch, seqlen, dim), dtype=io, device=dev)
     _need(o, "out", io, (batch, seqlen, dim), dev)
+    _on_device(dev, x=x, weight=weight, bias=bias, out=o)
     st = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
-    rc = causal_conv1d_fwd_raw(_ptr(x), _ptr(weight), _ptr(bias), _ptr(o), batch, seqlen, dim, width,
-                               SSS_BF16 if io == torch.bfloat16 else SSS_F32, int(bool(silu)), st)
+    rc = causal_conv1d_fwd_raw(_ptr(x), _ptr(weight), _ptr(bias), _ptr(o), batch, seqlen, dim, width, io_code,
+                               int(bool(silu)), st)
     if rc != 0:
         raise SSSError(rc, "causal_conv1d_fwd")
     return o
@@ -188,17 +191,43 @@ def _ptr(t):
 
 
 def _need(t, name, dtype, shape, device):
-    import torch
+    """dtype, shape and contiguity of one tensor (its device is checked by _on_device once
+    every tensor of the call has passed these): a mismatch raises before any device work."""
     if t is None:
         return
-    if not t.is_cuda or t.device != device:
-        raise ValueError(f"{name} must be on {device}")
     if t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _on_device(device, **tensors):
+    """Every given tensor (None skipped) is on the call's GPU."""
+    for name, t in tensors.items():
+        if t is not None and (not t.is_cuda or t.device != device):
+            raise ValueError(f"{name} must be on a GPU ({device}), got {t.device}")
+
+
+def _io_dtype(x):
+    """x/delta/z dtype code; anything but float32 and bfloat16 is rejected."""
+    import torch
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"x must be float32 or bfloat16, got {x.dtype}")
+    return SSS_BF16 if x.dtype == torch.bfloat16 else SSS_F32
+
+
+def _workspace(ws, device):
+    """(pointer, size in bytes) of a caller-given workspace, checked to be contiguous device
+    memory on the call's device."""
+    if ws is None:
+        return 0, 0
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    if not ws.is_cuda or ws.device != device:
+        raise ValueError(f"workspace must be on {device}")
+    return ws.data_ptr(), ws.numel() * ws.element_size()
 
 
 def selective_scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, return_last=True, out=None,
@@ -223,8 +252,7 @@ def selective_scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, return_las
         batch, seqlen, dim = x.shape
     dstate = A.shape[1]
     io = x.dtype
-    if io not in (torch.float32, torch.bfloat16):
-        raise ValueError("x must be float32 or bfloat16")
+    io_code = _io_dtype(x)
     f32 = torch.float32
     io_shape = (batch, dim, seqlen) if bdl else (batch, seqlen, dim)
     bc_shape = (batch, dstate, seqlen) if bdl else (batch, seqlen, dstate)
@@ -243,15 +271,16 @@ def selective_scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, return_las
     _need(hl, "out_last", f32, (batch, dim, dstate), dev)
     flags = ((SSS_EXACT_ZOH if exact_zoh else 0) | (SSS_DELTA_SOFTPLUS if delta_softplus else 0)
              | (SSS_LAYOUT_BDL if bdl else 0))
+    _need(delta_bias, "delta_bias", f32, (dim,), dev)
+    _on_device(dev, x=x, delta=delta, z=z, A=A, B=B, C=C, D=D, h0=h0, out=y, out_last=hl, delta_bias=delta_bias)
     wsb = selective_scan_fwd_ex_workspace_size(batch, seqlen, dim, dstate, flags, dev.index or 0)
     if workspace is None and wsb > 0:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
-    _need(delta_bias, "delta_bias", f32, (dim,), dev)
+    wsp, wsn = _workspace(workspace, dev)
     st = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
     rc = selective_scan_fwd_ex_raw(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
-                                   _ptr(y), _ptr(hl), _ptr(delta_bias), flags, batch, seqlen, dim, dstate,
-                                   SSS_BF16 if io == torch.bfloat16 else SSS_F32, _ptr(workspace),
-                                   0 if workspace is None else workspace.numel(), st)
+                                   _ptr(y), _ptr(hl), _ptr(delta_bias), flags, batch, seqlen, dim, dstate, io_code,
+                                   wsp, wsn, st)
     if rc != 0:
         raise SSSError(rc, "selective_scan_fwd")
     return (y, hl) if return_last or out_last is not None else y
@@ -266,8 +295,7 @@ def selective_state_update(x, delta, A, B, C, D=None, z=None, *, state, out=None
     batch, dim = x.shape
     dstate = A.shape[1]
     io = x.dtype
-    if io not in (torch.float32, torch.bfloat16):
-        raise ValueError("x must be float32 or bfloat16")
+    io_code = _io_dtype(x)
     f32 = torch.float32
     _need(x, "x", io, (batch, dim), dev)
     _need(delta, "delta", io, (batch, dim), dev)
@@ -279,9 +307,10 @@ def selective_state_update(x, delta, A, B, C, D=None, z=None, *, state, out=None
     _need(state, "state", f32, (batch, dim, dstate), dev)
     y = out if out is not None else torch.empty((batch, dim), dtype=f32, device=dev)
     _need(y, "out", f32, (batch, dim), dev)
+    _on_device(dev, x=x, delta=delta, z=z, A=A, B=B, C=C, D=D, state=state, out=y)
     st = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
     rc = selective_state_update_raw(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(state),
-                                    _ptr(y), batch, dim, dstate, SSS_BF16 if io == torch.bfloat16 else SSS_F32, st)
+                                    _ptr(y), batch, dim, dstate, io_code, st)
     if rc != 0:
         raise SSSError(rc, "selective_state_update")
     return y
@@ -300,12 +329,16 @@ def elementwise_scan(x, A, B, C, h0=None, *, return_last=True, out=None, out_las
     y = out if out is not None else torch.empty((batch, seqlen, dim), dtype=f32, device=dev)
     hl = out_last if out_last is not None else (
         torch.empty((batch, dim), dtype=f32, device=dev) if return_last else None)
+    _need(y, "out", f32, (batch, seqlen, dim), dev)
+    _need(hl, "out_last", f32, (batch, dim), dev)
+    _on_device(dev, x=x, A=A, B=B, C=C, h0=h0, out=y, out_last=hl)
     wsb = elementwise_scan_workspace_size(batch, seqlen, dim, dev.index or 0)
     if workspace is None and wsb > 0:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    wsp, wsn = _workspace(workspace, dev)
     st = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
     rc = elementwise_scan_raw(_ptr(x), _ptr(A), _ptr(B), _ptr(C), _ptr(h0), _ptr(y), _ptr(hl), batch, seqlen, dim,
-                              _ptr(workspace), 0 if workspace is None else workspace.numel(), st)
+                              wsp, wsn, st)
     if rc != 0:
         raise SSSError(rc, "elementwise_scan")
     return (y, hl) if return_last or out_last is not None else y
