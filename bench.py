@@ -14,6 +14,7 @@ once and every output written once, the state never counted) in GB/s.
   python bench.py --conv                  # the causal conv1d front end on the long layer
   python bench.py --backward              # selective_scan_bwd (all gradients) on the default workload
   python bench.py --copy-calibration      # plain copy of a known size, for counter scaling
+  python bench.py --probes                # roofline calibration: HBM stream rates, VALU/exp issue costs
 """
 from __future__ import annotations
 
@@ -160,6 +161,25 @@ def cpu_baseline(cfg, inp, budget_s=12.0):
                       f"{dt:.2f} s wall, {elems / dt:.4g} elements/s"}
 
 
+def copy_ceiling(dev, stream, nbytes=2 << 30, reps=5):
+    """What a plain device-to-device copy (torch's) reaches in this run, in GB/s counting
+    bytes read plus bytes written; buffers far larger than the last-level cache."""
+    import torch
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        b.copy_(a)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
+    del a, b
+    return 2.0 * nbytes / (ms * 1e-3) / 1e9
+
+
 def copy_calibration(nbytes=1 << 30, reps=5):
     """A plain device copy of a known size (for scaling FETCH_SIZE / WRITE_SIZE)."""
     import torch
@@ -169,6 +189,106 @@ def copy_calibration(nbytes=1 << 30, reps=5):
         b.copy_(a)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_each_way": nbytes, "reps": reps}))
+
+
+PROBE_KINDS = {  # main instructions per probe iteration: name, VALU-class count, transcendental count, MFMA count
+    0: ("v_fma_f32", 16, 0, 0), 1: ("v_exp_f32", 0, 16, 0), 2: ("v_mul_f32 (SGPR operand)", 16, 0, 0),
+    3: ("scan step, 16 states: mul, exp, mul, fma", 48 + 2, 16, 0),
+    4: ("scan step + read-out, 16 states: mul, exp, mul, fma, fma", 64 + 2, 16, 0),
+    5: ("kind 3 + 4 independent v_mfma_f32_4x4x1f32", 48 + 2, 16, 4),
+    6: ("v_mfma_f32_4x4x1f32", 0, 0, 16),
+    7: ("v_mul_f32 (VGPR operands)", 16, 0, 0),
+    8: ("kind 4 with B/C rows from LDS (8 broadcast ds_read_b128)", 64 + 2, 16, 0),
+    9: ("role 0: v_exp_f32 / role 1: v_fma_f32 (two roles per SIMD)", 16, 0, 0),
+    10: ("v_fmac_f32 (three VGPR operands)", 16, 0, 0),
+    11: ("role 0: v_exp_f32 / role 1: v_fmac_f32 (two roles per SIMD)", 16, 0, 0),
+    12: ("kind 4 with B/C in one VGPR each, taken through DPP row_newbcast", 64 + 4, 16, 0),
+    13: ("kind 8 in phases per step: 16 mul | 16 exp | 64 VALU", 64 + 2, 16, 0),
+    14: ("kind 4 (SGPR rows) in phases per step: 16 mul | 16 exp | 64 VALU", 64 + 2, 16, 0),
+}
+
+
+def probes(stream_bytes=4 << 30, iters=4000, kinds=None):
+    """Roofline calibration on the GPU (libsss_probes.so): what plain 16-byte-per-lane HBM
+    streams reach (read-only, write-only, copy), and the issue cost of the VALU forms the scan
+    is made of, in shader clocks per wave64 instruction per SIMD, at 1, 2 and 4 resident waves
+    per SIMD (each wave times itself with s_memtime; s_memrealtime gives the clock)."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "selective_state_space_20_amd", "libsss_probes.so")
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with selective_state_space_20_amd.build.build()")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    lib.sss_probe_stream.argtypes = [i32, vp, vp, i64, vp, i32, vp]
+    lib.sss_probe_alu.argtypes = [i32, i32, i32, i32, vp, vp, vp]
+    dev = torch.device("cuda:0")
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    stream = torch.cuda.current_stream(dev)
+    sink = torch.zeros(1, dtype=torch.float32, device=dev)
+    res = {"probe": "roofline calibration", "compute_units": cus, "stream": [], "alu": []}
+    src = torch.ones(stream_bytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for mode, name, moved in ((0, "read", 1), (1, "write", 1), (2, "copy", 2)) if kinds is None else ():
+        best = None
+        for grid in (cus * 4, cus * 8, cus * 16, cus * 32):
+            def run():
+                rc = lib.sss_probe_stream(mode, src.data_ptr(), dst.data_ptr(), stream_bytes, sink.data_ptr(), grid,
+                                          ctypes.c_void_p(stream.cuda_stream))
+                if rc != 0:
+                    raise RuntimeError(f"sss_probe_stream: hip error {rc}")
+            run()
+            torch.cuda.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+            for e0, e1 in ev:
+                e0.record(stream)
+                run()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
+            gbs = moved * stream_bytes / (ms * 1e-3) / 1e9
+            if best is None or gbs > best["GB/s"]:
+                best = {"mode": name, "bytes_per_direction": stream_bytes, "workgroups": grid, "ms": round(ms, 4),
+                        "GB/s": round(gbs, 1), "frac_of_8TB/s": round(gbs / HBM_PEAK_GBS, 4)}
+        res["stream"].append(best)
+        log(f"[probe] {name}: {best['GB/s']} GB/s ({best['workgroups']} workgroups)")
+    del src, dst
+    for kind, (name, valu, trans, mfma) in PROBE_KINDS.items():
+        if kinds is not None and kind not in kinds:
+            continue
+        for w in (1, 2, 4):
+            nwaves = cus * 4 * w
+            out = torch.zeros(3 * nwaves, dtype=torch.int64, device=dev)
+            rc = lib.sss_probe_alu(kind, w, iters, cus, out.data_ptr(), sink.data_ptr(), ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"sss_probe_alu: hip error {rc}")
+            torch.cuda.synchronize()
+            o = out.cpu().numpy().reshape(-1, 3)
+            # the waves of one SIMD share its issue: the SIMD's time is that of its last wave
+            simd = (o[:, 2] >> 4) & 3
+            per_simd = np.bincount(simd, minlength=4)
+            clk = float(np.max(o[:, 0]))
+            slot = (o[:, 2] & 15)
+            ghz = float(np.median(o[:, 0] / (o[:, 1] / 1e8) / 1e9))
+            per_iter = clk / (iters * w)       # shader clocks per SIMD per loop iteration
+            main = max(valu + trans + mfma, 1)
+            rec = {"kind": kind, "form": name, "waves_per_simd": w, "clk_per_iteration_per_simd": round(per_iter, 2),
+                   "clk_per_main_instruction": round(per_iter / main if kind in (0, 1, 2, 6, 7, 10) else per_iter / 16, 3),
+                   "clock_GHz": round(ghz, 3), "waves_per_simd_id": per_simd.tolist(),
+                   "median_over_max_wave_clk": round(float(np.median(o[:, 0])) / clk, 3)}
+            if kind in (3, 4, 5, 8, 12, 13, 14):
+                rec["note"] = "clk_per_main_instruction is clocks per state-step (16 per iteration)"
+            if kind in (9, 11) and w > 1:
+                # each wave's own clocks by role (the waves of one role issue 16 instructions per
+                # iteration; the SIMD holds w/2 waves of each role)
+                wid = np.arange(o.shape[0]) % (4 * w)
+                role = (wid // 4) & 1
+                rec["max_clk_by_role"] = [float(np.max(o[role == r, 0])) for r in (0, 1)]
+                rec["note"] = ("role 0 exp, role 1 fma/fmac: if the roles co-issue, the SIMD time is the longer "
+                               "role's alone, not their sum")
+            res["alu"].append(rec)
+            log(f"[probe] kind {kind} ({name}) w={w}: {per_iter:.1f} clk/iteration/SIMD, {ghz:.3f} GHz")
+    print(json.dumps(res), flush=True)
 
 
 def bench_decode(batch, steps, warmup, dim=5120, dstate=16, flush=True):
@@ -225,7 +345,7 @@ def bench_decode(batch, steps, warmup, dim=5120, dstate=16, flush=True):
         "metric": "selective_state_update (one decode step) achieved HBM GB/s, 1 GPU", "value": round(gbs, 2),
         "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": round(mean_ms if flush else wall * 1e3 / steps, 5),
-        "higher_is_better": True, "dtype": "f32", "data": "synthetic",
+        "higher_is_better": True, "dtype": "f32", "io_dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"decode_bf16_b{batch}_D{dim}_N{dstate}", "batch": batch, "dim": dim, "dstate": dstate,
                    "algorithmic_bytes": nbytes, "caches_flushed_between_calls": flush},
         "tokens_per_s": round(batch / (mean_ms * 1e-3), 1),
@@ -266,7 +386,7 @@ def bench_conv(steps, warmup, batch=1, seqlen=65536, dim=5120, width=4):
     print(json.dumps({
         "metric": "causal_conv1d_fwd achieved HBM GB/s, 1 GPU", "value": round(gbs, 2), "unit": "GB/s",
         "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(mean_ms, 5), "higher_is_better": True,
-        "dtype": "f32", "data": "synthetic",
+        "dtype": "f32", "io_dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"conv1d_bf16_b{batch}_L{seqlen}_D{dim}_W{width}_silu", "algorithmic_bytes": nbytes},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("conv"), "kernel": "conv1d_kernel",
@@ -323,7 +443,7 @@ def bench_backward(steps, warmup):
     print(json.dumps({
         "metric": "selective_scan_bwd achieved HBM GB/s and elements/s, 1 GPU", "value": round(gbs, 2), "unit": "GB/s",
         "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(mean_ms, 5), "higher_is_better": True,
-        "dtype": "f32", "data": "synthetic",
+        "dtype": "f32", "io_dtype": "bf16", "data": "synthetic",
         "config": {"workload": "backward_" + cfg["name"], "algorithmic_bytes": nbytes, "elements": e},
         "elements_per_s": round(e / (mean_ms * 1e-3), 1),
         "roofline": {"bound": "alu", "achieved": round(alu_tflops, 3), "peak": VALU_FP32_TFLOPS, "unit": "TFLOP/s",
@@ -342,12 +462,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--probes", action="store_true", help="roofline calibration probes (HBM streams, VALU issue)")
+    ap.add_argument("--probe-kinds", type=str, default="", help="comma-separated ALU probe kinds only (no streams)")
     ap.add_argument("--workload", type=int, default=WORKLOAD_INDEX, help="configuration index 0..4")
     ap.add_argument("--conv", action="store_true", help="time the causal conv1d front end instead")
     ap.add_argument("--backward", action="store_true", help="time selective_scan_bwd on the default workload")
     ap.add_argument("--decode", type=int, default=0, metavar="BATCH",
                     help="time one decode step (selective_state_update) of BATCH tokens instead")
-    ap.add_argument("--no-flush", action="store_true", help="decode: do not evict the caches between calls")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="do not scrub the last-level cache between calls (decode, and workloads that fit it)")
     ap.add_argument("--delta-softplus", action="store_true",
                     help="selective: time the softplus front end (the stored delta taken as the raw step)")
     ap.add_argument("--exact-zoh", action="store_true", help="selective: time the exact zero-order-hold option")
@@ -361,6 +484,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.probes:
+        probes(kinds=[int(k) for k in args.probe_kinds.split(",")] if args.probe_kinds else None)
         return
     if args.conv:
         bench_conv(args.steps, args.warmup)
@@ -427,10 +553,18 @@ def main():
         step()
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} done")
+    # A workload whose footprint is within reach of the 256 MB last-level cache (the
+    # medium layer: 254.6 MB) is timed with that cache scrubbed before every call, so that
+    # each call reads its inputs from HBM; the long layers (3.4 and 21.5 GB) are not.
+    nbytes = algorithmic_bytes(cfg)
+    flush = nbytes < FLUSH_BYTES and not args.no_flush
+    scrub = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev) if flush else None
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for e0, e1 in ev:
+        if scrub is not None:
+            scrub.zero_()
         e0.record(stream)
         step()
         e1.record(stream)
@@ -438,11 +572,15 @@ def main():
     wall = time.perf_counter() - t_start
     per_call_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
     mean_ms = float(np.mean(per_call_ms))
-    ms_per_step = wall * 1e3 / args.steps
-    log(f"[bench] {args.steps} steps: wall {ms_per_step:.4f} ms/step, event mean {mean_ms:.4f} ms, "
-        f"min {min(per_call_ms):.4f}, max {max(per_call_ms):.4f}")
+    # with scrubs between calls the wall clock also holds the scrubs: the step time is then
+    # the calls' own (HIP events around each call on its stream)
+    ms_per_step = mean_ms if flush else wall * 1e3 / args.steps
+    log(f"[bench] {args.steps} steps: wall {wall * 1e3 / args.steps:.4f} ms/step, event mean {mean_ms:.4f} ms, "
+        f"median {float(np.median(per_call_ms)):.4f}, min {min(per_call_ms):.4f}, max {max(per_call_ms):.4f}, "
+        f"last-level cache scrubbed between calls: {flush}")
+    copy_gbs = copy_ceiling(dev, stream)
+    log(f"[bench] plain device copy in the same run: {copy_gbs:.1f} GB/s")
 
-    nbytes = algorithmic_bytes(cfg)
     elems = b * L * d
     gbs_wall = nbytes / (ms_per_step * 1e-3) / 1e9
     gbs_call = nbytes / (mean_ms * 1e-3) / 1e9
@@ -482,6 +620,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
+        "io_dtype": cfg.get("io", "f32"),
         "data": "synthetic",
         "config": {"workload": cfg["name"], "batch": b, "seqlen": L, "dim": d, "dstate": n if selective else None,
                    "io_dtype": cfg.get("io", "f32"), "z_gate": cfg.get("with_z", False),
@@ -489,6 +628,11 @@ def main():
                    "algorithmic_bytes": nbytes, "elements": elems},
         "elements_per_s": round(elems / (ms_per_step * 1e-3), 1),
         "pct_hbm_peak": round(100.0 * gbs_wall / HBM_PEAK_GBS, 2),
+        "copy_ceiling_GBs": round(copy_gbs, 1),
+        "pct_of_copy_ceiling": round(100.0 * gbs_wall / copy_gbs, 2),
+        "call_ms": {"mean": round(mean_ms, 5), "median": round(float(np.median(per_call_ms)), 5),
+                    "min": round(min(per_call_ms), 5), "max": round(max(per_call_ms), 5)},
+        "llc_scrubbed_between_calls": flush,
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:

@@ -16,6 +16,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsss.so")
+# roofline calibration kernels (bench.py --probes only): a library of their own, so that
+# libsss.so exports exactly the C ABI of include/sss.h
+PROBE_SRC = os.path.join(CSRC, "probes", "roofline_probes.hip")
+PROBE_LIB = os.path.join(PKG, "libsss_probes.so")
 ARCH = "gfx950"
 STATE_COUNTS = (1, 2, 4, 8, 16, 32, 64)
 
@@ -58,8 +62,12 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
     work = compile_jobs()
     cmds = [["hipcc", *FLAGS, *extra, *inc, "-c", src, "-o", obj] for obj, extra, src in work]
     workers = jobs or max(1, min(len(cmds), os.cpu_count() or 1, 16))
+    probe_cmd = ["hipcc", *FLAGS, "-shared", PROBE_SRC, "-o", PROBE_LIB + ".tmp"]
     with ThreadPoolExecutor(max_workers=workers) as ex:
+        probe_job = ex.submit(_run, probe_cmd)
         results = list(ex.map(_run, cmds))
+        results.append(probe_job.result())
+    cmds.append(probe_cmd)
     for cmd, (rc, msg) in zip(cmds, results):
         if verbose:
             print(" ".join(cmd))
@@ -67,6 +75,7 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
             raise RuntimeError(f"hipcc failed ({rc}): {' '.join(cmd)}\n{msg}")
         if msg.strip() and verbose:
             print(msg)
+    os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
     tmp = LIB + ".tmp"
     rc, msg = _run(["hipcc", "-shared", "-fPIC", f"--offload-arch={ARCH}", *[obj for obj, _, _ in work], "-o", tmp])
     if rc != 0:
