@@ -49,6 +49,19 @@ constexpr int min_waves_of(int ns, int fl) {
 constexpr int kStreamPolicy = 2;    // buffer cache policy of streamed x/delta/z/y: non-temporal
 constexpr int kTileBytes = 64;      // channel-major tiles: bytes of each row per tile
 
+// Time-major rows of B and C (4, 8 or 16 states) reach the VALU from VGPRs, not SGPRs: a
+// VALU instruction with a scalar operand never pairs with another wave's instruction in the
+// same issue cycle, one with vector operands only does (measured on gfx950).  Each wave
+// stages 1 KB of B rows (and of C rows in pass 2) in its own LDS tile, double-buffered, and
+// every step reads its rows with broadcast ds_read_b128 (all lanes one address).
+// (Not for the exact hold, whose extra per-state registers would spill in this form, nor for
+// channel-major rows, which stage x/delta/z in LDS instead.)
+constexpr bool lds_rows(int ns, int fl) { return (fl & 9) == 0 && (ns == 4 || ns == 8 || ns == 16); }
+constexpr int kRowTileBytes = 1024;  // per tensor: 256 / N steps of N fp32 states
+constexpr int ilog2_const(int v) { return v <= 1 ? 0 : 1 + ilog2_const(v / 2); }
+// LDS bytes per wave of the row tiles: two buffers of B (pass 1 and 3) or of B and C (pass 2)
+constexpr int row_tile_lds(int pass) { return 2 * (pass == 2 ? 2 : 1) * kRowTileBytes; }
+
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // bit casts through by-value arguments: __builtin_bit_cast applied directly to an element of
@@ -116,8 +129,14 @@ struct SelSeg {
 //     instead of (batch, seqlen, dim): each lane then walks its own row, loading 16 bytes
 //     (8 bf16 / 4 fp32 steps) and storing 4 fp32 outputs per access where the rows are
 //     16-byte aligned (g.vec), else one step per access.  B/C arrive time-major either way.
+// fp32 inputs in the pass-2 form with LDS rows keep more values in flight: 3 waves per SIMD
+constexpr int min_waves_sel(int ns, int fl, bool bf16, int pass) {
+  return (!bf16 && pass == 2 && (fl & 9) == 0 && (ns == 4 || ns == 8 || ns == 16) && min_waves_of(ns, fl) > 3)
+             ? 3 : min_waves_of(ns, fl);
+}
+
 template <int NS, bool BF16, int PASS, bool HAS_Z, int FL>
-__global__ __launch_bounds__(256, min_waves_of(NS, FL)) void sel_seq_kernel(const void* __restrict__ x, const void* __restrict__ delta,
+__global__ __launch_bounds__(256, min_waves_sel(NS, FL, BF16, PASS)) void sel_seq_kernel(const void* __restrict__ x, const void* __restrict__ delta,
                                                      const float* __restrict__ A, const float* __restrict__ Bm,
                                                      const float* __restrict__ Cm, const float* __restrict__ Dsk,
                                                      const void* __restrict__ z, const float* __restrict__ h0,
@@ -200,6 +219,34 @@ __global__ __launch_bounds__(256, min_waves_of(NS, FL)) void sel_seq_kernel(cons
   const float* Br = Bm + row0 * N;
   const float* Cr = Cm + row0 * N;
 
+  // B/C row tiles (time-major, 4/8/16 states): tile j holds segment steps [j*kRT, (j+1)*kRT),
+  // one 16-byte piece per lane; loads past the end of the sequence go through descriptors
+  // whose range stops there (the hardware returns zeros for them).  Each piece covers whole
+  // rows or whole quarters of a row, so the range check never splits a row.
+  constexpr bool kRows = lds_rows(NS, FL);
+  constexpr int kRT = kRows ? kRowTileBytes / (4 * NS) : 1;  // steps per row tile
+  constexpr int kRTShift = ilog2_const(kRT);
+  constexpr int kRowTensors = PASS == 2 ? 2 : 1;
+  extern __shared__ uint32_t sss_lds[];  // dynamic LDS: the row tiles or the channel-major tiles
+  float* const lrows = reinterpret_cast<float*>(sss_lds) + wave * (row_tile_lds(PASS) / 4);  // [buf][tensor][256]
+  const int64_t row_bytes_rem = (g.L - tbeg) * N * 4;  // rows of B/C from this segment to the end
+  const uint32_t row_bytes_left = row_bytes_rem < 0x7FFFFFF0 ? (uint32_t)row_bytes_rem : 0x7FFFFFF0u;
+  const __amdgpu_buffer_rsrc_t rrb = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(Br), 0, (int)row_bytes_left, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(Cr), 0, (int)row_bytes_left, 0x00020000);
+  u32x4 grb = {0u, 0u, 0u, 0u}, grc = {0u, 0u, 0u, 0u};
+  auto rows_load = [&](int j) {  // row tile j -> registers
+    if constexpr (kRows) {
+      grb = __builtin_amdgcn_raw_buffer_load_b128(rrb, lane * 16, j * kRowTileBytes, 0);
+      if constexpr (PASS == 2) grc = __builtin_amdgcn_raw_buffer_load_b128(rrc, lane * 16, j * kRowTileBytes, 0);
+    }
+  };
+  auto rows_store = [&](int buf) {  // registers -> LDS buffer buf
+    if constexpr (kRows) {
+      *reinterpret_cast<u32x4*>(lrows + buf * (kRowTensors * 256) + lane * 4) = grb;
+      if constexpr (PASS == 2) *reinterpret_cast<u32x4*>(lrows + buf * (kRowTensors * 256) + 256 + lane * 4) = grc;
+    }
+  };
+
   // steps per load batch: 2 time-major steps, or one 16-byte piece of a channel-major row
   constexpr int U = bdl ? 16 / ES : kStepsPerBatch;
   constexpr int QW = bdl ? 4 : U;  // raw dwords per tensor and batch
@@ -250,7 +297,7 @@ __global__ __launch_bounds__(256, min_waves_of(NS, FL)) void sel_seq_kernel(cons
   // bank line), so that the lanes' 16-byte reads of one batch fall in distinct banks.
   constexpr int kNT = has_z ? 3 : 2;  // tensors staged: x, delta (, z)
   constexpr int kPieces = 4;          // 16-byte pieces per lane, tensor and tile
-  extern __shared__ uint32_t sss_lds[];  // [wave][tensor][64 rows][16 dwords]
+  // channel-major tiles in the same dynamic LDS: [wave][tensor][64 rows][16 dwords]
   uint32_t* const ltile = sss_lds + wave * (kNT * 64 * 16);
   uint32_t gq[kNT][kPieces][4];
   uint32_t gvo[kPieces];  // lane's byte offset of piece i: row 16 i + lane / 4, chunk lane % 4
@@ -401,6 +448,74 @@ __global__ __launch_bounds__(256, min_waves_of(NS, FL)) void sel_seq_kernel(cons
     }                                                                            \
   } while (0)
 
+  // One step at segment-relative time t with B/C rows from the LDS tile, each group of
+  // states in three phases separated by scheduling barriers that only memory and scalar
+  // instructions may cross: the exponent arguments, the exps, then the multiplies and fmas
+  // of the update and read-out.  Grouped like this, the VGPR-only instructions of one wave meet those of
+  // another more often and issue in pairs (measured: the per-state cost of the pass-2
+  // pattern drops from ~24 to ~21 clocks).
+  auto lstep = [&](const uint32_t (&xs)[QW], const uint32_t (&dqs)[QW], const uint32_t (&zs)[QW], int i, int t) {
+    if constexpr (kRows) {
+      const float* brow = lrows + ((t >> kRTShift) & 1) * (kRowTensors * 256) + (t & (kRT - 1)) * NS;
+      if (PASS == 3 && (t & kmask) == 0) {
+        /* checkpoint j = t >> kshift: [s][b][grp][j][n][lane] */
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(
+            seg_state + ((((int64_t)s * g.batch + b) * g.ngroups + grp) * g.nsub + (t >> g.kshift)) * N * 64);
+#pragma unroll
+        for (int n = 0; n < NS; ++n)
+          __builtin_amdgcn_raw_buffer_store_b32(f32_as_u32(h[n]), rk, lane * 4, n * 256, kStreamPolicy);
+      }
+      const float xv = val(xs, i);
+      const float dl = step_size<FL>(val(dqs, i), dbv);
+      const float dx = dl * xv;
+      float y0 = Dd * xv, y1 = 0.0f;
+      // states in groups of GS (the phases of one group hold GS arguments, GS decays and GS
+      // rows of B and C in registers)
+      constexpr int GS = NS < 8 ? NS : (BF16 && PASS != 2 ? 8 : 4);  // pass 2 and fp32 inputs hold more registers
+#pragma unroll
+      for (int n0 = 0; n0 < NS; n0 += GS) {
+        float bq[GS], cq[PASS == 2 ? GS : 1];
+#pragma unroll
+        for (int q = 0; q < GS / 4; ++q) {
+          const float4 v = reinterpret_cast<const float4*>(brow + n0)[q];
+          bq[4 * q] = v.x; bq[4 * q + 1] = v.y; bq[4 * q + 2] = v.z; bq[4 * q + 3] = v.w;
+          if constexpr (PASS == 2) {
+            const float4 c = reinterpret_cast<const float4*>(brow + 256 + n0)[q];
+            cq[4 * q] = c.x; cq[4 * q + 1] = c.y; cq[4 * q + 2] = c.z; cq[4 * q + 3] = c.w;
+          }
+        }
+        float arg[GS], ab[GS];
+#pragma unroll
+        for (int k = 0; k < GS; ++k) arg[k] = dl * a2[n0 + k];
+        __builtin_amdgcn_sched_barrier(0x14);
+#pragma unroll
+        for (int k = 0; k < GS; ++k) ab[k] = fast_exp2(arg[k]);
+        __builtin_amdgcn_sched_barrier(0x14);
+#pragma unroll
+        for (int k = 0; k < GS; ++k) {
+          const int n = n0 + k;
+          if constexpr (zoh) {
+            h[n] = __builtin_fmaf(ab[k], h[n], zoh_coef(arg[k], ab[k], dl, ia[n]) * (xv * bq[k]));
+          } else {
+            h[n] = __builtin_fmaf(ab[k], h[n], dx * bq[k]);
+          }
+          if constexpr (PASS == 2) {
+            if (n & 1) y1 = __builtin_fmaf(cq[k], h[n], y1);
+            else y0 = __builtin_fmaf(cq[k], h[n], y0);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0x14);
+      }
+      if constexpr (PASS == 1) {
+        dsum += dl;
+      } else if constexpr (PASS == 2) {
+        float out = y0 + y1;
+        if constexpr (has_z) out *= silu(val(zs, i));
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, out), ry, (int)yvo, t * ystride, kYPolicy);
+      }
+    }
+  };
+
   int t0 = 0;
   if constexpr (kTiles) {
     // Channel-major tiles (len is a multiple of the tile): one tile per iteration, its
@@ -512,6 +627,48 @@ __global__ __launch_bounds__(256, min_waves_of(NS, FL)) void sel_seq_kernel(cons
 #undef SSS_TILE_READ
   }
   if (!tiled) SSS_LOAD_BATCH(0, 0);
+  if constexpr (kRows) {
+    // row tile 0 in LDS, tile 1 in flight
+    rows_load(0);
+    rows_store(0);
+    rows_load(1);
+    // whole row tiles: kRT steps per iteration, then the next tile (loaded a whole tile
+    // earlier) goes to the other buffer and the one after it is loaded
+    for (; t0 + kRT <= len; t0 += kRT) {
+#pragma unroll
+      for (int q = 0; q < kRT; q += 2 * U) {
+        SSS_LOAD_BATCH(1, t0 + q + U);
+#pragma unroll
+        for (int i = 0; i < U; ++i) lstep(xq[0], dq[0], zq[0], i, t0 + q + i);
+        SSS_LOAD_BATCH(0, t0 + q + 2 * U);
+#pragma unroll
+        for (int i = 0; i < U; ++i) lstep(xq[1], dq[1], zq[1], i, t0 + q + U + i);
+      }
+      rows_store(((t0 >> kRTShift) + 1) & 1);
+      rows_load((t0 >> kRTShift) + 2);
+    }
+    // fewer than kRT steps left, all in the tile now in LDS
+    for (; t0 + 2 * U <= len; t0 += 2 * U) {
+      SSS_LOAD_BATCH(1, t0 + U);
+#pragma unroll
+      for (int i = 0; i < U; ++i) lstep(xq[0], dq[0], zq[0], i, t0 + i);
+      SSS_LOAD_BATCH(0, t0 + 2 * U);
+#pragma unroll
+      for (int i = 0; i < U; ++i) lstep(xq[1], dq[1], zq[1], i, t0 + U + i);
+    }
+    if (t0 < len) {
+      SSS_LOAD_BATCH(1, t0 + U);
+#pragma unroll
+      for (int i = 0; i < U; ++i)
+        if (t0 + i < len) lstep(xq[0], dq[0], zq[0], i, t0 + i);
+      if (t0 + U < len) {
+#pragma unroll
+        for (int i = 0; i < U; ++i)
+          if (t0 + U + i < len) lstep(xq[1], dq[1], zq[1], i, t0 + U + i);
+      }
+    }
+    t0 = len;
+  }
   // full blocks of 2U steps: straight-line code, no per-step branches
   for (; t0 + 2 * U <= len; t0 += 2 * U) {
     SSS_LOAD_BATCH(1, t0 + U);
@@ -639,7 +796,8 @@ static hipError_t run_states(const SelArgs& a, const SelPlan& pl, hipStream_t st
   float* st = reinterpret_cast<float*>(ws + pl.ws_state);
   float* ds = reinterpret_cast<float*>(ws + pl.ws_dsum);
   const int64_t per_seg = (int64_t)g.nblk * g.batch;
-  const size_t lds1 = g.vec == 2 ? (size_t)g.gpb * 2 * 64 * kTileBytes : 0;  // x, delta tiles
+  const size_t lds1 = g.vec == 2 ? (size_t)g.gpb * 2 * 64 * kTileBytes  // x, delta tiles
+                                  : lds_rows(NS, FL) ? (size_t)g.gpb * row_tile_lds(1) : 0;  // B row tiles
   hipLaunchKernelGGL((sel_seq_kernel<NS, BF16, 1, false, FL>), dim3((unsigned)(per_seg * (pl.segments - 1))),
                      dim3(64u * (unsigned)g.gpb), lds1, stream, a.x, a.delta, a.A, a.B, a.C, a.Dsk, a.z, a.h0,
                      (const float*)nullptr, a.y, a.h_last, st, ds, a.delta_bias, g);
@@ -660,7 +818,8 @@ static hipError_t run_selective(const SelArgs& a, const SelPlan& pl, hipStream_t
   const float* st = pl.segments > 1 ? reinterpret_cast<const float*>(ws + pl.ws_state) : nullptr;
   const int64_t per_seg = (int64_t)g.nblk * g.batch;
   const dim3 grid((unsigned)(per_seg * pl.segments)), block(64u * (unsigned)g.gpb);
-  const size_t lds2 = g.vec == 2 ? (size_t)g.gpb * (a.z != nullptr ? 3 : 2) * 64 * kTileBytes : 0;
+  const size_t lds2 = g.vec == 2 ? (size_t)g.gpb * (a.z != nullptr ? 3 : 2) * 64 * kTileBytes
+                                  : lds_rows(NS, FL) ? (size_t)g.gpb * row_tile_lds(2) : 0;  // B, C row tiles
   if (a.z != nullptr)
     hipLaunchKernelGGL((sel_seq_kernel<NS, BF16, 2, true, FL>), grid, block, lds2, stream, a.x, a.delta, a.A, a.B, a.C,
                        a.Dsk, a.z, a.h0, st, a.y, a.h_last, (float*)nullptr, (float*)nullptr, a.delta_bias, g);
@@ -687,8 +846,9 @@ hipError_t run_checkpoints(const SelArgs& a, const SelPlan& pl, float* ckpt, int
   unsigned char* ws = static_cast<unsigned char*>(a.workspace);
   const float* st = pl.segments > 1 ? reinterpret_cast<const float*>(ws + pl.ws_state) : nullptr;
   const int64_t per_seg = (int64_t)g.nblk * g.batch;
+  const size_t lds3 = lds_rows(NS, 0) ? (size_t)g.gpb * row_tile_lds(3) : 0;  // B row tiles
   hipLaunchKernelGGL((sel_seq_kernel<NS, BF16, 3, false, 0>), dim3((unsigned)(per_seg * pl.segments)),
-                     dim3(64u * (unsigned)g.gpb), 0, stream, a.x, a.delta, a.A, a.B, a.C, a.Dsk, a.z, a.h0, st,
+                     dim3(64u * (unsigned)g.gpb), lds3, stream, a.x, a.delta, a.A, a.B, a.C, a.Dsk, a.z, a.h0, st,
                      (float*)nullptr, (float*)nullptr, ckpt, (float*)nullptr, (const float*)nullptr, g);
   return hipGetLastError();
 }

@@ -69,6 +69,27 @@ def test_selective_two_pass_forced(oracle_lib, monkeypatch, segments):
     _check_sel(oracle_lib, inp, f"S={segments}")
 
 
+ROW_CASES = [  # (batch, seqlen, dim, dstate, io, forced segments): B/C rows staged through LDS tiles
+    (1, 4099, 70, 4, "bf16", 0),    # 64-step tiles, a ragged last tile, tiles past the sequence end
+    (2, 517, 130, 16, "f32", 3),    # 16-step tiles; segments of 174 steps end inside a tile
+    (1, 1601, 257, 8, "f32", 5),    # 32-step tiles, ragged channel group
+    (3, 45, 64, 16, "bf16", 1),     # one segment: two whole tiles and 13 steps
+    (1, 18, 5, 16, "bf16", 2),      # segments of 10 and 8 steps, inside one tile
+]
+
+
+@pytest.mark.parametrize("case", ROW_CASES, ids=[f"B{c[0]}L{c[1]}D{c[2]}N{c[3]}{c[4]}S{c[5]}" for c in ROW_CASES])
+def test_selective_row_tiles(oracle_lib, monkeypatch, case):
+    """Time-major B/C rows through the per-wave LDS tiles (4, 8 and 16 states), with whole
+    and partial tiles, segment ends inside a tile and tile loads past the end of the sequence."""
+    bt, L, dm, n, io, S = case
+    if S:
+        monkeypatch.setenv("SSS_FORCE_SEGMENTS", str(S))
+    inp = gen.selective_inputs(bt, L, dm, n, io=io, with_z=True, with_D=True, h0=True,
+                               seed=zlib.crc32(repr(case).encode()) % 100000)
+    _check_sel(oracle_lib, inp, f"rows S={S}")
+
+
 def test_selective_special_values(oracle_lib):
     """A = 0 (no decay: long carries), A = -inf (memoryless), z = 0 (gate closes)."""
     inp = gen.selective_inputs(2, 3000, 8, 16, io="f32", with_z=False, with_D=True, h0=True, seed=61)
