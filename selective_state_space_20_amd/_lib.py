@@ -35,11 +35,16 @@ _lib = None
 
 
 def load() -> ctypes.CDLL:
-    """Load libsss.so (raises if it has not been built)."""
+    """Load libsss.so (raises if it has not been built).
+
+    torch is imported first: it ships its own HIP runtime, and libsss.so must bind to that
+    same runtime.  Loaded first, the library would pull in the system ROCm's runtime and the
+    process would hold two, of which torch's then finds no GPU."""
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with selective_state_space_20_amd.build.build()")
+        import torch  # noqa: F401  (see above: one HIP runtime per process)
         lib = ctypes.CDLL(LIB_PATH)
         vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
         lib.selective_scan_fwd.argtypes = [vp] * 10 + [i64] * 4 + [i32, vp, sz, vp]
