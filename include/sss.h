@@ -183,6 +183,27 @@ int elementwise_scan(const float* x, const float* A, const float* B, const float
                      float* h_last, int64_t batch, int64_t seqlen, int64_t dim, void* workspace,
                      size_t workspace_bytes, sss_stream_t stream);
 
+/* Scratch bytes of selective_scan_fwd_noalloc (a device array held by every GPU the library
+ * runs on, until the process ends). */
+#define SSS_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
+
+/* selective_scan_fwd for callers that cannot allocate device memory: code being captured into
+ * a HIP graph, tight serving loops, harnesses that forbid hipMalloc.  Same arguments, layouts,
+ * results and errors as selective_scan_fwd, without the workspace: the call's scratch (the
+ * segment states of the time split) lives in a file-scope device array of
+ * SSS_NOALLOC_SCRATCH_BYTES per GPU, and the call allocates nothing (no hipMalloc, no
+ * allocating library routine).  The launch plan is sized to that array (fewer time segments
+ * where the usual plan would need more scratch; a single segment needs none, so no valid shape
+ * is refused for its size), so results may differ from selective_scan_fwd's by rounding order.
+ * All calls on one GPU share its array: calls that may overlap on one GPU (other streams or
+ * host threads) race, and the caller must order them.  The array keeps the last call's
+ * contents; nothing in it needs clearing.  Returns an sss_status (SSS_ERR_HIP if the array's
+ * address cannot be obtained on the current device). */
+int selective_scan_fwd_noalloc(const void* x, const void* delta, const float* A, const float* B, const float* C,
+                               const float* D_skip, const void* z, const float* h0, float* y, float* h_last,
+                               int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
+                               sss_stream_t stream);
+
 /* Human-readable name of a status code (static string). */
 const char* sss_status_string(int status);
 

@@ -22,7 +22,8 @@ SSS_EXACT_ZOH, SSS_DELTA_SOFTPLUS, SSS_LAYOUT_BDL = 1, 2, 4
 EXPORTED = ("selective_scan_fwd", "selective_scan_fwd_ex", "selective_scan_fwd_workspace_size",
             "selective_scan_fwd_ex_workspace_size", "selective_state_update",
             "causal_conv1d_fwd", "selective_scan_bwd", "selective_scan_bwd_workspace_size",
-            "elementwise_scan", "elementwise_scan_workspace_size", "sss_status_string")
+            "elementwise_scan", "elementwise_scan_workspace_size", "sss_status_string",
+            "selective_scan_fwd_noalloc")
 
 
 class SSSError(RuntimeError):
@@ -67,6 +68,8 @@ def load() -> ctypes.CDLL:
         lib.elementwise_scan.restype = i32
         lib.elementwise_scan_workspace_size.argtypes = [i64] * 3 + [i32]
         lib.elementwise_scan_workspace_size.restype = sz
+        lib.selective_scan_fwd_noalloc.argtypes = [vp] * 10 + [i64] * 4 + [i32, vp]
+        lib.selective_scan_fwd_noalloc.restype = i32
         lib.sss_status_string.argtypes = [i32]
         lib.sss_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -83,6 +86,13 @@ def selective_scan_fwd_raw(x, delta, A, B, C, D_skip, z, h0, y, h_last, batch, s
     """Direct call of the C function with integer pointers (0 = NULL)."""
     return load().selective_scan_fwd(x, delta, A, B, C, D_skip, z, h0, y, h_last, batch, seqlen, dim, dstate,
                                      io_dtype, workspace, workspace_bytes, stream)
+
+
+def selective_scan_fwd_noalloc_raw(x, delta, A, B, C, D_skip, z, h0, y, h_last, batch, seqlen, dim, dstate, io_dtype,
+                                   stream) -> int:
+    """selective_scan_fwd_noalloc: no workspace (the library's per-GPU scratch array)."""
+    return load().selective_scan_fwd_noalloc(x, delta, A, B, C, D_skip, z, h0, y, h_last, batch, seqlen, dim, dstate,
+                                             io_dtype, stream)
 
 
 def selective_scan_fwd_ex_raw(x, delta, A, B, C, D_skip, z, h0, y, h_last, delta_bias, flags, batch, seqlen, dim,

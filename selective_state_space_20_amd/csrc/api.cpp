@@ -128,11 +128,16 @@ int selective_scan_fwd(const void* x, const void* delta, const float* A, const f
                                io_dtype, workspace, workspace_bytes, stream);
 }
 
-int selective_scan_fwd_ex(const void* x, const void* delta, const float* A, const float* B, const float* C,
-                          const float* D_skip, const void* z, const float* h0, float* y, float* h_last,
-                          const float* delta_bias, unsigned flags, int64_t batch, int64_t seqlen, int64_t dim,
-                          int64_t dstate, int io_dtype, void* workspace, size_t workspace_bytes,
-                          sss_stream_t stream) {
+}  // extern "C"
+
+namespace sss {
+// Validation, planning and launch of the forward call.  max_ws > 0 limits the plan's
+// workspace to max_ws bytes (fewer time segments when the usual plan needs more).
+int sel_fwd_impl(const void* x, const void* delta, const float* A, const float* B, const float* C,
+                 const float* D_skip, const void* z, const float* h0, float* y, float* h_last,
+                 const float* delta_bias, unsigned flags, int64_t batch, int64_t seqlen, int64_t dim,
+                 int64_t dstate, int io_dtype, void* workspace, size_t workspace_bytes, size_t max_ws,
+                 void* stream) {
   if (!x || !delta || !A || !B || !C || !y) return SSS_ERR_NULL_ARG;
   int st = sel_dims_ok(batch, seqlen, dim, dstate);
   if (st != SSS_OK) return st;
@@ -156,7 +161,7 @@ int selective_scan_fwd_ex(const void* x, const void* delta, const float* A, cons
   if (overlap(y, y_bytes, h_last, hl_bytes)) return SSS_ERR_ALIAS;
   const int cus = current_device_cus();
   if (cus <= 0) return SSS_ERR_HIP;
-  const SelPlan pl = plan_selective(batch, seqlen, dim, dstate, cus, bdl);
+  const SelPlan pl = plan_selective(batch, seqlen, dim, dstate, cus, bdl, max_ws);
   // threads of the widest launch: 64 per channel group (padded to whole workgroups of 4)
   // and segment; must fit a 1-D grid
   const int64_t wg_groups = ((dim + 63) / 64 + 3) / 4 * 4;
@@ -201,6 +206,19 @@ int selective_scan_fwd_ex(const void* x, const void* delta, const float* A, cons
   hipError_t e = launch_selective(a, pl, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? SSS_OK : SSS_ERR_HIP;
 }
+}  // namespace sss
+
+extern "C" {
+
+int selective_scan_fwd_ex(const void* x, const void* delta, const float* A, const float* B, const float* C,
+                          const float* D_skip, const void* z, const float* h0, float* y, float* h_last,
+                          const float* delta_bias, unsigned flags, int64_t batch, int64_t seqlen, int64_t dim,
+                          int64_t dstate, int io_dtype, void* workspace, size_t workspace_bytes,
+                          sss_stream_t stream) {
+  return sel_fwd_impl(x, delta, A, B, C, D_skip, z, h0, y, h_last, delta_bias, flags, batch, seqlen, dim, dstate,
+                      io_dtype, workspace, workspace_bytes, 0, stream);
+}
+
 
 size_t selective_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int device) {
   if (sel_dims_ok(batch, seqlen, dim, dstate) != SSS_OK) return 0;

@@ -34,8 +34,17 @@ struct SelArgs {
   int bdl;                  // x/delta/z/y (batch, dim, seqlen), B/C (batch, dstate, seqlen)
 };
 
-SelPlan plan_selective(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int num_cus, bool bdl = false);
+// max_ws > 0: at most max_ws bytes of workspace (fewer segments if the usual plan needs more)
+SelPlan plan_selective(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int num_cus, bool bdl = false,
+                       size_t max_ws = 0);
 hipError_t launch_selective(const SelArgs& a, const SelPlan& plan, hipStream_t stream);
+// the whole forward call (api.cpp): validation, plan (workspace at most max_ws bytes when
+// max_ws > 0), launch; returns an sss_status
+int sel_fwd_impl(const void* x, const void* delta, const float* A, const float* B, const float* C,
+                 const float* D_skip, const void* z, const float* h0, float* y, float* h_last,
+                 const float* delta_bias, unsigned flags, int64_t batch, int64_t seqlen, int64_t dim,
+                 int64_t dstate, int io_dtype, void* workspace, size_t workspace_bytes, size_t max_ws,
+                 void* stream);
 // how the forward kernels walk the rows: 0 time-major; channel-major 1 one step per access,
 // 2 16-byte pieces per lane, 3 tiles staged through LDS
 int selective_row_mode(const SelArgs& a, const SelPlan& plan);

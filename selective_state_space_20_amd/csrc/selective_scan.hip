@@ -924,7 +924,8 @@ SSS_EXTERN_INSTANCES(64)
 // ------------------------------------------------------------------ host side
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-SelPlan plan_selective(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int num_cus, bool bdl) {
+SelPlan plan_selective(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int num_cus, bool bdl,
+                       size_t max_ws) {
   SelPlan pl{};
   // segments start on whole load batches: 2 steps, or whole channel-major tiles (32 steps)
   const int64_t unit = bdl ? 32 : kStepsPerBatch;
@@ -943,6 +944,13 @@ SelPlan plan_selective(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstat
   const int forced = env_int("SSS_FORCE_SEGMENTS", 0);
   if (forced > 0) S = std::min<int64_t>(forced, (seqlen + unit - 1) / unit);
   if (S < 1) S = 1;
+  if (max_ws > 0 && S > 1) {
+    // workspace of S segments <= S * (states + delta sums) + two 256-byte roundings (+ B/C rows)
+    const int64_t per_seg = batch * dim * (dstate + 1) * 4;
+    const int64_t fixed = 512 + (bdl ? (int64_t)align_up((size_t)2 * batch * seqlen * dstate * 4, 256) : 0);
+    const int64_t room = (int64_t)max_ws - fixed;
+    S = std::max<int64_t>(1, std::min<int64_t>(S, room > 0 ? room / per_seg : 1));
+  }
   // buffer offsets inside one segment (seg_len rows of dim fp32 values) must stay below
   // 2^30 bytes; dim <= 2^24 is checked by the caller, so max_len >= 16 steps (the B/C row
   // pointers advance by dstate floats per step, also kept below 2^30 bytes)
