@@ -49,7 +49,10 @@
  *    two-pass split) for testing; SSS_LOG=1 prints the chosen launch plan to stderr;
  *    SSS_WAVES_PER_SIMD / SSS_CONV_WAVES_PER_CU override the occupancy targets the
  *    selective-scan and convolution plans aim at, SSS_EW_CPL (1, 2 or 4) the channels per
- *    lane of the elementwise scan (tuning only).
+ *    lane of the elementwise scan (tuning only).  SSS_CHUNKED=1 runs the plain time-major
+ *    forward call (4, 8 or 16 states, no options) as one pass with a workgroup-level scan of the
+ *    affine pairs instead of the two-pass split (measured slower on MI355X; kept for comparison
+ *    and tests).
  */
 #ifndef SSS_H_
 #define SSS_H_

@@ -194,16 +194,25 @@ int sel_fwd_impl(const void* x, const void* delta, const float* A, const float* 
   a.softplus = (flags & SSS_DELTA_SOFTPLUS) != 0;
   a.exact_zoh = (flags & SSS_EXACT_ZOH) != 0;
   a.bdl = bdl;
+  // the single-pass form with the workgroup pair scan: forced on (1) or off (0) by SSS_CHUNKED
+  const int chunked_env = env_int("SSS_CHUNKED", -1);
+  const bool chunked = chunk_scan_supported(a) && chunked_env == 1;
   if (env_int("SSS_LOG", 0)) {
     static const char* const kRows[] = {"time-major", "step", "piece", "tile"};
-    std::fprintf(stderr,
-                 "[sss] selective_scan_fwd B=%lld L=%lld D=%lld N=%lld %s flags=%u: segments=%d seg_len=%lld rows=%s "
-                 "ws=%zu\n",
-                 (long long)batch, (long long)seqlen, (long long)dim, (long long)dstate,
-                 io_dtype == SSS_BF16 ? "bf16" : "f32", flags, pl.segments, (long long)pl.seg_len,
-                 kRows[selective_row_mode(a, pl)], pl.ws_total);
+    if (chunked)
+      std::fprintf(stderr, "[sss] selective_scan_fwd B=%lld L=%lld D=%lld N=%lld %s flags=%u: single pass, "
+                   "workgroup pair scan\n", (long long)batch, (long long)seqlen, (long long)dim, (long long)dstate,
+                   io_dtype == SSS_BF16 ? "bf16" : "f32", flags);
+    else
+      std::fprintf(stderr,
+                   "[sss] selective_scan_fwd B=%lld L=%lld D=%lld N=%lld %s flags=%u: segments=%d seg_len=%lld rows=%s "
+                   "ws=%zu\n",
+                   (long long)batch, (long long)seqlen, (long long)dim, (long long)dstate,
+                   io_dtype == SSS_BF16 ? "bf16" : "f32", flags, pl.segments, (long long)pl.seg_len,
+                   kRows[selective_row_mode(a, pl)], pl.ws_total);
   }
-  hipError_t e = launch_selective(a, pl, reinterpret_cast<hipStream_t>(stream));
+  hipError_t e = chunked ? launch_chunk_scan(a, reinterpret_cast<hipStream_t>(stream))
+                         : launch_selective(a, pl, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? SSS_OK : SSS_ERR_HIP;
 }
 }  // namespace sss

@@ -38,6 +38,10 @@ struct SelArgs {
 SelPlan plan_selective(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int num_cus, bool bdl = false,
                        size_t max_ws = 0);
 hipError_t launch_selective(const SelArgs& a, const SelPlan& plan, hipStream_t stream);
+// single-pass form with the workgroup-level pair scan (chunk_scan.hip): which calls it takes,
+// and the launch (no workspace)
+bool chunk_scan_supported(const SelArgs& a);
+hipError_t launch_chunk_scan(const SelArgs& a, hipStream_t stream);
 // the whole forward call (api.cpp): validation, plan (workspace at most max_ws bytes when
 // max_ws > 0), launch; returns an sss_status
 int sel_fwd_impl(const void* x, const void* delta, const float* A, const float* B, const float* C,

@@ -21,6 +21,7 @@ pytestmark = pytest.mark.gpu
 @pytest.fixture(autouse=True)
 def _no_forced_segments(monkeypatch):
     monkeypatch.delenv("SSS_FORCE_SEGMENTS", raising=False)
+    monkeypatch.delenv("SSS_CHUNKED", raising=False)
     yield
 
 
@@ -88,6 +89,28 @@ def test_selective_row_tiles(oracle_lib, monkeypatch, case):
     inp = gen.selective_inputs(bt, L, dm, n, io=io, with_z=True, with_D=True, h0=True,
                                seed=zlib.crc32(repr(case).encode()) % 100000)
     _check_sel(oracle_lib, inp, f"rows S={S}")
+
+
+CHUNK_CASES = [  # (batch, seqlen, dim, dstate, io, z, D, h0): the single-pass workgroup pair scan
+    (2, 1000, 100, 16, "bf16", True, True, True),   # ragged last chunk, ragged channel group
+    (1, 32, 64, 16, "f32", False, True, False),     # exactly one chunk
+    (3, 33, 70, 8, "bf16", True, False, True),      # one step past a chunk
+    (1, 4097, 130, 4, "f32", True, True, True),
+    (2, 5, 3, 16, "bf16", True, True, True),        # shorter than one wave's steps
+]
+
+
+@pytest.mark.parametrize("case", CHUNK_CASES, ids=[f"B{c[0]}L{c[1]}D{c[2]}N{c[3]}{c[4]}" for c in CHUNK_CASES])
+def test_selective_workgroup_pair_scan(oracle_lib, monkeypatch, capfd, case):
+    """The single-pass form (SSS_CHUNKED=1): waves of one workgroup take consecutive sub-chunks
+    of the same channels, exchange their (decay product, state) pairs through LDS and scan
+    them; the library logs that this path ran."""
+    monkeypatch.setenv("SSS_CHUNKED", "1")
+    monkeypatch.setenv("SSS_LOG", "1")
+    bt, L, dm, n, io, z, D, h0 = case
+    inp = gen.selective_inputs(bt, L, dm, n, io=io, with_z=z, with_D=D, h0=h0, seed=zlib.crc32(repr(case).encode()) % 100000)
+    _check_sel(oracle_lib, inp, "pair scan")
+    assert "workgroup pair scan" in capfd.readouterr().err
 
 
 def test_selective_special_values(oracle_lib):
