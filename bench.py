@@ -205,6 +205,8 @@ PROBE_KINDS = {  # main instructions per probe iteration: name, VALU-class count
     12: ("kind 4 with B/C in one VGPR each, taken through DPP row_newbcast", 64 + 4, 16, 0),
     13: ("kind 8 in phases per step: 16 mul | 16 exp | 64 VALU", 64 + 2, 16, 0),
     14: ("kind 4 (SGPR rows) in phases per step: 16 mul | 16 exp | 64 VALU", 64 + 2, 16, 0),
+    15: ("kind 13, update phase by instruction: 16 mul | 16 fma | 16 fma", 64 + 2, 16, 0),
+    16: ("kind 15 in groups of 4 states", 64 + 2, 16, 0),
 }
 
 
@@ -276,7 +278,7 @@ def probes(stream_bytes=4 << 30, iters=4000, kinds=None):
                    "clk_per_main_instruction": round(per_iter / main if kind in (0, 1, 2, 6, 7, 10) else per_iter / 16, 3),
                    "clock_GHz": round(ghz, 3), "waves_per_simd_id": per_simd.tolist(),
                    "median_over_max_wave_clk": round(float(np.median(o[:, 0])) / clk, 3)}
-            if kind in (3, 4, 5, 8, 12, 13, 14):
+            if kind in (3, 4, 5, 8, 12, 13, 14, 15, 16):
                 rec["note"] = "clk_per_main_instruction is clocks per state-step (16 per iteration)"
             if kind in (9, 11) and w > 1:
                 # each wave's own clocks by role (the waves of one role issue 16 instructions per

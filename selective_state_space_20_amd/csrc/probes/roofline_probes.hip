@@ -96,6 +96,9 @@ constexpr int kOps = 16;  // independent chains per wave
 // kind 13: kind 8 with each step's instructions in phases: the 16 argument multiplies, then
 //          the 16 exps, then the 64 remaining VALU instructions (scheduling barriers between)
 // kind 14: kind 13 without the LDS rows (B and C as SGPR operands, as kind 4)
+// kind 15: kind 13 with the update phase ordered by instruction: the 16 input-term multiplies,
+//          then the 16 state fmas, then the 16 read-out fmas (no dependent neighbours)
+// kind 16: kind 15 in groups of 4 states (each group: 4 mul | 4 exp | 4 mul | 4 fma | 4 fma)
 // kind 12: kind 4 with the B and C rows in one VGPR each (lane i of every 16-lane row holds
 //          element i) and B[n], C[n] taken by the VALU ops through DPP row_newbcast:n
 // Roles (kinds 9, 11): waves 4r .. 4r+3 of a workgroup fill one slot on each SIMD, so slot r
@@ -133,7 +136,40 @@ __global__ __launch_bounds__(1024) void alu_kernel(int iters, Rows rows, uint64_
 #pragma unroll
   for (int k = 0; k < kOps; ++k) u[k] = 1e-3f * (float)(k + 1);
   auto step = [&]() {
-    if constexpr (KIND == 13 || KIND == 14) {
+    if constexpr (KIND == 15 || KIND == 16) {
+      float bv[kOps], cv[kOps], e[kOps], uu[kOps];
+      const f32x4* row = reinterpret_cast<const f32x4*>(pad + ((rowsel++) & 63) * 32);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 b4 = row[q], c4 = row[4 + q];
+        bv[4 * q] = b4.x; bv[4 * q + 1] = b4.y; bv[4 * q + 2] = b4.z; bv[4 * q + 3] = b4.w;
+        cv[4 * q] = c4.x; cv[4 * q + 1] = c4.y; cv[4 * q + 2] = c4.z; cv[4 * q + 3] = c4.w;
+      }
+      constexpr int G = KIND == 15 ? kOps : 4;
+#pragma unroll
+      for (int g0 = 0; g0 < kOps; g0 += G) {
+#pragma unroll
+        for (int k = g0; k < g0 + G; ++k) e[k] = dl * a[k];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = g0; k < g0 + G; ++k) e[k] = __builtin_amdgcn_exp2f(e[k]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = g0; k < g0 + G; ++k) uu[k] = dx * bv[k];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = g0; k < g0 + G; ++k) v[k] = __builtin_fmaf(e[k], v[k], uu[k]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = g0; k < g0 + G; ++k) {
+          if (k & 1) y1 = __builtin_fmaf(cv[k], v[k], y1);
+          else y0 = __builtin_fmaf(cv[k], v[k], y0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      dl = __builtin_fmaf(dl, 0.9999f, 1e-6f);
+      dx = __builtin_fmaf(dx, 0.999f, 1e-4f);
+    } else if constexpr (KIND == 13 || KIND == 14) {
       float bv[kOps], cv[kOps], e[kOps];
 #pragma unroll
       for (int k = 0; k < kOps; ++k) {
@@ -314,6 +350,8 @@ int sss_probe_alu(int kind, int waves_per_simd, int iters, int grid, uint64_t* o
     case 12: hipLaunchKernelGGL(alu_kernel<12>, dim3((unsigned)grid), block, lds, st, iters, rows, out, sink); break;
     case 13: hipLaunchKernelGGL(alu_kernel<13>, dim3((unsigned)grid), block, lds, st, iters, rows, out, sink); break;
     case 14: hipLaunchKernelGGL(alu_kernel<14>, dim3((unsigned)grid), block, lds, st, iters, rows, out, sink); break;
+    case 15: hipLaunchKernelGGL(alu_kernel<15>, dim3((unsigned)grid), block, lds, st, iters, rows, out, sink); break;
+    case 16: hipLaunchKernelGGL(alu_kernel<16>, dim3((unsigned)grid), block, lds, st, iters, rows, out, sink); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();
