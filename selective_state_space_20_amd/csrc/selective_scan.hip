@@ -54,9 +54,8 @@ constexpr int kTileBytes = 64;      // channel-major tiles: bytes of each row pe
 // same issue cycle, one with vector operands only does (measured on gfx950).  Each wave
 // stages 1 KB of B rows (and of C rows in pass 2) in its own LDS tile, double-buffered, and
 // every step reads its rows with broadcast ds_read_b128 (all lanes one address).
-// (Not for the exact hold, whose extra per-state registers would spill in this form, nor for
-// channel-major rows, which stage x/delta/z in LDS instead.)
-constexpr bool lds_rows(int ns, int fl) { return (fl & 9) == 0 && (ns == 4 || ns == 8 || ns == 16); }
+// (Not for channel-major rows, which stage x/delta/z in LDS instead.)
+constexpr bool lds_rows(int ns, int fl) { return (fl & 8) == 0 && (ns == 4 || ns == 8 || ns == 16); }
 constexpr int kRowTileBytes = 1024;  // per tensor: 256 / N steps of N fp32 states
 constexpr int ilog2_const(int v) { return v <= 1 ? 0 : 1 + ilog2_const(v / 2); }
 // LDS bytes per wave of the row tiles: two buffers of B (pass 1 and 3) or of B and C (pass 2)
@@ -129,11 +128,16 @@ struct SelSeg {
 //     instead of (batch, seqlen, dim): each lane then walks its own row, loading 16 bytes
 //     (8 bf16 / 4 fp32 steps) and storing 4 fp32 outputs per access where the rows are
 //     16-byte aligned (g.vec), else one step per access.  B/C arrive time-major either way.
-// fp32 inputs in the pass-2 form with LDS rows keep more values in flight: 3 waves per SIMD
+// fp32 inputs in the pass-2 form with LDS rows, and the exact hold (1/A per state) in either
+// pass, keep more values in flight: 3 waves per SIMD
 constexpr int min_waves_sel(int ns, int fl, bool bf16, int pass) {
-  return (!bf16 && pass == 2 && (fl & 9) == 0 && (ns == 4 || ns == 8 || ns == 16) && min_waves_of(ns, fl) > 3)
+  return (lds_rows(ns, fl) && ((!bf16 && pass == 2) || (fl & 1) != 0) && min_waves_of(ns, fl) > 3)
              ? 3 : min_waves_of(ns, fl);
 }
+// Exact hold: where |delta * A| >= 2^-10 in every lane of a step (checked once per step from
+// the lane's smallest |A|), (2^arg - 1) / A needs no series: its cancellation error is at most
+// an ulp of 1 over |delta * A|, below 6e-5 relative there.
+constexpr float kZFast = 1.0f / 1024.0f;
 
 template <int NS, bool BF16, int PASS, bool HAS_Z, int FL>
 __global__ __launch_bounds__(256, min_waves_sel(NS, FL, BF16, PASS)) void sel_seq_kernel(const void* __restrict__ x, const void* __restrict__ delta,
@@ -167,12 +171,18 @@ __global__ __launch_bounds__(256, min_waves_sel(NS, FL, BF16, PASS)) void sel_se
 
   constexpr bool zoh = (FL & kZoh) != 0;
   float a2[NS], h[NS];
-  float ia[zoh ? NS : 1];  // exact hold: 1/A[n] (A = 0 takes the series, which needs none)
+  // exact hold: 1/A[n]; |A| below 2^-64 (A = 0 included) gets 0 and takes the series, which
+  // needs no 1/A (and covers every |delta * A| below 1/16, i.e. any delta below 2^60 there)
+  float ia[zoh ? NS : 1];
+  float amin = 3.402823466e+38f;  // exact hold: the lane's smallest |A[n]|
 #pragma unroll
   for (int n = 0; n < NS; ++n) {
     const float an = A[dc * N + n];
     a2[n] = fmaxf(an * kLog2e, -kFltMax);  // -inf clamped so that 0*a2 = 0
-    if constexpr (zoh) ia[n] = an != 0.0f ? 1.0f / an : 0.0f;
+    if constexpr (zoh) {
+      ia[n] = fabsf(an) >= 0x1p-64f ? 1.0f / an : 0.0f;
+      amin = fminf(amin, fabsf(an));
+    }
     if (PASS == 1) {
       h[n] = 0.0f;
     } else if (g.S > 1) {
@@ -471,7 +481,7 @@ __global__ __launch_bounds__(256, min_waves_sel(NS, FL, BF16, PASS)) void sel_se
       float y0 = Dd * xv, y1 = 0.0f;
       // states in groups of GS (the phases of one group hold GS arguments, GS decays and GS
       // rows of B and C in registers)
-      constexpr int GS = NS < 8 ? NS : (BF16 && PASS != 2 ? 8 : 4);  // pass 2 and fp32 inputs hold more registers
+      constexpr int GS = NS < 8 ? NS : (BF16 && PASS != 2 && !zoh ? 8 : 4);  // pass 2, fp32 inputs, exact hold: more registers
 #pragma unroll
       for (int n0 = 0; n0 < NS; n0 += GS) {
         float bq[GS], cq[PASS == 2 ? GS : 1];
@@ -494,8 +504,9 @@ __global__ __launch_bounds__(256, min_waves_sel(NS, FL, BF16, PASS)) void sel_se
 #pragma unroll
         for (int k = 0; k < GS; ++k) {
           const int n = n0 + k;
-          if constexpr (zoh) {
-            h[n] = __builtin_fmaf(ab[k], h[n], zoh_coef(arg[k], ab[k], dl, ia[n]) * (xv * bq[k]));
+          if constexpr (zoh) {  // direct form: (2^arg - 1) / A * x B = fma(2^arg, w, -w), w = x B / A
+            const float w = ia[n] * (xv * bq[k]);
+            h[n] = __builtin_fmaf(ab[k], h[n], __builtin_fmaf(ab[k], w, -w));
           } else {
             h[n] = __builtin_fmaf(ab[k], h[n], dx * bq[k]);
           }
@@ -505,6 +516,39 @@ __global__ __launch_bounds__(256, min_waves_sel(NS, FL, BF16, PASS)) void sel_se
           }
         }
         __builtin_amdgcn_sched_barrier(0x14);
+      }
+      if constexpr (zoh) {
+        // Exact hold, a step where some lane has |delta * A| below 2^-10 for one of its states:
+        // the direct form above loses accuracy to cancellation there, so each state gets the
+        // difference between the exact coefficient (series for small arguments) and the
+        // direct one added afterwards.  The direct term is recomputed here by the same
+        // operations, from a copy of the step size that the compiler cannot see through, so
+        // that none of it is kept live from the common path (which needs no branch join).
+        if (__builtin_amdgcn_ballot_w64(fabsf(dl) * amin >= kZFast) != __builtin_amdgcn_read_exec()) {
+          float dls = dl;
+          asm volatile("; exact hold, series correction" : "+v"(dls));
+#pragma unroll
+          for (int n0 = 0; n0 < NS; n0 += 4) {
+            const float4 v = reinterpret_cast<const float4*>(brow + n0)[0];
+            const float bq[4] = {v.x, v.y, v.z, v.w};
+            float cq[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            if constexpr (PASS == 2) {
+              const float4 c = reinterpret_cast<const float4*>(brow + 256 + n0)[0];
+              cq[0] = c.x; cq[1] = c.y; cq[2] = c.z; cq[3] = c.w;
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const int n = n0 + k;
+              const float arg = dls * a2[n];
+              const float e = fast_exp2(arg);
+              const float xb = xv * bq[k];
+              const float w = ia[n] * xb;
+              const float d = zoh_coef(arg, e, dls, ia[n]) * xb - __builtin_fmaf(e, w, -w);
+              h[n] += d;
+              if constexpr (PASS == 2) y0 = __builtin_fmaf(cq[k], d, y0);
+            }
+          }
+        }
       }
       if constexpr (PASS == 1) {
         dsum += dl;

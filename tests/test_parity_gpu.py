@@ -202,17 +202,38 @@ def test_selective_options(oracle_lib, monkeypatch, case):
     assert ey <= tol and eh <= tol
 
 
-def test_selective_exact_zoh_special_values(oracle_lib):
-    """Exact hold where A = 0 (input term delta*B), A = -inf (no input term) and for tiny
-    delta*A (the series branch of expm1)."""
-    inp = gen.selective_inputs(2, 2000, 12, 16, io="f32", with_D=True, with_z=False, h0=True, seed=95)
-    inp["A"][:, :4] = 0.0
-    inp["A"][:, 4:6] = -np.inf
-    inp["delta"][:, :, 6:] *= 1e-4
+ZOH_SPECIAL_CASES = [(16, "f32", 0), (8, "bf16", 0), (4, "f32", 3), (16, "bf16", 2)]
+
+
+@pytest.mark.parametrize("case", ZOH_SPECIAL_CASES, ids=[f"N{c[0]}{c[1]}S{c[2]}" for c in ZOH_SPECIAL_CASES])
+def test_selective_exact_zoh_special_values(oracle_lib, monkeypatch, case):
+    """Exact hold where A = 0 (input term delta*B), A = -inf (no input term), |A| below 2^-64,
+    and tiny delta*A (the series branch of expm1): small steps in whole channels, and in a
+    few scattered steps of the other channels, so that both the steps that take the direct
+    coefficient in every lane and those that need the series in some lanes occur."""
+    n, io, segs = case
+    if segs:
+        monkeypatch.setenv("SSS_FORCE_SEGMENTS", str(segs))
+    inp = gen.selective_inputs(2, 2000, 140, n, io="f32", with_D=True, with_z=False, h0=True, seed=95 + n)
+    inp["A"][:4, :] = 0.0
+    inp["A"][4:8, : n // 2] = -np.inf
+    inp["A"][8:12, : n // 2] = -1e-30
+    inp["delta"][:, :, 12:20] *= 1e-4
+    rng = np.random.default_rng(96 + n)
+    t_small = rng.choice(2000, size=40, replace=False)
+    inp["delta"][:, t_small, 70:] *= 1e-3
+    if io == "bf16":
+        for k in ("x", "delta"):
+            inp[k] = gen.f32_to_bf16_bits(inp[k])
+        inp["io"] = "bf16"
+    note(f"[exact hold special] N={n} {io} S={segs}")
     y, hl = run_selective(inp, exact_zoh=True)
     yr, hr = oracle_lib.selective_scan(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
                                        inp["h0"], exact_zoh=True)
-    assert rel_err(y, yr) <= TOL_F32 and rel_err(hl, hr) <= TOL_F32
+    tol = TOL_BF16 if io == "bf16" else TOL_F32
+    ey, eh = rel_err(y, yr), rel_err(hl, hr)
+    note(f"    err y={ey:.3e} h_last={eh:.3e}")
+    assert ey <= tol and eh <= tol
 
 
 # ---------------------------------------------------------------- channel-major (B,D,L) layout
