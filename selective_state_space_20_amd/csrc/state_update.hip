@@ -11,7 +11,7 @@
 // order, four states per lane, so that every state load and store of a wave is one
 // contiguous 1 KiB piece of 16-byte vectors, and each thread carries four batch rows whose
 // loads are all in flight together.  The lanes of a channel are adjacent and reduce C*h
-// with cross-lane xor shuffles; the first of them writes y.
+// with DPP lane permutes inside their 16-lane row; the first of them writes y.
 #include "common.h"
 #include "kernels.h"
 
@@ -25,9 +25,29 @@ __device__ __forceinline__ float load_io(const void* p, int64_t i) {
 
 typedef float f4v __attribute__((ext_vector_type(4)));
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over each group of LPC adjacent lanes (LPC = 1, 2, 4, 8 or 16, groups aligned to LPC);
+// every lane of a group ends with the sum.  Pairs first (quad_perm 1,0,3,2), then pairs of
+// pairs (quad_perm 2,3,0,1); each quad then holds one value, so mirroring the 8-lane half-row
+// (row_half_mirror) and then the 16-lane row (row_mirror) meets the partner quad and the
+// partner half.  All inside one DPP row: no LDS round trip.
+template <int LPC>
+__device__ __forceinline__ float group_sum(float p) {
+  static_assert(LPC == 1 || LPC == 2 || LPC == 4 || LPC == 8 || LPC == 16, "lanes per channel");
+  if constexpr (LPC >= 2) p += dpp_mov<0xB1>(p);   // quad_perm [1,0,3,2]
+  if constexpr (LPC >= 4) p += dpp_mov<0x4E>(p);   // quad_perm [2,3,0,1]
+  if constexpr (LPC >= 8) p += dpp_mov<0x141>(p);  // row_half_mirror
+  if constexpr (LPC >= 16) p += dpp_mov<0x140>(p); // row_mirror
+  return p;
+}
+
 // Each lane owns PL = min(4, NS) adjacent states of one channel (a 16-byte piece of the
 // state, of A and of B/C) for R batch rows; the LPC = NS / PL lanes of a channel are
-// adjacent and reduce C*h with xor shuffles.  All R rows' loads are issued before any of
+// adjacent and reduce C*h through DPP (group_sum).  All R rows' loads are issued before any of
 // them is used, so that a wave keeps R KiB of state in flight (one KiB per row and wave).
 // blockIdx.x = row group * bpb + k; rows past the batch load the last row and store nothing.
 template <int NS, bool BF16, bool HAS_Z, int R>
@@ -106,8 +126,7 @@ __global__ __launch_bounds__(256) void sel_update_kernel(const void* __restrict_
         for (int i = 0; i < PL; ++i) state[c * NS + i] = hv[r][i];
       }
     }
-#pragma unroll
-    for (int off = LPC / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, LPC);
+    part = group_sum<LPC>(part);
     if (live && row && j == 0) {
       float out = __builtin_fmaf(dd, xv[r], part);
       if (HAS_Z) out *= silu(zv[r]);
