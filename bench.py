@@ -44,14 +44,14 @@ COPY_WRITE_SCALE = 1048576.0 / 1048576.0
 CSRC = "selective_state_space_20_amd/csrc/"
 PMC_TRAFFIC = {
     # default workload: sel_seq_kernel pass 1 + sel_carry_kernel + pass 2
-    "selective": {"sources": (CSRC + "selective_scan.hip", CSRC + "common.h"), "digest": "3f77316f7d10dabd",
-                  "fetch_kib": 659063.8 + 46571.7 + 1034269.7, "write_kib": 86700.0 + 81920.0 + 1311040.0},
+    "selective": {"sources": (CSRC + "selective_scan.hip", CSRC + "common.h"), "digest": "11f4ddcc36ca4d7f",
+                  "fetch_kib": 656603.7 + 46577.0 + 1030438.6, "write_kib": 86700.0 + 81920.0 + 1311040.0},
     # 8 x 32768 x 4096 fp32
     "elementwise": {"sources": (CSRC + "elementwise_scan.hip", CSRC + "common.h"), "digest": "4b0239623ce7466b",
                     "fetch_kib": 8388744.2, "write_kib": 4194432.0},
     # 256 tokens x 5120 x 16
-    "decode": {"sources": (CSRC + "state_update.hip", CSRC + "common.h"), "digest": "a48994a23866d68b",
-               "fetch_kib": 45119.9, "write_kib": 87040.4},
+    "decode": {"sources": (CSRC + "state_update.hip", CSRC + "common.h"), "digest": "454225efc541ef58",
+               "fetch_kib": 45119.1, "write_kib": 87040.5},
     # 1 x 65536 x 5120 bf16, width 4
     "conv": {"sources": (CSRC + "conv1d.hip", CSRC + "common.h"), "digest": "0525304aa8e7045b",
              "fetch_kib": 328260.8, "write_kib": 655360.3},
