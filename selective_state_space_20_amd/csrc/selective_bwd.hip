@@ -188,6 +188,42 @@ __global__ __launch_bounds__(256) void sel_bwd_carry(const float* __restrict__ A
 __device__ __forceinline__ uint32_t bwd_u32(float f) { return __builtin_bit_cast(uint32_t, f); }
 __device__ __forceinline__ float bwd_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
 
+// v + (v of the partner lane) for every lane, the partner given by the DPP control of
+// level LV (2: row_mirror, 3: row_half_mirror, 4: quad_perm [2,3,0,1], 5: quad_perm
+// [1,0,3,2]): one v_add_f32_dpp.  (The s_nop covers the DPP read-after-VALU-write hazard.)
+template <int LV>
+__device__ __forceinline__ float dpp_self_sum(float v) {
+  float r;
+  if constexpr (LV == 2)
+    asm("s_nop 1\n\tv_add_f32_dpp %0, %1, %1 row_mirror row_mask:0xf bank_mask:0xf" : "=v"(r) : "v"(v));
+  else if constexpr (LV == 3)
+    asm("s_nop 1\n\tv_add_f32_dpp %0, %1, %1 row_half_mirror row_mask:0xf bank_mask:0xf" : "=v"(r) : "v"(v));
+  else if constexpr (LV == 4)
+    asm("s_nop 1\n\tv_add_f32_dpp %0, %1, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf" : "=v"(r) : "v"(v));
+  else
+    asm("s_nop 1\n\tv_add_f32_dpp %0, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf" : "=v"(r) : "v"(v));
+  return r;
+}
+
+// Levels 2 and 3 pair lanes across 4-lane banks (bit 3: banks 0,1 against 2,3; bit 2: banks
+// 0,2 against 1,3), so each half of the lanes takes its kept value in one DPP add whose bank
+// mask writes only that half: low lanes a + partner's a, high lanes b + partner's b.  (The
+// result register is written in two halves; it must not be a or b, whose low lanes the
+// second add still reads from the partners.)
+template <int LV>
+__device__ __forceinline__ float dpp_split_sum(float a, float b) {
+  float r;
+  if constexpr (LV == 2)
+    asm("s_nop 1\n\tv_add_f32_dpp %0, %1, %1 row_mirror row_mask:0xf bank_mask:0x3\n\t"
+        "v_add_f32_dpp %0, %2, %2 row_mirror row_mask:0xf bank_mask:0xc"
+        : "=&v"(r) : "v"(a), "v"(b));
+  else
+    asm("s_nop 1\n\tv_add_f32_dpp %0, %1, %1 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
+        "v_add_f32_dpp %0, %2, %2 row_half_mirror row_mask:0xf bank_mask:0xa"
+        : "=&v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // a: the value lanes without the level's bit keep, b: the value lanes with it keep
 template <int LV>
 __device__ __forceinline__ float pair_sum(float a, float b, bool hi) {
@@ -213,10 +249,14 @@ __device__ __forceinline__ void reduce_scatter_level(float (&p)[V], int lane) {
     if constexpr (CNT > 1) {
       constexpr int half = CNT / 2;
 #pragma unroll
-      for (int i = 0; i < half; ++i) p[i] = pair_sum<LV>(p[i], p[half + i], hi);
+      for (int i = 0; i < half; ++i) {
+        if constexpr (LV == 2 || LV == 3) p[i] = dpp_split_sum<LV>(p[i], p[half + i]);
+        else p[i] = pair_sum<LV>(p[i], p[half + i], hi);
+      }
       reduce_scatter_level<LV + 1, half, V>(p, lane);
     } else {
-      p[0] = pair_sum<LV>(p[0], p[0], hi);
+      if constexpr (LV >= 2) p[0] = dpp_self_sum<LV>(p[0]);
+      else p[0] = pair_sum<LV>(p[0], p[0], hi);
       reduce_scatter_level<LV + 1, 1, V>(p, lane);
     }
   }
