@@ -52,6 +52,12 @@ PMC_TRAFFIC = {
     # 256 tokens x 5120 x 16
     "decode": {"sources": (CSRC + "state_update.hip", CSRC + "common.h"), "digest": "454225efc541ef58",
                "fetch_kib": 45119.1, "write_kib": 87040.5},
+    # selective_scan_bwd on the default workload: the forward pass 1 + carry, the checkpoint
+    # pass, the adjoint's segment fold + carry, the main kernel and the two reductions
+    "backward": {"sources": (CSRC + "selective_bwd.hip", CSRC + "selective_scan.hip", CSRC + "common.h"),
+                 "digest": "02f152ba9d1ae3c2",
+                 "fetch_kib": 656561.2 + 46576.9 + 701724.9 + 1329355.3 + 46575.2 + 4471981.9 + 327699.1 + 43549.5,
+                 "write_kib": 86700.0 + 81920.0 + 5242883.2 + 86700.0 + 81920.0 + 4685535.8 + 8192.0 + 660.0},
     # 1 x 65536 x 5120 bf16, width 4
     "conv": {"sources": (CSRC + "conv1d.hip", CSRC + "common.h"), "digest": "0525304aa8e7045b",
              "fetch_kib": 328260.8, "write_kib": 655360.3},
@@ -449,7 +455,7 @@ def bench_backward(steps, warmup):
         "config": {"workload": "backward_" + cfg["name"], "algorithmic_bytes": nbytes, "elements": e},
         "elements_per_s": round(e / (mean_ms * 1e-3), 1),
         "roofline": {"bound": "alu", "achieved": round(alu_tflops, 3), "peak": VALU_FP32_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(alu_tflops / VALU_FP32_TFLOPS, 4), "traffic": None,
+                     "frac": round(alu_tflops / VALU_FP32_TFLOPS, 4), "traffic": measured_traffic("backward"),
                      "kernel": "one selective_scan_bwd call (8 launches)", "call_ms_event_mean": round(mean_ms, 5),
                      "alu_ops_per_call": alu,
                      "hbm": {"achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
