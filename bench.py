@@ -148,8 +148,24 @@ def cpu_baseline(cfg, inp, budget_s=12.0):
         run = oracle.selective_scan_channels
     if cfg["api"] != "elementwise":
         plain = run
-        run = lambda *a, channels: plain(*a, channels=channels, delta_softplus=bool(cfg.get("delta_softplus")),
-                                         exact_zoh=bool(cfg.get("exact_zoh")), layout=cfg.get("layout", "bld"))
+        run = lambda *a, channels, nthreads=0: plain(*a, channels=channels, nthreads=nthreads,
+                                                     delta_softplus=bool(cfg.get("delta_softplus")),
+                                                     exact_zoh=bool(cfg.get("exact_zoh")),
+                                                     layout=cfg.get("layout", "bld"))
+    bpe = algorithmic_bytes(cfg) / (cfg["batch"] * cfg["seqlen"] * cfg["dim"])
+    # one thread: the per-core figure, on channels spread over the workload (about 2 s)
+    k1 = 1
+    while True:
+        ch1 = np.linspace(0, nch - 1, k1).astype(np.int64)
+        t0 = time.perf_counter()
+        run(*args, channels=ch1, nthreads=1)
+        dt1 = time.perf_counter() - t0
+        if dt1 >= 0.5 or k1 >= nch:
+            break
+        k1 = int(min(nch, max(k1 * 2, k1 * 2.0 / max(dt1, 1e-4))))
+    per_core = {"value": round(k1 * cfg["seqlen"] * bpe / dt1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                "sample": f"{k1} of {nch} channels x {cfg['seqlen']} steps, {dt1:.2f} s wall, "
+                          f"{k1 * cfg['seqlen'] / dt1:.4g} elements/s"}
     k = min(nch, max(cores, 1) * 2)
     t0 = time.perf_counter()
     run(*args, channels=np.arange(k, dtype=np.int64))
@@ -161,10 +177,10 @@ def cpu_baseline(cfg, inp, budget_s=12.0):
     run(*args, channels=ch)
     dt = time.perf_counter() - t0
     elems = k2 * cfg["seqlen"]
-    bpe = algorithmic_bytes(cfg) / (cfg["batch"] * cfg["seqlen"] * cfg["dim"])
     return {"value": round(elems * bpe / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"{k2} of {nch} channels x {cfg['seqlen']} steps (all {cfg.get('dstate') or 1} states), fp64, "
-                      f"{dt:.2f} s wall, {elems / dt:.4g} elements/s"}
+                      f"{dt:.2f} s wall, {elems / dt:.4g} elements/s",
+            "per_core": per_core}
 
 
 def copy_ceiling(dev, stream, nbytes=2 << 30, reps=5):

@@ -66,9 +66,14 @@ static double delta_value(const void* delta, int64_t e, int dtype, const float* 
   return sp ? softplus(v) : v;
 }
 
+/* Thread count of the next parallel region: nthreads if positive, else the process default
+ * (taken on first use), so that a call with an explicit count does not change later calls. */
+static int g_default_threads = 0;
+
 static void set_threads(int nthreads) {
 #ifdef _OPENMP
-  if (nthreads > 0) omp_set_num_threads(nthreads);
+  if (g_default_threads == 0) g_default_threads = omp_get_max_threads();
+  omp_set_num_threads(nthreads > 0 ? nthreads : g_default_threads);
 #else
   (void)nthreads;
 #endif
@@ -76,7 +81,7 @@ static void set_threads(int nthreads) {
 
 int oracle_max_threads(void) {
 #ifdef _OPENMP
-  return omp_get_max_threads();
+  return g_default_threads > 0 ? g_default_threads : omp_get_max_threads();
 #else
   return 1;
 #endif
