@@ -55,9 +55,12 @@ int selective_row_mode(const SelArgs& a, const SelPlan& plan);
 // pass 1 + carry only: the workspace's state slots hold the state entering each segment
 hipError_t launch_segment_states(const SelArgs& a, const SelPlan& plan, hipStream_t stream);
 // after launch_segment_states: the state before every 2^kshift-th step of every segment,
-// into ckpt[s][batch][channel group][j][dstate][64 lanes] (ceil(dim / 64) groups)
+// into ckpt[s][batch][channel group][j][dstate][64 lanes] (ceil(dim / 64) groups); with
+// adj_mu (more than one segment) also the adjoint of every segment folded from zero at its
+// end into adj_mu[s][batch][dstate][dim], dy (batch, seqlen, dim) being the output gradient,
+// and every segment's delta sum into the workspace's sums
 hipError_t launch_checkpoints(const SelArgs& a, const SelPlan& plan, float* ckpt, int kshift, int nsub,
-                              hipStream_t stream);
+                              const float* dy, float* adj_mu, hipStream_t stream);
 
 // Backward pass of the selective scan (selective_bwd.hip).
 struct BwdPlan {

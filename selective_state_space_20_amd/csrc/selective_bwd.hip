@@ -14,10 +14,11 @@
 //
 // Mapping (lanes = 64 adjacent channels, time split into the forward pass's segments):
 //   1. forward pass 1 + carry (selective_scan.hip): the state entering every segment;
-//   2. sel_bwd_local: each segment's adjoint folded backwards from zero, mu = a (mu + C dv);
+//   2. the forward scan's checkpoint pass stores the state before every K-th step and, from
+//      the decays it forms anyway, each segment's adjoint folded from zero at its end
+//      (mu = a (mu + C dv) backwards, summed forwards as sum_t a_first..a_t C_t dv_t);
 //   3. sel_bwd_carry: the adjoint entering every segment from its right end (from dh_last);
-//   4. the forward scan's checkpoint pass stores the state before every K-th step; then
-//      sel_bwd_kernel takes each segment's K-step sub-chunks in reverse order: their states
+//   4. sel_bwd_kernel takes each segment's K-step sub-chunks in reverse order: their states
 //      are re-formed in registers from the checkpoint and the adjoint walks them backwards, writing dx,
 //      ddelta, dz and per-wave partial sums of dB/dC (a cross-lane reduce-scatter over the
 //      64 channels) and per-segment partials of dA/dD;
@@ -98,47 +99,6 @@ __device__ __forceinline__ BwdLane bwd_lane(const BwdSeg& g, int seg_offset) {
   r.tbeg = (int64_t)r.s * g.seg_len;
   r.len = (int)(min(r.tbeg + g.seg_len, g.L) - r.tbeg);
   return r;
-}
-
-// ------------------------------------------------------------------ 2. reverse-local fold
-// Segments 1..S-1: mu_loc[s][b][n][d] = adjoint at the segment's first step from a zero
-// adjoint at its end, mu = a_t (mu + C_t dv_t) walked from the last step down; also the
-// segment's delta sum (the forward pass 1 has none for the last segment).
-template <int NS, bool BF16, bool HAS_Z>
-__global__ __launch_bounds__(64) void sel_bwd_local(const void* __restrict__ delta, const float* __restrict__ A,
-                                                    const float* __restrict__ Cm, const void* __restrict__ z,
-                                                    const float* __restrict__ dy, float* __restrict__ mu_loc,
-                                                    float* __restrict__ seg_dsum, BwdSeg g) {
-  const BwdLane q = bwd_lane(g, 1);
-  constexpr int ES = BF16 ? 2 : 4;
-  float a2[NS], mu[NS];
-#pragma unroll
-  for (int n = 0; n < NS; ++n) {
-    a2[n] = fmaxf(A[q.dc * NS + n] * kLog2e, -kFltMax);
-    mu[n] = 0.0f;
-  }
-  const int64_t row0 = (q.b * g.L + q.tbeg) * g.D + q.d0;
-  const __amdgpu_buffer_rsrc_t rd = bwd_rsrc((const char*)delta + row0 * ES);
-  const __amdgpu_buffer_rsrc_t rz = bwd_rsrc(HAS_Z ? (const char*)z + row0 * ES : (const char*)delta);
-  const __amdgpu_buffer_rsrc_t rg = bwd_rsrc(dy + row0);
-  const int rs = (int)(g.D * ES), rs4 = (int)(g.D * 4);
-  const float* Cr = Cm + (q.b * g.L + q.tbeg) * NS;
-  float dsum = 0.0f;
-  for (int t = q.len - 1; t >= 0; --t) {
-    const float dl = ld_io<BF16>(rd, q.loff * ES, t * rs);
-    dsum += dl;
-    float dv = ld_f32(rg, q.loff * 4, t * rs4);
-    if (HAS_Z) {
-      const float zv = ld_io<BF16>(rz, q.loff * ES, t * rs);
-      dv *= zv * sigmoid_f(zv);
-    }
-    const float* Ct = Cr + t * NS;
-#pragma unroll
-    for (int n = 0; n < NS; ++n) mu[n] = fast_exp2(dl * a2[n]) * __builtin_fmaf(Ct[n], dv, mu[n]);
-  }
-#pragma unroll
-  for (int n = 0; n < NS; ++n) mu_loc[(((int64_t)q.s * g.batch + q.b) * NS + n) * g.D + q.dc] = mu[n];
-  seg_dsum[((int64_t)q.s * g.batch + q.b) * g.D + q.dc] = dsum;
 }
 
 // ------------------------------------------------------------------ 3. reverse carry
@@ -562,14 +522,7 @@ static hipError_t run_bwd(const BwdArgs& a, const BwdPlan& bp, hipStream_t strea
   float* pd = reinterpret_cast<float*>(ws + bp.off_pd);
   const int64_t per_seg = (int64_t)g.ngroups * g.batch;
   hipError_t e;
-  if (S > 1) {
-    if (a.fwd.z != nullptr)
-      hipLaunchKernelGGL((sel_bwd_local<NS, BF16, true>), dim3((unsigned)(per_seg * (S - 1))), dim3(64), 0, stream,
-                         a.fwd.delta, a.fwd.A, a.fwd.C, a.fwd.z, a.dy, mu, dsum, g);
-    else
-      hipLaunchKernelGGL((sel_bwd_local<NS, BF16, false>), dim3((unsigned)(per_seg * (S - 1))), dim3(64), 0, stream,
-                         a.fwd.delta, a.fwd.A, a.fwd.C, a.fwd.z, a.dy, mu, dsum, g);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (S > 1) {  // the segments' local folds are in mu (checkpoint pass)
     const int64_t nthr = g.batch * (int64_t)NS * g.D;
     hipLaunchKernelGGL(sel_bwd_carry, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, stream, a.fwd.A, a.dh_last,
                        mu, (const float*)dsum, g.batch, g.D, NS, S);
@@ -609,12 +562,13 @@ static hipError_t dispatch_bwd(const BwdArgs& a, const BwdPlan& bp, hipStream_t 
 }
 
 hipError_t launch_selective_bwd(const BwdArgs& a, const BwdPlan& bp, hipStream_t stream) {
-  // 1. the state entering every segment (pass 1 + carry of the forward scan), then the
-  //    state before every K-th step (its checkpoint pass)
+  // 1. the state entering every segment (pass 1 + carry of the forward scan), then 2. the
+  //    state before every K-th step and the segments' adjoint folds (its checkpoint pass)
   hipError_t e = launch_segment_states(a.fwd, bp.fwd, stream);
   if (e != hipSuccess) return e;
   unsigned char* ws = static_cast<unsigned char*>(a.fwd.workspace);
-  e = launch_checkpoints(a.fwd, bp.fwd, reinterpret_cast<float*>(ws + bp.off_ckpt), ilog2c(bp.KC), bp.nsub, stream);
+  e = launch_checkpoints(a.fwd, bp.fwd, reinterpret_cast<float*>(ws + bp.off_ckpt), ilog2c(bp.KC), bp.nsub, a.dy,
+                         bp.fwd.segments > 1 ? reinterpret_cast<float*>(ws + bp.off_mu) : nullptr, stream);
   if (e != hipSuccess) return e;
   return a.fwd.bf16 ? dispatch_bwd<true>(a, bp, stream) : dispatch_bwd<false>(a, bp, stream);
 }

@@ -58,8 +58,9 @@ constexpr int kTileBytes = 64;      // channel-major tiles: bytes of each row pe
 constexpr bool lds_rows(int ns, int fl) { return (fl & 8) == 0 && (ns == 4 || ns == 8 || ns == 16); }
 constexpr int kRowTileBytes = 1024;  // per tensor: 256 / N steps of N fp32 states
 constexpr int ilog2_const(int v) { return v <= 1 ? 0 : 1 + ilog2_const(v / 2); }
-// LDS bytes per wave of the row tiles: two buffers of B (pass 1 and 3) or of B and C (pass 2)
-constexpr int row_tile_lds(int pass) { return 2 * (pass == 2 ? 2 : 1) * kRowTileBytes; }
+// LDS bytes per wave of the row tiles: two buffers of B (pass 1 and 3) or of B and C (pass 2,
+// and pass 3 with the adjoint fold)
+constexpr int row_tile_lds(int pass, bool adj = false) { return 2 * (pass == 2 || adj ? 2 : 1) * kRowTileBytes; }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -74,6 +75,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
 }
 
 constexpr int kZoh = 1, kFront = 2, kSoftplus = 4, kBdl = 8;
+// PASS 3 only: the adjoint's segment fold alongside the checkpoints (see the kernel comment)
+constexpr int kAdj = 16;
+
+// Marks running sums as needed at this point of the step.  Sums that nothing reads until the
+// end of the segment are otherwise moved by the compiler to the end of the unrolled row tile,
+// which keeps every step's inputs to them alive until then (hundreds of spilled registers).
+template <int M>
+__device__ __forceinline__ void keep_here(const float (&v)[M]) {
+#pragma unroll
+  for (int i = 0; i < M; ++i) asm volatile("" ::"v"(v[i]));
+}
+__device__ __forceinline__ void keep_here(float v) { asm volatile("" ::"v"(v)); }
 
 // softplus(v) = max(v, 0) + log1p(e^-|v|); log1p through the log(u) * e / (u - 1) form so
 // that small e keeps its relative precision.
@@ -121,7 +134,13 @@ struct SelSeg {
 //         carry[s][b][n][d] (S > 1) or h0 (S == 1).
 // PASS 3 (segments 0..S-1, for the backward pass): from the same entering state, the state
 //         before every 2^kshift-th step into seg_state[s][b][grp][j][n][lane] (each wave's
-//         checkpoints are one contiguous stream of 256-byte rows).
+//         checkpoints are one contiguous stream of 256-byte rows).  With kAdj it also folds
+//         the segment's adjoint from a zero adjoint at its end: the backward recurrence
+//         mu_{t} = a_t (mu_{t+1} + C_t dv_t) gives at the segment's first step
+//         adj_mu[s][b][n][d] = sum_t P_t[n] C_t[n] dv_t with P_t = a_first ... a_t, the decays
+//         this pass already forms, and dv_t = dy_t silu(z_t) (dy_t without the gate); plus the
+//         segment's delta sum into seg_dsum.  (The same sum the reverse walk forms, accumulated
+//         forward so that each exp serves both.)
 // FL: bit kZoh -- exact zero-order-hold input term, expm1(delta*A)/A * B instead of
 //     delta * B; bits kFront / kSoftplus -- the step size is delta + bias[d], then (with
 //     kSoftplus) softplus of it; bit kBdl -- x/delta/z/y channel-major (batch, dim, seqlen)
@@ -130,8 +149,12 @@ struct SelSeg {
 //     16-byte aligned (g.vec), else one step per access.  B/C arrive time-major either way.
 // fp32 inputs in the pass-2 form with LDS rows, and the exact hold (1/A per state) in either
 // pass, keep more values in flight: 3 waves per SIMD
+// (pass 3 with the adjoint fold keeps its decay products and sums: 3 as well, 2 from 32
+// states on)
 constexpr int min_waves_sel(int ns, int fl, bool bf16, int pass) {
-  return (lds_rows(ns, fl) && ((!bf16 && pass == 2) || (fl & 1) != 0) && min_waves_of(ns, fl) > 3)
+  return (pass == 3 && (fl & 16) != 0)
+             ? (min_waves_of(ns, fl) < (ns >= 32 ? 2 : 3) ? min_waves_of(ns, fl) : (ns >= 32 ? 2 : 3))
+         : (lds_rows(ns, fl) && ((!bf16 && pass == 2) || (fl & 1) != 0) && min_waves_of(ns, fl) > 3)
              ? 3 : min_waves_of(ns, fl);
 }
 // Exact hold: where |delta * A| >= 2^-10 in every lane of a step (checked once per step from
@@ -147,6 +170,7 @@ __global__ __launch_bounds__(256, min_waves_sel(NS, FL, BF16, PASS)) void sel_se
                                                      const float* __restrict__ carry, float* __restrict__ y,
                                                      float* __restrict__ h_last, float* __restrict__ seg_state,
                                                      float* __restrict__ seg_dsum, const float* __restrict__ dbias,
+                                                     const float* __restrict__ dy, float* __restrict__ adj_mu,
                                                      SelSeg g) {
   // Workgroup = gpb waves on adjacent channel groups and the SAME time segment, so that the
   // scalar B_t/C_t rows one wave fetches are scalar-cache hits for the others.
@@ -170,7 +194,9 @@ __global__ __launch_bounds__(256, min_waves_sel(NS, FL, BF16, PASS)) void sel_se
   const int N = NS;
 
   constexpr bool zoh = (FL & kZoh) != 0;
+  constexpr bool adj = PASS == 3 && (FL & kAdj) != 0;
   float a2[NS], h[NS];
+  float pp[adj ? NS : 1], mu[adj ? NS : 1];  // adjoint fold: decay product P and the sum
   // exact hold: 1/A[n]; |A| below 2^-64 (A = 0 included) gets 0 and takes the series, which
   // needs no 1/A (and covers every |delta * A| below 1/16, i.e. any delta below 2^60 there)
   float ia[zoh ? NS : 1];
@@ -183,6 +209,10 @@ __global__ __launch_bounds__(256, min_waves_sel(NS, FL, BF16, PASS)) void sel_se
       ia[n] = fabsf(an) >= 0x1p-64f ? 1.0f / an : 0.0f;
       amin = fminf(amin, fabsf(an));
     }
+    if constexpr (adj) {
+      pp[n] = 1.0f;
+      mu[n] = 0.0f;
+    }
     if (PASS == 1) {
       h[n] = 0.0f;
     } else if (g.S > 1) {
@@ -194,7 +224,7 @@ __global__ __launch_bounds__(256, min_waves_sel(NS, FL, BF16, PASS)) void sel_se
   const float Dd = (PASS == 2 && Dsk != nullptr) ? Dsk[dc] : 0.0f;
   const int kmask = (1 << g.kshift) - 1;
   const float dbv = ((FL & kFront) != 0 && dbias != nullptr) ? dbias[dc] : 0.0f;
-  constexpr bool has_z = PASS == 2 && HAS_Z;
+  constexpr bool has_z = (PASS == 2 || adj) && HAS_Z;
   float dsum = 0.0f;
 
   // Buffer descriptors based at this wave's first element of the segment: per-step offsets
@@ -220,6 +250,7 @@ __global__ __launch_bounds__(256, min_waves_sel(NS, FL, BF16, PASS)) void sel_se
   const __amdgpu_buffer_rsrc_t rd = make_rsrc(db);
   const __amdgpu_buffer_rsrc_t rz = make_rsrc(zb);
   const __amdgpu_buffer_rsrc_t ry = make_rsrc(PASS == 2 ? (const char*)(y + ebase) : (const char*)x);
+  const __amdgpu_buffer_rsrc_t rdy = make_rsrc(adj ? (const char*)(dy + ebase) : (const char*)x);
   const int ystride = bdl ? 4 : (int)(g.D * 4);
   const uint32_t yvo = bdl ? (uint32_t)(loff * g.L * 4) : (uint32_t)loff * 4;
   // channel-major output goes through the caches so that the row pieces of consecutive
@@ -236,9 +267,9 @@ __global__ __launch_bounds__(256, min_waves_sel(NS, FL, BF16, PASS)) void sel_se
   constexpr bool kRows = lds_rows(NS, FL);
   constexpr int kRT = kRows ? kRowTileBytes / (4 * NS) : 1;  // steps per row tile
   constexpr int kRTShift = ilog2_const(kRT);
-  constexpr int kRowTensors = PASS == 2 ? 2 : 1;
+  constexpr int kRowTensors = PASS == 2 || adj ? 2 : 1;
   extern __shared__ uint32_t sss_lds[];  // dynamic LDS: the row tiles or the channel-major tiles
-  float* const lrows = reinterpret_cast<float*>(sss_lds) + wave * (row_tile_lds(PASS) / 4);  // [buf][tensor][256]
+  float* const lrows = reinterpret_cast<float*>(sss_lds) + wave * (row_tile_lds(PASS, adj) / 4);  // [buf][tensor][256]
   const int64_t row_bytes_rem = (g.L - tbeg) * N * 4;  // rows of B/C from this segment to the end
   const uint32_t row_bytes_left = row_bytes_rem < 0x7FFFFFF0 ? (uint32_t)row_bytes_rem : 0x7FFFFFF0u;
   const __amdgpu_buffer_rsrc_t rrb = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(Br), 0, (int)row_bytes_left, 0x00020000);
@@ -247,13 +278,13 @@ __global__ __launch_bounds__(256, min_waves_sel(NS, FL, BF16, PASS)) void sel_se
   auto rows_load = [&](int j) {  // row tile j -> registers
     if constexpr (kRows) {
       grb = __builtin_amdgcn_raw_buffer_load_b128(rrb, lane * 16, j * kRowTileBytes, 0);
-      if constexpr (PASS == 2) grc = __builtin_amdgcn_raw_buffer_load_b128(rrc, lane * 16, j * kRowTileBytes, 0);
+      if constexpr (kRowTensors == 2) grc = __builtin_amdgcn_raw_buffer_load_b128(rrc, lane * 16, j * kRowTileBytes, 0);
     }
   };
   auto rows_store = [&](int buf) {  // registers -> LDS buffer buf
     if constexpr (kRows) {
       *reinterpret_cast<u32x4*>(lrows + buf * (kRowTensors * 256) + lane * 4) = grb;
-      if constexpr (PASS == 2) *reinterpret_cast<u32x4*>(lrows + buf * (kRowTensors * 256) + 256 + lane * 4) = grc;
+      if constexpr (kRowTensors == 2) *reinterpret_cast<u32x4*>(lrows + buf * (kRowTensors * 256) + 256 + lane * 4) = grc;
     }
   };
 
@@ -264,6 +295,7 @@ __global__ __launch_bounds__(256, min_waves_sel(NS, FL, BF16, PASS)) void sel_se
   // raw loaded values (bf16 bits or fp32 bits) are widened only when used, so that the
   // loads of the next batch stay in flight while the current batch is computed
   uint32_t xq[2][QW], dq[2][QW], zq[2][QW];
+  uint32_t gq_dy[2][adj ? QW : 1];  // adjoint fold: dy bits (time-major only)
   // channel-major: outputs stored together -- a batch, or a whole tile (a full row piece
   // of y per lane, written by consecutive stores) when tiles are used
   constexpr int YT = kTileBytes / ES;  // tiled: y steps per store group (a whole tile)
@@ -379,6 +411,8 @@ __global__ __launch_bounds__(256, min_waves_sel(NS, FL, BF16, PASS)) void sel_se
         xq[SLOT][i_] = ld(rx, t_ * rstride);                                     \
         dq[SLOT][i_] = ld(rd, t_ * rstride);                                     \
         if (has_z) zq[SLOT][i_] = ld(rz, t_ * rstride);                          \
+        if constexpr (adj)                                                       \
+          gq_dy[SLOT][i_] = __builtin_amdgcn_raw_buffer_load_b32(rdy, (int)yvo, t_ * ystride, kInPolicy); \
       }                                                                          \
     } else if (vec) { /* len is a multiple of U: the clamp stays aligned */      \
       const int so_ = min((T0), len - U) * ES;                                   \
@@ -409,9 +443,18 @@ __global__ __launch_bounds__(256, min_waves_sel(NS, FL, BF16, PASS)) void sel_se
     const float dl = step_size<FL>(val(dq[SLOT], I), dbv);                       \
     const float dx = dl * xv;                                                    \
     float y0 = Dd * xv, y1 = 0.0f;                                               \
+    float dvv = 0.0f; /* adjoint fold: dy silu(z) */                             \
+    if constexpr (adj) {                                                         \
+      dvv = u32_as_f32(gq_dy[SLOT][I]);                         \
+      if (has_z) dvv *= silu(val(zq[SLOT], I));                                  \
+    }                                                                            \
     _Pragma("unroll") for (int n = 0; n < NS; ++n) {                             \
       const float arg = dl * a2[n];                                              \
       const float ab = fast_exp2(arg);                                           \
+      if constexpr (adj) {                                                       \
+        pp[n] *= ab;                                                             \
+        mu[n] = __builtin_fmaf(pp[n], Ct[n] * dvv, mu[n]);                       \
+      }                                                                          \
       if constexpr (zoh) {                                                       \
         const float cf = zoh_coef(arg, ab, dl, ia[n]);                          \
         h[n] = __builtin_fmaf(ab, h[n], cf * (xv * Bt[n]));                      \
@@ -423,8 +466,10 @@ __global__ __launch_bounds__(256, min_waves_sel(NS, FL, BF16, PASS)) void sel_se
         else y0 = __builtin_fmaf(Ct[n], h[n], y0);                               \
       }                                                                          \
     }                                                                            \
-    if (PASS == 1) {                                                             \
+    if (PASS == 1 || adj) {                                                      \
       dsum += dl;                                                                \
+      if constexpr (adj) keep_here(mu);                                          \
+      keep_here(dsum);                                                           \
     } else if (PASS == 2) {                                                      \
       float out = y0 + y1;                                                       \
       if (has_z) out *= silu(val(zq[SLOT], I));                                  \
@@ -464,7 +509,8 @@ __global__ __launch_bounds__(256, min_waves_sel(NS, FL, BF16, PASS)) void sel_se
   // of the update and read-out.  Grouped like this, the VGPR-only instructions of one wave meet those of
   // another more often and issue in pairs (measured: the per-state cost of the pass-2
   // pattern drops from ~24 to ~21 clocks).
-  auto lstep = [&](const uint32_t (&xs)[QW], const uint32_t (&dqs)[QW], const uint32_t (&zs)[QW], int i, int t) {
+  auto lstep = [&](const uint32_t (&xs)[QW], const uint32_t (&dqs)[QW], const uint32_t (&zs)[QW],
+                   const uint32_t (&dys)[adj ? QW : 1], int i, int t) {
     if constexpr (kRows) {
       const float* brow = lrows + ((t >> kRTShift) & 1) * (kRowTensors * 256) + (t & (kRT - 1)) * NS;
       if (PASS == 3 && (t & kmask) == 0) {
@@ -479,17 +525,23 @@ __global__ __launch_bounds__(256, min_waves_sel(NS, FL, BF16, PASS)) void sel_se
       const float dl = step_size<FL>(val(dqs, i), dbv);
       const float dx = dl * xv;
       float y0 = Dd * xv, y1 = 0.0f;
+      float dvv = 0.0f;  // adjoint fold: dy silu(z)
+      if constexpr (adj) {
+        dvv = u32_as_f32(dys[i]);
+        if constexpr (has_z) dvv *= silu(val(zs, i));
+      }
       // states in groups of GS (the phases of one group hold GS arguments, GS decays and GS
       // rows of B and C in registers)
-      constexpr int GS = NS < 8 ? NS : (BF16 && PASS != 2 && !zoh ? 8 : 4);  // pass 2, fp32 inputs, exact hold: more registers
+      constexpr int GS = NS < 8 ? NS : (BF16 && PASS != 2 && !zoh && !adj ? 8 : 4);  // pass 2, fp32 inputs, exact hold, adjoint: more registers
+      constexpr bool kC = PASS == 2 || adj;  // C rows used
 #pragma unroll
       for (int n0 = 0; n0 < NS; n0 += GS) {
-        float bq[GS], cq[PASS == 2 ? GS : 1];
+        float bq[GS], cq[kC ? GS : 1];
 #pragma unroll
         for (int q = 0; q < GS / 4; ++q) {
           const float4 v = reinterpret_cast<const float4*>(brow + n0)[q];
           bq[4 * q] = v.x; bq[4 * q + 1] = v.y; bq[4 * q + 2] = v.z; bq[4 * q + 3] = v.w;
-          if constexpr (PASS == 2) {
+          if constexpr (kC) {
             const float4 c = reinterpret_cast<const float4*>(brow + 256 + n0)[q];
             cq[4 * q] = c.x; cq[4 * q + 1] = c.y; cq[4 * q + 2] = c.z; cq[4 * q + 3] = c.w;
           }
@@ -513,6 +565,10 @@ __global__ __launch_bounds__(256, min_waves_sel(NS, FL, BF16, PASS)) void sel_se
           if constexpr (PASS == 2) {
             if (n & 1) y1 = __builtin_fmaf(cq[k], h[n], y1);
             else y0 = __builtin_fmaf(cq[k], h[n], y0);
+          }
+          if constexpr (adj) {
+            pp[n] *= ab[k];
+            mu[n] = __builtin_fmaf(pp[n], cq[k] * dvv, mu[n]);
           }
         }
         __builtin_amdgcn_sched_barrier(0x14);
@@ -550,8 +606,10 @@ __global__ __launch_bounds__(256, min_waves_sel(NS, FL, BF16, PASS)) void sel_se
           }
         }
       }
-      if constexpr (PASS == 1) {
+      if constexpr (PASS == 1 || adj) {
         dsum += dl;
+        if constexpr (adj) keep_here(mu);
+        keep_here(dsum);
       } else if constexpr (PASS == 2) {
         float out = y0 + y1;
         if constexpr (has_z) out *= silu(val(zs, i));
@@ -683,10 +741,10 @@ __global__ __launch_bounds__(256, min_waves_sel(NS, FL, BF16, PASS)) void sel_se
       for (int q = 0; q < kRT; q += 2 * U) {
         SSS_LOAD_BATCH(1, t0 + q + U);
 #pragma unroll
-        for (int i = 0; i < U; ++i) lstep(xq[0], dq[0], zq[0], i, t0 + q + i);
+        for (int i = 0; i < U; ++i) lstep(xq[0], dq[0], zq[0], gq_dy[0], i, t0 + q + i);
         SSS_LOAD_BATCH(0, t0 + q + 2 * U);
 #pragma unroll
-        for (int i = 0; i < U; ++i) lstep(xq[1], dq[1], zq[1], i, t0 + q + U + i);
+        for (int i = 0; i < U; ++i) lstep(xq[1], dq[1], zq[1], gq_dy[1], i, t0 + q + U + i);
       }
       rows_store(((t0 >> kRTShift) + 1) & 1);
       rows_load((t0 >> kRTShift) + 2);
@@ -695,20 +753,20 @@ __global__ __launch_bounds__(256, min_waves_sel(NS, FL, BF16, PASS)) void sel_se
     for (; t0 + 2 * U <= len; t0 += 2 * U) {
       SSS_LOAD_BATCH(1, t0 + U);
 #pragma unroll
-      for (int i = 0; i < U; ++i) lstep(xq[0], dq[0], zq[0], i, t0 + i);
+      for (int i = 0; i < U; ++i) lstep(xq[0], dq[0], zq[0], gq_dy[0], i, t0 + i);
       SSS_LOAD_BATCH(0, t0 + 2 * U);
 #pragma unroll
-      for (int i = 0; i < U; ++i) lstep(xq[1], dq[1], zq[1], i, t0 + U + i);
+      for (int i = 0; i < U; ++i) lstep(xq[1], dq[1], zq[1], gq_dy[1], i, t0 + U + i);
     }
     if (t0 < len) {
       SSS_LOAD_BATCH(1, t0 + U);
 #pragma unroll
       for (int i = 0; i < U; ++i)
-        if (t0 + i < len) lstep(xq[0], dq[0], zq[0], i, t0 + i);
+        if (t0 + i < len) lstep(xq[0], dq[0], zq[0], gq_dy[0], i, t0 + i);
       if (t0 + U < len) {
 #pragma unroll
         for (int i = 0; i < U; ++i)
-          if (t0 + U + i < len) lstep(xq[1], dq[1], zq[1], i, t0 + U + i);
+          if (t0 + U + i < len) lstep(xq[1], dq[1], zq[1], gq_dy[1], i, t0 + U + i);
       }
     }
     t0 = len;
@@ -748,6 +806,10 @@ __global__ __launch_bounds__(256, min_waves_sel(NS, FL, BF16, PASS)) void sel_se
     if (lane == 0 || d0 + lane < g.D) seg_dsum[((int64_t)s * g.batch + b) * g.D + dc] = dsum;
 #pragma unroll
     for (int n = 0; n < NS; ++n) seg_state[(((int64_t)s * g.batch + b) * N + n) * g.D + dc] = h[n];
+  } else if (adj) {
+    if (lane == 0 || d0 + lane < g.D) seg_dsum[((int64_t)s * g.batch + b) * g.D + dc] = dsum;
+#pragma unroll
+    for (int n = 0; n < NS; ++n) adj_mu[(((int64_t)s * g.batch + b) * N + n) * g.D + dc] = mu[n];
   } else if (PASS == 2 && h_last != nullptr && s == g.S - 1) {
 #pragma unroll
     for (int n = 0; n < NS; ++n) h_last[(b * g.D + dc) * N + n] = h[n];
@@ -844,7 +906,8 @@ static hipError_t run_states(const SelArgs& a, const SelPlan& pl, hipStream_t st
                                   : lds_rows(NS, FL) ? (size_t)g.gpb * row_tile_lds(1) : 0;  // B row tiles
   hipLaunchKernelGGL((sel_seq_kernel<NS, BF16, 1, false, FL>), dim3((unsigned)(per_seg * (pl.segments - 1))),
                      dim3(64u * (unsigned)g.gpb), lds1, stream, a.x, a.delta, a.A, a.B, a.C, a.Dsk, a.z, a.h0,
-                     (const float*)nullptr, a.y, a.h_last, st, ds, a.delta_bias, g);
+                     (const float*)nullptr, a.y, a.h_last, st, ds, a.delta_bias, (const float*)nullptr,
+                     (float*)nullptr, g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t nthr = g.batch * (int64_t)NS * g.D;
@@ -866,10 +929,12 @@ static hipError_t run_selective(const SelArgs& a, const SelPlan& pl, hipStream_t
                                   : lds_rows(NS, FL) ? (size_t)g.gpb * row_tile_lds(2) : 0;  // B, C row tiles
   if (a.z != nullptr)
     hipLaunchKernelGGL((sel_seq_kernel<NS, BF16, 2, true, FL>), grid, block, lds2, stream, a.x, a.delta, a.A, a.B, a.C,
-                       a.Dsk, a.z, a.h0, st, a.y, a.h_last, (float*)nullptr, (float*)nullptr, a.delta_bias, g);
+                       a.Dsk, a.z, a.h0, st, a.y, a.h_last, (float*)nullptr, (float*)nullptr, a.delta_bias,
+                       (const float*)nullptr, (float*)nullptr, g);
   else
     hipLaunchKernelGGL((sel_seq_kernel<NS, BF16, 2, false, FL>), grid, block, lds2, stream, a.x, a.delta, a.A, a.B,
-                       a.C, a.Dsk, a.z, a.h0, st, a.y, a.h_last, (float*)nullptr, (float*)nullptr, a.delta_bias, g);
+                       a.C, a.Dsk, a.z, a.h0, st, a.y, a.h_last, (float*)nullptr, (float*)nullptr, a.delta_bias,
+                       (const float*)nullptr, (float*)nullptr, g);
   return hipGetLastError();
 }
 
@@ -880,20 +945,38 @@ hipError_t run_segment_states(const SelArgs& a, const SelPlan& pl, hipStream_t s
 }
 
 // Checkpoints for the backward pass (after run_segment_states): the state before every
-// 2^kshift-th step of every segment, into ckpt[s][b][grp][j][n][lane].
+// 2^kshift-th step of every segment, into ckpt[s][b][grp][j][n][lane].  With adj_mu (S > 1)
+// the same pass folds each segment's adjoint from a zero adjoint at its end into
+// adj_mu[s][b][n][d] (dy and the z gate give the read-out's gradient) and writes every
+// segment's delta sum into the forward workspace's sums (the forward carry has used them
+// by then).
 template <int NS, bool BF16>
-hipError_t run_checkpoints(const SelArgs& a, const SelPlan& pl, float* ckpt, int kshift, int nsub,
-                           hipStream_t stream) {
+hipError_t run_checkpoints(const SelArgs& a, const SelPlan& pl, float* ckpt, int kshift, int nsub, const float* dy,
+                           float* adj_mu, hipStream_t stream) {
   SelSeg g = make_seg(a, pl, NS);
   g.kshift = kshift;
   g.nsub = nsub;
   unsigned char* ws = static_cast<unsigned char*>(a.workspace);
   const float* st = pl.segments > 1 ? reinterpret_cast<const float*>(ws + pl.ws_state) : nullptr;
   const int64_t per_seg = (int64_t)g.nblk * g.batch;
+  const dim3 grid((unsigned)(per_seg * pl.segments)), block(64u * (unsigned)g.gpb);
+  if (adj_mu != nullptr && pl.segments > 1) {
+    float* ds = reinterpret_cast<float*>(ws + pl.ws_dsum);
+    const size_t lds3 = lds_rows(NS, kAdj) ? (size_t)g.gpb * row_tile_lds(3, true) : 0;  // B, C row tiles
+    if (a.z != nullptr)
+      hipLaunchKernelGGL((sel_seq_kernel<NS, BF16, 3, true, kAdj>), grid, block, lds3, stream, a.x, a.delta, a.A, a.B,
+                         a.C, a.Dsk, a.z, a.h0, st, (float*)nullptr, (float*)nullptr, ckpt, ds,
+                         (const float*)nullptr, dy, adj_mu, g);
+    else
+      hipLaunchKernelGGL((sel_seq_kernel<NS, BF16, 3, false, kAdj>), grid, block, lds3, stream, a.x, a.delta, a.A,
+                         a.B, a.C, a.Dsk, a.z, a.h0, st, (float*)nullptr, (float*)nullptr, ckpt, ds,
+                         (const float*)nullptr, dy, adj_mu, g);
+    return hipGetLastError();
+  }
   const size_t lds3 = lds_rows(NS, 0) ? (size_t)g.gpb * row_tile_lds(3) : 0;  // B row tiles
-  hipLaunchKernelGGL((sel_seq_kernel<NS, BF16, 3, false, 0>), dim3((unsigned)(per_seg * pl.segments)),
-                     dim3(64u * (unsigned)g.gpb), lds3, stream, a.x, a.delta, a.A, a.B, a.C, a.Dsk, a.z, a.h0, st,
-                     (float*)nullptr, (float*)nullptr, ckpt, (float*)nullptr, (const float*)nullptr, g);
+  hipLaunchKernelGGL((sel_seq_kernel<NS, BF16, 3, false, 0>), grid, block, lds3, stream, a.x, a.delta, a.A, a.B, a.C,
+                     a.Dsk, a.z, a.h0, st, (float*)nullptr, (float*)nullptr, ckpt, (float*)nullptr,
+                     (const float*)nullptr, (const float*)nullptr, (float*)nullptr, g);
   return hipGetLastError();
 }
 
@@ -939,8 +1022,10 @@ template hipError_t run_flags<SSS_INST_NS, false>(const SelArgs&, const SelPlan&
 template hipError_t run_flags<SSS_INST_NS, true>(const SelArgs&, const SelPlan&, hipStream_t);
 template hipError_t run_segment_states<SSS_INST_NS, false>(const SelArgs&, const SelPlan&, hipStream_t);
 template hipError_t run_segment_states<SSS_INST_NS, true>(const SelArgs&, const SelPlan&, hipStream_t);
-template hipError_t run_checkpoints<SSS_INST_NS, false>(const SelArgs&, const SelPlan&, float*, int, int, hipStream_t);
-template hipError_t run_checkpoints<SSS_INST_NS, true>(const SelArgs&, const SelPlan&, float*, int, int, hipStream_t);
+template hipError_t run_checkpoints<SSS_INST_NS, false>(const SelArgs&, const SelPlan&, float*, int, int, const float*,
+                                                        float*, hipStream_t);
+template hipError_t run_checkpoints<SSS_INST_NS, true>(const SelArgs&, const SelPlan&, float*, int, int, const float*,
+                                                       float*, hipStream_t);
 #else
 int selective_row_mode(const SelArgs& a, const SelPlan& pl) {
   if (!a.bdl) return 0;
@@ -954,8 +1039,10 @@ int selective_row_mode(const SelArgs& a, const SelPlan& pl) {
   extern template hipError_t run_flags<N, true>(const SelArgs&, const SelPlan&, hipStream_t);            \
   extern template hipError_t run_segment_states<N, false>(const SelArgs&, const SelPlan&, hipStream_t);  \
   extern template hipError_t run_segment_states<N, true>(const SelArgs&, const SelPlan&, hipStream_t);            \
-  extern template hipError_t run_checkpoints<N, false>(const SelArgs&, const SelPlan&, float*, int, int, hipStream_t); \
-  extern template hipError_t run_checkpoints<N, true>(const SelArgs&, const SelPlan&, float*, int, int, hipStream_t);
+  extern template hipError_t run_checkpoints<N, false>(const SelArgs&, const SelPlan&, float*, int, int, const float*, \
+                                                      float*, hipStream_t);                                         \
+  extern template hipError_t run_checkpoints<N, true>(const SelArgs&, const SelPlan&, float*, int, int, const float*,  \
+                                                     float*, hipStream_t);
 SSS_EXTERN_INSTANCES(1)
 SSS_EXTERN_INSTANCES(2)
 SSS_EXTERN_INSTANCES(4)
@@ -1056,23 +1143,23 @@ hipError_t launch_segment_states(const SelArgs& a, const SelPlan& pl, hipStream_
 
 template <bool BF16>
 static hipError_t dispatch_ckpt(const SelArgs& a, const SelPlan& pl, float* ckpt, int kshift, int nsub,
-                                hipStream_t stream) {
+                                const float* dy, float* adj_mu, hipStream_t stream) {
   switch (a.dstate) {
-    case 1: return run_checkpoints<1, BF16>(a, pl, ckpt, kshift, nsub, stream);
-    case 2: return run_checkpoints<2, BF16>(a, pl, ckpt, kshift, nsub, stream);
-    case 4: return run_checkpoints<4, BF16>(a, pl, ckpt, kshift, nsub, stream);
-    case 8: return run_checkpoints<8, BF16>(a, pl, ckpt, kshift, nsub, stream);
-    case 16: return run_checkpoints<16, BF16>(a, pl, ckpt, kshift, nsub, stream);
-    case 32: return run_checkpoints<32, BF16>(a, pl, ckpt, kshift, nsub, stream);
-    case 64: return run_checkpoints<64, BF16>(a, pl, ckpt, kshift, nsub, stream);
+    case 1: return run_checkpoints<1, BF16>(a, pl, ckpt, kshift, nsub, dy, adj_mu, stream);
+    case 2: return run_checkpoints<2, BF16>(a, pl, ckpt, kshift, nsub, dy, adj_mu, stream);
+    case 4: return run_checkpoints<4, BF16>(a, pl, ckpt, kshift, nsub, dy, adj_mu, stream);
+    case 8: return run_checkpoints<8, BF16>(a, pl, ckpt, kshift, nsub, dy, adj_mu, stream);
+    case 16: return run_checkpoints<16, BF16>(a, pl, ckpt, kshift, nsub, dy, adj_mu, stream);
+    case 32: return run_checkpoints<32, BF16>(a, pl, ckpt, kshift, nsub, dy, adj_mu, stream);
+    case 64: return run_checkpoints<64, BF16>(a, pl, ckpt, kshift, nsub, dy, adj_mu, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_checkpoints(const SelArgs& a, const SelPlan& pl, float* ckpt, int kshift, int nsub,
-                              hipStream_t stream) {
-  return a.bf16 ? dispatch_ckpt<true>(a, pl, ckpt, kshift, nsub, stream)
-                : dispatch_ckpt<false>(a, pl, ckpt, kshift, nsub, stream);
+hipError_t launch_checkpoints(const SelArgs& a, const SelPlan& pl, float* ckpt, int kshift, int nsub, const float* dy,
+                              float* adj_mu, hipStream_t stream) {
+  return a.bf16 ? dispatch_ckpt<true>(a, pl, ckpt, kshift, nsub, dy, adj_mu, stream)
+                : dispatch_ckpt<false>(a, pl, ckpt, kshift, nsub, dy, adj_mu, stream);
 }
 
 #endif  // SSS_INST_NS
