@@ -53,11 +53,12 @@ PMC_TRAFFIC = {
     "decode": {"sources": (CSRC + "state_update.hip", CSRC + "common.h"), "digest": "454225efc541ef58",
                "fetch_kib": 45119.1, "write_kib": 87040.5},
     # selective_scan_bwd on the default workload: the forward pass 1 + carry, the checkpoint
-    # pass, the adjoint's segment fold + carry, the main kernel and the two reductions
+    # pass (with the adjoint's segment folds), the adjoint carry, the main kernel and the two
+    # reductions
     "backward": {"sources": (CSRC + "selective_bwd.hip", CSRC + "selective_scan.hip", CSRC + "common.h"),
-                 "digest": "02f152ba9d1ae3c2",
-                 "fetch_kib": 656561.2 + 46576.9 + 701724.9 + 1329355.3 + 46575.2 + 4471981.9 + 327699.1 + 43549.5,
-                 "write_kib": 86700.0 + 81920.0 + 5242883.2 + 86700.0 + 81920.0 + 4685535.8 + 8192.0 + 660.0},
+                 "digest": "3b99dd2357befdb1",
+                 "fetch_kib": 656871.0 + 46577.0 + 1690466.9 + 46577.9 + 4464972.4 + 327698.6 + 43549.4,
+                 "write_kib": 86700.0 + 81920.0 + 5329922.1 + 81920.0 + 4685562.8 + 8192.0 + 660.0},
     # 1 x 65536 x 5120 bf16, width 4
     "conv": {"sources": (CSRC + "conv1d.hip", CSRC + "common.h"), "digest": "0525304aa8e7045b",
              "fetch_kib": 328260.8, "write_kib": 655360.3},
