@@ -8,7 +8,10 @@ seeded inputs already resident in HBM.  A step is one selective_scan_fwd call.
 Prints ONE JSON line.  `value` is the achieved algorithmic HBM bandwidth (every input read
 once and every output written once, the state never counted) in GB/s.
 
-  python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+  python bench.py [--gpus 1] [--steps 20] [--warmup 30] [--no-cpu-baseline]
+
+The default warm-up of 30 calls brings the GPU to its sustained clock before the timed calls
+(with 3, the first timed calls of the long layer ran up to 25% slower and the mean 6% slower).
   python bench.py --workload 4            # another configuration (0..4); the default is 3
   python bench.py --decode 64             # one decode step of 64 tokens (selective_state_update)
   python bench.py --conv                  # the causal conv1d front end on the long layer
@@ -484,7 +487,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--probes", action="store_true", help="roofline calibration probes (HBM streams, VALU issue)")
