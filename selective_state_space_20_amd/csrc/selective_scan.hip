@@ -1064,12 +1064,15 @@ SelPlan plan_selective(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstat
   const int64_t simds = (int64_t)std::max(num_cus, 1) * 4;
   // One wave per (channel group, segment).  Splitting time costs a second pass over the
   // inputs, so it is only worth it when the channel groups alone leave most SIMDs idle;
-  // then aim at ~20 waves per SIMD: short segments keep every SIMD busy to the end.
+  // then aim at ~20 waves per SIMD: short segments keep every SIMD busy to the end.  Below
+  // 64 steps a segment's fixed costs (entering state, end state, carry) outweigh that
+  // (measured: 8 x 2048 x 1536 at 32 segments 0.166 ms, at 64 0.175; 16 x 2048 x 1024 at 32
+  // segments 0.184, at 64 0.198; 2 x 8192 x 2560 at 128 segments 0.229, at 256 0.253).
   int64_t S = 1;
   if (groups < 2 * simds) {
     const int64_t target = simds * env_int("SSS_WAVES_PER_SIMD", 20);
     S = std::max<int64_t>(1, (target + groups / 2) / groups);
-    S = std::min<int64_t>(S, std::max<int64_t>(1, seqlen / 32));  // segments of >= 32 steps
+    S = std::min<int64_t>(S, std::max<int64_t>(1, seqlen / 64));  // segments of >= 64 steps
     S = std::min<int64_t>(S, 4096);
   }
   const int forced = env_int("SSS_FORCE_SEGMENTS", 0);
