@@ -16,6 +16,8 @@ The default warm-up of 30 calls brings the GPU to its sustained clock before the
   python bench.py --decode 64             # one decode step of 64 tokens (selective_state_update)
   python bench.py --conv                  # the causal conv1d front end on the long layer
   python bench.py --backward              # selective_scan_bwd (all gradients) on the default workload
+  python bench.py --train-step [--saved-states]  # forward + gradients together (optionally keeping
+                                          # the forward's segment entering states for the gradients)
   python bench.py --copy-calibration      # plain copy of a known size, for counter scaling
   python bench.py --probes                # roofline calibration: HBM stream rates, VALU/exp issue costs
 """
@@ -483,6 +485,68 @@ def bench_backward(steps, warmup):
     }), flush=True)
 
 
+def bench_train_step(steps, warmup, saved):
+    """One training step of the default layer: selective_scan_fwd then selective_scan_bwd on
+    the same inputs (dy given), timed together.  With saved=True the pair that keeps the
+    forward's segment entering states for the gradients call (selective_scan_fwd_save /
+    selective_scan_bwd_saved), which skips the gradients call's recomputation of them."""
+    import torch
+    import selective_state_space_20_amd as sss
+    from selective_state_space_20_amd import inputs as gen
+    cfg, inp = gen.config_inputs(WORKLOAD_INDEX)
+    dev = torch.device("cuda:0")
+
+    def td(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    t = {k: td(v) for k, v in inp.items() if k != "io"}
+    b, L, d, n = cfg["batch"], cfg["seqlen"], cfg["dim"], cfg["dstate"]
+    g = torch.Generator(device=dev)
+    g.manual_seed(5000)
+    dy = torch.randn((b, L, d), device=dev, generator=g)
+    dhl = torch.randn((b, d, n), device=dev, generator=g)
+    y = torch.empty((b, L, d), dtype=torch.float32, device=dev)
+    hl = torch.empty((b, d, n), dtype=torch.float32, device=dev)
+    ws = torch.empty(sss.selective_scan_bwd_workspace_size(b, L, d, n, 0), dtype=torch.uint8, device=dev)
+    sbytes = sss.selective_scan_states_size(b, L, d, n, 0)
+    states = torch.empty(max(sbytes, 4) // 4, dtype=torch.float32, device=dev) if saved else None
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        sss.selective_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"], out=y,
+                               out_last=hl, workspace=ws, states=states)
+        sss.selective_scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"], dy=dy,
+                               dh_last=dhl, workspace=ws, states=states)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    mean_ms = float(np.mean(ms))
+    e = b * L * d
+    log(f"[bench] train step ({'saved states' if saved else 'states recomputed'}) {cfg['name']}: event mean "
+        f"{mean_ms:.4f} ms, median {float(np.median(ms)):.4f}, min {min(ms):.4f}, states {sbytes / 1e6:.1f} MB")
+    print(json.dumps({
+        "metric": "selective scan training step (forward + gradients) elements/s, 1 GPU",
+        "value": round(e / (mean_ms * 1e-3), 1), "unit": "elements/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(mean_ms, 5), "higher_is_better": True, "dtype": "f32", "io_dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "train_step_" + cfg["name"], "saved_states": bool(saved), "states_bytes": sbytes,
+                   "elements": e},
+        "call_ms": {"mean": round(mean_ms, 5), "median": round(float(np.median(ms)), 5), "min": round(min(ms), 5),
+                    "max": round(max(ms), 5)},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -495,6 +559,10 @@ def main():
     ap.add_argument("--workload", type=int, default=WORKLOAD_INDEX, help="configuration index 0..4")
     ap.add_argument("--conv", action="store_true", help="time the causal conv1d front end instead")
     ap.add_argument("--backward", action="store_true", help="time selective_scan_bwd on the default workload")
+    ap.add_argument("--train-step", action="store_true",
+                    help="time selective_scan_fwd + selective_scan_bwd together on the default workload")
+    ap.add_argument("--saved-states", action="store_true",
+                    help="with --train-step: keep the forward's segment entering states for the gradients call")
     ap.add_argument("--decode", type=int, default=0, metavar="BATCH",
                     help="time one decode step (selective_state_update) of BATCH tokens instead")
     ap.add_argument("--no-flush", action="store_true",
@@ -521,6 +589,9 @@ def main():
         return
     if args.backward:
         bench_backward(args.steps, args.warmup)
+        return
+    if args.train_step:
+        bench_train_step(args.steps, args.warmup, args.saved_states)
         return
     if args.decode > 0:
         bench_decode(args.decode, args.steps, args.warmup, flush=not args.no_flush)

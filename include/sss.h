@@ -15,7 +15,9 @@
  *      delta, B and C are outside this library ("15. Selective (Data-Dependent) SSM
  *      Scan", Problem: the data-dependent parameters are given).
  *
- *  selective_scan_bwd -- its gradients (training), with the states recomputed.
+ *  selective_scan_bwd -- its gradients (training), with the states recomputed;
+ *      selective_scan_fwd_save / selective_scan_bwd_saved the same pair with the forward
+ *      call's segment entering states kept for the gradients call.
  *
  *  selective_state_update -- one decode step of the same recurrence on a carried state
  *      (in place), for token-by-token generation.
@@ -119,6 +121,42 @@ int selective_scan_bwd(const void* x, const void* delta, const float* A, const f
                        float* dx, float* ddelta, float* dA, float* dB, float* dC, float* dD, float* dz, float* dh0,
                        int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype, void* workspace,
                        size_t workspace_bytes, sss_stream_t stream);
+
+/* Training pair that keeps the forward call's segment entering states instead of recomputing
+ * them in the gradients call.  Only the state at each time segment's start is kept, a
+ * fraction (segments / seqlen) of the state the recurrence forms; everything else is still
+ * recomputed ("Selective Scan trong Mamba toi uu chuoi dai the nao?", section
+ * "Recomputation: doi mot it compute lay it memory hon").
+ *
+ * selective_scan_states_size: bytes of that buffer for these sizes on `device` (0 when the
+ * plan has a single time segment: nothing to keep; 0 as well on invalid sizes).  Layout
+ * [segments][batch][dstate][dim] float32, opaque to the caller; it depends only on the sizes
+ * and the device (the forward call's plan), so the size query is the contract. */
+size_t selective_scan_states_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int device);
+
+/* selective_scan_fwd_save: exactly selective_scan_fwd (same arguments, results bitwise the
+ * same), and the segment entering states left in `states` (caller-owned device buffer of at
+ * least selective_scan_states_size() bytes; may be NULL when that is 0; it may not overlap
+ * any input, output or the workspace: SSS_ERR_ALIAS; too small: SSS_ERR_WORKSPACE). */
+int selective_scan_fwd_save(const void* x, const void* delta, const float* A, const float* B, const float* C,
+                            const float* D_skip, const void* z, const float* h0, float* y, float* h_last,
+                            float* states, size_t states_bytes, int64_t batch, int64_t seqlen, int64_t dim,
+                            int64_t dstate, int io_dtype, void* workspace, size_t workspace_bytes,
+                            sss_stream_t stream);
+
+/* selective_scan_bwd_saved: exactly selective_scan_bwd (same arguments and results, bitwise)
+ * with the segment entering states read from `states` instead of recomputed (the forward
+ * scan's first pass and carry are skipped).  `states` must hold what selective_scan_fwd_save
+ * wrote for the same x, delta, A, B, h0, sizes, dtype and device (C, D, z do not enter the
+ * states), unmodified since; the library cannot check that, and anything else gives wrong
+ * gradients.  Read only; NULL allowed when selective_scan_states_size() is 0.  Size and
+ * overlap rules as for selective_scan_fwd_save (the inputs may share it: it is read only). */
+int selective_scan_bwd_saved(const void* x, const void* delta, const float* A, const float* B, const float* C,
+                             const float* D_skip, const void* z, const float* h0, const float* dy,
+                             const float* dh_last, const float* states, size_t states_bytes, float* dx, float* ddelta,
+                             float* dA, float* dB, float* dC, float* dD, float* dz, float* dh0, int64_t batch,
+                             int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype, void* workspace,
+                             size_t workspace_bytes, sss_stream_t stream);
 
 /* One decode step of the selective scan ("Selective Scan trong Mamba toi uu chuoi dai the
  * nao?", section "Selective Scan thay doi inference chuoi dai nhu the nao?": generation

@@ -23,7 +23,8 @@ EXPORTED = ("selective_scan_fwd", "selective_scan_fwd_ex", "selective_scan_fwd_w
             "selective_scan_fwd_ex_workspace_size", "selective_state_update",
             "causal_conv1d_fwd", "selective_scan_bwd", "selective_scan_bwd_workspace_size",
             "elementwise_scan", "elementwise_scan_workspace_size", "sss_status_string",
-            "selective_scan_fwd_noalloc")
+            "selective_scan_fwd_noalloc", "selective_scan_states_size", "selective_scan_fwd_save",
+            "selective_scan_bwd_saved")
 
 
 class SSSError(RuntimeError):
@@ -70,6 +71,12 @@ def load() -> ctypes.CDLL:
         lib.elementwise_scan_workspace_size.restype = sz
         lib.selective_scan_fwd_noalloc.argtypes = [vp] * 10 + [i64] * 4 + [i32, vp]
         lib.selective_scan_fwd_noalloc.restype = i32
+        lib.selective_scan_states_size.argtypes = [i64] * 4 + [i32]
+        lib.selective_scan_states_size.restype = sz
+        lib.selective_scan_fwd_save.argtypes = [vp] * 11 + [sz] + [i64] * 4 + [i32, vp, sz, vp]
+        lib.selective_scan_fwd_save.restype = i32
+        lib.selective_scan_bwd_saved.argtypes = [vp] * 11 + [sz] + [vp] * 8 + [i64] * 4 + [i32, vp, sz, vp]
+        lib.selective_scan_bwd_saved.restype = i32
         lib.sss_status_string.argtypes = [i32]
         lib.sss_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -111,9 +118,51 @@ def selective_scan_bwd_workspace_size(batch, seqlen, dim, dstate, device=0) -> i
     return int(load().selective_scan_bwd_workspace_size(batch, seqlen, dim, dstate, device))
 
 
+def selective_scan_states_size(batch, seqlen, dim, dstate, device=0) -> int:
+    """Bytes of the segment entering states selective_scan_fwd_save keeps (0: nothing to keep)."""
+    return int(load().selective_scan_states_size(batch, seqlen, dim, dstate, device))
+
+
+def selective_scan_fwd_save_raw(x, delta, A, B, C, D_skip, z, h0, y, h_last, states, states_bytes, batch, seqlen, dim,
+                                dstate, io_dtype, workspace, workspace_bytes, stream) -> int:
+    return load().selective_scan_fwd_save(x, delta, A, B, C, D_skip, z, h0, y, h_last, states, states_bytes, batch,
+                                          seqlen, dim, dstate, io_dtype, workspace, workspace_bytes, stream)
+
+
+def selective_scan_bwd_saved_raw(x, delta, A, B, C, D_skip, z, h0, dy, dh_last, states, states_bytes, dx, ddelta, dA,
+                                 dB, dC, dD, dz, dh0, batch, seqlen, dim, dstate, io_dtype, workspace, workspace_bytes,
+                                 stream) -> int:
+    return load().selective_scan_bwd_saved(x, delta, A, B, C, D_skip, z, h0, dy, dh_last, states, states_bytes, dx,
+                                           ddelta, dA, dB, dC, dD, dz, dh0, batch, seqlen, dim, dstate, io_dtype,
+                                           workspace, workspace_bytes, stream)
+
+
+def _states_buffer(states, nbytes, dev):
+    """(pointer, bytes) of a caller's saved-states buffer: a uint8 or float32 CUDA tensor of at
+    least nbytes on dev; None only when nothing is kept (nbytes == 0)."""
+    import torch
+    if states is None:
+        if nbytes > 0:
+            raise ValueError(f"states: a buffer of {nbytes} bytes is needed (selective_scan_states_size)")
+        return 0, 0
+    if not isinstance(states, torch.Tensor) or states.dtype not in (torch.uint8, torch.float32):
+        raise ValueError("states must be a uint8 or float32 torch tensor")
+    if not states.is_contiguous():
+        raise ValueError("states must be contiguous")
+    if states.device != dev:
+        raise ValueError(f"states is on {states.device}, the inputs on {dev}")
+    have = states.numel() * states.element_size()
+    if have < nbytes:
+        raise ValueError(f"states holds {have} bytes, {nbytes} are needed")
+    return states.data_ptr(), have
+
+
 def selective_scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, *, dy, dh_last=None, want_dh0=True,
-                       workspace=None, stream=None):
+                       workspace=None, stream=None, states=None):
     """Gradients of sum(dy * y) + sum(dh_last * h_last) of selective_scan_fwd (plain form).
+
+    states: the buffer a selective_scan_fwd(..., states=...) call on the same x, delta, A, B,
+    h0 filled (selective_scan_bwd_saved); None recomputes them (selective_scan_bwd).
 
     Returns a dict of float32 tensors: dx, ddelta, dA, dB, dC, and dD (with D), dz (with z),
     dh0 (if want_dh0)."""
@@ -142,12 +191,21 @@ def selective_scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, *, dy, dh_las
         workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
     wsp, wsn = _workspace(workspace, dev)
     st = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
-    rc = selective_scan_bwd_raw(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(dy),
-                                _ptr(dh_last), _ptr(g["dx"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]),
-                                _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["dh0"]), batch, seqlen, dim, dstate,
-                                io_code, wsp, wsn, st)
+    if states is None:
+        rc = selective_scan_bwd_raw(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+                                    _ptr(dy), _ptr(dh_last), _ptr(g["dx"]), _ptr(g["ddelta"]), _ptr(g["dA"]),
+                                    _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["dh0"]), batch,
+                                    seqlen, dim, dstate, io_code, wsp, wsn, st)
+        if rc != 0:
+            raise SSSError(rc, "selective_scan_bwd")
+        return g
+    sp, sn = _states_buffer(states, selective_scan_states_size(batch, seqlen, dim, dstate, dev.index or 0), dev)
+    rc = selective_scan_bwd_saved_raw(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+                                      _ptr(dy), _ptr(dh_last), sp, sn, _ptr(g["dx"]), _ptr(g["ddelta"]), _ptr(g["dA"]),
+                                      _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["dh0"]), batch,
+                                      seqlen, dim, dstate, io_code, wsp, wsn, st)
     if rc != 0:
-        raise SSSError(rc, "selective_scan_bwd")
+        raise SSSError(rc, "selective_scan_bwd_saved")
     return g
 
 
@@ -247,7 +305,7 @@ def _workspace(ws, device):
 
 def selective_scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, return_last=True, out=None,
                        out_last=None, workspace=None, stream=None, delta_bias=None, delta_softplus=False,
-                       exact_zoh=False, layout="bld"):
+                       exact_zoh=False, layout="bld", states=None):
     """y (batch, seqlen, dim) float32 [, h_last (batch, dim, dstate) float32].
 
     x, delta, z: float32 or bfloat16 (one dtype); A (dim, dstate), B, C (batch, seqlen,
@@ -293,6 +351,15 @@ def selective_scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, return_las
         workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
     wsp, wsn = _workspace(workspace, dev)
     st = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
+    if states is not None:  # selective_scan_fwd_save: the plain form, keeping the segment entering states
+        if flags != 0 or delta_bias is not None:
+            raise ValueError("states: the forward that keeps its states is the plain form (no options)")
+        sp, sn = _states_buffer(states, selective_scan_states_size(batch, seqlen, dim, dstate, dev.index or 0), dev)
+        rc = selective_scan_fwd_save_raw(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+                                         _ptr(y), _ptr(hl), sp, sn, batch, seqlen, dim, dstate, io_code, wsp, wsn, st)
+        if rc != 0:
+            raise SSSError(rc, "selective_scan_fwd_save")
+        return (y, hl) if return_last or out_last is not None else y
     rc = selective_scan_fwd_ex_raw(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
                                    _ptr(y), _ptr(hl), _ptr(delta_bias), flags, batch, seqlen, dim, dstate, io_code,
                                    wsp, wsn, st)

@@ -137,7 +137,7 @@ int sel_fwd_impl(const void* x, const void* delta, const float* A, const float* 
                  const float* D_skip, const void* z, const float* h0, float* y, float* h_last,
                  const float* delta_bias, unsigned flags, int64_t batch, int64_t seqlen, int64_t dim,
                  int64_t dstate, int io_dtype, void* workspace, size_t workspace_bytes, size_t max_ws,
-                 void* stream) {
+                 void* stream, bool save_states, float* states, size_t states_bytes) {
   if (!x || !delta || !A || !B || !C || !y) return SSS_ERR_NULL_ARG;
   int st = sel_dims_ok(batch, seqlen, dim, dstate);
   if (st != SSS_OK) return st;
@@ -145,7 +145,7 @@ int sel_fwd_impl(const void* x, const void* delta, const float* A, const float* 
   if ((flags & ~kKnownFlags) != 0) return SSS_ERR_UNSUPPORTED;
   const bool bdl = (flags & SSS_LAYOUT_BDL) != 0;
   if (bdl && seqlen > kMaxBdlSeqlen) return SSS_ERR_BAD_DIM;
-  const void* ptrs[] = {x, delta, A, B, C, D_skip, z, h0, y, h_last, workspace, delta_bias};
+  const void* ptrs[] = {x, delta, A, B, C, D_skip, z, h0, y, h_last, workspace, delta_bias, states};
   for (const void* p : ptrs)
     if (!aligned16(p)) return SSS_ERR_UNSUPPORTED;
   const int64_t es = io_dtype == SSS_BF16 ? 2 : 4;
@@ -173,6 +173,21 @@ int sel_fwd_impl(const void* x, const void* delta, const float* A, const float* 
     for (int i = 0; i < 9; ++i)
       if (overlap(workspace, wb, in_p[i], in_b[i])) return SSS_ERR_ALIAS;
   }
+  // the saved segment entering states (plain form only): a caller buffer in place of the
+  // workspace's slots, so that they outlive the call
+  const int64_t sb = save_states && pl.segments > 1 ? (int64_t)pl.segments * batch * dstate * dim * 4 : 0;
+  if (save_states) {
+    if (flags != 0) return SSS_ERR_UNSUPPORTED;
+    if (sb > 0) {
+      if (states == nullptr) return SSS_ERR_NULL_ARG;
+      if (states_bytes < (size_t)sb) return SSS_ERR_WORKSPACE;
+      if (overlap(states, sb, y, y_bytes) || overlap(states, sb, h_last, hl_bytes) ||
+          overlap(states, sb, workspace, (int64_t)pl.ws_total))
+        return SSS_ERR_ALIAS;
+      for (int i = 0; i < 9; ++i)
+        if (overlap(states, sb, in_p[i], in_b[i])) return SSS_ERR_ALIAS;
+    }
+  }
   SelArgs a{};
   a.x = x;
   a.delta = delta;
@@ -194,9 +209,11 @@ int sel_fwd_impl(const void* x, const void* delta, const float* A, const float* 
   a.softplus = (flags & SSS_DELTA_SOFTPLUS) != 0;
   a.exact_zoh = (flags & SSS_EXACT_ZOH) != 0;
   a.bdl = bdl;
+  a.states = sb > 0 ? states : nullptr;
   // the single-pass form with the workgroup pair scan: forced on (1) or off (0) by SSS_CHUNKED
+  // (never when the states are saved: it forms none)
   const int chunked_env = env_int("SSS_CHUNKED", -1);
-  const bool chunked = chunk_scan_supported(a) && chunked_env == 1;
+  const bool chunked = !save_states && chunk_scan_supported(a) && chunked_env == 1;
   if (env_int("SSS_LOG", 0)) {
     static const char* const kRows[] = {"time-major", "step", "piece", "tile"};
     if (chunked)
@@ -228,6 +245,23 @@ int selective_scan_fwd_ex(const void* x, const void* delta, const float* A, cons
                       io_dtype, workspace, workspace_bytes, 0, stream);
 }
 
+size_t selective_scan_states_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int device) {
+  if (sel_dims_ok(batch, seqlen, dim, dstate) != SSS_OK) return 0;
+  int cus = device_cus(device);
+  if (cus <= 0) cus = 256;
+  const SelPlan pl = plan_selective(batch, seqlen, dim, dstate, cus);
+  return pl.segments > 1 ? (size_t)pl.segments * batch * dstate * dim * 4 : 0;
+}
+
+int selective_scan_fwd_save(const void* x, const void* delta, const float* A, const float* B, const float* C,
+                            const float* D_skip, const void* z, const float* h0, float* y, float* h_last,
+                            float* states, size_t states_bytes, int64_t batch, int64_t seqlen, int64_t dim,
+                            int64_t dstate, int io_dtype, void* workspace, size_t workspace_bytes,
+                            sss_stream_t stream) {
+  return sel_fwd_impl(x, delta, A, B, C, D_skip, z, h0, y, h_last, nullptr, 0u, batch, seqlen, dim, dstate, io_dtype,
+                      workspace, workspace_bytes, 0, stream, true, states, states_bytes);
+}
+
 
 size_t selective_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int device) {
   if (sel_dims_ok(batch, seqlen, dim, dstate) != SSS_OK) return 0;
@@ -236,18 +270,25 @@ size_t selective_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t 
   return plan_selective_bwd(batch, seqlen, dim, dstate, cus).ws_total;
 }
 
-int selective_scan_bwd(const void* x, const void* delta, const float* A, const float* B, const float* C,
-                       const float* D_skip, const void* z, const float* h0, const float* dy, const float* dh_last,
-                       float* dx, float* ddelta, float* dA, float* dB, float* dC, float* dD, float* dz, float* dh0,
-                       int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype, void* workspace,
-                       size_t workspace_bytes, sss_stream_t stream) {
+}  // extern "C"
+
+namespace sss {
+// The gradients call: validation, plan, launch.  states: the segment entering states a
+// selective_scan_fwd_save call left (nullptr: recomputed).
+static int sel_bwd_impl(const void* x, const void* delta, const float* A, const float* B, const float* C,
+                        const float* D_skip, const void* z, const float* h0, const float* dy, const float* dh_last,
+                        float* dx, float* ddelta, float* dA, float* dB, float* dC, float* dD, float* dz, float* dh0,
+                        int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype, const float* states,
+                        size_t states_bytes, bool use_states, void* workspace, size_t workspace_bytes,
+                        sss_stream_t stream) {
   if (!x || !delta || !A || !B || !C || !dy || !dx || !ddelta || !dA || !dB || !dC) return SSS_ERR_NULL_ARG;
   if ((D_skip && !dD) || (z && !dz)) return SSS_ERR_NULL_ARG;
   int st = sel_dims_ok(batch, seqlen, dim, dstate);
   if (st != SSS_OK) return st;
   if (dim * dstate * 4 >= ((int64_t)1 << 31)) return SSS_ERR_BAD_DIM;  // checkpoint rows: 32-bit offsets
   if (io_dtype != SSS_F32 && io_dtype != SSS_BF16) return SSS_ERR_UNSUPPORTED;
-  const void* ptrs[] = {x, delta, A, B, C, D_skip, z, h0, dy, dh_last, dx, ddelta, dA, dB, dC, dD, dz, dh0, workspace};
+  const void* ptrs[] = {x, delta, A, B, C, D_skip, z, h0, dy, dh_last, dx, ddelta, dA, dB, dC, dD, dz, dh0, workspace,
+                        states};
   for (const void* p : ptrs)
     if (!aligned16(p)) return SSS_ERR_UNSUPPORTED;
   const int64_t es = io_dtype == SSS_BF16 ? 2 : 4;
@@ -273,6 +314,15 @@ int selective_scan_bwd(const void* x, const void* delta, const float* A, const f
     if (overlap(workspace, wb, in_p[i], in_b[i])) return SSS_ERR_ALIAS;
   for (int i = 0; i < 8; ++i)
     if (overlap(workspace, wb, out_p[i], out_b[i])) return SSS_ERR_ALIAS;
+  // saved states: exactly the forward plan's slots
+  const int64_t sb = bp.fwd.segments > 1 ? (int64_t)bp.fwd.segments * batch * dstate * dim * 4 : 0;
+  if (use_states && sb > 0) {
+    if (states == nullptr) return SSS_ERR_NULL_ARG;
+    if (states_bytes < (size_t)sb) return SSS_ERR_WORKSPACE;
+    if (overlap(states, sb, workspace, wb)) return SSS_ERR_ALIAS;
+    for (int i = 0; i < 8; ++i)
+      if (overlap(states, sb, out_p[i], out_b[i])) return SSS_ERR_ALIAS;
+  }
   if (env_int("SSS_LOG", 0))
     std::fprintf(stderr,
                  "[sss] selective_scan_bwd B=%lld L=%lld D=%lld N=%lld: segments=%d seg_len=%lld K=%d checkpoint every %d "
@@ -304,7 +354,31 @@ int selective_scan_bwd(const void* x, const void* delta, const float* A, const f
   a.dD = dD;
   a.dz = dz;
   a.dh0 = dh0;
+  a.states_ready = use_states && sb > 0;
+  a.fwd.states = a.states_ready ? const_cast<float*>(states) : nullptr;  // read only
   return launch_selective_bwd(a, bp, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? SSS_OK : SSS_ERR_HIP;
+}
+}  // namespace sss
+
+extern "C" {
+
+int selective_scan_bwd(const void* x, const void* delta, const float* A, const float* B, const float* C,
+                       const float* D_skip, const void* z, const float* h0, const float* dy, const float* dh_last,
+                       float* dx, float* ddelta, float* dA, float* dB, float* dC, float* dD, float* dz, float* dh0,
+                       int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype, void* workspace,
+                       size_t workspace_bytes, sss_stream_t stream) {
+  return sel_bwd_impl(x, delta, A, B, C, D_skip, z, h0, dy, dh_last, dx, ddelta, dA, dB, dC, dD, dz, dh0, batch,
+                      seqlen, dim, dstate, io_dtype, nullptr, 0, false, workspace, workspace_bytes, stream);
+}
+
+int selective_scan_bwd_saved(const void* x, const void* delta, const float* A, const float* B, const float* C,
+                             const float* D_skip, const void* z, const float* h0, const float* dy,
+                             const float* dh_last, const float* states, size_t states_bytes, float* dx, float* ddelta,
+                             float* dA, float* dB, float* dC, float* dD, float* dz, float* dh0, int64_t batch,
+                             int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype, void* workspace,
+                             size_t workspace_bytes, sss_stream_t stream) {
+  return sel_bwd_impl(x, delta, A, B, C, D_skip, z, h0, dy, dh_last, dx, ddelta, dA, dB, dC, dD, dz, dh0, batch,
+                      seqlen, dim, dstate, io_dtype, states, states_bytes, true, workspace, workspace_bytes, stream);
 }
 
 int selective_state_update(const void* x, const void* delta, const float* A, const float* B, const float* C,

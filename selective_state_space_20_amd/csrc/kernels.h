@@ -32,6 +32,8 @@ struct SelArgs {
   int softplus;             // step size = softplus(delta (+ bias))
   int exact_zoh;            // input term expm1(delta*A)/A * B instead of delta * B
   int bdl;                  // x/delta/z/y (batch, dim, seqlen), B/C (batch, dstate, seqlen)
+  float* states;            // nullable: the segment entering states [S][batch][dstate][dim] live
+                            // here instead of in the workspace (kept for the backward pass)
 };
 
 // max_ws > 0: at most max_ws bytes of workspace (fewer segments if the usual plan needs more)
@@ -48,7 +50,7 @@ int sel_fwd_impl(const void* x, const void* delta, const float* A, const float* 
                  const float* D_skip, const void* z, const float* h0, float* y, float* h_last,
                  const float* delta_bias, unsigned flags, int64_t batch, int64_t seqlen, int64_t dim,
                  int64_t dstate, int io_dtype, void* workspace, size_t workspace_bytes, size_t max_ws,
-                 void* stream);
+                 void* stream, bool save_states = false, float* states = nullptr, size_t states_bytes = 0);
 // how the forward kernels walk the rows: 0 time-major; channel-major 1 one step per access,
 // 2 16-byte pieces per lane, 3 tiles staged through LDS
 int selective_row_mode(const SelArgs& a, const SelPlan& plan);
@@ -82,6 +84,7 @@ struct BwdArgs {
   float* dD;
   float* dz;
   float* dh0;
+  bool states_ready;  // fwd.states already holds the segment entering states (saved by the forward)
 };
 
 BwdPlan plan_selective_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int num_cus);

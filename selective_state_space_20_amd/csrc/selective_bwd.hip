@@ -562,9 +562,10 @@ static hipError_t dispatch_bwd(const BwdArgs& a, const BwdPlan& bp, hipStream_t 
 }
 
 hipError_t launch_selective_bwd(const BwdArgs& a, const BwdPlan& bp, hipStream_t stream) {
-  // 1. the state entering every segment (pass 1 + carry of the forward scan), then 2. the
-  //    state before every K-th step and the segments' adjoint folds (its checkpoint pass)
-  hipError_t e = launch_segment_states(a.fwd, bp.fwd, stream);
+  // 1. the state entering every segment (pass 1 + carry of the forward scan; skipped when
+  //    the forward call saved them), then 2. the state before every K-th step and the
+  //    segments' adjoint folds (its checkpoint pass)
+  hipError_t e = a.states_ready ? hipSuccess : launch_segment_states(a.fwd, bp.fwd, stream);
   if (e != hipSuccess) return e;
   unsigned char* ws = static_cast<unsigned char*>(a.fwd.workspace);
   e = launch_checkpoints(a.fwd, bp.fwd, reinterpret_cast<float*>(ws + bp.off_ckpt), ilog2c(bp.KC), bp.nsub, a.dy,

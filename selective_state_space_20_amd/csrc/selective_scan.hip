@@ -892,14 +892,19 @@ static __global__ __launch_bounds__(256) void bc_rows_kernel(const float* __rest
   }
 }
 
-// Pass 1 and the carry: the workspace's state slots end up holding the state entering
-// every segment (S > 1; nothing to do for a single segment).
+// The segment state slots: the caller's buffer when one is given, else the workspace's.
+static float* state_slots(const SelArgs& a, const SelPlan& pl) {
+  return a.states != nullptr ? a.states : reinterpret_cast<float*>(static_cast<unsigned char*>(a.workspace) + pl.ws_state);
+}
+
+// Pass 1 and the carry: the state slots end up holding the state entering every segment
+// (S > 1; nothing to do for a single segment).
 template <int NS, bool BF16, int FL>
 static hipError_t run_states(const SelArgs& a, const SelPlan& pl, hipStream_t stream) {
   if (pl.segments <= 1) return hipSuccess;
   const SelSeg g = make_seg(a, pl, NS);
   unsigned char* ws = static_cast<unsigned char*>(a.workspace);
-  float* st = reinterpret_cast<float*>(ws + pl.ws_state);
+  float* st = state_slots(a, pl);
   float* ds = reinterpret_cast<float*>(ws + pl.ws_dsum);
   const int64_t per_seg = (int64_t)g.nblk * g.batch;
   const size_t lds1 = g.vec == 2 ? (size_t)g.gpb * 2 * 64 * kTileBytes  // x, delta tiles
@@ -921,8 +926,7 @@ static hipError_t run_selective(const SelArgs& a, const SelPlan& pl, hipStream_t
   hipError_t e = run_states<NS, BF16, FL>(a, pl, stream);
   if (e != hipSuccess) return e;
   const SelSeg g = make_seg(a, pl, NS);
-  unsigned char* ws = static_cast<unsigned char*>(a.workspace);
-  const float* st = pl.segments > 1 ? reinterpret_cast<const float*>(ws + pl.ws_state) : nullptr;
+  const float* st = pl.segments > 1 ? state_slots(a, pl) : nullptr;
   const int64_t per_seg = (int64_t)g.nblk * g.batch;
   const dim3 grid((unsigned)(per_seg * pl.segments)), block(64u * (unsigned)g.gpb);
   const size_t lds2 = g.vec == 2 ? (size_t)g.gpb * (a.z != nullptr ? 3 : 2) * 64 * kTileBytes
@@ -957,7 +961,7 @@ hipError_t run_checkpoints(const SelArgs& a, const SelPlan& pl, float* ckpt, int
   g.kshift = kshift;
   g.nsub = nsub;
   unsigned char* ws = static_cast<unsigned char*>(a.workspace);
-  const float* st = pl.segments > 1 ? reinterpret_cast<const float*>(ws + pl.ws_state) : nullptr;
+  const float* st = pl.segments > 1 ? state_slots(a, pl) : nullptr;
   const int64_t per_seg = (int64_t)g.nblk * g.batch;
   const dim3 grid((unsigned)(per_seg * pl.segments)), block(64u * (unsigned)g.gpb);
   if (adj_mu != nullptr && pl.segments > 1) {

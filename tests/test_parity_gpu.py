@@ -371,6 +371,75 @@ def test_backward(oracle_lib, monkeypatch, case):
     assert all(v <= tol for v in errs.values()), errs
 
 
+SAVED_CASES = [(2, 1500, 100, 16, "bf16", 5), (1, 777, 70, 8, "f32", 3), (1, 900, 64, 4, "bf16", 0),
+               (2, 96, 64, 16, "f32", 1), (1, 700, 20, 64, "bf16", 0)]
+
+
+@pytest.mark.parametrize("case", SAVED_CASES, ids=[f"B{c[0]}L{c[1]}D{c[2]}N{c[3]}{c[4]}S{c[5]}" for c in SAVED_CASES])
+def test_backward_saved_states(monkeypatch, case):
+    """selective_scan_fwd_save gives selective_scan_fwd's outputs bitwise and keeps the segment
+    entering states; selective_scan_bwd_saved from them gives selective_scan_bwd's gradients
+    bitwise (the same kernels on the same states), on two calls in a row; a single-segment
+    plan keeps nothing (size 0, no buffer needed)."""
+    import torch
+    import selective_state_space_20_amd as sss
+    bt, L, dm, n, io, segs = case
+    if segs:
+        monkeypatch.setenv("SSS_FORCE_SEGMENTS", str(segs))
+    seed = zlib.crc32(repr(case).encode()) % 100000
+    inp = gen.selective_inputs(bt, L, dm, n, io=io, with_z=True, with_D=True, h0=True, seed=seed)
+    rng = np.random.default_rng(seed + 5)
+    dy = to_dev(rng.standard_normal((bt, L, dm)).astype(np.float32), "cuda:0")
+    dhl = to_dev(rng.standard_normal((bt, dm, n)).astype(np.float32), "cuda:0")
+    t = {k: to_dev(v, "cuda:0") for k, v in inp.items() if k != "io"}
+    nbytes = sss.selective_scan_states_size(bt, L, dm, n, 0)
+    note(f"[saved states] {case} states {nbytes} bytes")
+    if segs == 1:
+        assert nbytes == 0
+    y_ref, hl_ref = sss.selective_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"])
+    g_ref = sss.selective_scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"], dy=dy,
+                                   dh_last=dhl)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        states = torch.full((max(nbytes // 4, 1),), float("nan"), dtype=torch.float32, device="cuda:0")
+        y, hl = sss.selective_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"],
+                                       states=states)
+        g = sss.selective_scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"], dy=dy,
+                                   dh_last=dhl, states=states)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref) and torch.equal(hl, hl_ref)
+        for k, v in g_ref.items():
+            if v is not None:
+                assert torch.equal(g[k], v), k
+
+
+def test_saved_states_errors(monkeypatch):
+    """Too small a states buffer, or one overlapping an output, is refused before any work."""
+    import torch
+    import selective_state_space_20_amd as sss
+    monkeypatch.setenv("SSS_FORCE_SEGMENTS", "4")
+    inp = gen.selective_inputs(1, 512, 64, 16, io="f32", with_z=False, with_D=False, h0=False, seed=11)
+    t = {k: to_dev(v, "cuda:0") for k, v in inp.items() if k != "io"}
+    nbytes = sss.selective_scan_states_size(1, 512, 64, 16, 0)
+    assert nbytes == 4 * 1 * 16 * 64 * 4
+    small = torch.empty(nbytes // 4 - 1, dtype=torch.float32, device="cuda:0")
+    with pytest.raises(ValueError):
+        sss.selective_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], states=small)
+    y = torch.empty((1, 512, 64), dtype=torch.float32, device="cuda:0")
+    ws = torch.empty(sss.selective_scan_fwd_workspace_size(1, 512, 64, 16, 0), dtype=torch.uint8, device="cuda:0")
+    rc = sss.selective_scan_fwd_save_raw(t["x"].data_ptr(), t["delta"].data_ptr(), t["A"].data_ptr(),
+                                         t["B"].data_ptr(), t["C"].data_ptr(), 0, 0, 0, y.data_ptr(), 0,
+                                         y.data_ptr(), nbytes, 1, 512, 64, 16, sss.SSS_F32, ws.data_ptr(),
+                                         ws.numel(), torch.cuda.current_stream().cuda_stream)
+    assert rc == -5  # SSS_ERR_ALIAS: states over y
+    rc = sss.selective_scan_fwd_save_raw(t["x"].data_ptr(), t["delta"].data_ptr(), t["A"].data_ptr(),
+                                         t["B"].data_ptr(), t["C"].data_ptr(), 0, 0, 0, y.data_ptr(), 0,
+                                         small.data_ptr(), small.numel() * 4, 1, 512, 64, 16, sss.SSS_F32,
+                                         ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream)
+    assert rc == -4  # SSS_ERR_WORKSPACE: states too small
+    torch.cuda.synchronize()
+
+
 @pytest.mark.timeout(600)
 def test_backward_long_layer_full():
     """Gradients of the full-size long layer (B=1, D=5120, N=16, L=65536, bf16, gated, h0,
