@@ -1076,7 +1076,11 @@ SelPlan plan_selective(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstat
   if (groups < 2 * simds) {
     const int64_t target = simds * env_int("SSS_WAVES_PER_SIMD", 20);
     S = std::max<int64_t>(1, (target + groups / 2) / groups);
-    S = std::min<int64_t>(S, std::max<int64_t>(1, seqlen / 64));  // segments of >= 64 steps
+    // segments of >= 64 steps, or >= 32 where even those would leave most SIMDs without a
+    // wave: such small calls are bound by each wave's serial walk (2 x 512 x 64: 41 us at 8
+    // segments, 28 us at 16)
+    const int64_t min_len = groups * std::max<int64_t>(1, seqlen / 64) >= simds ? 64 : 32;
+    S = std::min<int64_t>(S, std::max<int64_t>(1, seqlen / min_len));
     S = std::min<int64_t>(S, 4096);
   }
   const int forced = env_int("SSS_FORCE_SEGMENTS", 0);
