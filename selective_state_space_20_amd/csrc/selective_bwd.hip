@@ -45,6 +45,31 @@ __device__ __forceinline__ float ld_io(__amdgpu_buffer_rsrc_t r, int vo, int so)
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, vo, so, 0));
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// one element per lane copied straight into LDS (the lane's dword of the destination; a
+// 2-byte element lands zero-extended in its low half).  The size operand must be a literal.
+template <bool BF16>
+__device__ __forceinline__ void copy_io_lds(__amdgpu_buffer_rsrc_t r, lds_void* dst, int vo, int so) {
+  if constexpr (BF16) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 2, vo, so, 0, 0);
+  else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 4, vo, so, 0, 0);
+}
+
+// NS rows of 64 dwords (a checkpoint as stored) copied straight into LDS at dst: 1 KB (four
+// rows) per copy, lane i taking bytes 16 i .. 16 i + 15 of it, or a row per copy below 4 rows
+template <int NS>
+__device__ __forceinline__ void copy_rows_lds(__amdgpu_buffer_rsrc_t r, uint32_t* dst, int lane) {
+  if constexpr (NS % 4 == 0) {
+#pragma unroll
+    for (int c = 0; c < NS / 4; ++c)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + c * 256), 16, lane * 16, c * 1024, 0, 0);
+  } else {
+#pragma unroll
+    for (int n = 0; n < NS; ++n)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + n * 64), 4, lane * 4, n * 256, 0, 0);
+  }
+}
+
 __device__ __forceinline__ float ld_f32(__amdgpu_buffer_rsrc_t r, int vo, int so) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, vo, so, 0));
 }
@@ -232,9 +257,9 @@ constexpr int ilog2c(int v) { return v <= 1 ? 0 : 1 + ilog2c(v / 2); }
 // ------------------------------------------------------------------ 4. main backward pass
 // Checkpoints (the state before every K-th step, from the forward scan's PASS 3) are taken
 // in reverse order; for each K-step sub-chunk the states are re-formed in registers and the
-// adjoint walks the sub-chunk backwards.  (Prefetching the next sub-chunk into a second
-// register slot pushed the kernel into scratch spills; two resident waves per SIMD hide
-// the loads instead.)
+// adjoint walks the sub-chunk backwards.  A checkpoint and the inputs of the steps it
+// covers reach LDS through direct-to-LDS buffer loads one checkpoint group ahead, so no
+// VGPRs wait on them (a prefetch into a second register slot spilled at 168 VGPRs).
 template <int NS, bool BF16, bool HAS_Z>
 __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
     const void* __restrict__ x, const void* __restrict__ delta, const float* __restrict__ A,
@@ -256,12 +281,20 @@ __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
   const int64_t chl = (q.b * g.D + q.dc) * NS;  // (b, d) row of dh_last / dh0
 
   float a2[NS], mu[NS], dacc[NS];  // A' = A log2 e (for exp2; A itself is A' ln 2), clamped
+  // the adjoint entering from the right: the carried one (state n at stride D), else dh_last
+  // (contiguous), else zero -- one source for all n, so that the loads go out together
+  const float* mu_src = g.S > 1 ? mu_right + ((int64_t)q.s * g.batch + q.b) * NS * g.D + q.dc
+                                : (dh_last ? dh_last + chl : nullptr);
+  const int64_t mu_stride = g.S > 1 ? g.D : 1;
 #pragma unroll
   for (int n = 0; n < NS; ++n) {
     a2[n] = fmaxf(A[q.dc * NS + n] * kLog2e, -kFltMax);
-    mu[n] = g.S > 1 ? mu_right[(((int64_t)q.s * g.batch + q.b) * NS + n) * g.D + q.dc]
-                    : (dh_last ? dh_last[chl + n] : 0.0f);
+    mu[n] = 0.0f;
     dacc[n] = 0.0f;
+  }
+  if (mu_src != nullptr) {
+#pragma unroll
+    for (int n = 0; n < NS; ++n) mu[n] = mu_src[n * mu_stride];
   }
   const float Dd = Dsk ? Dsk[q.dc] : 0.0f;
   float ddacc = 0.0f;
@@ -284,15 +317,45 @@ __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
   const float* Cr = Cm + (q.b * g.L + q.tbeg) * NS;
   const int last = (q.len - 1) / K;
 
+  // LDS staging (one wave per workgroup).  A checkpoint group is the R sub-chunks (KC = R K
+  // steps) that start from one checkpoint.  Its checkpoint (NS rows of 256 B, as stored) and,
+  // per step, one dword per lane of x, delta, dy and z are copied into LDS by buffer loads
+  // that write LDS directly (no VGPRs held), issued one group ahead: the group's last
+  // sub-chunk issues the next group's copies once it has read its own inputs.  A 2-byte
+  // element lands zero-extended in the low half of the lane's dword.  Every copy reads the
+  // same in-range addresses the lanes' own loads would (rows clamped to the segment, lanes
+  // past the last channel on channel D-1).
+  constexpr int KC = K * R;
+  constexpr int kOffX = NS * 64, kOffD = kOffX + KC * 64, kOffG = kOffD + KC * 64, kOffZ = kOffG + KC * 64;
+  __shared__ __attribute__((aligned(16))) uint32_t stage[kOffZ + (HAS_Z ? KC * 64 : 0)];
+  auto lds_at = [&](int word) { return (lds_void*)&stage[word]; };
+  auto issue_group = [&](int grp_j) {
+    copy_rows_lds<NS>(ck_rsrc(grp_j), stage, q.lane);
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+      const int t_ = min(grp_j * KC + i, q.len - 1);
+      copy_io_lds<BF16>(rx, lds_at(kOffX + i * 64), vo, t_ * rs);
+      copy_io_lds<BF16>(rd, lds_at(kOffD + i * 64), vo, t_ * rs);
+      copy_io_lds<false>(rg, lds_at(kOffG + i * 64), vo4, t_ * rs4);
+      if constexpr (HAS_Z) copy_io_lds<BF16>(rz, lds_at(kOffZ + i * 64), vo, t_ * rs);
+    }
+  };
+  // a staged element of the lane: bf16 bits widened to fp32
+  auto lds_in = [&](int word) {
+    const uint32_t u = stage[word + q.lane];
+    return __builtin_bit_cast(float, BF16 ? u << 16 : u);
+  };
+  auto lds_f32 = [&](int word) { return __builtin_bit_cast(float, stage[word + q.lane]); };
+
   float xs[1][K], ds[1][K], gs[1][K], zs[1][K];
 #define BWD_LOAD(SLOT, J)                                                                  \
   do {                                                                                     \
+    const int li_ = ((J) % R) * K; /* the sub-chunk's first step within its group */       \
     _Pragma("unroll") for (int i = 0; i < K; ++i) {                                        \
-      const int t_ = min((J) * K + i, q.len - 1); /* clamped: tail values are not used */  \
-      xs[SLOT][i] = ld_io<BF16>(rx, vo, t_ * rs);                                          \
-      ds[SLOT][i] = ld_io<BF16>(rd, vo, t_ * rs);                                          \
-      gs[SLOT][i] = ld_f32(rg, vo4, t_ * rs4);                                             \
-      if (HAS_Z) zs[SLOT][i] = ld_io<BF16>(rz, vo, t_ * rs);                               \
+      xs[SLOT][i] = lds_in(kOffX + (li_ + i) * 64);                                        \
+      ds[SLOT][i] = lds_in(kOffD + (li_ + i) * 64);                                        \
+      gs[SLOT][i] = lds_f32(kOffG + (li_ + i) * 64);                                       \
+      if (HAS_Z) zs[SLOT][i] = lds_in(kOffZ + (li_ + i) * 64);                             \
     }                                                                                      \
   } while (0)
 
@@ -301,8 +364,7 @@ __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
     const int tb = (J) * K;                                                                \
     const int k = min(K, q.len - tb);                                                      \
     float hs[K + 1][NS], ea[K][NS]; /* states and decays of the sub-chunk */               \
-    const __amdgpu_buffer_rsrc_t rc_ = ck_rsrc((J) / R);                                   \
-    _Pragma("unroll") for (int n = 0; n < NS; ++n) hs[0][n] = ld_f32(rc_, q.lane * 4, n * 256); \
+    _Pragma("unroll") for (int n = 0; n < NS; ++n) hs[0][n] = h0[n];                       \
     if (R == 2 && ((J) & 1)) { /* the checkpoint is K steps before the sub-chunk */        \
       _Pragma("unroll") for (int i = 0; i < K; ++i) {                                      \
         const int ta = ((J) - 1) * K + i;                                                  \
@@ -386,19 +448,31 @@ __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
     }                                                                                      \
   } while (0)
 
+  issue_group(last / R);
   for (int j = last; j >= 0; --j) {
-    // inputs of the sub-chunk before, for the checkpoint advance of odd sub-chunks: loaded
-    // with the others (unconditionally, clamped) so that they are in flight together
+    // the group's copies have landed once every vector memory operation issued so far has
+    // completed (the first sub-chunk taken from a group waits for them)
+    if (j == last || (j % R) == R - 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // inputs of the sub-chunk before, for the checkpoint advance of odd sub-chunks (the
+    // first steps of the same group)
     float xa[K], da[K];
     if constexpr (R == 2) {
 #pragma unroll
       for (int i = 0; i < K; ++i) {
-        const int ta = max((j - 1) * K + i, 0);
-        xa[i] = ld_io<BF16>(rx, vo, ta * rs);
-        da[i] = ld_io<BF16>(rd, vo, ta * rs);
+        xa[i] = lds_in(kOffX + i * 64);
+        da[i] = lds_in(kOffD + i * 64);
       }
     }
     BWD_LOAD(0, j);
+    float h0[NS];  // the checkpoint
+#pragma unroll
+    for (int n = 0; n < NS; ++n) h0[n] = lds_f32(n * 64);
+    if (j % R == 0 && j > 0) {
+      // the group's last sub-chunk: once its reads of the staging area have returned, the
+      // next group's copies may overwrite it
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      issue_group(j / R - 1);
+    }
     BWD_CHUNK(0, j);
   }
 #undef BWD_LOAD
