@@ -15,7 +15,8 @@ The default warm-up of 30 calls brings the GPU to its sustained clock before the
   python bench.py --workload 4            # another configuration (0..4); the default is 3
   python bench.py --decode 64             # one decode step of 64 tokens (selective_state_update)
   python bench.py --conv                  # the causal conv1d front end on the long layer
-  python bench.py --backward              # selective_scan_bwd (all gradients) on the default workload
+  python bench.py --backward [--saved-states]  # selective_scan_bwd (all gradients) on the default
+                                          # workload (or the training pair's selective_scan_bwd_saved)
   python bench.py --train-step [--saved-states]  # forward + gradients together (optionally keeping
                                           # the forward's segment entering states for the gradients)
   python bench.py --copy-calibration      # plain copy of a known size, for counter scaling
@@ -49,8 +50,8 @@ COPY_WRITE_SCALE = 1048576.0 / 1048576.0
 CSRC = "selective_state_space_20_amd/csrc/"
 PMC_TRAFFIC = {
     # default workload: sel_seq_kernel pass 1 + sel_carry_kernel + pass 2
-    "selective": {"sources": (CSRC + "selective_scan.hip", CSRC + "common.h"), "digest": "11f4ddcc36ca4d7f",
-                  "fetch_kib": 656603.7 + 46577.0 + 1030438.6, "write_kib": 86700.0 + 81920.0 + 1311040.0},
+    "selective": {"sources": (CSRC + "selective_scan.hip", CSRC + "common.h"), "digest": "07f0735a53b19af8",
+                  "fetch_kib": 656862.8 + 46577.5 + 1030507.0, "write_kib": 86700.0 + 81920.0 + 1311040.0},
     # 8 x 32768 x 4096 fp32
     "elementwise": {"sources": (CSRC + "elementwise_scan.hip", CSRC + "common.h"), "digest": "4b0239623ce7466b",
                     "fetch_kib": 8388744.2, "write_kib": 4194432.0},
@@ -61,9 +62,9 @@ PMC_TRAFFIC = {
     # pass (with the adjoint's segment folds), the adjoint carry, the main kernel and the two
     # reductions
     "backward": {"sources": (CSRC + "selective_bwd.hip", CSRC + "selective_scan.hip", CSRC + "common.h"),
-                 "digest": "3b99dd2357befdb1",
-                 "fetch_kib": 656871.0 + 46577.0 + 1690466.9 + 46577.9 + 4464972.4 + 327698.6 + 43549.4,
-                 "write_kib": 86700.0 + 81920.0 + 5329922.1 + 81920.0 + 4685562.8 + 8192.0 + 660.0},
+                 "digest": "623684dc8f8e7504",
+                 "fetch_kib": 656838.6 + 46576.9 + 1690458.9 + 46577.3 + 4353978.8 + 327696.6 + 43547.9,
+                 "write_kib": 86700.0 + 81920.0 + 5329921.0 + 81920.0 + 4695413.6 + 8192.0 + 660.0},
     # 1 x 65536 x 5120 bf16, width 4
     "conv": {"sources": (CSRC + "conv1d.hip", CSRC + "common.h"), "digest": "0525304aa8e7045b",
              "fetch_kib": 328260.8, "write_kib": 655360.3},
@@ -424,10 +425,13 @@ def bench_conv(steps, warmup, batch=1, seqlen=65536, dim=5120, width=4):
     }), flush=True)
 
 
-def bench_backward(steps, warmup):
+def bench_backward(steps, warmup, saved=False):
     """selective_scan_bwd on the default workload (the long Mamba-2.8B-shaped layer, bf16,
-    gated, h0, dh_last): every gradient, states recomputed.  Algorithmic bytes: every input
-    (x, delta, z, dy, B, C, A, D, h0, dh_last) read once and every gradient written once."""
+    gated, h0, dh_last): every gradient, states recomputed.  With saved=True the gradients
+    call of the training pair (selective_scan_bwd_saved) is timed alone, on the segment
+    entering states one selective_scan_fwd_save call kept before the timed region.
+    Algorithmic bytes: every input (x, delta, z, dy, B, C, A, D, h0, dh_last) read once and
+    every gradient written once."""
     import torch
     import selective_state_space_20_amd as sss
     from selective_state_space_20_amd import inputs as gen
@@ -448,10 +452,18 @@ def bench_backward(steps, warmup):
     dhl = torch.randn((b, d, n), device=dev, generator=g)
     ws = torch.empty(sss.selective_scan_bwd_workspace_size(b, L, d, n, 0), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
+    states = None
+    if saved:
+        sbytes = sss.selective_scan_states_size(b, L, d, n, 0)
+        states = torch.empty(max(sbytes, 4) // 4, dtype=torch.float32, device=dev)
+        y = torch.empty((b, L, d), dtype=torch.float32, device=dev)
+        sss.selective_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"], out=y,
+                               workspace=ws, states=states)
+        del y
 
     def step():
         sss.selective_scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"], dy=dy,
-                               dh_last=dhl, workspace=ws)
+                               dh_last=dhl, workspace=ws, states=states)
 
     for _ in range(warmup):
         step()
@@ -469,16 +481,20 @@ def bench_backward(steps, warmup):
     gbs = nbytes / (mean_ms * 1e-3) / 1e9
     alu = backward_alu_ops(b, L, d, n)
     alu_tflops = 2.0 * alu / (mean_ms * 1e-3) / 1e12
-    log(f"[bench] backward {cfg['name']}: event mean {mean_ms:.4f} ms, workspace {ws.numel() / 1e9:.2f} GB")
+    log(f"[bench] backward{' (saved states)' if saved else ''} {cfg['name']}: event mean {mean_ms:.4f} ms, "
+        f"workspace {ws.numel() / 1e9:.2f} GB")
     print(json.dumps({
         "metric": "selective_scan_bwd achieved HBM GB/s and elements/s, 1 GPU", "value": round(gbs, 2), "unit": "GB/s",
         "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(mean_ms, 5), "higher_is_better": True,
         "dtype": "f32", "io_dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "backward_" + cfg["name"], "algorithmic_bytes": nbytes, "elements": e},
+        "config": {"workload": ("backward_saved_" if saved else "backward_") + cfg["name"],
+                   "algorithmic_bytes": nbytes, "elements": e, "saved_states": bool(saved)},
         "elements_per_s": round(e / (mean_ms * 1e-3), 1),
         "roofline": {"bound": "alu", "achieved": round(alu_tflops, 3), "peak": VALU_FP32_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(alu_tflops / VALU_FP32_TFLOPS, 4), "traffic": measured_traffic("backward"),
-                     "kernel": "one selective_scan_bwd call (8 launches)", "call_ms_event_mean": round(mean_ms, 5),
+                     "frac": round(alu_tflops / VALU_FP32_TFLOPS, 4),
+                     "traffic": None if saved else measured_traffic("backward"),
+                     "kernel": "one selective_scan_bwd%s call" % ("_saved" if saved else ""),
+                     "call_ms_event_mean": round(mean_ms, 5),
                      "alu_ops_per_call": alu,
                      "hbm": {"achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": round(gbs / HBM_PEAK_GBS, 4)}},
@@ -562,7 +578,7 @@ def main():
     ap.add_argument("--train-step", action="store_true",
                     help="time selective_scan_fwd + selective_scan_bwd together on the default workload")
     ap.add_argument("--saved-states", action="store_true",
-                    help="with --train-step: keep the forward's segment entering states for the gradients call")
+                    help="with --train-step or --backward: the training pair that keeps the forward's segment entering states")
     ap.add_argument("--decode", type=int, default=0, metavar="BATCH",
                     help="time one decode step (selective_state_update) of BATCH tokens instead")
     ap.add_argument("--no-flush", action="store_true",
@@ -588,7 +604,7 @@ def main():
         bench_conv(args.steps, args.warmup)
         return
     if args.backward:
-        bench_backward(args.steps, args.warmup)
+        bench_backward(args.steps, args.warmup, args.saved_states)
         return
     if args.train_step:
         bench_train_step(args.steps, args.warmup, args.saved_states)
