@@ -63,8 +63,8 @@ PMC_TRAFFIC = {
     # reductions
     "backward": {"sources": (CSRC + "selective_bwd.hip", CSRC + "selective_scan.hip", CSRC + "common.h"),
                  "digest": "623684dc8f8e7504",
-                 "fetch_kib": 656838.6 + 46576.9 + 1690458.9 + 46577.3 + 4353978.8 + 327696.6 + 43547.9,
-                 "write_kib": 86700.0 + 81920.0 + 5329921.0 + 81920.0 + 4695413.6 + 8192.0 + 660.0},
+                 "fetch_kib": 656854.5 + 46576.9 + 1690469.1 + 46577.4 + 4349023.9 + 327696.6 + 43547.9,
+                 "write_kib": 86700.0 + 81920.0 + 5329921.1 + 81920.0 + 4685368.6 + 8192.0 + 660.0},
     # 1 x 65536 x 5120 bf16, width 4
     "conv": {"sources": (CSRC + "conv1d.hip", CSRC + "common.h"), "digest": "0525304aa8e7045b",
              "fetch_kib": 328260.8, "write_kib": 655360.3},
