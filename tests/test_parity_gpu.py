@@ -336,6 +336,11 @@ BWD_CASES = [  # (batch, seqlen, dim, dstate, io, z, D, h0, dh_last, forced segm
     (1, 665, 40, 16, "bf16", True, True, True, True, 2),
     (2, 1001, 24, 16, "f32", True, False, True, True, 3),
     (1, 7, 70, 16, "f32", True, True, True, True, 0),
+    # bf16 with an odd channel count (the last group's lanes past D read channel D-1's 2-byte
+    # elements), very short sequences, and a two-state bf16 layer split in segments
+    (2, 130, 97, 16, "bf16", True, True, False, True, 2),
+    (1, 3, 33, 16, "bf16", True, True, True, True, 0),
+    (2, 257, 65, 2, "bf16", True, True, True, True, 4),
 ]
 
 
