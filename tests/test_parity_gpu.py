@@ -448,7 +448,8 @@ def test_saved_states_errors(monkeypatch):
 @pytest.mark.timeout(600)
 def test_backward_long_layer_full():
     """Gradients of the full-size long layer (B=1, D=5120, N=16, L=65536, bf16, gated, h0,
-    dh_last) against the oracle, every element of every gradient tensor."""
+    dh_last) against the oracle, every element of every gradient tensor; the saved-states
+    training pair gives the same gradients bitwise at this size too."""
     import torch
     import oracle
     import selective_state_space_20_amd as sss
@@ -458,9 +459,22 @@ def test_backward_long_layer_full():
     dhl = rng.standard_normal(inp["h0"].shape, dtype=np.float32)
     note(f"[backward] {cfg['name']} inputs generated")
     t = {k: to_dev(v, "cuda:0") for k, v in inp.items() if k != "io"}
+    dy_d, dhl_d = to_dev(dy, "cuda:0"), to_dev(dhl, "cuda:0")
     g = sss.selective_scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"],
-                               dy=to_dev(dy, "cuda:0"), dh_last=to_dev(dhl, "cuda:0"))
+                               dy=dy_d, dh_last=dhl_d)
+    # the training pair at full size: the forward keeps its segment entering states and the
+    # gradients call starts from them -- the same gradients, bit for bit
+    b, L, d, n = cfg["batch"], cfg["seqlen"], cfg["dim"], cfg["dstate"]
+    states = torch.empty(max(sss.selective_scan_states_size(b, L, d, n), 4) // 4, dtype=torch.float32,
+                         device="cuda:0")
+    sss.selective_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"], states=states)
+    g2 = sss.selective_scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"],
+                                dy=dy_d, dh_last=dhl_d, states=states)
     torch.cuda.synchronize()
+    same = {k: bool(torch.equal(g[k], g2[k])) for k in g if g[k] is not None}
+    note(f"    saved-states pair bitwise equal: {same}")
+    assert all(same.values()), same
+    del g2, states
     g = {k: (v.cpu().numpy() if v is not None else None) for k, v in g.items()}
     note("    GPU done")
     r = oracle.selective_scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], inp["h0"],
