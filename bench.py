@@ -10,8 +10,9 @@ once and every output written once, the state never counted) in GB/s.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 30] [--no-cpu-baseline]
 
-The default warm-up of 30 calls brings the GPU to its sustained clock before the timed calls
-(with 3, the first timed calls of the long layer ran up to 25% slower and the mean 6% slower).
+Warm-up runs at least --warmup calls and keeps calling until the device has been busy for
+0.4 s, so that the timed calls run at the sustained clock (with 3 calls, the first timed calls
+of the long layer ran up to 25% slower and the mean 6% slower); the line reports the count run.
   python bench.py --workload 4            # another configuration (0..4); the default is 3
   python bench.py --decode 64             # one decode step of 64 tokens (selective_state_update)
   python bench.py --conv                  # the causal conv1d front end on the long layer
@@ -73,6 +74,33 @@ PMC_TRAFFIC = {
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+# The GPU's clock settles only after some hundreds of milliseconds of sustained load: with a
+# handful of warm-up calls the first timed calls of the long layer ran up to 25% slower.
+# Warm-up therefore runs the requested number of calls and then keeps calling (untimed)
+# until the device has been busy for at least this long; the count actually run is reported.
+MIN_WARMUP_S = 0.4
+
+
+def dtype_label(io):
+    """The arithmetic is fp32 throughout (state, products, sums); with bf16 operands the label
+    says so as well."""
+    return "f32" if io in (None, "f32") else f"f32-compute/{io}-io"
+
+
+def warm_up(call, warmup):
+    """Run `call` at least `warmup` times and for at least MIN_WARMUP_S; returns the count."""
+    import torch
+    n = 0
+    t0 = time.perf_counter()
+    while n < warmup or time.perf_counter() - t0 < MIN_WARMUP_S:
+        call()
+        n += 1
+        if n >= warmup and n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
 
 
 def algorithmic_bytes(cfg):
@@ -352,9 +380,7 @@ def bench_decode(batch, steps, warmup, dim=5120, dstate=16, flush=True):
     # The state of a few hundred tokens fits in the 256 MB last-level cache: without a flush
     # between calls, repeated steps would be timed out of that cache instead of HBM.
     scrub = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev) if flush else None
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_calls = warm_up(step, warmup)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t_start = time.perf_counter()
     for e0, e1 in ev:
@@ -374,9 +400,9 @@ def bench_decode(batch, steps, warmup, dim=5120, dstate=16, flush=True):
     gbs = nbytes / (mean_ms * 1e-3) / 1e9
     print(json.dumps({
         "metric": "selective_state_update (one decode step) achieved HBM GB/s, 1 GPU", "value": round(gbs, 2),
-        "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup, "warmup_calls_run": warm_calls,
         "ms_per_step": round(mean_ms if flush else wall * 1e3 / steps, 5),
-        "higher_is_better": True, "dtype": "f32", "io_dtype": "bf16", "data": "synthetic",
+        "higher_is_better": True, "dtype": dtype_label("bf16"), "io_dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"decode_bf16_b{batch}_D{dim}_N{dstate}", "batch": batch, "dim": dim, "dstate": dstate,
                    "algorithmic_bytes": nbytes, "caches_flushed_between_calls": flush},
         "tokens_per_s": round(batch / (mean_ms * 1e-3), 1),
@@ -401,9 +427,7 @@ def bench_conv(steps, warmup, batch=1, seqlen=65536, dim=5120, width=4):
     bias = torch.randn((dim,), device=dev, generator=g)
     out = torch.empty_like(x)
     stream = torch.cuda.current_stream(dev)
-    for _ in range(warmup):
-        sss.causal_conv1d_fwd(x, w, bias, silu=True, out=out)
-    torch.cuda.synchronize()
+    warm_calls = warm_up(lambda: sss.causal_conv1d_fwd(x, w, bias, silu=True, out=out), warmup)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for e0, e1 in ev:
         e0.record(stream)
@@ -416,8 +440,8 @@ def bench_conv(steps, warmup, batch=1, seqlen=65536, dim=5120, width=4):
     log(f"[bench] conv1d {batch}x{seqlen}x{dim} W={width}: event mean {mean_ms:.4f} ms")
     print(json.dumps({
         "metric": "causal_conv1d_fwd achieved HBM GB/s, 1 GPU", "value": round(gbs, 2), "unit": "GB/s",
-        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(mean_ms, 5), "higher_is_better": True,
-        "dtype": "f32", "io_dtype": "bf16", "data": "synthetic",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "warmup_calls_run": warm_calls, "ms_per_step": round(mean_ms, 5), "higher_is_better": True,
+        "dtype": dtype_label("bf16"), "io_dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"conv1d_bf16_b{batch}_L{seqlen}_D{dim}_W{width}_silu", "algorithmic_bytes": nbytes},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("conv"), "kernel": "conv1d_kernel",
@@ -465,9 +489,7 @@ def bench_backward(steps, warmup, saved=False):
         sss.selective_scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"], dy=dy,
                                dh_last=dhl, workspace=ws, states=states)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_calls = warm_up(step, warmup)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for e0, e1 in ev:
         e0.record(stream)
@@ -485,8 +507,8 @@ def bench_backward(steps, warmup, saved=False):
         f"workspace {ws.numel() / 1e9:.2f} GB")
     print(json.dumps({
         "metric": "selective_scan_bwd achieved HBM GB/s and elements/s, 1 GPU", "value": round(gbs, 2), "unit": "GB/s",
-        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(mean_ms, 5), "higher_is_better": True,
-        "dtype": "f32", "io_dtype": "bf16", "data": "synthetic",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "warmup_calls_run": warm_calls, "ms_per_step": round(mean_ms, 5), "higher_is_better": True,
+        "dtype": dtype_label("bf16"), "io_dtype": "bf16", "data": "synthetic",
         "config": {"workload": ("backward_saved_" if saved else "backward_") + cfg["name"],
                    "algorithmic_bytes": nbytes, "elements": e, "saved_states": bool(saved)},
         "elements_per_s": round(e / (mean_ms * 1e-3), 1),
@@ -537,9 +559,7 @@ def bench_train_step(steps, warmup, saved):
         sss.selective_scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"], dy=dy,
                                dh_last=dhl, workspace=ws, states=states)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_calls = warm_up(step, warmup)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for e0, e1 in ev:
         e0.record(stream)
@@ -553,8 +573,8 @@ def bench_train_step(steps, warmup, saved):
         f"{mean_ms:.4f} ms, median {float(np.median(ms)):.4f}, min {min(ms):.4f}, states {sbytes / 1e6:.1f} MB")
     print(json.dumps({
         "metric": "selective scan training step (forward + gradients) elements/s, 1 GPU",
-        "value": round(e / (mean_ms * 1e-3), 1), "unit": "elements/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
-        "ms_per_step": round(mean_ms, 5), "higher_is_better": True, "dtype": "f32", "io_dtype": "bf16",
+        "value": round(e / (mean_ms * 1e-3), 1), "unit": "elements/s", "n_gpus": 1, "steps": steps, "warmup": warmup, "warmup_calls_run": warm_calls,
+        "ms_per_step": round(mean_ms, 5), "higher_is_better": True, "dtype": dtype_label("bf16"), "io_dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "train_step_" + cfg["name"], "saved_states": bool(saved), "states_bytes": sbytes,
                    "elements": e},
@@ -664,10 +684,8 @@ def main():
             sss.elementwise_scan(t["x"], t["A"], t["B"], t["C"], t["h0"], out=y,
                                  out_last=hl if cfg.get("h_last", False) else None, workspace=ws)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    log(f"[bench] warmup {args.warmup} done")
+    warm_calls = warm_up(step, args.warmup)
+    log(f"[bench] warmup {args.warmup} requested, {warm_calls} calls run (at least {MIN_WARMUP_S} s)")
     # A workload whose footprint is within reach of the 256 MB last-level cache (the
     # medium layer: 254.6 MB) is timed with that cache scrubbed before every call, so that
     # each call reads its inputs from HBM; the long layers (3.4 and 21.5 GB) are not.
@@ -730,11 +748,12 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_calls_run": warm_calls,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": dtype_label(cfg.get("io", "f32")),
         "io_dtype": cfg.get("io", "f32"),
         "data": "synthetic",
         "config": {"workload": cfg["name"], "batch": b, "seqlen": L, "dim": d, "dstate": n if selective else None,
