@@ -79,8 +79,9 @@ def log(msg):
 # The GPU's clock settles only after some hundreds of milliseconds of sustained load: with a
 # handful of warm-up calls the first timed calls of the long layer ran up to 25% slower.
 # Warm-up therefore runs the requested number of calls and then keeps calling (untimed)
-# until the device has been busy for at least this long; the count actually run is reported.
-MIN_WARMUP_S = 0.4
+# until the device has been busy for at least this long (--min-warmup-s; 0 for profiler
+# runs); the count actually run is reported.
+WARMUP = {"min_s": 0.4}
 
 
 def dtype_label(io):
@@ -90,11 +91,11 @@ def dtype_label(io):
 
 
 def warm_up(call, warmup):
-    """Run `call` at least `warmup` times and for at least MIN_WARMUP_S; returns the count."""
+    """Run `call` at least `warmup` times and for at least WARMUP["min_s"]; returns the count."""
     import torch
     n = 0
     t0 = time.perf_counter()
-    while n < warmup or time.perf_counter() - t0 < MIN_WARMUP_S:
+    while n < warmup or time.perf_counter() - t0 < WARMUP["min_s"]:
         call()
         n += 1
         if n >= warmup and n % 8 == 0:
@@ -589,6 +590,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--min-warmup-s", type=float, default=WARMUP["min_s"],
+                    help="keep warming up until this much time has passed (profiler runs: 0)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--probes", action="store_true", help="roofline calibration probes (HBM streams, VALU issue)")
     ap.add_argument("--probe-kinds", type=str, default="", help="comma-separated ALU probe kinds only (no streams)")
@@ -609,6 +612,7 @@ def main():
     ap.add_argument("--layout", choices=("bld", "bdl"), default="bld",
                     help="selective: operand layout (bdl = channel-major x/delta/z/y and B/C)")
     args = ap.parse_args()
+    WARMUP["min_s"] = args.min_warmup_s
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE={world}): the scan is built "
@@ -685,7 +689,7 @@ def main():
                                  out_last=hl if cfg.get("h_last", False) else None, workspace=ws)
 
     warm_calls = warm_up(step, args.warmup)
-    log(f"[bench] warmup {args.warmup} requested, {warm_calls} calls run (at least {MIN_WARMUP_S} s)")
+    log(f"[bench] warmup {args.warmup} requested, {warm_calls} calls run (at least {WARMUP['min_s']} s)")
     # A workload whose footprint is within reach of the 256 MB last-level cache (the
     # medium layer: 254.6 MB) is timed with that cache scrubbed before every call, so that
     # each call reads its inputs from HBM; the long layers (3.4 and 21.5 GB) are not.

@@ -144,9 +144,12 @@ int selective_scan_fwd_save(const void* x, const void* delta, const float* A, co
                             int64_t dstate, int io_dtype, void* workspace, size_t workspace_bytes,
                             sss_stream_t stream);
 
-/* selective_scan_bwd_saved: exactly selective_scan_bwd (same arguments and results, bitwise)
- * with the segment entering states read from `states` instead of recomputed (the forward
- * scan's first pass and carry are skipped).  `states` must hold what selective_scan_fwd_save
+/* selective_scan_bwd_saved: selective_scan_bwd (same arguments, the same gradients up to
+ * rounding) with the segment entering states read from `states` instead of recomputed: its
+ * checkpoint pass starts every time segment from its kept entering state, where
+ * selective_scan_bwd starts each from zero and adds the decayed entering state to the
+ * checkpoints afterwards (the scan is linear in its state: the same values summed in another
+ * order; bitwise the same when the plan has a single segment).  `states` must hold what selective_scan_fwd_save
  * wrote for the same x, delta, A, B, h0, sizes, dtype and device (C, D, z do not enter the
  * states), unmodified since; the library cannot check that, and anything else gives wrong
  * gradients.  Read only; NULL allowed when selective_scan_states_size() is 0.  Size and

@@ -56,13 +56,18 @@ int sel_fwd_impl(const void* x, const void* delta, const float* A, const float* 
 int selective_row_mode(const SelArgs& a, const SelPlan& plan);
 // pass 1 + carry only: the workspace's state slots hold the state entering each segment
 hipError_t launch_segment_states(const SelArgs& a, const SelPlan& plan, hipStream_t stream);
-// after launch_segment_states: the state before every 2^kshift-th step of every segment,
-// into ckpt[s][batch][channel group][j][dstate][64 lanes] (ceil(dim / 64) groups); with
-// adj_mu (more than one segment) also the adjoint of every segment folded from zero at its
-// end into adj_mu[s][batch][dstate][dim], dy (batch, seqlen, dim) being the output gradient,
-// and every segment's delta sum into the workspace's sums
+// the state before every 2^kshift-th step of every segment, into
+// ckpt[s][batch][channel group][j][dstate + 1][64 lanes] (ceil(dim / 64) groups); with adj_mu
+// (more than one segment) also the adjoint of every segment folded from zero at its end into
+// adj_mu[s][batch][dstate][dim], dy (batch, seqlen, dim) being the output gradient, and every
+// segment's delta sum into the workspace's sums.  Without `local`, after
+// launch_segment_states (or with states kept by the forward call): the checkpoints are the
+// states.  With `local` (adj_mu, more than one segment) every segment starts from zero: the
+// checkpoints hold the states from zero and, in row dstate, the delta sum of the segment's
+// steps before them, and the state slots end up holding the entering states (end states
+// from zero, then the carry)
 hipError_t launch_checkpoints(const SelArgs& a, const SelPlan& plan, float* ckpt, int kshift, int nsub,
-                              const float* dy, float* adj_mu, hipStream_t stream);
+                              const float* dy, float* adj_mu, bool local, hipStream_t stream);
 
 // Backward pass of the selective scan (selective_bwd.hip).
 struct BwdPlan {

@@ -13,10 +13,15 @@
 //   dC_t[n] = sum_d dv_t h_t,  dD = sum dv_t x_t,  dz_t = dy_t v_t silu'(z_t),  dh0 = a_0 lambda_0.
 //
 // Mapping (lanes = 64 adjacent channels, time split into the forward pass's segments):
-//   1. forward pass 1 + carry (selective_scan.hip): the state entering every segment;
-//   2. the forward scan's checkpoint pass stores the state before every K-th step and, from
-//      the decays it forms anyway, each segment's adjoint folded from zero at its end
-//      (mu = a (mu + C dv) backwards, summed forwards as sum_t a_first..a_t C_t dv_t);
+//   1.+2. the forward scan's checkpoint pass (selective_scan.hip) runs every segment from a
+//      zero state: it stores that state and the delta sum before every K-th step, the
+//      segment's end state, and, from the decays it forms anyway, each segment's adjoint
+//      folded from zero at its end (mu = a (mu + C dv) backwards, summed forwards as
+//      sum_t a_first..a_t C_t dv_t); the forward carry turns the end states into the state
+//      entering every segment.  Since the scan is linear in its state, the true state at a
+//      checkpoint is the stored one plus exp2(A' * S) times the entering state (S the delta
+//      sum before it), which the main kernel adds once per checkpoint.  (When the forward
+//      call kept the entering states, the checkpoint pass starts from them instead.)
 //   3. sel_bwd_carry: the adjoint entering every segment from its right end (from dh_last);
 //   4. sel_bwd_kernel takes each segment's K-step sub-chunks in reverse order: their states
 //      are re-formed in registers from the checkpoint and the adjoint walks them backwards, writing dx,
@@ -33,6 +38,7 @@ namespace sss {
 struct BwdSeg {
   int64_t batch, L, D, seg_len;
   int S, ngroups, nsub, K;
+  int local;  // checkpoints from zero-started segments: add the decayed entering state
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t bwd_rsrc(const void* base) {
@@ -265,7 +271,8 @@ __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
     const void* __restrict__ x, const void* __restrict__ delta, const float* __restrict__ A,
     const float* __restrict__ Bm, const float* __restrict__ Cm, const float* __restrict__ Dsk,
     const void* __restrict__ z, const float* __restrict__ dy, const float* __restrict__ dh_last,
-    const float* __restrict__ mu_right, const float* __restrict__ ckpt, float* __restrict__ dx,
+    const float* __restrict__ mu_right, const float* __restrict__ ckpt, const float* __restrict__ hin,
+    float* __restrict__ dx,
     float* __restrict__ ddelta, float* __restrict__ dz, float* __restrict__ part_bc, float* __restrict__ part_a,
     float* __restrict__ part_d, float* __restrict__ dh0, BwdSeg g) {
   constexpr int K = bwd_k(NS);
@@ -307,9 +314,10 @@ __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
   const __amdgpu_buffer_rsrc_t rdx = bwd_rsrc(dx + row0);
   const __amdgpu_buffer_rsrc_t rdd = bwd_rsrc(ddelta + row0);
   const __amdgpu_buffer_rsrc_t rdz = bwd_rsrc(HAS_Z ? dz + row0 : dx + row0);
-  // checkpoint j of this wave: [s][b][grp][j][n][lane], one contiguous 256-byte row per state
+  // checkpoint j of this wave: [s][b][grp][j][row][lane], one contiguous 256-byte row per
+  // state and one for the delta sum before it (written for zero-started segments)
   auto ck_rsrc = [&](int j) {
-    return bwd_rsrc(ckpt + ((((int64_t)q.s * g.batch + q.b) * g.ngroups + q.grp) * g.nsub + j) * NS * 64);
+    return bwd_rsrc(ckpt + ((((int64_t)q.s * g.batch + q.b) * g.ngroups + q.grp) * g.nsub + j) * (NS + 1) * 64);
   };
   const int rs = (int)(g.D * ES), rs4 = (int)(g.D * 4);
   const int vo = q.loff * ES, vo4 = q.loff * 4;
@@ -326,11 +334,13 @@ __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
   // same in-range addresses the lanes' own loads would (rows clamped to the segment, lanes
   // past the last channel on channel D-1).
   constexpr int KC = K * R;
-  constexpr int kOffX = NS * 64, kOffD = kOffX + KC * 64, kOffG = kOffD + KC * 64, kOffZ = kOffG + KC * 64;
+  constexpr int kOffX = (NS + 1) * 64, kOffD = kOffX + KC * 64, kOffG = kOffD + KC * 64, kOffZ = kOffG + KC * 64;
   __shared__ __attribute__((aligned(16))) uint32_t stage[kOffZ + (HAS_Z ? KC * 64 : 0)];
   auto lds_at = [&](int word) { return (lds_void*)&stage[word]; };
   auto issue_group = [&](int grp_j) {
-    copy_rows_lds<NS>(ck_rsrc(grp_j), stage, q.lane);
+    const __amdgpu_buffer_rsrc_t rk = ck_rsrc(grp_j);
+    copy_rows_lds<NS>(rk, stage, q.lane);
+    if (g.local) __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, lds_at(NS * 64), 4, q.lane * 4, NS * 256, 0, 0);
 #pragma unroll
     for (int i = 0; i < KC; ++i) {
       const int t_ = min(grp_j * KC + i, q.len - 1);
@@ -448,11 +458,31 @@ __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
     }                                                                                      \
   } while (0)
 
+  // Zero-started segments: the state entering the segment, [n][lane] in LDS, for the
+  // checkpoints' correction (the state at a checkpoint is the one from zero plus
+  // exp2(A' * S) times the entering state, S the delta sum of the steps before it)
+  __shared__ float hin_s[NS * 64];
+  if (g.local) {
+    const float* hp = hin + ((int64_t)q.s * g.batch + q.b) * NS * g.D + q.dc;
+#pragma unroll
+    for (int n = 0; n < NS; ++n) hin_s[n * 64 + q.lane] = hp[n * g.D];
+  }
   issue_group(last / R);
   for (int j = last; j >= 0; --j) {
     // the group's copies have landed once every vector memory operation issued so far has
-    // completed (the first sub-chunk taken from a group waits for them)
-    if (j == last || (j % R) == R - 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // completed (the first sub-chunk taken from a group waits for them); that sub-chunk also
+    // corrects the staged checkpoint of a zero-started segment in place, for the whole group
+    if (j == last || (j % R) == R - 1) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (g.local) {
+        const float sck = lds_f32(NS * 64);
+#pragma unroll
+        for (int n = 0; n < NS; ++n) {
+          const float v = __builtin_fmaf(fast_exp2(a2[n] * sck), hin_s[n * 64 + q.lane], lds_f32(n * 64));
+          stage[n * 64 + q.lane] = __builtin_bit_cast(uint32_t, v);
+        }
+      }
+    }
     // inputs of the sub-chunk before, for the checkpoint advance of odd sub-chunks (the
     // first steps of the same group)
     float xa[K], da[K];
@@ -564,7 +594,7 @@ BwdPlan plan_selective_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t d
   bp.off_mu = off;
   off = align256(off + (S > 1 ? (size_t)S * batch * dstate * dim * 4 : 0));
   bp.off_ckpt = off;
-  off = align256(off + (size_t)S * bp.nsub * batch * dstate * ((dim + 63) / 64) * 64 * 4);
+  off = align256(off + (size_t)S * bp.nsub * batch * (dstate + 1) * ((dim + 63) / 64) * 64 * 4);
   bp.off_bc = off;
   off = align256(off + (size_t)ngroups * batch * seqlen * 2 * dstate * 4);
   bp.off_pa = off;
@@ -591,6 +621,9 @@ static hipError_t run_bwd(const BwdArgs& a, const BwdPlan& bp, hipStream_t strea
   float* dsum = reinterpret_cast<float*>(ws + bp.fwd.ws_dsum);
   float* mu = reinterpret_cast<float*>(ws + bp.off_mu);
   float* ckpt = reinterpret_cast<float*>(ws + bp.off_ckpt);
+  // entering states of zero-started segments: the forward plan's state slots
+  g.local = (!a.states_ready && S > 1) ? 1 : 0;
+  const float* hin = g.local ? reinterpret_cast<const float*>(ws + bp.fwd.ws_state) : nullptr;
   float* pbc = reinterpret_cast<float*>(ws + bp.off_bc);
   float* pa = reinterpret_cast<float*>(ws + bp.off_pa);
   float* pd = reinterpret_cast<float*>(ws + bp.off_pd);
@@ -605,11 +638,11 @@ static hipError_t run_bwd(const BwdArgs& a, const BwdPlan& bp, hipStream_t strea
   const dim3 grid((unsigned)(per_seg * S)), block(64);
   if (a.fwd.z != nullptr)
     hipLaunchKernelGGL((sel_bwd_kernel<NS, BF16, true>), grid, block, 0, stream, a.fwd.x, a.fwd.delta, a.fwd.A,
-                       a.fwd.B, a.fwd.C, a.fwd.Dsk, a.fwd.z, a.dy, a.dh_last, (const float*)mu, (const float*)ckpt,
+                       a.fwd.B, a.fwd.C, a.fwd.Dsk, a.fwd.z, a.dy, a.dh_last, (const float*)mu, (const float*)ckpt, hin,
                        a.dx, a.ddelta, a.dz, pbc, pa, pd, a.dh0, g);
   else
     hipLaunchKernelGGL((sel_bwd_kernel<NS, BF16, false>), grid, block, 0, stream, a.fwd.x, a.fwd.delta, a.fwd.A,
-                       a.fwd.B, a.fwd.C, a.fwd.Dsk, a.fwd.z, a.dy, a.dh_last, (const float*)mu, (const float*)ckpt,
+                       a.fwd.B, a.fwd.C, a.fwd.Dsk, a.fwd.z, a.dy, a.dh_last, (const float*)mu, (const float*)ckpt, hin,
                        a.dx, a.ddelta, a.dz, pbc, pa, pd, a.dh0, g);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t rows = g.batch * g.L;
@@ -636,14 +669,17 @@ static hipError_t dispatch_bwd(const BwdArgs& a, const BwdPlan& bp, hipStream_t 
 }
 
 hipError_t launch_selective_bwd(const BwdArgs& a, const BwdPlan& bp, hipStream_t stream) {
-  // 1. the state entering every segment (pass 1 + carry of the forward scan; skipped when
-  //    the forward call saved them), then 2. the state before every K-th step and the
-  //    segments' adjoint folds (its checkpoint pass)
-  hipError_t e = a.states_ready ? hipSuccess : launch_segment_states(a.fwd, bp.fwd, stream);
+  // 1. the state before every K-th step and the segments' adjoint folds (the forward scan's
+  //    checkpoint pass).  With several segments and no entering states kept by the forward
+  //    call, every segment starts from zero and the same pass leaves the end states for the
+  //    carry (no separate pass over the inputs for the entering states); with kept states
+  //    the checkpoints start from them.
+  const bool local = !a.states_ready && bp.fwd.segments > 1;
+  hipError_t e = (a.states_ready || local) ? hipSuccess : launch_segment_states(a.fwd, bp.fwd, stream);
   if (e != hipSuccess) return e;
   unsigned char* ws = static_cast<unsigned char*>(a.fwd.workspace);
   e = launch_checkpoints(a.fwd, bp.fwd, reinterpret_cast<float*>(ws + bp.off_ckpt), ilog2c(bp.KC), bp.nsub, a.dy,
-                         bp.fwd.segments > 1 ? reinterpret_cast<float*>(ws + bp.off_mu) : nullptr, stream);
+                         bp.fwd.segments > 1 ? reinterpret_cast<float*>(ws + bp.off_mu) : nullptr, local, stream);
   if (e != hipSuccess) return e;
   return a.fwd.bf16 ? dispatch_bwd<true>(a, bp, stream) : dispatch_bwd<false>(a, bp, stream);
 }

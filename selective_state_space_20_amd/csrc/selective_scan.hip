@@ -124,6 +124,7 @@ struct SelSeg {
   int gpb;            // channel groups (waves) per workgroup, all on the same segment
   int nblk;           // workgroups per (batch, segment) = ceil(ngroups / gpb)
   int kshift, nsub;   // PASS 3: a checkpoint every 2^kshift steps, nsub per segment
+  int local;          // PASS 3 with the adjoint fold: every segment from a zero state (see below)
   int vec;            // channel-major layout: 0 one step per access, 1 16-byte row pieces per
                       // lane, 2 whole tiles staged through LDS (see kTileBytes)
 };
@@ -140,7 +141,14 @@ struct SelSeg {
 //         adj_mu[s][b][n][d] = sum_t P_t[n] C_t[n] dv_t with P_t = a_first ... a_t, the decays
 //         this pass already forms, and dv_t = dy_t silu(z_t) (dy_t without the gate); plus the
 //         segment's delta sum into seg_dsum.  (The same sum the reverse walk forms, accumulated
-//         forward so that each exp serves both.)
+//         forward so that each exp serves both.)  With g.local every segment starts from a
+//         zero state instead (no entering state needed, so no pass 1 before it): each
+//         checkpoint then holds the state from zero plus one more row, the delta sum of the
+//         segment's steps before it, and the segment's end state from zero goes to the state
+//         slots passed as h_last (what pass 1 writes), for the carry.  The true state at a
+//         checkpoint is that state plus exp2(A' * sum) times the segment's entering state: the
+//         decays from the segment's start multiply the entering state, and their product is
+//         the exponential of the summed exponents.
 // FL: bit kZoh -- exact zero-order-hold input term, expm1(delta*A)/A * B instead of
 //     delta * B; bits kFront / kSoftplus -- the step size is delta + bias[d], then (with
 //     kSoftplus) softplus of it; bit kBdl -- x/delta/z/y channel-major (batch, dim, seqlen)
@@ -213,7 +221,7 @@ __global__ __launch_bounds__(256, min_waves_sel(NS, FL, BF16, PASS)) void sel_se
       pp[n] = 1.0f;
       mu[n] = 0.0f;
     }
-    if (PASS == 1) {
+    if (PASS == 1 || (adj && g.local)) {
       h[n] = 0.0f;
     } else if (g.S > 1) {
       h[n] = carry[(((int64_t)s * g.batch + b) * N + n) * g.D + dc];
@@ -403,6 +411,17 @@ __global__ __launch_bounds__(256, min_waves_sel(NS, FL, BF16, PASS)) void sel_se
     tile_store();
     tile_load(TT);
   }
+  // PASS 3: the checkpoint before segment step t, [s][b][grp][j][row][lane] with NS + 1
+  // rows of 256 bytes per checkpoint (the states, then the delta sum of the steps before it
+  // when every segment starts from zero)
+  auto ck_store = [&](int t) {
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(
+        seg_state + ((((int64_t)s * g.batch + b) * g.ngroups + grp) * g.nsub + (t >> g.kshift)) * (N + 1) * 64);
+#pragma unroll
+    for (int n = 0; n < NS; ++n)
+      __builtin_amdgcn_raw_buffer_store_b32(f32_as_u32(h[n]), rk, lane * 4, n * 256, kStreamPolicy);
+    if (adj && g.local) __builtin_amdgcn_raw_buffer_store_b32(f32_as_u32(dsum), rk, lane * 4, N * 256, kStreamPolicy);
+  };
 #define SSS_LOAD_BATCH(SLOT, T0)                                                 \
   do {                                                                           \
     if constexpr (!bdl) {                                                        \
@@ -432,13 +451,7 @@ __global__ __launch_bounds__(256, min_waves_sel(NS, FL, BF16, PASS)) void sel_se
   do {                                                                           \
     const float* Bt = (BT);                                                      \
     const float* Ct = (CT);                                                      \
-    if (PASS == 3 && ((T) & kmask) == 0) {                                       \
-      /* checkpoint j = T >> kshift: [s][b][grp][j][n][lane] */                 \
-      const __amdgpu_buffer_rsrc_t rk_ = make_rsrc(                              \
-          seg_state + ((((int64_t)s * g.batch + b) * g.ngroups + grp) * g.nsub + ((T) >> g.kshift)) * N * 64); \
-      _Pragma("unroll") for (int n = 0; n < NS; ++n)                             \
-        __builtin_amdgcn_raw_buffer_store_b32(f32_as_u32(h[n]), rk_, lane * 4, n * 256, kStreamPolicy); \
-    }                                                                            \
+    if (PASS == 3 && ((T) & kmask) == 0) ck_store(T);                            \
     const float xv = val(xq[SLOT], I);                                           \
     const float dl = step_size<FL>(val(dq[SLOT], I), dbv);                       \
     const float dx = dl * xv;                                                    \
@@ -513,14 +526,7 @@ __global__ __launch_bounds__(256, min_waves_sel(NS, FL, BF16, PASS)) void sel_se
                    const uint32_t (&dys)[adj ? QW : 1], int i, int t) {
     if constexpr (kRows) {
       const float* brow = lrows + ((t >> kRTShift) & 1) * (kRowTensors * 256) + (t & (kRT - 1)) * NS;
-      if (PASS == 3 && (t & kmask) == 0) {
-        /* checkpoint j = t >> kshift: [s][b][grp][j][n][lane] */
-        const __amdgpu_buffer_rsrc_t rk = make_rsrc(
-            seg_state + ((((int64_t)s * g.batch + b) * g.ngroups + grp) * g.nsub + (t >> g.kshift)) * N * 64);
-#pragma unroll
-        for (int n = 0; n < NS; ++n)
-          __builtin_amdgcn_raw_buffer_store_b32(f32_as_u32(h[n]), rk, lane * 4, n * 256, kStreamPolicy);
-      }
+      if (PASS == 3 && (t & kmask) == 0) ck_store(t);
       const float xv = val(xs, i);
       const float dl = step_size<FL>(val(dqs, i), dbv);
       const float dx = dl * xv;
@@ -810,6 +816,10 @@ __global__ __launch_bounds__(256, min_waves_sel(NS, FL, BF16, PASS)) void sel_se
     if (lane == 0 || d0 + lane < g.D) seg_dsum[((int64_t)s * g.batch + b) * g.D + dc] = dsum;
 #pragma unroll
     for (int n = 0; n < NS; ++n) adj_mu[(((int64_t)s * g.batch + b) * N + n) * g.D + dc] = mu[n];
+    if (g.local && s < g.S - 1) {  // end state from zero, as pass 1 leaves it for the carry
+#pragma unroll
+      for (int n = 0; n < NS; ++n) h_last[(((int64_t)s * g.batch + b) * N + n) * g.D + dc] = h[n];
+    }
   } else if (PASS == 2 && h_last != nullptr && s == g.S - 1) {
 #pragma unroll
     for (int n = 0; n < NS; ++n) h_last[(b * g.D + dc) * N + n] = h[n];
@@ -948,33 +958,45 @@ hipError_t run_segment_states(const SelArgs& a, const SelPlan& pl, hipStream_t s
   return run_states<NS, BF16, 0>(a, pl, stream);
 }
 
-// Checkpoints for the backward pass (after run_segment_states): the state before every
-// 2^kshift-th step of every segment, into ckpt[s][b][grp][j][n][lane].  With adj_mu (S > 1)
-// the same pass folds each segment's adjoint from a zero adjoint at its end into
+// Checkpoints for the backward pass: the state before every 2^kshift-th step of every
+// segment, into ckpt[s][b][grp][j][row][lane] (NS + 1 rows per checkpoint).  With adj_mu
+// (S > 1) the same pass folds each segment's adjoint from a zero adjoint at its end into
 // adj_mu[s][b][n][d] (dy and the z gate give the read-out's gradient) and writes every
-// segment's delta sum into the forward workspace's sums (the forward carry has used them
-// by then).
+// segment's delta sum into the forward workspace's sums.  Without `local` the state slots
+// already hold the segments' entering states (run_segment_states, or states the forward
+// call kept) and the checkpoints are the states themselves; with `local` every segment
+// starts from zero, the checkpoints carry their delta sums, and the carry then turns the
+// end states this pass leaves in the slots into the entering states (the backward kernel
+// adds their decayed contribution to each checkpoint).
 template <int NS, bool BF16>
 hipError_t run_checkpoints(const SelArgs& a, const SelPlan& pl, float* ckpt, int kshift, int nsub, const float* dy,
-                           float* adj_mu, hipStream_t stream) {
+                           float* adj_mu, bool local, hipStream_t stream) {
   SelSeg g = make_seg(a, pl, NS);
   g.kshift = kshift;
   g.nsub = nsub;
   unsigned char* ws = static_cast<unsigned char*>(a.workspace);
-  const float* st = pl.segments > 1 ? state_slots(a, pl) : nullptr;
+  float* st = pl.segments > 1 ? state_slots(a, pl) : nullptr;
   const int64_t per_seg = (int64_t)g.nblk * g.batch;
   const dim3 grid((unsigned)(per_seg * pl.segments)), block(64u * (unsigned)g.gpb);
   if (adj_mu != nullptr && pl.segments > 1) {
     float* ds = reinterpret_cast<float*>(ws + pl.ws_dsum);
+    g.local = local ? 1 : 0;
+    const float* carry = local ? nullptr : st;  // entering states (read), or
+    float* ends = local ? st : nullptr;         // end states from zero (written)
     const size_t lds3 = lds_rows(NS, kAdj) ? (size_t)g.gpb * row_tile_lds(3, true) : 0;  // B, C row tiles
     if (a.z != nullptr)
       hipLaunchKernelGGL((sel_seq_kernel<NS, BF16, 3, true, kAdj>), grid, block, lds3, stream, a.x, a.delta, a.A, a.B,
-                         a.C, a.Dsk, a.z, a.h0, st, (float*)nullptr, (float*)nullptr, ckpt, ds,
+                         a.C, a.Dsk, a.z, a.h0, carry, (float*)nullptr, ends, ckpt, ds,
                          (const float*)nullptr, dy, adj_mu, g);
     else
       hipLaunchKernelGGL((sel_seq_kernel<NS, BF16, 3, false, kAdj>), grid, block, lds3, stream, a.x, a.delta, a.A,
-                         a.B, a.C, a.Dsk, a.z, a.h0, st, (float*)nullptr, (float*)nullptr, ckpt, ds,
+                         a.B, a.C, a.Dsk, a.z, a.h0, carry, (float*)nullptr, ends, ckpt, ds,
                          (const float*)nullptr, dy, adj_mu, g);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !local) return e;
+    const int64_t nthr = g.batch * (int64_t)NS * g.D;
+    hipLaunchKernelGGL(sel_carry_kernel, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, stream, a.A, a.h0, st,
+                       (const float*)ds, g);
     return hipGetLastError();
   }
   const size_t lds3 = lds_rows(NS, 0) ? (size_t)g.gpb * row_tile_lds(3) : 0;  // B row tiles
@@ -1027,9 +1049,9 @@ template hipError_t run_flags<SSS_INST_NS, true>(const SelArgs&, const SelPlan&,
 template hipError_t run_segment_states<SSS_INST_NS, false>(const SelArgs&, const SelPlan&, hipStream_t);
 template hipError_t run_segment_states<SSS_INST_NS, true>(const SelArgs&, const SelPlan&, hipStream_t);
 template hipError_t run_checkpoints<SSS_INST_NS, false>(const SelArgs&, const SelPlan&, float*, int, int, const float*,
-                                                        float*, hipStream_t);
+                                                        float*, bool, hipStream_t);
 template hipError_t run_checkpoints<SSS_INST_NS, true>(const SelArgs&, const SelPlan&, float*, int, int, const float*,
-                                                       float*, hipStream_t);
+                                                       float*, bool, hipStream_t);
 #else
 int selective_row_mode(const SelArgs& a, const SelPlan& pl) {
   if (!a.bdl) return 0;
@@ -1044,9 +1066,9 @@ int selective_row_mode(const SelArgs& a, const SelPlan& pl) {
   extern template hipError_t run_segment_states<N, false>(const SelArgs&, const SelPlan&, hipStream_t);  \
   extern template hipError_t run_segment_states<N, true>(const SelArgs&, const SelPlan&, hipStream_t);            \
   extern template hipError_t run_checkpoints<N, false>(const SelArgs&, const SelPlan&, float*, int, int, const float*, \
-                                                      float*, hipStream_t);                                         \
+                                                      float*, bool, hipStream_t);                                   \
   extern template hipError_t run_checkpoints<N, true>(const SelArgs&, const SelPlan&, float*, int, int, const float*,  \
-                                                     float*, hipStream_t);
+                                                     float*, bool, hipStream_t);
 SSS_EXTERN_INSTANCES(1)
 SSS_EXTERN_INSTANCES(2)
 SSS_EXTERN_INSTANCES(4)
@@ -1154,23 +1176,23 @@ hipError_t launch_segment_states(const SelArgs& a, const SelPlan& pl, hipStream_
 
 template <bool BF16>
 static hipError_t dispatch_ckpt(const SelArgs& a, const SelPlan& pl, float* ckpt, int kshift, int nsub,
-                                const float* dy, float* adj_mu, hipStream_t stream) {
+                                const float* dy, float* adj_mu, bool local, hipStream_t stream) {
   switch (a.dstate) {
-    case 1: return run_checkpoints<1, BF16>(a, pl, ckpt, kshift, nsub, dy, adj_mu, stream);
-    case 2: return run_checkpoints<2, BF16>(a, pl, ckpt, kshift, nsub, dy, adj_mu, stream);
-    case 4: return run_checkpoints<4, BF16>(a, pl, ckpt, kshift, nsub, dy, adj_mu, stream);
-    case 8: return run_checkpoints<8, BF16>(a, pl, ckpt, kshift, nsub, dy, adj_mu, stream);
-    case 16: return run_checkpoints<16, BF16>(a, pl, ckpt, kshift, nsub, dy, adj_mu, stream);
-    case 32: return run_checkpoints<32, BF16>(a, pl, ckpt, kshift, nsub, dy, adj_mu, stream);
-    case 64: return run_checkpoints<64, BF16>(a, pl, ckpt, kshift, nsub, dy, adj_mu, stream);
+    case 1: return run_checkpoints<1, BF16>(a, pl, ckpt, kshift, nsub, dy, adj_mu, local, stream);
+    case 2: return run_checkpoints<2, BF16>(a, pl, ckpt, kshift, nsub, dy, adj_mu, local, stream);
+    case 4: return run_checkpoints<4, BF16>(a, pl, ckpt, kshift, nsub, dy, adj_mu, local, stream);
+    case 8: return run_checkpoints<8, BF16>(a, pl, ckpt, kshift, nsub, dy, adj_mu, local, stream);
+    case 16: return run_checkpoints<16, BF16>(a, pl, ckpt, kshift, nsub, dy, adj_mu, local, stream);
+    case 32: return run_checkpoints<32, BF16>(a, pl, ckpt, kshift, nsub, dy, adj_mu, local, stream);
+    case 64: return run_checkpoints<64, BF16>(a, pl, ckpt, kshift, nsub, dy, adj_mu, local, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_checkpoints(const SelArgs& a, const SelPlan& pl, float* ckpt, int kshift, int nsub, const float* dy,
-                              float* adj_mu, hipStream_t stream) {
-  return a.bf16 ? dispatch_ckpt<true>(a, pl, ckpt, kshift, nsub, dy, adj_mu, stream)
-                : dispatch_ckpt<false>(a, pl, ckpt, kshift, nsub, dy, adj_mu, stream);
+                              float* adj_mu, bool local, hipStream_t stream) {
+  return a.bf16 ? dispatch_ckpt<true>(a, pl, ckpt, kshift, nsub, dy, adj_mu, local, stream)
+                : dispatch_ckpt<false>(a, pl, ckpt, kshift, nsub, dy, adj_mu, local, stream);
 }
 
 #endif  // SSS_INST_NS

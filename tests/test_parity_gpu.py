@@ -376,6 +376,11 @@ def test_backward(oracle_lib, monkeypatch, case):
     assert all(v <= tol for v in errs.values()), errs
 
 
+# The saved-states gradients against the recompute path's: fp32 arithmetic on the same
+# values in a different order (a checkpoint from the kept state against the state from zero
+# plus the decayed entering state), far below the oracle tolerances.
+SAVED_TOL = 1e-5
+
 SAVED_CASES = [(2, 1500, 100, 16, "bf16", 5), (1, 777, 70, 8, "f32", 3), (1, 900, 64, 4, "bf16", 0),
                (2, 96, 64, 16, "f32", 1), (1, 700, 20, 64, "bf16", 0)]
 
@@ -383,9 +388,11 @@ SAVED_CASES = [(2, 1500, 100, 16, "bf16", 5), (1, 777, 70, 8, "f32", 3), (1, 900
 @pytest.mark.parametrize("case", SAVED_CASES, ids=[f"B{c[0]}L{c[1]}D{c[2]}N{c[3]}{c[4]}S{c[5]}" for c in SAVED_CASES])
 def test_backward_saved_states(monkeypatch, case):
     """selective_scan_fwd_save gives selective_scan_fwd's outputs bitwise and keeps the segment
-    entering states; selective_scan_bwd_saved from them gives selective_scan_bwd's gradients
-    bitwise (the same kernels on the same states), on two calls in a row; a single-segment
-    plan keeps nothing (size 0, no buffer needed)."""
+    entering states; selective_scan_bwd_saved from them gives selective_scan_bwd's gradients up
+    to rounding (its checkpoints start from the kept states, while selective_scan_bwd runs the
+    segments from zero and adds the decayed entering state: the same values in different
+    order), on two calls in a row; a single-segment plan keeps nothing (size 0, no buffer
+    needed) and takes the same kernels, bitwise."""
     import torch
     import selective_state_space_20_amd as sss
     bt, L, dm, n, io, segs = case
@@ -415,7 +422,11 @@ def test_backward_saved_states(monkeypatch, case):
         assert torch.equal(y, y_ref) and torch.equal(hl, hl_ref)
         for k, v in g_ref.items():
             if v is not None:
-                assert torch.equal(g[k], v), k
+                if nbytes == 0:
+                    assert torch.equal(g[k], v), k
+                else:
+                    e = rel_err(g[k].cpu().numpy(), v.cpu().numpy())
+                    assert e <= SAVED_TOL, (k, e)
 
 
 def test_saved_states_errors(monkeypatch):
@@ -449,7 +460,7 @@ def test_saved_states_errors(monkeypatch):
 def test_backward_long_layer_full():
     """Gradients of the full-size long layer (B=1, D=5120, N=16, L=65536, bf16, gated, h0,
     dh_last) against the oracle, every element of every gradient tensor; the saved-states
-    training pair gives the same gradients bitwise at this size too."""
+    training pair gives the same gradients up to rounding at this size too."""
     import torch
     import oracle
     import selective_state_space_20_amd as sss
@@ -463,7 +474,7 @@ def test_backward_long_layer_full():
     g = sss.selective_scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"],
                                dy=dy_d, dh_last=dhl_d)
     # the training pair at full size: the forward keeps its segment entering states and the
-    # gradients call starts from them -- the same gradients, bit for bit
+    # gradients call starts its checkpoints from them -- the same gradients up to rounding
     b, L, d, n = cfg["batch"], cfg["seqlen"], cfg["dim"], cfg["dstate"]
     states = torch.empty(max(sss.selective_scan_states_size(b, L, d, n), 4) // 4, dtype=torch.float32,
                          device="cuda:0")
@@ -471,9 +482,9 @@ def test_backward_long_layer_full():
     g2 = sss.selective_scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"],
                                 dy=dy_d, dh_last=dhl_d, states=states)
     torch.cuda.synchronize()
-    same = {k: bool(torch.equal(g[k], g2[k])) for k in g if g[k] is not None}
-    note(f"    saved-states pair bitwise equal: {same}")
-    assert all(same.values()), same
+    diff = {k: rel_err(g2[k].cpu().numpy(), g[k].cpu().numpy()) for k in g if g[k] is not None}
+    note("    saved-states pair against the recompute path: " + " ".join(f"{k}={v:.1e}" for k, v in diff.items()))
+    assert all(v <= SAVED_TOL for v in diff.values()), diff
     del g2, states
     g = {k: (v.cpu().numpy() if v is not None else None) for k, v in g.items()}
     note("    GPU done")
