@@ -51,21 +51,22 @@ COPY_WRITE_SCALE = 1048576.0 / 1048576.0
 CSRC = "selective_state_space_20_amd/csrc/"
 PMC_TRAFFIC = {
     # default workload: sel_seq_kernel pass 1 + sel_carry_kernel + pass 2
-    "selective": {"sources": (CSRC + "selective_scan.hip", CSRC + "common.h"), "digest": "07f0735a53b19af8",
-                  "fetch_kib": 656862.8 + 46577.5 + 1030507.0, "write_kib": 86700.0 + 81920.0 + 1311040.0},
+    "selective": {"sources": (CSRC + "selective_scan.hip", CSRC + "common.h"), "digest": "87be974d8050cbfa",
+                  "fetch_kib": 656849.0 + 46577.5 + 1030490.0, "write_kib": 86700.0 + 81920.0 + 1311040.0},
     # 8 x 32768 x 4096 fp32
     "elementwise": {"sources": (CSRC + "elementwise_scan.hip", CSRC + "common.h"), "digest": "4b0239623ce7466b",
                     "fetch_kib": 8388744.2, "write_kib": 4194432.0},
     # 256 tokens x 5120 x 16
     "decode": {"sources": (CSRC + "state_update.hip", CSRC + "common.h"), "digest": "454225efc541ef58",
                "fetch_kib": 45119.1, "write_kib": 87040.5},
-    # selective_scan_bwd on the default workload: the forward pass 1 + carry, the checkpoint
-    # pass (with the adjoint's segment folds), the adjoint carry, the main kernel and the two
-    # reductions
+    # selective_scan_bwd on the default workload: the checkpoint pass (segments from zero, with
+    # the adjoint's segment folds), the forward carry, the adjoint carry, the main kernel and
+    # the two reductions
     "backward": {"sources": (CSRC + "selective_bwd.hip", CSRC + "selective_scan.hip", CSRC + "common.h"),
-                 "digest": "623684dc8f8e7504",
-                 "fetch_kib": 656854.5 + 46576.9 + 1690469.1 + 46577.4 + 4349023.9 + 327696.6 + 43547.9,
-                 "write_kib": 86700.0 + 81920.0 + 5329921.1 + 81920.0 + 4685368.6 + 8192.0 + 660.0},
+                 "digest": "ee87b33cd77314bb",
+                 # checkpoint pass (from zero) + forward carry + adjoint carry + main kernel + reductions
+                 "fetch_kib": 1649280.0 + 46576.9 + 46577.7 + 4559090.0 + 327701.0 + 43549.3,
+                 "write_kib": 5739200.0 + 81920.0 + 81920.0 + 4695590.0 + 8192.0 + 660.0},
     # 1 x 65536 x 5120 bf16, width 4
     "conv": {"sources": (CSRC + "conv1d.hip", CSRC + "common.h"), "digest": "0525304aa8e7045b",
              "fetch_kib": 328260.8, "write_kib": 655360.3},
@@ -265,6 +266,8 @@ PROBE_KINDS = {  # main instructions per probe iteration: name, VALU-class count
     14: ("kind 4 (SGPR rows) in phases per step: 16 mul | 16 exp | 64 VALU", 64 + 2, 16, 0),
     15: ("kind 13, update phase by instruction: 16 mul | 16 fma | 16 fma", 64 + 2, 16, 0),
     16: ("kind 15 in groups of 4 states", 64 + 2, 16, 0),
+    17: ("kind 13, priority 2 for the mul and update phases, 0 for the exps", 64 + 2, 16, 0),
+    18: ("kind 13, priority 2 for the exps, 0 for the rest", 64 + 2, 16, 0),
 }
 
 

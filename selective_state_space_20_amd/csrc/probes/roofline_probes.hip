@@ -99,6 +99,9 @@ constexpr int kOps = 16;  // independent chains per wave
 // kind 15: kind 13 with the update phase ordered by instruction: the 16 input-term multiplies,
 //          then the 16 state fmas, then the 16 read-out fmas (no dependent neighbours)
 // kind 16: kind 15 in groups of 4 states (each group: 4 mul | 4 exp | 4 mul | 4 fma | 4 fma)
+// kind 17: kind 13 with the wave's priority raised (s_setprio 2) for its pairable phases
+//          (argument multiplies, update) and lowered (0) for its exps
+// kind 18: kind 13 with the priority raised for the exps and lowered for the rest
 // kind 12: kind 4 with the B and C rows in one VGPR each (lane i of every 16-lane row holds
 //          element i) and B[n], C[n] taken by the VALU ops through DPP row_newbcast:n
 // Roles (kinds 9, 11): waves 4r .. 4r+3 of a workgroup fill one slot on each SIMD, so slot r
@@ -169,14 +172,16 @@ __global__ __launch_bounds__(1024) void alu_kernel(int iters, Rows rows, uint64_
       }
       dl = __builtin_fmaf(dl, 0.9999f, 1e-6f);
       dx = __builtin_fmaf(dx, 0.999f, 1e-4f);
-    } else if constexpr (KIND == 13 || KIND == 14) {
+    } else if constexpr (KIND == 13 || KIND == 14 || KIND == 17 || KIND == 18) {
+      constexpr int kPv = KIND == 17 ? 2 : 0, kPe = KIND == 18 ? 2 : 0;  // phase priorities
+      constexpr bool kPrio = KIND == 17 || KIND == 18;
       float bv[kOps], cv[kOps], e[kOps];
 #pragma unroll
       for (int k = 0; k < kOps; ++k) {
         bv[k] = rows.b[k];
         cv[k] = rows.c[k];
       }
-      if constexpr (KIND == 13) {
+      if constexpr (KIND != 14) {
         const f32x4* row = reinterpret_cast<const f32x4*>(pad + ((rowsel++) & 63) * 32);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -185,11 +190,17 @@ __global__ __launch_bounds__(1024) void alu_kernel(int iters, Rows rows, uint64_
           cv[4 * q] = c4.x; cv[4 * q + 1] = c4.y; cv[4 * q + 2] = c4.z; cv[4 * q + 3] = c4.w;
         }
       }
+      if constexpr (kPrio) __builtin_amdgcn_s_setprio(kPv);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int k = 0; k < kOps; ++k) e[k] = dl * a[k];
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (kPrio) __builtin_amdgcn_s_setprio(kPe);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int k = 0; k < kOps; ++k) e[k] = __builtin_amdgcn_exp2f(e[k]);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (kPrio) __builtin_amdgcn_s_setprio(kPv);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int k = 0; k < kOps; ++k) {
@@ -352,6 +363,8 @@ int sss_probe_alu(int kind, int waves_per_simd, int iters, int grid, uint64_t* o
     case 14: hipLaunchKernelGGL(alu_kernel<14>, dim3((unsigned)grid), block, lds, st, iters, rows, out, sink); break;
     case 15: hipLaunchKernelGGL(alu_kernel<15>, dim3((unsigned)grid), block, lds, st, iters, rows, out, sink); break;
     case 16: hipLaunchKernelGGL(alu_kernel<16>, dim3((unsigned)grid), block, lds, st, iters, rows, out, sink); break;
+    case 17: hipLaunchKernelGGL(alu_kernel<17>, dim3((unsigned)grid), block, lds, st, iters, rows, out, sink); break;
+    case 18: hipLaunchKernelGGL(alu_kernel<18>, dim3((unsigned)grid), block, lds, st, iters, rows, out, sink); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();
