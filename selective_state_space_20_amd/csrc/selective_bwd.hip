@@ -266,6 +266,10 @@ constexpr int ilog2c(int v) { return v <= 1 ? 0 : 1 + ilog2c(v / 2); }
 // adjoint walks the sub-chunk backwards.  A checkpoint and the inputs of the steps it
 // covers reach LDS through direct-to-LDS buffer loads one checkpoint group ahead, so no
 // VGPRs wait on them (a prefetch into a second register slot spilled at 168 VGPRs).
+// scheduling barrier between the phases of a recomputed step: memory, scalar and LDS
+// instructions may cross it, VALU instructions may not
+constexpr int kBwdPhase = 0x3FC;
+
 template <int NS, bool BF16, bool HAS_Z>
 __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
     const void* __restrict__ x, const void* __restrict__ delta, const float* __restrict__ A,
@@ -389,10 +393,21 @@ __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
       if (i < k) {                                                                         \
         const float* Bt = Br + (tb + i) * NS;                                              \
         const float dxv = ds[SLOT][i] * xs[SLOT][i];                                       \
-        _Pragma("unroll") for (int n = 0; n < NS; ++n) {                                   \
-          ea[i][n] = fast_exp2(ds[SLOT][i] * a2[n]);                                       \
-          hs[i + 1][n] = __builtin_fmaf(ea[i][n], hs[i][n], dxv * Bt[n]);                  \
-        }                                                                                  \
+        /* arguments, then the exps at a raised wave priority, then the updates (as the    \
+           forward step: the other waves' VALU work pairs more often); the B_t row is       \
+           loaded ahead of the phases */                                                   \
+        float bt_[NS];                                                                     \
+        _Pragma("unroll") for (int n = 0; n < NS; ++n) bt_[n] = Bt[n];                     \
+        _Pragma("unroll") for (int n = 0; n < NS; ++n) ea[i][n] = ds[SLOT][i] * a2[n];     \
+        __builtin_amdgcn_sched_barrier(kBwdPhase);                                         \
+        __builtin_amdgcn_s_setprio(2);                                                     \
+        __builtin_amdgcn_sched_barrier(kBwdPhase);                                         \
+        _Pragma("unroll") for (int n = 0; n < NS; ++n) ea[i][n] = fast_exp2(ea[i][n]);     \
+        __builtin_amdgcn_sched_barrier(kBwdPhase);                                         \
+        __builtin_amdgcn_s_setprio(0);                                                     \
+        __builtin_amdgcn_sched_barrier(kBwdPhase);                                         \
+        _Pragma("unroll") for (int n = 0; n < NS; ++n)                                     \
+          hs[i + 1][n] = __builtin_fmaf(ea[i][n], hs[i][n], dxv * bt_[n]);                 \
       }                                                                                    \
     }                                                                                      \
     _Pragma("unroll") for (int i = K - 1; i >= 0; --i) {                                   \
