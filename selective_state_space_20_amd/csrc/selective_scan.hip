@@ -461,23 +461,42 @@ __global__ __launch_bounds__(256, min_waves_sel(NS, FL, BF16, PASS)) void sel_se
       dvv = u32_as_f32(gq_dy[SLOT][I]);                         \
       if (has_z) dvv *= silu(val(zq[SLOT], I));                                  \
     }                                                                            \
+    /* states in groups of 4: the arguments, the exps at a raised wave priority,   \
+       then the updates (as the row-tile step); the rows are read ahead of them */ \
+    float bt_[NS], ct_[(PASS == 2 || adj) ? NS : 1];                             \
     _Pragma("unroll") for (int n = 0; n < NS; ++n) {                             \
-      const float arg = dl * a2[n];                                              \
-      const float ab = fast_exp2(arg);                                           \
+      bt_[n] = Bt[n];                                                            \
+      if constexpr (PASS == 2 || adj) ct_[n] = Ct[n];                            \
+    }                                                                            \
+    constexpr int GB_ = NS < 4 ? NS : 4;                                         \
+    _Pragma("unroll") for (int n0 = 0; n0 < NS; n0 += GB_) {                     \
+    float args_[GB_], abs_[GB_];                                                 \
+    _Pragma("unroll") for (int k = 0; k < GB_; ++k) args_[k] = dl * a2[n0 + k];  \
+    __builtin_amdgcn_sched_barrier(0x14);                                        \
+    __builtin_amdgcn_s_setprio(2);                                               \
+    _Pragma("unroll") for (int k = 0; k < GB_; ++k) abs_[k] = fast_exp2(args_[k]); \
+    __builtin_amdgcn_s_setprio(0);                                               \
+    __builtin_amdgcn_sched_barrier(0x14);                                        \
+    _Pragma("unroll") for (int k = 0; k < GB_; ++k) {                            \
+      const int n = n0 + k;                                                      \
+      const float arg = args_[k];                                                \
+      const float ab = abs_[k];                                                  \
       if constexpr (adj) {                                                       \
         pp[n] *= ab;                                                             \
-        mu[n] = __builtin_fmaf(pp[n], Ct[n] * dvv, mu[n]);                       \
+        mu[n] = __builtin_fmaf(pp[n], ct_[n] * dvv, mu[n]);                      \
       }                                                                          \
       if constexpr (zoh) {                                                       \
         const float cf = zoh_coef(arg, ab, dl, ia[n]);                          \
-        h[n] = __builtin_fmaf(ab, h[n], cf * (xv * Bt[n]));                      \
+        h[n] = __builtin_fmaf(ab, h[n], cf * (xv * bt_[n]));                     \
       } else {                                                                   \
-        h[n] = __builtin_fmaf(ab, h[n], dx * Bt[n]);                             \
+        h[n] = __builtin_fmaf(ab, h[n], dx * bt_[n]);                            \
       }                                                                          \
-      if (PASS == 2) {                                                           \
-        if (n & 1) y1 = __builtin_fmaf(Ct[n], h[n], y1);                         \
-        else y0 = __builtin_fmaf(Ct[n], h[n], y0);                               \
+      if constexpr (PASS == 2) {                                                 \
+        if (n & 1) y1 = __builtin_fmaf(ct_[n], h[n], y1);                        \
+        else y0 = __builtin_fmaf(ct_[n], h[n], y0);                              \
       }                                                                          \
+    }                                                                            \
+    __builtin_amdgcn_sched_barrier(0x14);                                        \
     }                                                                            \
     if (PASS == 1 || adj) {                                                      \
       dsum += dl;                                                                \
