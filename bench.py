@@ -51,8 +51,8 @@ COPY_WRITE_SCALE = 1048576.0 / 1048576.0
 CSRC = "selective_state_space_20_amd/csrc/"
 PMC_TRAFFIC = {
     # default workload: sel_seq_kernel pass 1 + sel_carry_kernel + pass 2
-    "selective": {"sources": (CSRC + "selective_scan.hip", CSRC + "common.h"), "digest": "87be974d8050cbfa",
-                  "fetch_kib": 656849.0 + 46577.5 + 1030490.0, "write_kib": 86700.0 + 81920.0 + 1311040.0},
+    "selective": {"sources": (CSRC + "selective_scan.hip", CSRC + "common.h"), "digest": "10fd837ef8324558",
+                  "fetch_kib": 656888.0 + 46577.5 + 1031030.0, "write_kib": 86700.0 + 81920.0 + 1311040.0},
     # 8 x 32768 x 4096 fp32
     "elementwise": {"sources": (CSRC + "elementwise_scan.hip", CSRC + "common.h"), "digest": "4b0239623ce7466b",
                     "fetch_kib": 8388744.2, "write_kib": 4194432.0},
@@ -63,10 +63,10 @@ PMC_TRAFFIC = {
     # the adjoint's segment folds), the forward carry, the adjoint carry, the main kernel and
     # the two reductions
     "backward": {"sources": (CSRC + "selective_bwd.hip", CSRC + "selective_scan.hip", CSRC + "common.h"),
-                 "digest": "ee87b33cd77314bb",
+                 "digest": "70a00784234de472",
                  # checkpoint pass (from zero) + forward carry + adjoint carry + main kernel + reductions
-                 "fetch_kib": 1649280.0 + 46576.9 + 46577.7 + 4559090.0 + 327701.0 + 43549.3,
-                 "write_kib": 5739200.0 + 81920.0 + 81920.0 + 4695590.0 + 8192.0 + 660.0},
+                 "fetch_kib": 1649340.0 + 46577.0 + 46577.7 + 4558480.0 + 327701.0 + 43549.4,
+                 "write_kib": 5739200.0 + 81920.0 + 81920.0 + 4695630.0 + 8192.0 + 660.0},
     # 1 x 65536 x 5120 bf16, width 4
     "conv": {"sources": (CSRC + "conv1d.hip", CSRC + "common.h"), "digest": "0525304aa8e7045b",
              "fetch_kib": 328260.8, "write_kib": 655360.3},
