@@ -385,8 +385,19 @@ __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
         const float dla = da[i];                                                           \
         const float dxa = dla * xa[i];                                                     \
         const float* Ba = Br + ta * NS;                                                    \
+        /* phased like the steps below; the decays go through ea[0], not yet in use */     \
+        float ba_[NS];                                                                     \
+        _Pragma("unroll") for (int n = 0; n < NS; ++n) ba_[n] = Ba[n];                     \
+        _Pragma("unroll") for (int n = 0; n < NS; ++n) ea[0][n] = dla * a2[n];             \
+        __builtin_amdgcn_sched_barrier(kBwdPhase);                                         \
+        __builtin_amdgcn_s_setprio(2);                                                     \
+        __builtin_amdgcn_sched_barrier(kBwdPhase);                                         \
+        _Pragma("unroll") for (int n = 0; n < NS; ++n) ea[0][n] = fast_exp2(ea[0][n]);     \
+        __builtin_amdgcn_sched_barrier(kBwdPhase);                                         \
+        __builtin_amdgcn_s_setprio(0);                                                     \
+        __builtin_amdgcn_sched_barrier(kBwdPhase);                                         \
         _Pragma("unroll") for (int n = 0; n < NS; ++n)                                     \
-          hs[0][n] = __builtin_fmaf(fast_exp2(dla * a2[n]), hs[0][n], dxa * Ba[n]);        \
+          hs[0][n] = __builtin_fmaf(ea[0][n], hs[0][n], dxa * ba_[n]);                     \
       }                                                                                    \
     }                                                                                      \
     _Pragma("unroll") for (int i = 0; i < K; ++i) {                                        \
