@@ -63,10 +63,10 @@ PMC_TRAFFIC = {
     # the adjoint's segment folds), the forward carry, the adjoint carry, the main kernel and
     # the two reductions
     "backward": {"sources": (CSRC + "selective_bwd.hip", CSRC + "selective_scan.hip", CSRC + "common.h"),
-                 "digest": "70a00784234de472",
+                 "digest": "30b872aa973586fa",
                  # checkpoint pass (from zero) + forward carry + adjoint carry + main kernel + reductions
-                 "fetch_kib": 1649340.0 + 46577.0 + 46577.7 + 4558480.0 + 327701.0 + 43549.4,
-                 "write_kib": 5739200.0 + 81920.0 + 81920.0 + 4695630.0 + 8192.0 + 660.0},
+                 "fetch_kib": 1649520.0 + 46576.9 + 46577.7 + 4558120.0 + 327701.0 + 43549.4,
+                 "write_kib": 5739200.0 + 81920.0 + 81920.0 + 4695720.0 + 8192.0 + 660.0},
     # 1 x 65536 x 5120 bf16, width 4
     "conv": {"sources": (CSRC + "conv1d.hip", CSRC + "common.h"), "digest": "0525304aa8e7045b",
              "fetch_kib": 328260.8, "write_kib": 655360.3},
