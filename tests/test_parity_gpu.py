@@ -376,6 +376,43 @@ def test_backward(oracle_lib, monkeypatch, case):
     assert all(v <= tol for v in errs.values()), errs
 
 
+BWD_SPECIAL_CASES = [(2, 777, 40, 16, "f32", 5), (1, 1000, 70, 16, "bf16", 4), (2, 513, 33, 8, "f32", 3)]
+
+
+@pytest.mark.parametrize("case", BWD_SPECIAL_CASES, ids=[f"B{c[0]}L{c[1]}D{c[2]}N{c[3]}{c[4]}S{c[5]}"
+                                                        for c in BWD_SPECIAL_CASES])
+def test_backward_special_values(oracle_lib, monkeypatch, case):
+    """Gradients where the zero-started checkpoints' correction exp2(A' * S) * h_enter meets its
+    limits: states with A = 0 (no decay: the entering state carries unchanged, factor 1), a
+    run of zero step sizes across segment boundaries (S = 0 at checkpoints past a segment's
+    start, a = 1), and a large initial state (the correction dominates the first segment);
+    against the oracle on every gradient element."""
+    import torch
+    import selective_state_space_20_amd as sss
+    bt, L, dm, n, io, segs = case
+    monkeypatch.setenv("SSS_FORCE_SEGMENTS", str(segs))
+    seed = zlib.crc32(repr(case).encode()) % 100000
+    inp = gen.selective_inputs(bt, L, dm, n, io=io, with_z=True, with_D=True, h0=True, seed=seed)
+    inp["A"][:, : n // 4] = 0.0
+    lo, hi = L // 5, L // 5 + L // 4  # zero steps over at least one segment boundary
+    inp["delta"][:, lo:hi, :] = 0
+    inp["h0"] = (inp["h0"] * 10.0).astype(np.float32)
+    rng = np.random.default_rng(seed + 3)
+    dy = rng.standard_normal((bt, L, dm)).astype(np.float32)
+    dhl = rng.standard_normal((bt, dm, n)).astype(np.float32)
+    note(f"[backward special] {case}")
+    t = {k: to_dev(v, "cuda:0") for k, v in inp.items() if k != "io"}
+    g = sss.selective_scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"],
+                               dy=to_dev(dy, "cuda:0"), dh_last=to_dev(dhl, "cuda:0"))
+    torch.cuda.synchronize()
+    r = oracle_lib.selective_scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                                      inp["h0"], dy=dy, dh_last=dhl)
+    tol = TOL_BF16 if io == "bf16" else TOL_F32
+    errs = {k: rel_err(g[k].cpu().numpy(), r[k]) for k in ("dx", "ddelta", "dA", "dB", "dC", "dD", "dz", "dh0")}
+    note("    " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    assert all(v <= tol for v in errs.values()), errs
+
+
 # The saved-states gradients against the recompute path's: fp32 arithmetic on the same
 # values in a different order (a checkpoint from the kept state against the state from zero
 # plus the decayed entering state), far below the oracle tolerances.
