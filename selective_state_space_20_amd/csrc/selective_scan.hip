@@ -462,14 +462,22 @@ __global__ __launch_bounds__(256, min_waves_sel(NS, FL, BF16, PASS)) void sel_se
       if (has_z) dvv *= silu(val(zq[SLOT], I));                                  \
     }                                                                            \
     /* states in groups of 4: the arguments, the exps at a raised wave priority,   \
-       then the updates (as the row-tile step); the rows are read ahead of them */ \
-    float bt_[NS], ct_[(PASS == 2 || adj) ? NS : 1];                             \
-    _Pragma("unroll") for (int n = 0; n < NS; ++n) {                             \
-      bt_[n] = Bt[n];                                                            \
-      if constexpr (PASS == 2 || adj) ct_[n] = Ct[n];                            \
-    }                                                                            \
+       then the updates (as the row-tile step); the rows are read ahead of them,   \
+       all at once up to 32 states, a group at a time above (64 states' rows of B  \
+       and C would not fit the scalar registers) */                                \
     constexpr int GB_ = NS < 4 ? NS : 4;                                         \
+    constexpr int RA_ = NS <= 32 ? NS : GB_;                                     \
+    float bt_[RA_], ct_[(PASS == 2 || adj) ? RA_ : 1];                           \
+    auto rows_ahead_ = [&](int r0) {                                             \
+      _Pragma("unroll") for (int r = 0; r < RA_; ++r) {                          \
+        bt_[r] = Bt[r0 + r];                                                     \
+        if constexpr (PASS == 2 || adj) ct_[r] = Ct[r0 + r];                     \
+      }                                                                          \
+    };                                                                           \
+    if constexpr (RA_ == NS) rows_ahead_(0);                                     \
     _Pragma("unroll") for (int n0 = 0; n0 < NS; n0 += GB_) {                     \
+    if constexpr (RA_ != NS) rows_ahead_(n0);                                    \
+    constexpr int RB_ = RA_ == NS ? 1 : 0; /* row index base: n, or n - n0 */    \
     float args_[GB_], abs_[GB_];                                                 \
     _Pragma("unroll") for (int k = 0; k < GB_; ++k) args_[k] = dl * a2[n0 + k];  \
     __builtin_amdgcn_sched_barrier(0x14);                                        \
@@ -479,21 +487,22 @@ __global__ __launch_bounds__(256, min_waves_sel(NS, FL, BF16, PASS)) void sel_se
     __builtin_amdgcn_sched_barrier(0x14);                                        \
     _Pragma("unroll") for (int k = 0; k < GB_; ++k) {                            \
       const int n = n0 + k;                                                      \
+      const int r_ = RB_ ? n : k; /* the state's row entry */                    \
       const float arg = args_[k];                                                \
       const float ab = abs_[k];                                                  \
       if constexpr (adj) {                                                       \
         pp[n] *= ab;                                                             \
-        mu[n] = __builtin_fmaf(pp[n], ct_[n] * dvv, mu[n]);                      \
+        mu[n] = __builtin_fmaf(pp[n], ct_[r_] * dvv, mu[n]);                     \
       }                                                                          \
       if constexpr (zoh) {                                                       \
         const float cf = zoh_coef(arg, ab, dl, ia[n]);                          \
-        h[n] = __builtin_fmaf(ab, h[n], cf * (xv * bt_[n]));                     \
+        h[n] = __builtin_fmaf(ab, h[n], cf * (xv * bt_[r_]));                    \
       } else {                                                                   \
-        h[n] = __builtin_fmaf(ab, h[n], dx * bt_[n]);                            \
+        h[n] = __builtin_fmaf(ab, h[n], dx * bt_[r_]);                           \
       }                                                                          \
       if constexpr (PASS == 2) {                                                 \
-        if (n & 1) y1 = __builtin_fmaf(ct_[n], h[n], y1);                        \
-        else y0 = __builtin_fmaf(ct_[n], h[n], y0);                              \
+        if (n & 1) y1 = __builtin_fmaf(ct_[r_], h[n], y1);                       \
+        else y0 = __builtin_fmaf(ct_[r_], h[n], y0);                             \
       }                                                                          \
     }                                                                            \
     __builtin_amdgcn_sched_barrier(0x14);                                        \
