@@ -51,8 +51,8 @@ COPY_WRITE_SCALE = 1048576.0 / 1048576.0
 CSRC = "selective_state_space_20_amd/csrc/"
 PMC_TRAFFIC = {
     # default workload: sel_seq_kernel pass 1 + sel_carry_kernel + pass 2
-    "selective": {"sources": (CSRC + "selective_scan.hip", CSRC + "common.h"), "digest": "10fd837ef8324558",
-                  "fetch_kib": 656888.0 + 46577.5 + 1031030.0, "write_kib": 86700.0 + 81920.0 + 1311040.0},
+    "selective": {"sources": (CSRC + "selective_scan.hip", CSRC + "common.h"), "digest": "75a9c1fc574abfbd",
+                  "fetch_kib": 656927.0 + 46577.4 + 1031110.0, "write_kib": 86700.0 + 81920.0 + 1311040.0},
     # 8 x 32768 x 4096 fp32
     "elementwise": {"sources": (CSRC + "elementwise_scan.hip", CSRC + "common.h"), "digest": "4b0239623ce7466b",
                     "fetch_kib": 8388744.2, "write_kib": 4194432.0},
@@ -63,10 +63,10 @@ PMC_TRAFFIC = {
     # the adjoint's segment folds), the forward carry, the adjoint carry, the main kernel and
     # the two reductions
     "backward": {"sources": (CSRC + "selective_bwd.hip", CSRC + "selective_scan.hip", CSRC + "common.h"),
-                 "digest": "30b872aa973586fa",
+                 "digest": "57e5eed17d251b75",
                  # checkpoint pass (from zero) + forward carry + adjoint carry + main kernel + reductions
-                 "fetch_kib": 1649520.0 + 46576.9 + 46577.7 + 4558120.0 + 327701.0 + 43549.4,
-                 "write_kib": 5739200.0 + 81920.0 + 81920.0 + 4695720.0 + 8192.0 + 660.0},
+                 "fetch_kib": 1649350.0 + 46576.9 + 46577.7 + 4557810.0 + 327701.0 + 43549.4,
+                 "write_kib": 5739210.0 + 81920.0 + 81920.0 + 4695670.0 + 8192.0 + 660.0},
     # 1 x 65536 x 5120 bf16, width 4
     "conv": {"sources": (CSRC + "conv1d.hip", CSRC + "common.h"), "digest": "0525304aa8e7045b",
              "fetch_kib": 328260.8, "write_kib": 655360.3},
