@@ -63,8 +63,10 @@ def _load():
         lib.oracle_selective_state_update.argtypes = [vp] * 10 + [i64] * 3 + [i32] * 2
         lib.oracle_causal_conv1d.argtypes = [vp] * 4 + [i64] * 4 + [i32] * 3
         lib.oracle_selective_scan_bwd.argtypes = [vp] * 18 + [i64] * 4 + [i32] * 2
+        lib.oracle_selective_scan_bwd_ex.argtypes = [vp] * 11 + [i32] + [vp] * 9 + [i64] * 4 + [i32] * 2
         for f in ("oracle_selective_scan", "oracle_selective_scan_channels", "oracle_selective_scan_chunked",
                   "oracle_selective_state_update", "oracle_causal_conv1d", "oracle_selective_scan_bwd",
+                  "oracle_selective_scan_bwd_ex",
                   "oracle_elementwise_scan", "oracle_elementwise_scan_channels",
                   "oracle_elementwise_scan_chunked", "oracle_max_threads"):
             getattr(lib, f).restype = ctypes.c_int
@@ -197,13 +199,17 @@ def selective_state_update(x, delta, A, B, C, D=None, z=None, state=None, *, nth
     return y, st
 
 
-def selective_scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, *, dy, dh_last=None, nthreads=0):
+def selective_scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, *, dy, dh_last=None, delta_bias=None,
+                       delta_softplus=False, nthreads=0):
     """Gradients of sum(dy * y) + sum(dh_last * h_last) with respect to every input.
 
     Returns a dict of float64 arrays: dx, ddelta (Bt, L, Dm); dz (only with z); dA (Dm, N);
-    dB, dC (Bt, L, N); dD (only with D); dh0 (Bt, Dm, N)."""
+    dB, dC (Bt, L, N); dD (only with D); dh0 (Bt, Dm, N); ddelta_bias (Dm,) (only with
+    delta_bias).  With delta_bias / delta_softplus the step size is the front end's
+    (softplus(delta + bias)) and ddelta is the gradient with respect to the stored delta."""
     x, delta, z = _io(x), _io(delta), _io(z)
     A, B, C, D, h0 = _f32(A), _f32(B), _f32(C), _f32(D), _f32(h0)
+    dbias = _f32(delta_bias)
     bt, L, dm = x.shape
     n = A.shape[1]
     dy = np.ascontiguousarray(dy, dtype=np.float64)
@@ -212,11 +218,15 @@ def selective_scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, *, dy, dh_las
                dB=np.empty((bt, L, n)), dC=np.empty((bt, L, n)), dh0=np.empty((bt, dm, n)))
     out["dD"] = np.empty(dm) if D is not None else None
     out["dz"] = np.empty((bt, L, dm)) if z is not None else None
-    rc = _load().oracle_selective_scan_bwd(_p(x), _p(delta), _p(A), _p(B), _p(C), _p(D), _p(z), _p(h0), _p(dy),
-                                           _p(dhl), _p(out["dx"]), _p(out["ddelta"]), _p(out["dA"]), _p(out["dB"]),
-                                           _p(out["dC"]), _p(out["dD"]), _p(out["dz"]), _p(out["dh0"]), bt, L, dm, n,
-                                           _io_code(x), nthreads)
+    out["ddelta_bias"] = np.empty(dm) if dbias is not None else None
+    rc = _load().oracle_selective_scan_bwd_ex(_p(x), _p(delta), _p(A), _p(B), _p(C), _p(D), _p(z), _p(h0), _p(dy),
+                                              _p(dhl), _p(dbias), int(bool(delta_softplus)), _p(out["dx"]),
+                                              _p(out["ddelta"]), _p(out["dA"]), _p(out["dB"]), _p(out["dC"]),
+                                              _p(out["dD"]), _p(out["dz"]), _p(out["dh0"]), _p(out["ddelta_bias"]),
+                                              bt, L, dm, n, _io_code(x), nthreads)
     _check(rc)
+    if dbias is None:
+        del out["ddelta_bias"]
     return out
 
 

@@ -245,11 +245,35 @@ int oracle_selective_state_update(const void* x, const void* delta, const float*
  * dz (B, L, D; dz only with z), dA (D, N), dB, dC (B, L, N), dD (D), dh0 (B, D, N) (each
  * nullable where its input is optional).
  */
+/*
+ * The same gradients with the front end (delta_value): the step size used is
+ * dt = softplus(delta + dbias[d]) (sp) or delta + dbias[d], and ddelta is the gradient with
+ * respect to the stored delta -- the step-size gradient times dsoftplus/dv = sigmoid(v),
+ * v = delta + dbias[d] -- and ddbias[d] (nullable) its sum over b and t (the chain rule through
+ * the front end; reading of the build, the pages give the front end but no gradient).
+ */
+int oracle_selective_scan_bwd_ex(const void* x, const void* delta, const float* A, const float* Bm, const float* Cm,
+                                 const float* Dsk, const void* z, const float* h0, const double* dy,
+                                 const double* dh_last, const float* dbias, int sp, double* dx, double* ddelta,
+                                 double* dA, double* dB, double* dC, double* dD, double* dz, double* dh0,
+                                 double* ddbias, int64_t batch, int64_t L, int64_t Dm, int64_t N, int dtype,
+                                 int nthreads);
+
 int oracle_selective_scan_bwd(const void* x, const void* delta, const float* A, const float* Bm, const float* Cm,
                               const float* Dsk, const void* z, const float* h0, const double* dy,
                               const double* dh_last, double* dx, double* ddelta, double* dA, double* dB, double* dC,
                               double* dD, double* dz, double* dh0, int64_t batch, int64_t L, int64_t Dm, int64_t N,
                               int dtype, int nthreads) {
+  return oracle_selective_scan_bwd_ex(x, delta, A, Bm, Cm, Dsk, z, h0, dy, dh_last, NULL, 0, dx, ddelta, dA, dB, dC,
+                                      dD, dz, dh0, NULL, batch, L, Dm, N, dtype, nthreads);
+}
+
+int oracle_selective_scan_bwd_ex(const void* x, const void* delta, const float* A, const float* Bm, const float* Cm,
+                                 const float* Dsk, const void* z, const float* h0, const double* dy,
+                                 const double* dh_last, const float* dbias, int sp, double* dx, double* ddelta,
+                                 double* dA, double* dB, double* dC, double* dD, double* dz, double* dh0,
+                                 double* ddbias, int64_t batch, int64_t L, int64_t Dm, int64_t N, int dtype,
+                                 int nthreads) {
   if (!sel_args_ok(x, delta, A, Bm, Cm, batch, L, Dm, N, dtype) || !dy || !dx || !ddelta || !dA || !dB || !dC)
     return OR_ERR_ARG;
   set_threads(nthreads);
@@ -258,6 +282,7 @@ int oracle_selective_scan_bwd(const void* x, const void* delta, const float* A, 
   memset(dB, 0, sizeof(double) * batch * L * N);
   memset(dC, 0, sizeof(double) * batch * L * N);
   if (dD) memset(dD, 0, sizeof(double) * Dm);
+  if (ddbias) memset(ddbias, 0, sizeof(double) * Dm);
 #pragma omp parallel
   {
     double* hs = (double*)malloc(sizeof(double) * (L + 1) * N);   /* h_{t-1} for t = 0..L */
@@ -267,6 +292,7 @@ int oracle_selective_scan_bwd(const void* x, const void* delta, const float* A, 
     double* lC = (double*)calloc((size_t)(batch * L * N), sizeof(double));
     double* lA = (double*)calloc((size_t)(Dm * N), sizeof(double));
     double* lD = (double*)calloc((size_t)Dm, sizeof(double));
+    double* lDb = (double*)calloc((size_t)Dm, sizeof(double));
 #pragma omp for schedule(dynamic, 1)
     for (int64_t c = 0; c < nch; ++c) {
       int64_t b = c / Dm, d = c % Dm;
@@ -274,7 +300,7 @@ int oracle_selective_scan_bwd(const void* x, const void* delta, const float* A, 
       for (int64_t n = 0; n < N; ++n) hs[n] = h0 ? (double)h0[c * N + n] : 0.0;
       for (int64_t t = 0; t < L; ++t) {
         int64_t e = (b * L + t) * Dm + d;
-        double xt = load_val(x, e, dtype), dt = load_val(delta, e, dtype);
+        double xt = load_val(x, e, dtype), dt = delta_value(delta, e, dtype, dbias, d, sp);
         double v = 0.0;
         for (int64_t n = 0; n < N; ++n) {
           double hn = exp(dt * (double)A[d * N + n]) * hs[t * N + n] + dt * (double)Bm[(b * L + t) * N + n] * xt;
@@ -288,7 +314,7 @@ int oracle_selective_scan_bwd(const void* x, const void* delta, const float* A, 
       for (int64_t n = 0; n < N; ++n) lam[n] = dh_last ? dh_last[c * N + n] : 0.0;
       for (int64_t t = L - 1; t >= 0; --t) {
         int64_t e = (b * L + t) * Dm + d;
-        double xt = load_val(x, e, dtype), dt = load_val(delta, e, dtype);
+        double xt = load_val(x, e, dtype), dt = delta_value(delta, e, dtype, dbias, d, sp);
         double g = 1.0;
         if (z) {
           double zt = load_val(z, e, dtype);
@@ -313,7 +339,12 @@ int oracle_selective_scan_bwd(const void* x, const void* delta, const float* A, 
         }
         if (Dsk) lD[d] += dv * xt;
         dx[e] = gx;
+        if (sp) { /* d softplus(v) / dv = sigmoid(v) */
+          double vr = load_val(delta, e, dtype) + (dbias ? (double)dbias[d] : 0.0);
+          gd *= 1.0 / (1.0 + exp(-vr));
+        }
         ddelta[e] = gd;
+        lDb[d] += gd;
       }
       if (dh0)
         for (int64_t n = 0; n < N; ++n) dh0[c * N + n] = lam[n];
@@ -327,7 +358,10 @@ int oracle_selective_scan_bwd(const void* x, const void* delta, const float* A, 
       for (int64_t i = 0; i < Dm * N; ++i) dA[i] += lA[i];
       if (dD)
         for (int64_t i = 0; i < Dm; ++i) dD[i] += lD[i];
+      if (ddbias)
+        for (int64_t i = 0; i < Dm; ++i) ddbias[i] += lDb[i];
     }
+    free(lDb);
     free(hs);
     free(vs);
     free(lam);

@@ -58,6 +58,12 @@ MUTANTS = {
     "bwd_delta_without_decay_term": ("gd += l * (Bn * xt + an * at * hp);", "gd += l * (Bn * xt);"),
     "bwd_dA_uses_new_state": ("lA[d * N + n] += l * dt * at * hp;", "lA[d * N + n] += l * dt * at * hs[(t + 1) * N + n];"),
     "bwd_dh_last_ignored": ("lam[n] = dh_last ? dh_last[c * N + n] : 0.0;", "lam[n] = 0.0;"),
+    "bwd_softplus_chain_dropped": ("gd *= 1.0 / (1.0 + exp(-vr));", "gd *= 1.0;"),
+    "bwd_softplus_chain_without_bias": ("double vr = load_val(delta, e, dtype) + (dbias ? (double)dbias[d] : 0.0);",
+                                        "double vr = load_val(delta, e, dtype);"),
+    "bwd_bias_grad_dropped": ("lDb[d] += gd;", "lDb[d] += 0.5 * gd;"),
+    "bwd_front_end_ignored": ("double xt = load_val(x, e, dtype), dt = delta_value(delta, e, dtype, dbias, d, sp);\n        double g = 1.0;",
+                              "double xt = load_val(x, e, dtype), dt = load_val(delta, e, dtype);\n        double g = 1.0;"),
     "bwd_adjoint_not_decayed": ("lam[n] = at * l;", "lam[n] = l;"),
     "bwd_silu_derivative": ("sg * (1.0 + zt * (1.0 - sg))", "sg"),
     "front_end_bias_ignored": ("  if (dbias) v += (double)dbias[d];", "  (void)dbias;"),

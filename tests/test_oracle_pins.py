@@ -537,18 +537,23 @@ def test_C2_conv_hand_worked(oracle_lib):
 
 
 # ---------------------------------------------------------------- backward (gradients)
-def _fd_check(oracle_lib, inp, dy, dhl, names, eps_rel=1e-4, seed=0):
+def _fd_check(oracle_lib, inp, dy, dhl, names, eps_rel=1e-4, seed=0, softplus=False):
     """Central differences of L = sum(dy*y) + sum(dh_last*h_last) (the pinned forward oracle)
     along a random direction per input, against the adjoint gradients.  The perturbed inputs
     are fp32; the difference actually applied (after rounding) is what the gradient is
-    contracted with, so rounding of the perturbation does not enter the comparison."""
+    contracted with, so rounding of the perturbation does not enter the comparison.  With
+    inp["delta_bias"] and/or softplus the forward's front end is on (the step size is
+    softplus(delta + bias)) in both the gradients and the differenced forward."""
+    bias = inp.get("delta_bias")
     g = oracle_lib.selective_scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
-                                      inp["h0"], dy=dy, dh_last=dhl)
-    key = {"x": "dx", "delta": "ddelta", "A": "dA", "B": "dB", "C": "dC", "D": "dD", "z": "dz", "h0": "dh0"}
+                                      inp["h0"], dy=dy, dh_last=dhl, delta_bias=bias, delta_softplus=softplus)
+    key = {"x": "dx", "delta": "ddelta", "A": "dA", "B": "dB", "C": "dC", "D": "dD", "z": "dz", "h0": "dh0",
+           "delta_bias": "ddelta_bias"}
     rng = np.random.default_rng(seed)
 
     def loss(d):
-        y, hl = oracle_lib.selective_scan(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["h0"])
+        y, hl = oracle_lib.selective_scan(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["h0"],
+                                          delta_bias=d.get("delta_bias"), delta_softplus=softplus)
         return float(np.sum(dy * y) + (np.sum(dhl * hl) if dhl is not None else 0.0))
 
     for name in names:
@@ -582,6 +587,33 @@ def test_G2_gradients_without_options(oracle_lib):
     _fd_check(oracle_lib, inp, dy, None, ["x", "delta", "A", "B", "C"], seed=206)
     g = oracle_lib.selective_scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], dy=dy)
     assert g["dD"] is None and g["dz"] is None
+
+
+def test_G3_gradients_through_the_softplus_front_end(oracle_lib):
+    """With the front end on (step size softplus(delta + bias)), every gradient -- the stored
+    delta's through sigmoid(delta + bias), and the bias's summed over batch and time --
+    against central differences of the forward oracle run with the same front end."""
+    inp = gen.selective_inputs(2, 40, 5, 4, io="f32", with_D=True, with_z=True, h0=True, h0_std=0.5, seed=207)
+    rng = np.random.default_rng(208)
+    inp["delta"] = rng.normal(-3.0, 2.5, inp["delta"].shape).astype(np.float32)   # raw, before softplus
+    inp["delta_bias"] = (0.4 * rng.standard_normal(inp["A"].shape[0])).astype(np.float32)
+    dy = rng.standard_normal(inp["x"].shape)
+    dhl = rng.standard_normal(inp["h0"].shape)
+    _fd_check(oracle_lib, inp, dy, dhl, ["x", "delta", "A", "B", "C", "D", "z", "h0", "delta_bias"], seed=209,
+              softplus=True)
+
+
+def test_G4_gradients_with_a_bias_and_no_softplus(oracle_lib):
+    """A bias alone (step size delta + bias): the bias gradient is the sum of the delta
+    gradient over batch and time, and both match central differences."""
+    inp = gen.selective_inputs(1, 50, 4, 8, io="f32", with_D=True, with_z=False, h0=True, seed=210)
+    rng = np.random.default_rng(211)
+    inp["delta_bias"] = (0.01 * rng.uniform(0.5, 1.5, inp["A"].shape[0])).astype(np.float32)
+    dy = rng.standard_normal(inp["x"].shape)
+    _fd_check(oracle_lib, inp, dy, None, ["delta", "delta_bias", "A"], seed=212)
+    g = oracle_lib.selective_scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                                      inp["h0"], dy=dy, delta_bias=inp["delta_bias"])
+    assert np.allclose(g["ddelta_bias"], g["ddelta"].sum(axis=(0, 1)), rtol=1e-12, atol=1e-12)
 
 
 # ---------------------------------------------------------------- channel-major (B,D,L) layout
