@@ -122,6 +122,29 @@ int selective_scan_bwd(const void* x, const void* delta, const float* A, const f
                        int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype, void* workspace,
                        size_t workspace_bytes, sss_stream_t stream);
 
+/* selective_scan_bwd_ex: the gradients through the delta front end of selective_scan_fwd_ex
+ * (the step size is delta + delta_bias[d], then softplus of it with SSS_DELTA_SOFTPLUS: "Selective
+ * Scan trong Mamba toi uu chuoi dai the nao?", section "Selection pha vo convolution kernel co
+ * dinh", where the step is a softplus of a bias plus a projection of the input; the pages give
+ * no gradient, this is the chain rule through that front end).  The loss is that of
+ * selective_scan_bwd over selective_scan_fwd_ex's outputs for the same delta_bias and flags.
+ * Arguments as selective_scan_bwd, plus:
+ *   delta_bias (dim) float32, nullable (no bias); flags: 0 or SSS_DELTA_SOFTPLUS (any other
+ *   bit, the exact hold and the channel-major layout included: SSS_ERR_UNSUPPORTED);
+ *   ddelta_bias (dim) float32 output, required when delta_bias is given (SSS_ERR_NULL_ARG),
+ *   ignored otherwise: the sum over batch and time of ddelta.
+ * ddelta is the gradient with respect to the STORED delta: the step size's gradient times
+ * sigmoid(delta + bias) under softplus (the slope of softplus), times 1 with the bias alone.
+ * With delta_bias NULL and flags 0 it is exactly selective_scan_bwd.  Same workspace size,
+ * overlap rules (delta_bias is an input, ddelta_bias an output) and determinism.  Returns an
+ * sss_status. */
+int selective_scan_bwd_ex(const void* x, const void* delta, const float* A, const float* B, const float* C,
+                          const float* D_skip, const void* z, const float* h0, const float* dy, const float* dh_last,
+                          const float* delta_bias, unsigned flags, float* dx, float* ddelta, float* dA, float* dB,
+                          float* dC, float* dD, float* dz, float* dh0, float* ddelta_bias, int64_t batch,
+                          int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype, void* workspace,
+                          size_t workspace_bytes, sss_stream_t stream);
+
 /* Training pair that keeps the forward call's segment entering states instead of recomputing
  * them in the gradients call.  Only the state at each time segment's start is kept, a
  * fraction (segments / seqlen) of the state the recurrence forms; everything else is still

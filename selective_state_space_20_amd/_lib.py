@@ -24,7 +24,7 @@ EXPORTED = ("selective_scan_fwd", "selective_scan_fwd_ex", "selective_scan_fwd_w
             "causal_conv1d_fwd", "selective_scan_bwd", "selective_scan_bwd_workspace_size",
             "elementwise_scan", "elementwise_scan_workspace_size", "sss_status_string",
             "selective_scan_fwd_noalloc", "selective_scan_states_size", "selective_scan_fwd_save",
-            "selective_scan_bwd_saved")
+            "selective_scan_bwd_saved", "selective_scan_bwd_ex")
 
 
 class SSSError(RuntimeError):
@@ -77,6 +77,8 @@ def load() -> ctypes.CDLL:
         lib.selective_scan_fwd_save.restype = i32
         lib.selective_scan_bwd_saved.argtypes = [vp] * 11 + [sz] + [vp] * 8 + [i64] * 4 + [i32, vp, sz, vp]
         lib.selective_scan_bwd_saved.restype = i32
+        lib.selective_scan_bwd_ex.argtypes = [vp] * 11 + [ctypes.c_uint] + [vp] * 9 + [i64] * 4 + [i32, vp, sz, vp]
+        lib.selective_scan_bwd_ex.restype = i32
         lib.sss_status_string.argtypes = [i32]
         lib.sss_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -112,6 +114,14 @@ def selective_scan_bwd_raw(x, delta, A, B, C, D_skip, z, h0, dy, dh_last, dx, dd
                            seqlen, dim, dstate, io_dtype, workspace, workspace_bytes, stream) -> int:
     return load().selective_scan_bwd(x, delta, A, B, C, D_skip, z, h0, dy, dh_last, dx, ddelta, dA, dB, dC, dD, dz, dh0,
                                      batch, seqlen, dim, dstate, io_dtype, workspace, workspace_bytes, stream)
+
+
+def selective_scan_bwd_ex_raw(x, delta, A, B, C, D_skip, z, h0, dy, dh_last, delta_bias, flags, dx, ddelta, dA, dB,
+                              dC, dD, dz, dh0, ddelta_bias, batch, seqlen, dim, dstate, io_dtype, workspace,
+                              workspace_bytes, stream) -> int:
+    return load().selective_scan_bwd_ex(x, delta, A, B, C, D_skip, z, h0, dy, dh_last, delta_bias, flags, dx, ddelta,
+                                        dA, dB, dC, dD, dz, dh0, ddelta_bias, batch, seqlen, dim, dstate, io_dtype,
+                                        workspace, workspace_bytes, stream)
 
 
 def selective_scan_bwd_workspace_size(batch, seqlen, dim, dstate, device=0) -> int:
@@ -158,14 +168,16 @@ def _states_buffer(states, nbytes, dev):
 
 
 def selective_scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, *, dy, dh_last=None, want_dh0=True,
-                       workspace=None, stream=None, states=None):
+                       workspace=None, stream=None, states=None, delta_bias=None, delta_softplus=False):
     """Gradients of sum(dy * y) + sum(dh_last * h_last) of selective_scan_fwd (plain form).
 
     states: the buffer a selective_scan_fwd(..., states=...) call on the same x, delta, A, B,
     h0 filled (selective_scan_bwd_saved); None recomputes them (selective_scan_bwd).
+    delta_bias (dim) float32 / delta_softplus: the delta front end of selective_scan_fwd_ex
+    (selective_scan_bwd_ex); ddelta is then the gradient with respect to the stored delta.
 
     Returns a dict of float32 tensors: dx, ddelta, dA, dB, dC, and dD (with D), dz (with z),
-    dh0 (if want_dh0)."""
+    dh0 (if want_dh0), ddelta_bias (with delta_bias)."""
     import torch
     dev = x.device
     batch, seqlen, dim = x.shape
@@ -177,20 +189,36 @@ def selective_scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, *, dy, dh_las
                          (z, "z", io, (batch, seqlen, dim)), (A, "A", f32, (dim, dstate)),
                          (B, "B", f32, (batch, seqlen, dstate)), (C, "C", f32, (batch, seqlen, dstate)),
                          (D, "D", f32, (dim,)), (h0, "h0", f32, (batch, dim, dstate)),
-                         (dy, "dy", f32, (batch, seqlen, dim)), (dh_last, "dh_last", f32, (batch, dim, dstate))):
+                         (dy, "dy", f32, (batch, seqlen, dim)), (dh_last, "dh_last", f32, (batch, dim, dstate)),
+                         (delta_bias, "delta_bias", f32, (dim,))):
         _need(t, n, dt, sh, dev)
-    _on_device(dev, x=x, delta=delta, z=z, A=A, B=B, C=C, D=D, h0=h0, dy=dy, dh_last=dh_last)
+    front = delta_bias is not None or bool(delta_softplus)
+    if front and states is not None:
+        raise ValueError("the delta front end has no saved-states form (states=)")
+    _on_device(dev, x=x, delta=delta, z=z, A=A, B=B, C=C, D=D, h0=h0, dy=dy, dh_last=dh_last, delta_bias=delta_bias)
     e = lambda *sh: torch.empty(sh, dtype=f32, device=dev)
     g = dict(dx=e(batch, seqlen, dim), ddelta=e(batch, seqlen, dim), dA=e(dim, dstate), dB=e(batch, seqlen, dstate),
              dC=e(batch, seqlen, dstate))
     g["dD"] = e(dim) if D is not None else None
     g["dz"] = e(batch, seqlen, dim) if z is not None else None
     g["dh0"] = e(batch, dim, dstate) if want_dh0 else None
+    if delta_bias is not None:
+        g["ddelta_bias"] = e(dim)
     wsb = selective_scan_bwd_workspace_size(batch, seqlen, dim, dstate, dev.index or 0)
     if workspace is None:
         workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
     wsp, wsn = _workspace(workspace, dev)
     st = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
+    if front:
+        rc = selective_scan_bwd_ex_raw(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+                                       _ptr(dy), _ptr(dh_last), _ptr(delta_bias),
+                                       SSS_DELTA_SOFTPLUS if delta_softplus else 0, _ptr(g["dx"]), _ptr(g["ddelta"]),
+                                       _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]),
+                                       _ptr(g["dh0"]), _ptr(g.get("ddelta_bias")), batch, seqlen, dim, dstate, io_code,
+                                       wsp, wsn, st)
+        if rc != 0:
+            raise SSSError(rc, "selective_scan_bwd_ex")
+        return g
     if states is None:
         rc = selective_scan_bwd_raw(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
                                     _ptr(dy), _ptr(dh_last), _ptr(g["dx"]), _ptr(g["ddelta"]), _ptr(g["dA"]),

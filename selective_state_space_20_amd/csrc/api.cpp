@@ -280,25 +280,27 @@ static int sel_bwd_impl(const void* x, const void* delta, const float* A, const 
                         float* dx, float* ddelta, float* dA, float* dB, float* dC, float* dD, float* dz, float* dh0,
                         int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype, const float* states,
                         size_t states_bytes, bool use_states, void* workspace, size_t workspace_bytes,
-                        sss_stream_t stream) {
+                        sss_stream_t stream, const float* delta_bias = nullptr, unsigned flags = 0u,
+                        float* ddelta_bias = nullptr) {
   if (!x || !delta || !A || !B || !C || !dy || !dx || !ddelta || !dA || !dB || !dC) return SSS_ERR_NULL_ARG;
-  if ((D_skip && !dD) || (z && !dz)) return SSS_ERR_NULL_ARG;
+  if ((D_skip && !dD) || (z && !dz) || (delta_bias && !ddelta_bias)) return SSS_ERR_NULL_ARG;
+  if ((flags & ~(unsigned)SSS_DELTA_SOFTPLUS) != 0) return SSS_ERR_UNSUPPORTED;
   int st = sel_dims_ok(batch, seqlen, dim, dstate);
   if (st != SSS_OK) return st;
   if (dim * dstate * 4 >= ((int64_t)1 << 31)) return SSS_ERR_BAD_DIM;  // checkpoint rows: 32-bit offsets
   if (io_dtype != SSS_F32 && io_dtype != SSS_BF16) return SSS_ERR_UNSUPPORTED;
   const void* ptrs[] = {x, delta, A, B, C, D_skip, z, h0, dy, dh_last, dx, ddelta, dA, dB, dC, dD, dz, dh0, workspace,
-                        states};
+                        states, delta_bias, ddelta_bias};
   for (const void* p : ptrs)
     if (!aligned16(p)) return SSS_ERR_UNSUPPORTED;
   const int64_t es = io_dtype == SSS_BF16 ? 2 : 4;
   const int64_t E = batch * seqlen * dim, H = batch * dim * dstate * 4, BC = batch * seqlen * dstate * 4;
-  const void* in_p[] = {x, delta, A, B, C, D_skip, z, h0, dy, dh_last};
-  const int64_t in_b[] = {E * es, E * es, dim * dstate * 4, BC, BC, dim * 4, E * es, H, E * 4, H};
-  void* out_p[] = {dx, ddelta, dA, dB, dC, dD, dz, dh0};
-  const int64_t out_b[] = {E * 4, E * 4, dim * dstate * 4, BC, BC, dim * 4, E * 4, H};
-  for (int i = 0; i < 8; ++i) {
-    for (int j = 0; j < 10; ++j)
+  const void* in_p[] = {x, delta, A, B, C, D_skip, z, h0, dy, dh_last, delta_bias};
+  const int64_t in_b[] = {E * es, E * es, dim * dstate * 4, BC, BC, dim * 4, E * es, H, E * 4, H, dim * 4};
+  void* out_p[] = {dx, ddelta, dA, dB, dC, dD, dz, dh0, delta_bias ? ddelta_bias : nullptr};
+  const int64_t out_b[] = {E * 4, E * 4, dim * dstate * 4, BC, BC, dim * 4, E * 4, H, dim * 4};
+  for (int i = 0; i < 9; ++i) {
+    for (int j = 0; j < 11; ++j)
       if (overlap(out_p[i], out_b[i], in_p[j], in_b[j])) return SSS_ERR_ALIAS;
     for (int j = 0; j < i; ++j)
       if (overlap(out_p[i], out_b[i], out_p[j], out_b[j])) return SSS_ERR_ALIAS;
@@ -310,9 +312,9 @@ static int sel_bwd_impl(const void* x, const void* delta, const float* A, const 
   if ((double)batch * (double)wg_groups * (double)bp.fwd.segments > 2147483647.0 / 64) return SSS_ERR_BAD_DIM;
   if (workspace == nullptr || workspace_bytes < bp.ws_total) return SSS_ERR_WORKSPACE;
   const int64_t wb = (int64_t)bp.ws_total;
-  for (int i = 0; i < 10; ++i)
+  for (int i = 0; i < 11; ++i)
     if (overlap(workspace, wb, in_p[i], in_b[i])) return SSS_ERR_ALIAS;
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 9; ++i)
     if (overlap(workspace, wb, out_p[i], out_b[i])) return SSS_ERR_ALIAS;
   // saved states: exactly the forward plan's slots
   const int64_t sb = bp.fwd.segments > 1 ? (int64_t)bp.fwd.segments * batch * dstate * dim * 4 : 0;
@@ -325,9 +327,10 @@ static int sel_bwd_impl(const void* x, const void* delta, const float* A, const 
   }
   if (env_int("SSS_LOG", 0))
     std::fprintf(stderr,
-                 "[sss] selective_scan_bwd B=%lld L=%lld D=%lld N=%lld: segments=%d seg_len=%lld K=%d checkpoint every %d "
-                 "ws=%zu\n",
-                 (long long)batch, (long long)seqlen, (long long)dim, (long long)dstate, bp.fwd.segments,
+                 "[sss] selective_scan_bwd B=%lld L=%lld D=%lld N=%lld flags=%u bias=%d: segments=%d seg_len=%lld K=%d "
+                 "checkpoint every %d ws=%zu\n",
+                 (long long)batch, (long long)seqlen, (long long)dim, (long long)dstate, flags, delta_bias ? 1 : 0,
+                 bp.fwd.segments,
                  (long long)bp.fwd.seg_len, bp.K, bp.KC, bp.ws_total);
   BwdArgs a{};
   a.fwd.x = x;
@@ -354,6 +357,9 @@ static int sel_bwd_impl(const void* x, const void* delta, const float* A, const 
   a.dD = dD;
   a.dz = dz;
   a.dh0 = dh0;
+  a.fwd.delta_bias = delta_bias;
+  a.fwd.softplus = (flags & SSS_DELTA_SOFTPLUS) != 0;
+  a.ddelta_bias = delta_bias ? ddelta_bias : nullptr;
   a.states_ready = use_states && sb > 0;
   a.fwd.states = a.states_ready ? const_cast<float*>(states) : nullptr;  // read only
   return launch_selective_bwd(a, bp, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? SSS_OK : SSS_ERR_HIP;
@@ -369,6 +375,17 @@ int selective_scan_bwd(const void* x, const void* delta, const float* A, const f
                        size_t workspace_bytes, sss_stream_t stream) {
   return sel_bwd_impl(x, delta, A, B, C, D_skip, z, h0, dy, dh_last, dx, ddelta, dA, dB, dC, dD, dz, dh0, batch,
                       seqlen, dim, dstate, io_dtype, nullptr, 0, false, workspace, workspace_bytes, stream);
+}
+
+int selective_scan_bwd_ex(const void* x, const void* delta, const float* A, const float* B, const float* C,
+                          const float* D_skip, const void* z, const float* h0, const float* dy, const float* dh_last,
+                          const float* delta_bias, unsigned flags, float* dx, float* ddelta, float* dA, float* dB,
+                          float* dC, float* dD, float* dz, float* dh0, float* ddelta_bias, int64_t batch,
+                          int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype, void* workspace,
+                          size_t workspace_bytes, sss_stream_t stream) {
+  return sel_bwd_impl(x, delta, A, B, C, D_skip, z, h0, dy, dh_last, dx, ddelta, dA, dB, dC, dD, dz, dh0, batch,
+                      seqlen, dim, dstate, io_dtype, nullptr, 0, false, workspace, workspace_bytes, stream, delta_bias,
+                      flags, ddelta_bias);
 }
 
 int selective_scan_bwd_saved(const void* x, const void* delta, const float* A, const float* B, const float* C,

@@ -74,7 +74,7 @@ struct BwdPlan {
   SelPlan fwd;     // segments of the forward pass (its workspace comes first)
   int K, KC, nsub; // steps per sub-chunk, checkpoint spacing (a multiple of K), checkpoints
                    // per segment
-  size_t off_mu, off_ckpt, off_bc, off_pa, off_pd, ws_total;
+  size_t off_mu, off_ckpt, off_bc, off_pa, off_pd, off_pdb, ws_total;
 };
 
 struct BwdArgs {
@@ -89,6 +89,7 @@ struct BwdArgs {
   float* dD;
   float* dz;
   float* dh0;
+  float* ddelta_bias;  // with the delta front end (fwd.delta_bias / fwd.softplus): d/d bias
   bool states_ready;  // fwd.states already holds the segment entering states (saved by the forward)
 };
 

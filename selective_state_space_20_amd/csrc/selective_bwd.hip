@@ -270,7 +270,12 @@ constexpr int ilog2c(int v) { return v <= 1 ? 0 : 1 + ilog2c(v / 2); }
 // instructions may cross it, VALU instructions may not
 constexpr int kBwdPhase = 0x3FC;
 
-template <int NS, bool BF16, bool HAS_Z>
+// FX: the delta front end's bits (kFront: the step size is delta + bias[d]; kSoftplus:
+// softplus of that).  The step sizes are formed from the staged raw delta exactly as the
+// forward call formed them; ddelta is then the gradient with respect to the raw delta (the
+// step size's gradient times sigmoid(delta + bias) under softplus), and part_db takes its
+// per-segment sums for the bias gradient.
+template <int NS, bool BF16, bool HAS_Z, int FX>
 __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
     const void* __restrict__ x, const void* __restrict__ delta, const float* __restrict__ A,
     const float* __restrict__ Bm, const float* __restrict__ Cm, const float* __restrict__ Dsk,
@@ -278,7 +283,8 @@ __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
     const float* __restrict__ mu_right, const float* __restrict__ ckpt, const float* __restrict__ hin,
     float* __restrict__ dx,
     float* __restrict__ ddelta, float* __restrict__ dz, float* __restrict__ part_bc, float* __restrict__ part_a,
-    float* __restrict__ part_d, float* __restrict__ dh0, BwdSeg g) {
+    float* __restrict__ part_d, float* __restrict__ dh0, const float* __restrict__ dbias,
+    float* __restrict__ part_db, BwdSeg g) {
   constexpr int K = bwd_k(NS);
   constexpr int R = bwd_r(NS);
   constexpr int ES = BF16 ? 2 : 4;
@@ -309,6 +315,8 @@ __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
   }
   const float Dd = Dsk ? Dsk[q.dc] : 0.0f;
   float ddacc = 0.0f;
+  const float dbv = ((FX & kFront) != 0 && dbias != nullptr) ? dbias[q.dc] : 0.0f;
+  float dbacc = 0.0f;  // sum of this lane's raw-delta gradients (bias gradient)
 
   const int64_t row0 = (q.b * g.L + q.tbeg) * g.D + q.d0;
   const __amdgpu_buffer_rsrc_t rx = bwd_rsrc((const char*)x + row0 * ES);
@@ -362,12 +370,15 @@ __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
   auto lds_f32 = [&](int word) { return __builtin_bit_cast(float, stage[word + q.lane]); };
 
   float xs[1][K], ds[1][K], gs[1][K], zs[1][K];
+  float sps[1][(FX & kSoftplus) != 0 ? K : 1];  // softplus' slope sigmoid(delta + bias)
 #define BWD_LOAD(SLOT, J)                                                                  \
   do {                                                                                     \
     const int li_ = ((J) % R) * K; /* the sub-chunk's first step within its group */       \
     _Pragma("unroll") for (int i = 0; i < K; ++i) {                                        \
       xs[SLOT][i] = lds_in(kOffX + (li_ + i) * 64);                                        \
-      ds[SLOT][i] = lds_in(kOffD + (li_ + i) * 64);                                        \
+      const float raw_ = lds_in(kOffD + (li_ + i) * 64);                                   \
+      ds[SLOT][i] = step_size<FX>(raw_, dbv);                                              \
+      if constexpr ((FX & kSoftplus) != 0) sps[SLOT][i] = sigmoid_f(raw_ + dbv);           \
       gs[SLOT][i] = lds_f32(kOffG + (li_ + i) * 64);                                       \
       if (HAS_Z) zs[SLOT][i] = lds_in(kOffZ + (li_ + i) * 64);                             \
     }                                                                                      \
@@ -474,7 +485,10 @@ __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
         const float gd = slb * xv;                                                         \
         ddacc = __builtin_fmaf(dv, xv, ddacc);                                             \
         st_f32(gx, rdx, vo4, t * rs4);                                                     \
-        st_f32(__builtin_fmaf(ga, kLn2, gd), rdd, vo4, t * rs4);                           \
+        float gdd = __builtin_fmaf(ga, kLn2, gd);                                          \
+        if constexpr ((FX & kSoftplus) != 0) gdd *= sps[SLOT][i];                          \
+        if constexpr ((FX & kFront) != 0) dbacc += gdd;                                    \
+        st_f32(gdd, rdd, vo4, t * rs4);                                                    \
         if (HAS_Z) st_f32(gy * vsum * sg * __builtin_fmaf(zv, 1.0f - sg, 1.0f), rdz, vo4, t * rs4); \
         reduce_scatter<kMerged ? 2 * NS : NS>(pv, q.lane);                                 \
         if (writer) {                                                                      \
@@ -516,7 +530,7 @@ __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
 #pragma unroll
       for (int i = 0; i < K; ++i) {
         xa[i] = lds_in(kOffX + i * 64);
-        da[i] = lds_in(kOffD + i * 64);
+        da[i] = step_size<FX>(lds_in(kOffD + i * 64), dbv);
       }
     }
     BWD_LOAD(0, j);
@@ -537,6 +551,7 @@ __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
 #pragma unroll
   for (int n = 0; n < NS; ++n) part_a[(((int64_t)q.s * g.batch + q.b) * NS + n) * g.D + q.dc] = dacc[n];
   part_d[((int64_t)q.s * g.batch + q.b) * g.D + q.dc] = ddacc;
+  if constexpr ((FX & kFront) != 0) part_db[((int64_t)q.s * g.batch + q.b) * g.D + q.dc] = dbacc;
   if (q.s == 0 && dh0 != nullptr) {
 #pragma unroll
     for (int n = 0; n < NS; ++n) dh0[chl + n] = mu[n];
@@ -568,10 +583,28 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc(const float* __restrict__ p
   else dC[r * N + (j - N)] = acc;
 }
 
-// dA[d][n] = sum_{s,b} part_a[s][b][n][d]; dD[d] = sum_{s,b} part_d[s][b][d].
+// dA[d][n] = sum_{s,b} part_a[s][b][n][d]; dD[d] = sum_{s,b} part_d[s][b][d]; with the delta
+// front end, ddbias[d] = sum_{s,b} part_db[s][b][d].
+__device__ __forceinline__ float sum_sb(const float* __restrict__ part, int64_t sb, int64_t stride) {
+  // the sequential order, with a batch of loads in flight ahead of the adds
+  constexpr int kAhead = 16;
+  float acc = 0.0f;
+  int64_t j = 0;
+  for (; j + kAhead <= sb; j += kAhead) {
+    float v[kAhead];
+#pragma unroll
+    for (int k = 0; k < kAhead; ++k) v[k] = part[(j + k) * stride];
+#pragma unroll
+    for (int k = 0; k < kAhead; ++k) acc += v[k];
+  }
+  for (; j < sb; ++j) acc += part[j * stride];
+  return acc;
+}
+
 __global__ __launch_bounds__(256) void bwd_reduce_ad(const float* __restrict__ part_a,
                                                      const float* __restrict__ part_d, float* __restrict__ dA,
-                                                     float* __restrict__ dD, int64_t sb /* S * batch */, int N,
+                                                     float* __restrict__ dD, const float* __restrict__ part_db,
+                                                     float* __restrict__ ddbias, int64_t sb /* S * batch */, int N,
                                                      int64_t D) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // n * D + d
   if (idx >= (int64_t)N * D) return;
@@ -602,6 +635,8 @@ __global__ __launch_bounds__(256) void bwd_reduce_ad(const float* __restrict__ p
     for (; j < sb; ++j) ad += part_d[j * D + d];
     dD[d] = ad;
   }
+  // the bias sums on another thread than dD's where there is one (n = 1)
+  if (n == (N > 1 ? 1 : 0) && ddbias != nullptr) ddbias[d] = sum_sb(part_db + d, sb, D);
 }
 
 // ------------------------------------------------------------------ host side
@@ -627,11 +662,13 @@ BwdPlan plan_selective_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t d
   off = align256(off + (size_t)S * batch * dstate * dim * 4);
   bp.off_pd = off;
   off = align256(off + (size_t)S * batch * dim * 4);
+  bp.off_pdb = off;  // bias-gradient partials (delta front end)
+  off = align256(off + (size_t)S * batch * dim * 4);
   bp.ws_total = off;
   return bp;
 }
 
-template <int NS, bool BF16>
+template <int NS, bool BF16, int FX>
 static hipError_t run_bwd(const BwdArgs& a, const BwdPlan& bp, hipStream_t stream) {
   unsigned char* ws = static_cast<unsigned char*>(a.fwd.workspace);
   const int S = bp.fwd.segments;
@@ -653,6 +690,7 @@ static hipError_t run_bwd(const BwdArgs& a, const BwdPlan& bp, hipStream_t strea
   float* pbc = reinterpret_cast<float*>(ws + bp.off_bc);
   float* pa = reinterpret_cast<float*>(ws + bp.off_pa);
   float* pd = reinterpret_cast<float*>(ws + bp.off_pd);
+  float* pdb = reinterpret_cast<float*>(ws + bp.off_pdb);
   const int64_t per_seg = (int64_t)g.ngroups * g.batch;
   hipError_t e;
   if (S > 1) {  // the segments' local folds are in mu (checkpoint pass)
@@ -663,35 +701,44 @@ static hipError_t run_bwd(const BwdArgs& a, const BwdPlan& bp, hipStream_t strea
   }
   const dim3 grid((unsigned)(per_seg * S)), block(64);
   if (a.fwd.z != nullptr)
-    hipLaunchKernelGGL((sel_bwd_kernel<NS, BF16, true>), grid, block, 0, stream, a.fwd.x, a.fwd.delta, a.fwd.A,
+    hipLaunchKernelGGL((sel_bwd_kernel<NS, BF16, true, FX>), grid, block, 0, stream, a.fwd.x, a.fwd.delta, a.fwd.A,
                        a.fwd.B, a.fwd.C, a.fwd.Dsk, a.fwd.z, a.dy, a.dh_last, (const float*)mu, (const float*)ckpt, hin,
-                       a.dx, a.ddelta, a.dz, pbc, pa, pd, a.dh0, g);
+                       a.dx, a.ddelta, a.dz, pbc, pa, pd, a.dh0, a.fwd.delta_bias, pdb, g);
   else
-    hipLaunchKernelGGL((sel_bwd_kernel<NS, BF16, false>), grid, block, 0, stream, a.fwd.x, a.fwd.delta, a.fwd.A,
+    hipLaunchKernelGGL((sel_bwd_kernel<NS, BF16, false, FX>), grid, block, 0, stream, a.fwd.x, a.fwd.delta, a.fwd.A,
                        a.fwd.B, a.fwd.C, a.fwd.Dsk, a.fwd.z, a.dy, a.dh_last, (const float*)mu, (const float*)ckpt, hin,
-                       a.dx, a.ddelta, a.dz, pbc, pa, pd, a.dh0, g);
+                       a.dx, a.ddelta, a.dz, pbc, pa, pd, a.dh0, a.fwd.delta_bias, pdb, g);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t rows = g.batch * g.L;
   hipLaunchKernelGGL(bwd_reduce_bc, dim3((unsigned)((rows * 2 * NS + 255) / 256)), dim3(256), 0, stream,
                      (const float*)pbc, a.dB, a.dC, rows, NS, g.ngroups);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_reduce_ad, dim3((unsigned)(((int64_t)NS * g.D + 255) / 256)), dim3(256), 0, stream,
-                     (const float*)pa, (const float*)pd, a.dA, a.dD, (int64_t)S * g.batch, NS, g.D);
+                     (const float*)pa, (const float*)pd, a.dA, a.dD, (const float*)pdb,
+                     (FX & kFront) != 0 ? a.ddelta_bias : nullptr, (int64_t)S * g.batch, NS, g.D);
   return hipGetLastError();
 }
 
-template <bool BF16>
-static hipError_t dispatch_bwd(const BwdArgs& a, const BwdPlan& bp, hipStream_t stream) {
+template <bool BF16, int FX>
+static hipError_t dispatch_bwd_n(const BwdArgs& a, const BwdPlan& bp, hipStream_t stream) {
   switch (a.fwd.dstate) {
-    case 1: return run_bwd<1, BF16>(a, bp, stream);
-    case 2: return run_bwd<2, BF16>(a, bp, stream);
-    case 4: return run_bwd<4, BF16>(a, bp, stream);
-    case 8: return run_bwd<8, BF16>(a, bp, stream);
-    case 16: return run_bwd<16, BF16>(a, bp, stream);
-    case 32: return run_bwd<32, BF16>(a, bp, stream);
-    case 64: return run_bwd<64, BF16>(a, bp, stream);
+    case 1: return run_bwd<1, BF16, FX>(a, bp, stream);
+    case 2: return run_bwd<2, BF16, FX>(a, bp, stream);
+    case 4: return run_bwd<4, BF16, FX>(a, bp, stream);
+    case 8: return run_bwd<8, BF16, FX>(a, bp, stream);
+    case 16: return run_bwd<16, BF16, FX>(a, bp, stream);
+    case 32: return run_bwd<32, BF16, FX>(a, bp, stream);
+    case 64: return run_bwd<64, BF16, FX>(a, bp, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+// the delta front end: none, bias only, or bias (optional) then softplus
+template <bool BF16>
+static hipError_t dispatch_bwd(const BwdArgs& a, const BwdPlan& bp, hipStream_t stream) {
+  if (a.fwd.softplus) return dispatch_bwd_n<BF16, kFront | kSoftplus>(a, bp, stream);
+  if (a.fwd.delta_bias != nullptr) return dispatch_bwd_n<BF16, kFront>(a, bp, stream);
+  return dispatch_bwd_n<BF16, 0>(a, bp, stream);
 }
 
 hipError_t launch_selective_bwd(const BwdArgs& a, const BwdPlan& bp, hipStream_t stream) {

@@ -74,7 +74,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7FFFFFFF, 0x00020000);
 }
 
-constexpr int kZoh = 1, kFront = 2, kSoftplus = 4, kBdl = 8;
+constexpr int kZoh = 1, kBdl = 8;  // kFront = 2, kSoftplus = 4: common.h
 // PASS 3 only: the adjoint's segment fold alongside the checkpoints (see the kernel comment)
 constexpr int kAdj = 16;
 
@@ -87,24 +87,6 @@ __device__ __forceinline__ void keep_here(const float (&v)[M]) {
   for (int i = 0; i < M; ++i) asm volatile("" ::"v"(v[i]));
 }
 __device__ __forceinline__ void keep_here(float v) { asm volatile("" ::"v"(v)); }
-
-// softplus(v) = max(v, 0) + log1p(e^-|v|); log1p through the log(u) * e / (u - 1) form so
-// that small e keeps its relative precision.
-__device__ __forceinline__ float softplus_f(float v) {
-  const float e = fast_exp2(-fabsf(v) * kLog2e);
-  const float u = 1.0f + e;
-  const float l = u == 1.0f ? e : __builtin_amdgcn_logf(u) * kLn2 * e * fast_rcp(u - 1.0f);
-  return fmaxf(v, 0.0f) + l;
-}
-
-// The step size the recurrence uses: the stored delta, or delta + bias (then softplus).
-template <int FL>
-__device__ __forceinline__ float step_size(float raw, float bias) {
-  if constexpr ((FL & kFront) == 0) return raw;
-  const float v = raw + bias;
-  if constexpr ((FL & kSoftplus) != 0) return softplus_f(v);
-  return v;
-}
 
 // Exact zero-order hold: the input coefficient expm1(u) / A with u = delta * A = arg * ln 2
 // (arg = delta * A * log2 e, e2 = 2^arg).  Where |u| < 1/16 it is delta * (1 + u/2 + u^2/6 +
@@ -1003,9 +985,11 @@ hipError_t run_segment_states(const SelArgs& a, const SelPlan& pl, hipStream_t s
 // starts from zero, the checkpoints carry their delta sums, and the carry then turns the
 // end states this pass leaves in the slots into the entering states (the backward kernel
 // adds their decayed contribution to each checkpoint).
-template <int NS, bool BF16>
-hipError_t run_checkpoints(const SelArgs& a, const SelPlan& pl, float* ckpt, int kshift, int nsub, const float* dy,
-                           float* adj_mu, bool local, hipStream_t stream) {
+// FX: the delta front end's bits (kFront, kSoftplus), so that the checkpoints, the delta sums
+// and the decays of the adjoint fold use the step sizes the forward call used.
+template <int NS, bool BF16, int FX>
+static hipError_t run_ckpt_fl(const SelArgs& a, const SelPlan& pl, float* ckpt, int kshift, int nsub, const float* dy,
+                              float* adj_mu, bool local, hipStream_t stream) {
   SelSeg g = make_seg(a, pl, NS);
   g.kshift = kshift;
   g.nsub = nsub;
@@ -1020,13 +1004,13 @@ hipError_t run_checkpoints(const SelArgs& a, const SelPlan& pl, float* ckpt, int
     float* ends = local ? st : nullptr;         // end states from zero (written)
     const size_t lds3 = lds_rows(NS, kAdj) ? (size_t)g.gpb * row_tile_lds(3, true) : 0;  // B, C row tiles
     if (a.z != nullptr)
-      hipLaunchKernelGGL((sel_seq_kernel<NS, BF16, 3, true, kAdj>), grid, block, lds3, stream, a.x, a.delta, a.A, a.B,
+      hipLaunchKernelGGL((sel_seq_kernel<NS, BF16, 3, true, kAdj | FX>), grid, block, lds3, stream, a.x, a.delta, a.A, a.B,
                          a.C, a.Dsk, a.z, a.h0, carry, (float*)nullptr, ends, ckpt, ds,
-                         (const float*)nullptr, dy, adj_mu, g);
+                         a.delta_bias, dy, adj_mu, g);
     else
-      hipLaunchKernelGGL((sel_seq_kernel<NS, BF16, 3, false, kAdj>), grid, block, lds3, stream, a.x, a.delta, a.A,
+      hipLaunchKernelGGL((sel_seq_kernel<NS, BF16, 3, false, kAdj | FX>), grid, block, lds3, stream, a.x, a.delta, a.A,
                          a.B, a.C, a.Dsk, a.z, a.h0, carry, (float*)nullptr, ends, ckpt, ds,
-                         (const float*)nullptr, dy, adj_mu, g);
+                         a.delta_bias, dy, adj_mu, g);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !local) return e;
     const int64_t nthr = g.batch * (int64_t)NS * g.D;
@@ -1035,10 +1019,18 @@ hipError_t run_checkpoints(const SelArgs& a, const SelPlan& pl, float* ckpt, int
     return hipGetLastError();
   }
   const size_t lds3 = lds_rows(NS, 0) ? (size_t)g.gpb * row_tile_lds(3) : 0;  // B row tiles
-  hipLaunchKernelGGL((sel_seq_kernel<NS, BF16, 3, false, 0>), grid, block, lds3, stream, a.x, a.delta, a.A, a.B, a.C,
+  hipLaunchKernelGGL((sel_seq_kernel<NS, BF16, 3, false, FX>), grid, block, lds3, stream, a.x, a.delta, a.A, a.B, a.C,
                      a.Dsk, a.z, a.h0, st, (float*)nullptr, (float*)nullptr, ckpt, (float*)nullptr,
-                     (const float*)nullptr, (const float*)nullptr, (float*)nullptr, g);
+                     a.delta_bias, (const float*)nullptr, (float*)nullptr, g);
   return hipGetLastError();
+}
+
+template <int NS, bool BF16>
+hipError_t run_checkpoints(const SelArgs& a, const SelPlan& pl, float* ckpt, int kshift, int nsub, const float* dy,
+                           float* adj_mu, bool local, hipStream_t stream) {
+  if (a.softplus) return run_ckpt_fl<NS, BF16, kFront | kSoftplus>(a, pl, ckpt, kshift, nsub, dy, adj_mu, local, stream);
+  if (a.delta_bias != nullptr) return run_ckpt_fl<NS, BF16, kFront>(a, pl, ckpt, kshift, nsub, dy, adj_mu, local, stream);
+  return run_ckpt_fl<NS, BF16, 0>(a, pl, ckpt, kshift, nsub, dy, adj_mu, local, stream);
 }
 
 // Front end / hold variants: plain, exact hold, delta + bias (+ softplus), and both; each in

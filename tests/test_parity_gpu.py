@@ -413,6 +413,90 @@ def test_backward_special_values(oracle_lib, monkeypatch, case):
     assert all(v <= tol for v in errs.values()), errs
 
 
+# Gradients through the delta front end (selective_scan_bwd_ex): (batch, seqlen, dim, dstate,
+# io, with z, bias, softplus, forced segments).  Single- and multi-segment plans, every state
+# count's checkpoint spacing, bf16 with an odd channel count, bias alone and softplus alone.
+BWD_FRONT_CASES = [
+    (1, 1, 1, 1, "f32", False, True, True, 0),
+    (2, 300, 33, 16, "f32", True, True, True, 0),
+    (2, 1000, 70, 16, "f32", True, True, True, 3),
+    (1, 2000, 64, 16, "bf16", True, True, True, 0),
+    (2, 130, 97, 16, "bf16", True, True, True, 2),
+    (3, 513, 20, 8, "bf16", False, True, True, 7),
+    (2, 777, 40, 4, "f32", True, True, False, 2),
+    (1, 400, 100, 2, "f32", True, False, True, 5),
+    (2, 300, 24, 32, "f32", True, True, True, 3),
+    (1, 200, 16, 64, "bf16", True, True, True, 2),
+    (1, 665, 40, 16, "bf16", True, False, True, 2),
+]
+
+
+@pytest.mark.parametrize("case", BWD_FRONT_CASES, ids=[f"B{c[0]}L{c[1]}D{c[2]}N{c[3]}{c[4]}b{int(c[6])}s{int(c[7])}S{c[8]}"
+                                                      for c in BWD_FRONT_CASES])
+def test_backward_front_end(oracle_lib, monkeypatch, case):
+    """selective_scan_bwd_ex against the oracle's gradients through the front end (step size
+    softplus(delta + bias), or delta + bias), every gradient tensor and the bias gradient."""
+    import torch
+    import selective_state_space_20_amd as sss
+    bt, L, dm, n, io, with_z, with_bias, sp, segs = case
+    if segs:
+        monkeypatch.setenv("SSS_FORCE_SEGMENTS", str(segs))
+    seed = zlib.crc32(repr(case).encode()) % 100000
+    inp = gen.selective_inputs(bt, L, dm, n, io=io, with_z=with_z, with_D=True, h0=True, seed=seed)
+    rng = np.random.default_rng(seed + 1)
+    if sp:  # raw step sizes before softplus: spread over both tails
+        raw = rng.normal(-3.0, 2.5, size=inp["x"].shape).astype(np.float32)
+        inp["delta"] = gen.f32_to_bf16_bits(raw) if io == "bf16" else raw
+    bias = None
+    if with_bias:  # without softplus the step must stay positive
+        bias = (0.5 * rng.standard_normal(dm) if sp else 0.01 * np.abs(rng.standard_normal(dm))).astype(np.float32)
+    dy = rng.standard_normal((bt, L, dm)).astype(np.float32)
+    dhl = rng.standard_normal((bt, dm, n)).astype(np.float32)
+    note(f"[backward front end] {case}")
+    t = {k: to_dev(v, "cuda:0") for k, v in inp.items() if k != "io"}
+    g = sss.selective_scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"],
+                               dy=to_dev(dy, "cuda:0"), dh_last=to_dev(dhl, "cuda:0"),
+                               delta_bias=to_dev(bias, "cuda:0"), delta_softplus=sp)
+    torch.cuda.synchronize()
+    r = oracle_lib.selective_scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                                      inp["h0"], dy=dy, dh_last=dhl, delta_bias=bias, delta_softplus=sp)
+    tol = TOL_BF16 if io == "bf16" else TOL_F32
+    errs = {}
+    for k in ("dx", "ddelta", "dA", "dB", "dC", "dD", "dz", "dh0", "ddelta_bias"):
+        if r.get(k) is None:
+            assert g.get(k) is None, k
+            continue
+        errs[k] = rel_err(g[k].cpu().numpy(), r[k])
+    note("    " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    assert all(v <= tol for v in errs.values()), errs
+
+
+def test_backward_front_end_off_is_plain():
+    """selective_scan_bwd_ex with no bias and no softplus gives selective_scan_bwd's gradients
+    bit for bit (the same kernels)."""
+    import torch
+    import selective_state_space_20_amd as sss
+    from selective_state_space_20_amd import _lib
+    bt, L, dm, n = 2, 700, 70, 16
+    inp = gen.selective_inputs(bt, L, dm, n, io="bf16", with_z=True, with_D=True, h0=True, seed=77)
+    rng = np.random.default_rng(78)
+    dy = to_dev(rng.standard_normal((bt, L, dm)).astype(np.float32), "cuda:0")
+    t = {k: to_dev(v, "cuda:0") for k, v in inp.items() if k != "io"}
+    g = sss.selective_scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"], dy=dy)
+    e = {k: torch.empty_like(v) for k, v in g.items()}
+    ws = torch.empty(_lib.selective_scan_bwd_workspace_size(bt, L, dm, n, 0), dtype=torch.uint8, device="cuda:0")
+    p = lambda v: 0 if v is None else v.data_ptr()
+    rc = _lib.selective_scan_bwd_ex_raw(p(t["x"]), p(t["delta"]), p(t["A"]), p(t["B"]), p(t["C"]), p(t["D"]),
+                                        p(t["z"]), p(t["h0"]), p(dy), 0, 0, 0, p(e["dx"]), p(e["ddelta"]), p(e["dA"]),
+                                        p(e["dB"]), p(e["dC"]), p(e["dD"]), p(e["dz"]), p(e["dh0"]), 0, bt, L, dm, n,
+                                        _lib.SSS_BF16, ws.data_ptr(), ws.numel(),
+                                        torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
+    torch.cuda.synchronize()
+    for k in g:
+        assert torch.equal(g[k], e[k]), k
+
+
 # The saved-states gradients against the recompute path's: fp32 arithmetic on the same
 # values in a different order (a checkpoint from the kept state against the state from zero
 # plus the decayed entering state), far below the oracle tolerances.
