@@ -51,8 +51,8 @@ COPY_WRITE_SCALE = 1048576.0 / 1048576.0
 CSRC = "selective_state_space_20_amd/csrc/"
 PMC_TRAFFIC = {
     # default workload: sel_seq_kernel pass 1 + sel_carry_kernel + pass 2
-    "selective": {"sources": (CSRC + "selective_scan.hip", CSRC + "common.h"), "digest": "75a9c1fc574abfbd",
-                  "fetch_kib": 656927.0 + 46577.4 + 1031110.0, "write_kib": 86700.0 + 81920.0 + 1311040.0},
+    "selective": {"sources": (CSRC + "selective_scan.hip", CSRC + "common.h", CSRC + "front.h"), "digest": "6a7bcad0acbb9a6a",
+                  "fetch_kib": 656911.6 + 46577.3 + 1031097.7, "write_kib": 86700.0 + 81920.0 + 1311040.0},
     # 8 x 32768 x 4096 fp32
     "elementwise": {"sources": (CSRC + "elementwise_scan.hip", CSRC + "common.h"), "digest": "4b0239623ce7466b",
                     "fetch_kib": 8388744.2, "write_kib": 4194432.0},
@@ -62,11 +62,12 @@ PMC_TRAFFIC = {
     # selective_scan_bwd on the default workload: the checkpoint pass (segments from zero, with
     # the adjoint's segment folds), the forward carry, the adjoint carry, the main kernel and
     # the two reductions
-    "backward": {"sources": (CSRC + "selective_bwd.hip", CSRC + "selective_scan.hip", CSRC + "common.h"),
-                 "digest": "57e5eed17d251b75",
+    "backward": {"sources": (CSRC + "selective_bwd.hip", CSRC + "selective_scan.hip", CSRC + "common.h",
+                             CSRC + "front.h"),
+                 "digest": "3e42b696cee42d34",
                  # checkpoint pass (from zero) + forward carry + adjoint carry + main kernel + reductions
-                 "fetch_kib": 1649350.0 + 46576.9 + 46577.7 + 4557810.0 + 327701.0 + 43549.4,
-                 "write_kib": 5739210.0 + 81920.0 + 81920.0 + 4695670.0 + 8192.0 + 660.0},
+                 "fetch_kib": 1649356.1 + 46576.8 + 46576.7 + 4557518.9 + 327696.9 + 43552.6,
+                 "write_kib": 5739202.2 + 81920.0 + 81920.0 + 4695733.6 + 8192.0 + 660.0},
     # 1 x 65536 x 5120 bf16, width 4
     "conv": {"sources": (CSRC + "conv1d.hip", CSRC + "common.h"), "digest": "0525304aa8e7045b",
              "fetch_kib": 328260.8, "write_kib": 655360.3},
@@ -453,11 +454,13 @@ def bench_conv(steps, warmup, batch=1, seqlen=65536, dim=5120, width=4):
     }), flush=True)
 
 
-def bench_backward(steps, warmup, saved=False):
+def bench_backward(steps, warmup, saved=False, softplus=False):
     """selective_scan_bwd on the default workload (the long Mamba-2.8B-shaped layer, bf16,
     gated, h0, dh_last): every gradient, states recomputed.  With saved=True the gradients
     call of the training pair (selective_scan_bwd_saved) is timed alone, on the segment
-    entering states one selective_scan_fwd_save call kept before the timed region.
+    entering states one selective_scan_fwd_save call kept before the timed region.  With
+    softplus=True the gradients through the delta front end (selective_scan_bwd_ex: step size
+    softplus(delta + bias), bias per channel, and its gradient).
     Algorithmic bytes: every input (x, delta, z, dy, B, C, A, D, h0, dh_last) read once and
     every gradient written once."""
     import torch
@@ -478,6 +481,7 @@ def bench_backward(steps, warmup, saved=False):
     g.manual_seed(5000)
     dy = torch.randn((b, L, d), device=dev, generator=g)
     dhl = torch.randn((b, d, n), device=dev, generator=g)
+    dbias = 0.5 * torch.randn((d,), device=dev, generator=g) if softplus else None
     ws = torch.empty(sss.selective_scan_bwd_workspace_size(b, L, d, n, 0), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     states = None
@@ -491,7 +495,7 @@ def bench_backward(steps, warmup, saved=False):
 
     def step():
         sss.selective_scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"], dy=dy,
-                               dh_last=dhl, workspace=ws, states=states)
+                               dh_last=dhl, workspace=ws, states=states, delta_bias=dbias, delta_softplus=softplus)
 
     warm_calls = warm_up(step, warmup)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
@@ -504,22 +508,27 @@ def bench_backward(steps, warmup, saved=False):
     e = b * L * d
     nbytes = e * (2 * 3 + 4) + 2 * b * L * n * 4 + d * n * 4 + d * 4 + 2 * b * d * n * 4   # inputs
     nbytes += e * 4 * 3 + d * n * 4 + 2 * b * L * n * 4 + d * 4 + b * d * n * 4               # gradients
+    if softplus:
+        nbytes += 2 * d * 4                                                                  # bias, its gradient
     gbs = nbytes / (mean_ms * 1e-3) / 1e9
     alu = backward_alu_ops(b, L, d, n)
     alu_tflops = 2.0 * alu / (mean_ms * 1e-3) / 1e12
-    log(f"[bench] backward{' (saved states)' if saved else ''} {cfg['name']}: event mean {mean_ms:.4f} ms, "
+    log(f"[bench] backward{' (saved states)' if saved else ''}{' (softplus front end)' if softplus else ''} "
+        f"{cfg['name']}: event mean {mean_ms:.4f} ms, "
         f"workspace {ws.numel() / 1e9:.2f} GB")
     print(json.dumps({
         "metric": "selective_scan_bwd achieved HBM GB/s and elements/s, 1 GPU", "value": round(gbs, 2), "unit": "GB/s",
         "n_gpus": 1, "steps": steps, "warmup": warmup, "warmup_calls_run": warm_calls, "ms_per_step": round(mean_ms, 5), "higher_is_better": True,
         "dtype": dtype_label("bf16"), "io_dtype": "bf16", "data": "synthetic",
-        "config": {"workload": ("backward_saved_" if saved else "backward_") + cfg["name"],
-                   "algorithmic_bytes": nbytes, "elements": e, "saved_states": bool(saved)},
+        "config": {"workload": ("backward_saved_" if saved else "backward_") + cfg["name"]
+                   + ("_softplus" if softplus else ""),
+                   "algorithmic_bytes": nbytes, "elements": e, "saved_states": bool(saved),
+                   "delta_softplus": bool(softplus)},
         "elements_per_s": round(e / (mean_ms * 1e-3), 1),
         "roofline": {"bound": "alu", "achieved": round(alu_tflops, 3), "peak": VALU_FP32_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(alu_tflops / VALU_FP32_TFLOPS, 4),
-                     "traffic": None if saved else measured_traffic("backward"),
-                     "kernel": "one selective_scan_bwd%s call" % ("_saved" if saved else ""),
+                     "traffic": None if (saved or softplus) else measured_traffic("backward"),
+                     "kernel": "one selective_scan_bwd%s call" % ("_saved" if saved else "_ex" if softplus else ""),
                      "call_ms_event_mean": round(mean_ms, 5),
                      "alu_ops_per_call": alu,
                      "hbm": {"achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -610,7 +619,8 @@ def main():
     ap.add_argument("--no-flush", action="store_true",
                     help="do not scrub the last-level cache between calls (decode, and workloads that fit it)")
     ap.add_argument("--delta-softplus", action="store_true",
-                    help="selective: time the softplus front end (the stored delta taken as the raw step)")
+                    help="selective: time the softplus front end (the stored delta taken as the raw step); "
+                         "with --backward the gradients through it (softplus(delta + bias), selective_scan_bwd_ex)")
     ap.add_argument("--exact-zoh", action="store_true", help="selective: time the exact zero-order-hold option")
     ap.add_argument("--layout", choices=("bld", "bdl"), default="bld",
                     help="selective: operand layout (bdl = channel-major x/delta/z/y and B/C)")
@@ -631,7 +641,9 @@ def main():
         bench_conv(args.steps, args.warmup)
         return
     if args.backward:
-        bench_backward(args.steps, args.warmup, args.saved_states)
+        if args.saved_states and args.delta_softplus:
+            sys.exit("--saved-states has no delta front end form")
+        bench_backward(args.steps, args.warmup, args.saved_states, softplus=args.delta_softplus)
         return
     if args.train_step:
         bench_train_step(args.steps, args.warmup, args.saved_states)

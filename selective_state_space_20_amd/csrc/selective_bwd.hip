@@ -29,6 +29,7 @@
 //      64 channels) and per-segment partials of dA/dD;
 //   5. small kernels add the partials up.
 #include "common.h"
+#include "front.h"
 #include "kernels.h"
 
 #include <algorithm>

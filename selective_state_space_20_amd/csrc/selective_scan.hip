@@ -26,6 +26,7 @@
 //       pass 2 replays every segment from its entering state and writes y (and h_last).
 //     With S = 1 only pass 2 runs, from h0.
 #include "common.h"
+#include "front.h"
 #include "kernels.h"
 
 #include <algorithm>

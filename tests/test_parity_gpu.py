@@ -617,6 +617,39 @@ def test_backward_long_layer_full():
     assert all(v <= TOL_BF16 for v in errs.values()), errs
 
 
+@pytest.mark.timeout(600)
+def test_backward_front_end_long_layer_full():
+    """Gradients through the softplus front end (step size softplus(delta + bias)) on the
+    full-size long layer (B=1, D=5120, N=16, L=65536, bf16, gated, h0, dh_last), in the plan
+    the benchmark times: every element of every gradient tensor and the bias gradient."""
+    import torch
+    import oracle
+    import selective_state_space_20_amd as sss
+    cfg, inp = gen.config_inputs(3)
+    rng = np.random.default_rng(4004)
+    # raw step sizes before softplus, spread over both tails, and a per-channel bias
+    inp["delta"] = gen.f32_to_bf16_bits(rng.normal(-3.0, 2.5, size=inp["x"].shape).astype(np.float32))
+    bias = (0.5 * rng.standard_normal(cfg["dim"])).astype(np.float32)
+    dy = rng.standard_normal(inp["x"].shape, dtype=np.float32)
+    dhl = rng.standard_normal(inp["h0"].shape, dtype=np.float32)
+    note(f"[backward front end] {cfg['name']} inputs generated")
+    t = {k: to_dev(v, "cuda:0") for k, v in inp.items() if k != "io"}
+    g = sss.selective_scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"],
+                               dy=to_dev(dy, "cuda:0"), dh_last=to_dev(dhl, "cuda:0"),
+                               delta_bias=to_dev(bias, "cuda:0"), delta_softplus=True)
+    torch.cuda.synchronize()
+    g = {k: (v.cpu().numpy() if v is not None else None) for k, v in g.items()}
+    del t
+    note("    GPU done")
+    r = oracle.selective_scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], inp["h0"],
+                                  dy=dy, dh_last=dhl, delta_bias=bias, delta_softplus=True)
+    note("    oracle done")
+    keys = ("dx", "ddelta", "dA", "dB", "dC", "dD", "dz", "dh0", "ddelta_bias")
+    errs = {k: rel_err(g[k], r[k]) for k in keys}
+    note("    " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    assert all(v <= TOL_BF16 for v in errs.values()), errs
+
+
 # ---------------------------------------------------------------- causal conv1d front end
 CONV_CASES = [  # (batch, seqlen, dim, width, io, silu, bias, forced segments)
     (1, 1, 1, 1, "f32", False, False, 0),
