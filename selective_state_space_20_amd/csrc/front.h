@@ -19,6 +19,13 @@ __device__ __forceinline__ float softplus_f(float v) {
   return fmaxf(v, 0.0f) + l;
 }
 
+// The slope of softplus at v, sigmoid(v) = 1 / (1 + e^-v): 1 / (1 + e) for v >= 0 and e / (1 + e)
+// below, e = e^-|v| (accurate in both tails; e and 1 + e are the ones softplus_f forms).
+__device__ __forceinline__ float softplus_slope(float v) {
+  const float e = fast_exp2(-fabsf(v) * kLog2e);
+  return (v >= 0.0f ? 1.0f : e) * fast_rcp(1.0f + e);
+}
+
 // The step size the recurrence uses: the stored delta, or delta + bias (then softplus).
 template <int FL>
 __device__ __forceinline__ float step_size(float raw, float bias) {

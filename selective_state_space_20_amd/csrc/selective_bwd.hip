@@ -316,8 +316,6 @@ __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
   }
   const float Dd = Dsk ? Dsk[q.dc] : 0.0f;
   float ddacc = 0.0f;
-  const float dbv = ((FX & kFront) != 0 && dbias != nullptr) ? dbias[q.dc] : 0.0f;
-  float dbacc = 0.0f;  // sum of this lane's raw-delta gradients (bias gradient)
 
   const int64_t row0 = (q.b * g.L + q.tbeg) * g.D + q.d0;
   const __amdgpu_buffer_rsrc_t rx = bwd_rsrc((const char*)x + row0 * ES);
@@ -348,7 +346,15 @@ __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
   // past the last channel on channel D-1).
   constexpr int KC = K * R;
   constexpr int kOffX = (NS + 1) * 64, kOffD = kOffX + KC * 64, kOffG = kOffD + KC * 64, kOffZ = kOffG + KC * 64;
-  __shared__ __attribute__((aligned(16))) uint32_t stage[kOffZ + (HAS_Z ? KC * 64 : 0)];
+  // with the delta front end: each group's step sizes replace its raw deltas in place once the
+  // group has landed, and the softplus slopes go to a region of their own that the copies
+  // never write (read at the gradient stores, after the next group's copies were issued)
+  constexpr int kOffS = kOffZ + (HAS_Z ? KC * 64 : 0);
+  __shared__ __attribute__((aligned(16))) uint32_t stage[kOffS + ((FX & kSoftplus) != 0 ? KC * 64 : 0)];
+  // the lane's bias, read at each group's conversion (kept out of the VGPR budget)
+  __shared__ float dbias_s[(FX & kFront) != 0 ? 64 : 1];
+  if constexpr ((FX & kFront) != 0) dbias_s[q.lane] = dbias != nullptr ? dbias[q.dc] : 0.0f;
+  float dbacc = 0.0f;  // sum of this lane's raw-delta gradients (bias gradient)
   auto lds_at = [&](int word) { return (lds_void*)&stage[word]; };
   auto issue_group = [&](int grp_j) {
     const __amdgpu_buffer_rsrc_t rk = ck_rsrc(grp_j);
@@ -369,17 +375,16 @@ __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
     return __builtin_bit_cast(float, BF16 ? u << 16 : u);
   };
   auto lds_f32 = [&](int word) { return __builtin_bit_cast(float, stage[word + q.lane]); };
+  // a staged delta: the raw one, or the step size the front end made of it
+  auto lds_dl = [&](int word) { return (FX & kFront) != 0 ? lds_f32(word) : lds_in(word); };
 
   float xs[1][K], ds[1][K], gs[1][K], zs[1][K];
-  float sps[1][(FX & kSoftplus) != 0 ? K : 1];  // softplus' slope sigmoid(delta + bias)
 #define BWD_LOAD(SLOT, J)                                                                  \
   do {                                                                                     \
     const int li_ = ((J) % R) * K; /* the sub-chunk's first step within its group */       \
     _Pragma("unroll") for (int i = 0; i < K; ++i) {                                        \
       xs[SLOT][i] = lds_in(kOffX + (li_ + i) * 64);                                        \
-      const float raw_ = lds_in(kOffD + (li_ + i) * 64);                                   \
-      ds[SLOT][i] = step_size<FX>(raw_, dbv);                                              \
-      if constexpr ((FX & kSoftplus) != 0) sps[SLOT][i] = sigmoid_f(raw_ + dbv);           \
+      ds[SLOT][i] = lds_dl(kOffD + (li_ + i) * 64);                                        \
       gs[SLOT][i] = lds_f32(kOffG + (li_ + i) * 64);                                       \
       if (HAS_Z) zs[SLOT][i] = lds_in(kOffZ + (li_ + i) * 64);                             \
     }                                                                                      \
@@ -487,7 +492,7 @@ __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
         ddacc = __builtin_fmaf(dv, xv, ddacc);                                             \
         st_f32(gx, rdx, vo4, t * rs4);                                                     \
         float gdd = __builtin_fmaf(ga, kLn2, gd);                                          \
-        if constexpr ((FX & kSoftplus) != 0) gdd *= sps[SLOT][i];                          \
+        if constexpr ((FX & kSoftplus) != 0) gdd *= lds_f32(kOffS + (((J) % R) * K + i) * 64); \
         if constexpr ((FX & kFront) != 0) dbacc += gdd;                                    \
         st_f32(gdd, rdd, vo4, t * rs4);                                                    \
         if (HAS_Z) st_f32(gy * vsum * sg * __builtin_fmaf(zv, 1.0f - sg, 1.0f), rdz, vo4, t * rs4); \
@@ -523,6 +528,17 @@ __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
           stage[n * 64 + q.lane] = __builtin_bit_cast(uint32_t, v);
         }
       }
+      if constexpr ((FX & kFront) != 0) {
+        // the group's step sizes (and softplus slopes), once per staged step
+        const float dbv = dbias_s[q.lane];
+#pragma unroll
+        for (int i = 0; i < KC; ++i) {
+          const float raw = lds_in(kOffD + i * 64);
+          stage[kOffD + i * 64 + q.lane] = __builtin_bit_cast(uint32_t, step_size<FX>(raw, dbv));
+          if constexpr ((FX & kSoftplus) != 0)
+            stage[kOffS + i * 64 + q.lane] = __builtin_bit_cast(uint32_t, softplus_slope(raw + dbv));
+        }
+      }
     }
     // inputs of the sub-chunk before, for the checkpoint advance of odd sub-chunks (the
     // first steps of the same group)
@@ -531,7 +547,7 @@ __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
 #pragma unroll
       for (int i = 0; i < K; ++i) {
         xa[i] = lds_in(kOffX + i * 64);
-        da[i] = step_size<FX>(lds_in(kOffD + i * 64), dbv);
+        da[i] = lds_dl(kOffD + i * 64);
       }
     }
     BWD_LOAD(0, j);
