@@ -19,7 +19,7 @@ include/sss.h); this package is its thin Python binding:
 """
 from ._lib import (EXPORTED, LIB_PATH, SSSError, SSS_BF16, SSS_DELTA_SOFTPLUS, SSS_EXACT_ZOH, SSS_F32, SSS_LAYOUT_BDL,
                    causal_conv1d_fwd, causal_conv1d_fwd_raw, elementwise_scan, elementwise_scan_raw,
-                   selective_scan_bwd, selective_scan_bwd_raw, selective_scan_bwd_workspace_size,
+                   selective_scan_bwd, selective_scan_bwd_raw, selective_scan_bwd_ex_raw, selective_scan_bwd_workspace_size,
                    selective_scan_fwd_ex_raw, selective_scan_fwd_noalloc_raw, selective_scan_states_size,
                    selective_scan_fwd_save_raw, selective_scan_bwd_saved_raw,
                    elementwise_scan_workspace_size, load, selective_scan_fwd, selective_scan_fwd_raw,
@@ -27,7 +27,7 @@ from ._lib import (EXPORTED, LIB_PATH, SSSError, SSS_BF16, SSS_DELTA_SOFTPLUS, S
                    selective_state_update, selective_state_update_raw,
                    status_string)
 
-__all__ = ["selective_scan_fwd", "selective_scan_bwd", "selective_scan_bwd_raw", "selective_scan_bwd_workspace_size",
+__all__ = ["selective_scan_fwd", "selective_scan_bwd", "selective_scan_bwd_raw", "selective_scan_bwd_ex_raw", "selective_scan_bwd_workspace_size",
            "selective_state_update", "causal_conv1d_fwd", "causal_conv1d_fwd_raw", "selective_state_update_raw", "elementwise_scan",
            "selective_scan_fwd_workspace_size",
            "elementwise_scan_workspace_size", "selective_scan_fwd_raw", "elementwise_scan_raw", "status_string",

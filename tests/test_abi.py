@@ -88,6 +88,27 @@ def bwd(**kw):
     return sss.selective_scan_bwd_raw(**a)
 
 
+def bwdx(**kw):
+    a = dict(x=P, delta=2 * P, A=3 * P, B=4 * P, C=5 * P, D_skip=0, z=0, h0=0, dy=6 * P, dh_last=0, delta_bias=7 * P,
+             flags=2, dx=64 * P, ddelta=65 * P, dA=66 * P, dB=67 * P, dC=68 * P, dD=0, dz=0, dh0=0,
+             ddelta_bias=69 * P, batch=2, seqlen=8, dim=4, dstate=4, io_dtype=0, workspace=80 * P,
+             workspace_bytes=1 << 30, stream=0)
+    a.update(kw)
+    return sss.selective_scan_bwd_ex_raw(**a)
+
+
+def test_backward_ex_rejections():
+    assert bwdx(ddelta_bias=0) == NULL_ARG             # a bias without its gradient
+    assert bwdx(flags=1) == UNSUPPORTED                # the exact hold has no gradients call
+    assert bwdx(flags=4) == UNSUPPORTED                # nor the channel-major layout
+    assert bwdx(flags=1 << 31) == UNSUPPORTED
+    assert bwdx(delta_bias=7 * P + 4) == UNSUPPORTED   # misaligned bias
+    assert bwdx(ddelta_bias=7 * P) == ALIAS            # the bias gradient over the bias
+    assert bwdx(ddelta_bias=65 * P + 16) == ALIAS      # the bias gradient over ddelta
+    assert bwdx(dx=7 * P) == ALIAS                     # dx over the bias
+    assert bwdx(dim=0) == BAD_DIM
+
+
 def test_backward_rejections():
     assert bwd(dy=0) == NULL_ARG
     assert bwd(dC=0) == NULL_ARG

@@ -54,3 +54,22 @@ def test_host_tensors_are_rejected():
     x = torch.zeros(2, 5, 3)
     with pytest.raises(ValueError, match="must be on a GPU"):
         sss.elementwise_scan(x, x, x, x)
+
+
+def test_backward_front_end_rejects_a_bad_bias():
+    a = _sel()
+    dy = torch.zeros(2, 5, 3)
+    with pytest.raises(ValueError, match="delta_bias must have shape"):
+        sss.selective_scan_bwd(a["x"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["h0"], dy=dy,
+                               delta_bias=torch.zeros(4), delta_softplus=True)
+    with pytest.raises(ValueError, match="delta_bias"):
+        sss.selective_scan_bwd(a["x"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["h0"], dy=dy,
+                               delta_bias=torch.zeros(3, dtype=torch.float64))
+
+
+def test_backward_front_end_has_no_saved_states_form():
+    a = _sel()
+    dy = torch.zeros(2, 5, 3)
+    with pytest.raises(ValueError, match="no saved-states form"):
+        sss.selective_scan_bwd(a["x"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["h0"], dy=dy,
+                               delta_softplus=True, states=torch.zeros(16))
