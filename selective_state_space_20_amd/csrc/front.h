@@ -19,11 +19,12 @@ __device__ __forceinline__ float softplus_f(float v) {
   return fmaxf(v, 0.0f) + l;
 }
 
-// The slope of softplus at v, sigmoid(v) = 1 / (1 + e^-v): 1 / (1 + e) for v >= 0 and e / (1 + e)
-// below, e = e^-|v| (accurate in both tails; e and 1 + e are the ones softplus_f forms).
-__device__ __forceinline__ float softplus_slope(float v) {
-  const float e = fast_exp2(-fabsf(v) * kLog2e);
-  return (v >= 0.0f ? 1.0f : e) * fast_rcp(1.0f + e);
+// The slope of softplus at v from the step size sp = softplus(v): sigmoid(v) = 1 - e^-sp.  Below sp = 1/16
+// the series sp (1 - sp/2 (1 - sp/3 (1 - sp/4))) (truncation below 2e-7 relative, no
+// cancellation), above it 1 - e^-sp (cancellation below 1e-6 relative).
+__device__ __forceinline__ float softplus_slope_of_step(float sp) {
+  const float ser = sp * (1.0f - 0.5f * sp * (1.0f - (1.0f / 3.0f) * sp * (1.0f - 0.25f * sp)));
+  return sp < 0.0625f ? ser : 1.0f - fast_exp2(-sp * kLog2e);
 }
 
 // The step size the recurrence uses: the stored delta, or delta + bias (then softplus).

@@ -274,8 +274,9 @@ constexpr int kBwdPhase = 0x3FC;
 // FX: the delta front end's bits (kFront: the step size is delta + bias[d]; kSoftplus:
 // softplus of that).  The step sizes are formed from the staged raw delta exactly as the
 // forward call formed them; ddelta is then the gradient with respect to the raw delta (the
-// step size's gradient times sigmoid(delta + bias) under softplus), and part_db takes its
-// per-segment sums for the bias gradient.
+// step size's gradient times sigmoid(delta + bias) under softplus, formed from the step size
+// at the store).  The bias gradient is summed from ddelta by a pass of its own: a running sum
+// here would hold one more VGPR through the loop, which at 16 states spills.
 template <int NS, bool BF16, bool HAS_Z, int FX>
 __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
     const void* __restrict__ x, const void* __restrict__ delta, const float* __restrict__ A,
@@ -284,8 +285,7 @@ __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
     const float* __restrict__ mu_right, const float* __restrict__ ckpt, const float* __restrict__ hin,
     float* __restrict__ dx,
     float* __restrict__ ddelta, float* __restrict__ dz, float* __restrict__ part_bc, float* __restrict__ part_a,
-    float* __restrict__ part_d, float* __restrict__ dh0, const float* __restrict__ dbias,
-    float* __restrict__ part_db, BwdSeg g) {
+    float* __restrict__ part_d, float* __restrict__ dh0, const float* __restrict__ dbias, BwdSeg g) {
   constexpr int K = bwd_k(NS);
   constexpr int R = bwd_r(NS);
   constexpr int ES = BF16 ? 2 : 4;
@@ -346,15 +346,12 @@ __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
   // past the last channel on channel D-1).
   constexpr int KC = K * R;
   constexpr int kOffX = (NS + 1) * 64, kOffD = kOffX + KC * 64, kOffG = kOffD + KC * 64, kOffZ = kOffG + KC * 64;
-  // with the delta front end: each group's step sizes replace its raw deltas in place once the
-  // group has landed, and the softplus slopes go to a region of their own that the copies
-  // never write (read at the gradient stores, after the next group's copies were issued)
-  constexpr int kOffS = kOffZ + (HAS_Z ? KC * 64 : 0);
-  __shared__ __attribute__((aligned(16))) uint32_t stage[kOffS + ((FX & kSoftplus) != 0 ? KC * 64 : 0)];
+  // with the delta front end each group's step sizes replace its raw deltas in place once the
+  // group has landed
+  __shared__ __attribute__((aligned(16))) uint32_t stage[kOffZ + (HAS_Z ? KC * 64 : 0)];
   // the lane's bias, read at each group's conversion (kept out of the VGPR budget)
   __shared__ float dbias_s[(FX & kFront) != 0 ? 64 : 1];
   if constexpr ((FX & kFront) != 0) dbias_s[q.lane] = dbias != nullptr ? dbias[q.dc] : 0.0f;
-  float dbacc = 0.0f;  // sum of this lane's raw-delta gradients (bias gradient)
   auto lds_at = [&](int word) { return (lds_void*)&stage[word]; };
   auto issue_group = [&](int grp_j) {
     const __amdgpu_buffer_rsrc_t rk = ck_rsrc(grp_j);
@@ -492,8 +489,7 @@ __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
         ddacc = __builtin_fmaf(dv, xv, ddacc);                                             \
         st_f32(gx, rdx, vo4, t * rs4);                                                     \
         float gdd = __builtin_fmaf(ga, kLn2, gd);                                          \
-        if constexpr ((FX & kSoftplus) != 0) gdd *= lds_f32(kOffS + (((J) % R) * K + i) * 64); \
-        if constexpr ((FX & kFront) != 0) dbacc += gdd;                                    \
+        if constexpr ((FX & kSoftplus) != 0) gdd *= softplus_slope_of_step(dl);            \
         st_f32(gdd, rdd, vo4, t * rs4);                                                    \
         if (HAS_Z) st_f32(gy * vsum * sg * __builtin_fmaf(zv, 1.0f - sg, 1.0f), rdz, vo4, t * rs4); \
         reduce_scatter<kMerged ? 2 * NS : NS>(pv, q.lane);                                 \
@@ -529,15 +525,11 @@ __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
         }
       }
       if constexpr ((FX & kFront) != 0) {
-        // the group's step sizes (and softplus slopes), once per staged step
+        // the group's step sizes, once per staged step
         const float dbv = dbias_s[q.lane];
 #pragma unroll
-        for (int i = 0; i < KC; ++i) {
-          const float raw = lds_in(kOffD + i * 64);
-          stage[kOffD + i * 64 + q.lane] = __builtin_bit_cast(uint32_t, step_size<FX>(raw, dbv));
-          if constexpr ((FX & kSoftplus) != 0)
-            stage[kOffS + i * 64 + q.lane] = __builtin_bit_cast(uint32_t, softplus_slope(raw + dbv));
-        }
+        for (int i = 0; i < KC; ++i)
+          stage[kOffD + i * 64 + q.lane] = __builtin_bit_cast(uint32_t, step_size<FX>(lds_in(kOffD + i * 64), dbv));
       }
     }
     // inputs of the sub-chunk before, for the checkpoint advance of odd sub-chunks (the
@@ -568,7 +560,6 @@ __global__ __launch_bounds__(64, bwd_min_waves(NS)) void sel_bwd_kernel(
 #pragma unroll
   for (int n = 0; n < NS; ++n) part_a[(((int64_t)q.s * g.batch + q.b) * NS + n) * g.D + q.dc] = dacc[n];
   part_d[((int64_t)q.s * g.batch + q.b) * g.D + q.dc] = ddacc;
-  if constexpr ((FX & kFront) != 0) part_db[((int64_t)q.s * g.batch + q.b) * g.D + q.dc] = dbacc;
   if (q.s == 0 && dh0 != nullptr) {
 #pragma unroll
     for (int n = 0; n < NS; ++n) dh0[chl + n] = mu[n];
@@ -598,6 +589,30 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc(const float* __restrict__ p
   const int64_t r = idx / V, j = idx - r * V;
   if (j < N) dB[r * N + j] = acc;
   else dC[r * N + (j - N)] = acc;
+}
+
+// Bias-gradient partials of the delta front end: part_db[s][b][d] = sum of ddelta[b][t][d] over
+// segment s's steps, in time order (a thread per (s, b, d); adjacent threads read adjacent
+// channels, so every row read is coalesced).
+__global__ __launch_bounds__(256) void bwd_bias_partials(const float* __restrict__ ddelta, float* __restrict__ part_db,
+                                                         int64_t batch, int64_t L, int64_t D, int64_t seg_len, int S) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (s * batch + b) * D + d
+  if (idx >= (int64_t)S * batch * D) return;
+  const int64_t d = idx % D, sb = idx / D, b = sb % batch, s = sb / batch;
+  const int64_t t0 = s * seg_len, t1 = t0 + seg_len < L ? t0 + seg_len : L;
+  const float* p = ddelta + (b * L + t0) * D + d;
+  constexpr int kAhead = 8;
+  float acc = 0.0f;
+  int64_t t = t0;
+  for (; t + kAhead <= t1; t += kAhead) {
+    float v[kAhead];
+#pragma unroll
+    for (int k = 0; k < kAhead; ++k) v[k] = p[(t - t0 + k) * D];
+#pragma unroll
+    for (int k = 0; k < kAhead; ++k) acc += v[k];
+  }
+  for (; t < t1; ++t) acc += p[(t - t0) * D];
+  part_db[idx] = acc;
 }
 
 // dA[d][n] = sum_{s,b} part_a[s][b][n][d]; dD[d] = sum_{s,b} part_d[s][b][d]; with the delta
@@ -720,12 +735,18 @@ static hipError_t run_bwd(const BwdArgs& a, const BwdPlan& bp, hipStream_t strea
   if (a.fwd.z != nullptr)
     hipLaunchKernelGGL((sel_bwd_kernel<NS, BF16, true, FX>), grid, block, 0, stream, a.fwd.x, a.fwd.delta, a.fwd.A,
                        a.fwd.B, a.fwd.C, a.fwd.Dsk, a.fwd.z, a.dy, a.dh_last, (const float*)mu, (const float*)ckpt, hin,
-                       a.dx, a.ddelta, a.dz, pbc, pa, pd, a.dh0, a.fwd.delta_bias, pdb, g);
+                       a.dx, a.ddelta, a.dz, pbc, pa, pd, a.dh0, a.fwd.delta_bias, g);
   else
     hipLaunchKernelGGL((sel_bwd_kernel<NS, BF16, false, FX>), grid, block, 0, stream, a.fwd.x, a.fwd.delta, a.fwd.A,
                        a.fwd.B, a.fwd.C, a.fwd.Dsk, a.fwd.z, a.dy, a.dh_last, (const float*)mu, (const float*)ckpt, hin,
-                       a.dx, a.ddelta, a.dz, pbc, pa, pd, a.dh0, a.fwd.delta_bias, pdb, g);
+                       a.dx, a.ddelta, a.dz, pbc, pa, pd, a.dh0, a.fwd.delta_bias, g);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((FX & kFront) != 0 && a.ddelta_bias != nullptr) {
+    const int64_t nthr = (int64_t)S * g.batch * g.D;
+    hipLaunchKernelGGL(bwd_bias_partials, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, stream,
+                       (const float*)a.ddelta, pdb, g.batch, g.L, g.D, g.seg_len, S);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   const int64_t rows = g.batch * g.L;
   hipLaunchKernelGGL(bwd_reduce_bc, dim3((unsigned)((rows * 2 * NS + 255) / 256)), dim3(256), 0, stream,
                      (const float*)pbc, a.dB, a.dC, rows, NS, g.ngroups);
