@@ -536,11 +536,13 @@ def bench_backward(steps, warmup, saved=False, softplus=False):
     }), flush=True)
 
 
-def bench_train_step(steps, warmup, saved):
+def bench_train_step(steps, warmup, saved, softplus=False):
     """One training step of the default layer: selective_scan_fwd then selective_scan_bwd on
     the same inputs (dy given), timed together.  With saved=True the pair that keeps the
     forward's segment entering states for the gradients call (selective_scan_fwd_save /
-    selective_scan_bwd_saved), which skips the gradients call's recomputation of them."""
+    selective_scan_bwd_saved), which skips the gradients call's recomputation of them.  With
+    softplus=True both calls take the delta front end, step size softplus(delta + bias)
+    (selective_scan_fwd_ex / selective_scan_bwd_ex, the bias gradient included)."""
     import torch
     import selective_state_space_20_amd as sss
     from selective_state_space_20_amd import inputs as gen
@@ -564,13 +566,14 @@ def bench_train_step(steps, warmup, saved):
     ws = torch.empty(sss.selective_scan_bwd_workspace_size(b, L, d, n, 0), dtype=torch.uint8, device=dev)
     sbytes = sss.selective_scan_states_size(b, L, d, n, 0)
     states = torch.empty(max(sbytes, 4) // 4, dtype=torch.float32, device=dev) if saved else None
+    dbias = 0.5 * torch.randn((d,), device=dev, generator=g) if softplus else None
     stream = torch.cuda.current_stream(dev)
 
     def step():
         sss.selective_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"], out=y,
-                               out_last=hl, workspace=ws, states=states)
+                               out_last=hl, workspace=ws, states=states, delta_bias=dbias, delta_softplus=softplus)
         sss.selective_scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["h0"], dy=dy,
-                               dh_last=dhl, workspace=ws, states=states)
+                               dh_last=dhl, workspace=ws, states=states, delta_bias=dbias, delta_softplus=softplus)
 
     warm_calls = warm_up(step, warmup)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
@@ -582,14 +585,16 @@ def bench_train_step(steps, warmup, saved):
     ms = [e0.elapsed_time(e1) for e0, e1 in ev]
     mean_ms = float(np.mean(ms))
     e = b * L * d
-    log(f"[bench] train step ({'saved states' if saved else 'states recomputed'}) {cfg['name']}: event mean "
+    log(f"[bench] train step ({'saved states' if saved else 'states recomputed'}"
+        f"{', softplus front end' if softplus else ''}) {cfg['name']}: event mean "
         f"{mean_ms:.4f} ms, median {float(np.median(ms)):.4f}, min {min(ms):.4f}, states {sbytes / 1e6:.1f} MB")
     print(json.dumps({
         "metric": "selective scan training step (forward + gradients) elements/s, 1 GPU",
         "value": round(e / (mean_ms * 1e-3), 1), "unit": "elements/s", "n_gpus": 1, "steps": steps, "warmup": warmup, "warmup_calls_run": warm_calls,
         "ms_per_step": round(mean_ms, 5), "higher_is_better": True, "dtype": dtype_label("bf16"), "io_dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "train_step_" + cfg["name"], "saved_states": bool(saved), "states_bytes": sbytes,
+        "config": {"workload": "train_step_" + cfg["name"] + ("_softplus" if softplus else ""),
+                   "saved_states": bool(saved), "delta_softplus": bool(softplus), "states_bytes": sbytes,
                    "elements": e},
         "call_ms": {"mean": round(mean_ms, 5), "median": round(float(np.median(ms)), 5), "min": round(min(ms), 5),
                     "max": round(max(ms), 5)},
@@ -620,7 +625,8 @@ def main():
                     help="do not scrub the last-level cache between calls (decode, and workloads that fit it)")
     ap.add_argument("--delta-softplus", action="store_true",
                     help="selective: time the softplus front end (the stored delta taken as the raw step); "
-                         "with --backward the gradients through it (softplus(delta + bias), selective_scan_bwd_ex)")
+                         "with --backward / --train-step the gradients through it (softplus(delta + bias), "
+                         "selective_scan_bwd_ex)")
     ap.add_argument("--exact-zoh", action="store_true", help="selective: time the exact zero-order-hold option")
     ap.add_argument("--layout", choices=("bld", "bdl"), default="bld",
                     help="selective: operand layout (bdl = channel-major x/delta/z/y and B/C)")
@@ -646,7 +652,9 @@ def main():
         bench_backward(args.steps, args.warmup, args.saved_states, softplus=args.delta_softplus)
         return
     if args.train_step:
-        bench_train_step(args.steps, args.warmup, args.saved_states)
+        if args.saved_states and args.delta_softplus:
+            sys.exit("--saved-states has no delta front end form")
+        bench_train_step(args.steps, args.warmup, args.saved_states, softplus=args.delta_softplus)
         return
     if args.decode > 0:
         bench_decode(args.decode, args.steps, args.warmup, flush=not args.no_flush)
