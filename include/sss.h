@@ -13,9 +13,11 @@
  *      h_{-1} = h0 (or 0), read-out after the update, final state h_{L-1} returned.
  *      delta arrives already passed through softplus: the projections that produce
  *      delta, B and C are outside this library ("15. Selective (Data-Dependent) SSM
- *      Scan", Problem: the data-dependent parameters are given).
+ *      Scan", Problem: the data-dependent parameters are given); selective_scan_fwd_ex
+ *      applies the bias and softplus itself, among its other options.
  *
  *  selective_scan_bwd -- its gradients (training), with the states recomputed;
+ *      selective_scan_bwd_ex the same through the delta bias and softplus;
  *      selective_scan_fwd_save / selective_scan_bwd_saved the same pair with the forward
  *      call's segment entering states kept for the gradients call.
  *
